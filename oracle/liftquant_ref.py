@@ -1,0 +1,208 @@
+"""CPU oracle of the LiftQuant lift-then-project decode operator.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module. The product path (the HIP library and
+its Python binding) never calls it and shares no code with it.
+
+Everything is plain numpy in float64, written for readability, not speed.
+
+Sources, cited by title and section:
+
+* [paper] "LiftQuant: Continuous Bit-Width LLM via Dimensional Lifting and
+  Projection" (arXiv 2606.04050), read in its Chinese translation
+  ("LiftQuant：基于维度提升与投影的连续比特宽度大语言模型量化框架").
+* [review] "Paper Review: LiftQuant: Continuous Bit-Width LLM via Dimensional
+  Lifting and Projection" (romaanj.github.io), the "Method" paragraph.
+
+What the operator computes, in the pages' notation:
+
+* A length-d weight block is stored as D signs w_q in {+1,-1}^D and decoded as
+  w = M w_q with one d x D mapping matrix M ([paper] §3.1; [review] Method).
+  The effective bit-width is D/d ([paper] §3 introduction; Fig. 2).
+* The fused decode operator is o = diag(s) W (M T a) ([paper] §3 introduction;
+  [review] Method: diag(s) W_q (T* a^T), an INT1 x FP GEMM plus small linear
+  maps). T is a layer-wise whitening: Hadamard mixing plus per-channel scaling
+  ([paper] §3 introduction, forward reference to §3.2; [review] Method).
+* Written out, o is the plain linear map y = diag(s) W_dense (T a), with
+  W_dense assembled block by block from w = M w_q. This oracle computes that
+  plain definition; the lifted route S (M^T T a) is the same map rearranged and
+  is provided separately (``lift`` and ``sign_matmul``) for the kernels that
+  compute the individual steps.
+
+Readings taken where the pages are silent (each is also listed in the design
+notes of the repository):
+
+* T = blockdiag_q(H_hb diag(c_q)) with H_hb the orthonormal Hadamard matrix in
+  Sylvester order, H[i, j] = (-1)^popcount(i & j) / sqrt(hb): scale each
+  channel, then mix each hb-block. T itself is not learned here.
+* K is zero-padded to K' = d * ceil(K / d) after T, before the lift.
+* Lifted column j of a row is j = b * D + e for block b and sign e.
+* The row scale is called ``row_scale`` (the paper's diag(s)); ``signs`` are
+  the w_q.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "hadamard", "whitening_block", "whiten", "pad_blocks", "decode_weight",
+    "linear", "lift", "sign_matmul", "packed_bits", "bits_per_weight",
+    "codebook", "sign_pattern",
+]
+
+
+def _popcount(a: np.ndarray) -> np.ndarray:
+    a = a.astype(np.int64)
+    count = np.zeros_like(a)
+    while np.any(a):
+        count += a & 1
+        a >>= 1
+    return count
+
+
+def hadamard(hb: int) -> np.ndarray:
+    """Orthonormal Hadamard matrix of order ``hb`` (a power of two), Sylvester
+    order: H[i, j] = (-1)^popcount(i & j) / sqrt(hb).
+
+    The channel mixing of the whitening transform starts from a Hadamard
+    matrix ([paper] §3 introduction; [review] Method). Order and normalisation
+    are not given on the pages; this is the reading taken.
+    """
+    if hb < 1 or hb & (hb - 1):
+        raise ValueError("Hadamard order must be a power of two")
+    i = np.arange(hb)
+    parity = _popcount(i[:, None] & i[None, :]) % 2
+    return np.where(parity == 0, 1.0, -1.0) / np.sqrt(hb)
+
+
+def whitening_block(c_block: np.ndarray) -> np.ndarray:
+    """One diagonal block of T: T_q = H_hb diag(c_q), as an explicit dense
+    hb x hb matrix: per-channel scaling followed by orthogonal mixing
+    ([paper] §3 introduction; [review] Method)."""
+    c_block = np.asarray(c_block, dtype=np.float64)
+    return hadamard(len(c_block)) @ np.diag(c_block)
+
+
+def whiten(x: np.ndarray, c: np.ndarray, hb: int) -> np.ndarray:
+    """xt = T x for every batch row: T is block diagonal with blocks
+    H_hb diag(c_q), one per consecutive run of hb channels.
+
+    x: (B, K); c: (K,); hb must divide K. Returns (B, K) float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    c = np.asarray(c, dtype=np.float64)
+    B, K = x.shape
+    if K % hb:
+        raise ValueError("hb must divide K")
+    xt = np.empty_like(x)
+    for q in range(K // hb):
+        sl = slice(q * hb, (q + 1) * hb)
+        Tq = whitening_block(c[sl])
+        xt[:, sl] = x[:, sl] @ Tq.T          # each row: Tq @ x_row
+    return xt
+
+
+def pad_blocks(xt: np.ndarray, d: int) -> np.ndarray:
+    """Append zero columns so the width becomes a multiple of the block
+    length d (K' = d * ceil(K / d))."""
+    xt = np.asarray(xt, dtype=np.float64)
+    B, K = xt.shape
+    Kp = -(-K // d) * d
+    out = np.zeros((B, Kp))
+    out[:, :K] = xt
+    return out
+
+
+def decode_weight(signs: np.ndarray, M: np.ndarray) -> np.ndarray:
+    """Dense weight rows from lifted signs: block b of row n is
+    w = M w_q with w_q = signs[n, b, :] ([paper] §3.1, definition of the
+    mapping matrix; [review] Method).
+
+    signs: (N, Kb, D) with entries +1/-1; M: (d, D). Returns (N, Kb * d).
+    """
+    signs = np.asarray(signs)
+    M = np.asarray(M, dtype=np.float64)
+    N, Kb, D = signs.shape
+    d = M.shape[0]
+    if M.shape[1] != D:
+        raise ValueError("M must be d x D")
+    W = np.empty((N, Kb * d))
+    for b in range(Kb):
+        s_b = signs[:, b, :].astype(np.float64)      # (N, D), one w_q per row
+        W[:, b * d:(b + 1) * d] = s_b @ M.T          # row n: M @ s_b[n]
+    return W
+
+
+def linear(x: np.ndarray, c: np.ndarray, hb: int, M: np.ndarray,
+           signs: np.ndarray, row_scale: np.ndarray) -> np.ndarray:
+    """The decode operator o = diag(s) W (T a) for a batch of activations
+    ([paper] §3 introduction, fused operator; [review] Method).
+
+    x: (B, K) activations; c: (K,) channel scales of T; hb: Hadamard block;
+    M: (d, D); signs: (N, Kb, D); row_scale: (N,). Returns y: (B, N) float64
+    with y[b, n] = row_scale[n] * sum_k W[n, k] * xt_pad[b, k].
+    """
+    d = np.asarray(M).shape[0]
+    xt = pad_blocks(whiten(x, c, hb), d)
+    W = decode_weight(signs, M)
+    if W.shape[1] != xt.shape[1]:
+        raise ValueError("signs do not match ceil(K/d) blocks")
+    y = xt @ W.T
+    return y * np.asarray(row_scale, dtype=np.float64)[None, :]
+
+
+def lift(xt_pad: np.ndarray, M: np.ndarray) -> np.ndarray:
+    """Lifted activations: z_b = M^T xt_b for each length-d block b, laid out
+    as z[:, b * D + e]. This is the M T a factor of the fused operator
+    ([paper] §3 introduction), written T* a^T in [review] Method.
+
+    xt_pad: (B, Kb * d); M: (d, D). Returns (B, Kb * D).
+    """
+    xt_pad = np.asarray(xt_pad, dtype=np.float64)
+    M = np.asarray(M, dtype=np.float64)
+    d, D = M.shape
+    B, Kp = xt_pad.shape
+    if Kp % d:
+        raise ValueError("width must be a multiple of d")
+    Kb = Kp // d
+    z = np.empty((B, Kb * D))
+    for b in range(Kb):
+        z[:, b * D:(b + 1) * D] = xt_pad[:, b * d:(b + 1) * d] @ M
+    return z
+
+
+def sign_matmul(signs_flat: np.ndarray, z: np.ndarray,
+                row_scale: np.ndarray) -> np.ndarray:
+    """The INT1 x FP product of the decode path with its row scale:
+    y = diag(s) W_q z ([review] Method; [paper] §3 introduction).
+
+    signs_flat: (N, L) +1/-1; z: (B, L); row_scale: (N,). Returns (B, N).
+    """
+    S = np.asarray(signs_flat).astype(np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    return (z @ S.T) * np.asarray(row_scale, dtype=np.float64)[None, :]
+
+
+def packed_bits(N: int, K: int, d: int, D: int) -> int:
+    """Storage of one quantized layer in bits: every one of the N rows holds
+    ceil(K / d) blocks of D one-bit signs ([paper] §3 introduction and §3.1)."""
+    return N * (-(-K // d)) * D
+
+
+def bits_per_weight(K: int, d: int, D: int) -> float:
+    """Effective bits per original weight, D/d when d divides K ([paper] §3
+    introduction; Fig. 2)."""
+    return (-(-K // d)) * D / K
+
+
+def sign_pattern(index: int, D: int) -> np.ndarray:
+    """The sign vector numbered ``index``: s_e = -1 when bit e of index is set."""
+    return np.array([-1.0 if (index >> e) & 1 else 1.0 for e in range(D)])
+
+
+def codebook(M: np.ndarray) -> np.ndarray:
+    """All 2^D codewords M s, s in {+1,-1}^D, in the order of ``sign_pattern``
+    (the implicit codebook of [paper] §3.1 and Fig. 2). Returns (2^D, d)."""
+    M = np.asarray(M, dtype=np.float64)
+    D = M.shape[1]
+    return np.stack([M @ sign_pattern(i, D) for i in range(1 << D)])
