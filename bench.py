@@ -1,0 +1,316 @@
+#!/usr/bin/env python3
+"""Benchmark of the LiftQuant decode operator on one MI355X.
+
+A step is one decode token through the three MLP projections of a
+Llama-3-8B layer at 2.4 bits per weight (d = 10, D = 24): gate and up
+(K = 4096 -> N = 14336) and down (K = 14336 -> N = 4096), batch 1, bf16
+activations, each a full lq_linear call (whitening, lift, sign product).
+Every step uses the next of `--weight-sets` distinct copies of the packed
+weights, so the 52.9 MB of packed bits a step reads cannot stay in the
+256 MB Infinity Cache (like a real 32-layer model, whose weights are all
+different). The steps are captured once in a HIP graph and replayed, so the
+timing is the GPU's, not Python's launch rate.
+
+Printed (one JSON line): whole-step packed-weight throughput in GB/s
+(`value`), the roofline of the dominant kernel (the sign product), timed
+with HIP events around each of its launches inside the timed graph, and the
+CPU oracle's rate on a bounded sample of the same workload. With
+`--prefill`, also the 2048-token prefill layer (d = 3, D = 8) in TFLOP/s.
+
+Synthetic data: packed weights are uniformly random bytes (i.e. independent
+fair signs), M ~ N(0, 1/D), row scales ~ U[0.5, 1.5], channel scales ~
+U[0.8, 1.2], activations ~ N(0, 1) rounded to bf16.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--weight-sets", type=int, default=24)
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="approximate CPU time budget of the oracle baseline sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--prefill", action="store_true",
+                   help="also time the 2048-token prefill layer (TFLOP/s)")
+    p.add_argument("--eager", action="store_true", help="launch eagerly instead of a HIP graph")
+    return p.parse_args()
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the same HIP runtime torch and liblq use)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+def build_decode_case(torch, lq, n_sets, seed=0):
+    from workloads import WORKLOADS, make_layer
+    wl = WORKLOADS["llama3_8b_mlp"]
+    gate_spec, down_spec = wl.layers
+    specs = [("gate", gate_spec), ("up", gate_spec), ("down", down_spec)]
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    host = {s.name: make_layer(s, wl, B_max=1) for s in (gate_spec, down_spec)}
+    M = torch.from_numpy(host[gate_spec.name].M).to(dev)        # one global mapping matrix
+    layers = []   # [set][proj] -> dict
+    for _ in range(n_sets):
+        row = []
+        for pname, s in specs:
+            nbytes = lq.lq_packed_size(s.N, s.K, s.d, s.D)
+            packed = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=dev, generator=gen)
+            r = torch.rand(s.N, device=dev, generator=gen) + 0.5
+            c = torch.rand(s.K, device=dev, generator=gen) * 0.4 + 0.8
+            st = lq.layer_struct(s.N, s.K, s.d, s.D, s.hb, packed, M, c, r)
+            row.append(dict(name=pname, spec=s, packed=packed, r=r, c=c, struct=st, bytes=nbytes))
+        layers.append(row)
+    x_in = {
+        "gate": torch.from_numpy(host[gate_spec.name].x(1)).to(dev).to(torch.bfloat16),
+        "down": torch.from_numpy(host[down_spec.name].x(1)).to(dev).to(torch.bfloat16),
+    }
+    ys = {p: torch.empty((1, s.N), dtype=torch.bfloat16, device=dev) for p, s in specs}
+    ws_bytes = max(lq.lq_linear_workspace_size(layers[0][i]["struct"], 1, torch.bfloat16) for i in range(3))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    return specs, layers, x_in, ys, ws, M
+
+
+def run_decode(args, torch, lq, ev):
+    specs, layers, x_in, ys, ws, M = build_decode_case(torch, lq, args.weight_sets)
+    n_sets = len(layers)
+    step_bytes = sum(l["bytes"] for l in layers[0])
+
+    def step(i):
+        for l in layers[i % n_sets]:
+            x = x_in["down"] if l["name"] == "down" else x_in["gate"]
+            lq.lq_linear(l["struct"], x, 1, ys[l["name"]], ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    n_launch = 3 * K
+    starts, stops = ev.create(n_launch), ev.create(n_launch)
+    lq.lq_profile_events(starts, stops)
+    if args.eager:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            step(i)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    else:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(K):
+                step(i)
+        lq.lq_profile_events([], [])
+        g.replay()                      # first replay uploads the graph (untimed)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    lq.lq_profile_events([], [])
+    durs = [ev.elapsed_ms(a, b) for a, b in zip(starts, stops)]
+    ev.destroy(starts)
+    ev.destroy(stops)
+
+    ms_step = (t1 - t0) * 1e3 / K
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    kern_ms = sum(durs) / len(durs)
+    bytes_per_launch = step_bytes / 3.0          # N*L/8 of the three layers, averaged
+    achieved = bytes_per_launch / (kern_ms * 1e-3) / 1e9
+    per_proj = {}
+    for j, (pname, s) in enumerate(specs):
+        d = durs[j::3]
+        per_proj[pname] = round(sum(d) / len(d) * 1e3, 3)
+    return dict(ms_step=ms_step, gbs=gbs, kern_ms=kern_ms, achieved=achieved,
+                step_bytes=step_bytes, bytes_per_launch=bytes_per_launch, per_proj_us=per_proj,
+                n_sets=n_sets)
+
+
+def run_prefill(args, torch, lq, ev, steps=10):
+    from workloads import WORKLOADS
+    wl = WORKLOADS["prefill"]
+    s = wl.layers[0]
+    B = 2048
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1)
+    nbytes = lq.lq_packed_size(s.N, s.K, s.d, s.D)
+    packed = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=dev, generator=gen)
+    M = (torch.randn(s.d, s.D, device=dev, generator=gen) / s.D ** 0.5).contiguous()
+    r = torch.rand(s.N, device=dev, generator=gen) + 0.5
+    c = torch.rand(s.K, device=dev, generator=gen) * 0.4 + 0.8
+    st = lq.layer_struct(s.N, s.K, s.d, s.D, s.hb, packed, M, c, r)
+    x = torch.randn(B, s.K, device=dev, generator=gen).to(torch.bfloat16)
+    y = torch.empty(B, s.N, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(lq.lq_linear_workspace_size(st, B, torch.bfloat16), dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        lq.lq_linear(st, x, B, y, ws)
+    torch.cuda.synchronize()
+    starts, stops = ev.create(steps), ev.create(steps)
+    lq.lq_profile_events(starts, stops)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        lq.lq_linear(st, x, B, y, ws)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    lq.lq_profile_events([], [])
+    durs = [ev.elapsed_ms(a, b) for a, b in zip(starts, stops)]
+    ev.destroy(starts)
+    ev.destroy(stops)
+    flops = 2.0 * B * s.N * s.L
+    kern_ms = sum(durs) / len(durs)
+    ms = (t1 - t0) * 1e3 / steps
+    return dict(workload=f"prefill K={s.K} N={s.N} d={s.d} D={s.D} B={B}",
+                tflops_linear=flops / (ms * 1e-3) / 1e12, ms_linear=ms,
+                kernel_ms=kern_ms, kernel_tflops=flops / (kern_ms * 1e-3) / 1e12,
+                lifted_flops=flops, dense_equiv_flops=2.0 * B * s.N * s.Kpad)
+
+
+def cpu_baseline(budget_s):
+    """The oracle as it stands, on rows sampled from the same three layers."""
+    import numpy as np
+    from oracle import liftquant_ref as ref
+    from workloads import WORKLOADS, make_layer
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    wl = WORKLOADS["llama3_8b_mlp"]
+    gate, down = wl.layers
+    inputs = {s.name: make_layer(s, wl, B_max=1) for s in (gate, down)}
+
+    def run(rows):
+        nbytes = 0
+        t = 0.0
+        for s in (gate, gate, down):
+            li = inputs[s.name]
+            idx = np.arange(rows)
+            signs = li.signs_rows(idx)
+            t0 = time.perf_counter()
+            ref.linear(li.x(1), li.c, s.hb, li.M, signs, li.row_scale[idx])
+            t += time.perf_counter() - t0
+            nbytes += rows * s.L // 8
+        return nbytes, t
+
+    rows = 64
+    nb, t = run(rows)
+    if t < budget_s / 4:
+        rows = int(min(4096, max(64, rows * (budget_s / 2) / max(t, 1e-3))) // 16 * 16)
+        nb, t = run(rows)
+    return dict(value=round(nb / t / 1e9, 6), unit="GB/s", cores=threads, kind="oracle",
+                sample=f"oracle linear() on the first {rows} rows of each of gate, up and down "
+                       f"(B=1, d=10, D=24): {nb} packed bytes in {t:.2f} s")
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures a single GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import torch
+    import bit_matmul_amd as lq
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    ev = HipEvents()
+    dec = run_decode(args, torch, lq, ev)
+    out = {
+        "metric": "LiftQuant linear: packed-weight HBM GB/s (batch 1) and TFLOP/s (batch 2048)",
+        "value": round(dec["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "Llama-3-8B MLP decode at 2.4 bit (d=10, D=24): gate and up "
+                        "K=4096->N=14336, down K=14336->N=4096, batch 1, bf16 activations, "
+                        "Hadamard block 1024; one step = the three lq_linear calls",
+            "global_batch": 1,
+            "weight_sets": dec["n_sets"],
+            "packed_bytes_per_step": dec["step_bytes"],
+            "graph": not args.eager,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "sign product (lq sign_mfma_small_kernel)",
+            "achieved": round(dec["achieved"], 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dec["achieved"] / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_launch_us": round(dec["kern_ms"] * 1e3, 3),
+            "per_layer_avg_us": dec["per_proj_us"],
+            "algorithmic_bytes_per_launch": dec["bytes_per_launch"],
+        },
+    }
+    if args.prefill:
+        pf = run_prefill(args, torch, lq, ev)
+        out["prefill"] = {
+            "metric": "TFLOP/s (batch 2048), lifted flops 2*B*N*L",
+            "workload": pf["workload"],
+            "value": round(pf["tflops_linear"], 2),
+            "unit": "TFLOP/s",
+            "ms_per_linear": round(pf["ms_linear"], 4),
+            "roofline": {"bound": "mfma", "achieved": round(pf["kernel_tflops"], 1),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(pf["kernel_tflops"] / BF16_PEAK_TFLOPS, 4),
+                         "avg_launch_us": round(pf["kernel_ms"] * 1e3, 2),
+                         "traffic": None},
+        }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

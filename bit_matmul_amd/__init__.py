@@ -1,0 +1,145 @@
+"""Python binding of liblq, the MI355X (gfx950) LiftQuant decode operator.
+
+Thin argument marshalling over the C ABI of include/lq.h: each function has
+the name of the C entry point it calls, takes torch tensors that live on the
+GPU (used only as device memory) plus the sizes, and enqueues on the current
+torch stream unless a stream handle is given. Every step of the computation
+runs in the library's HIP kernels; if liblq.so is missing, importing this
+package fails.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (LQ_ALGO_AUTO, LQ_ALGO_MFMA_LARGE, LQ_ALGO_MFMA_SMALL, LQ_ALGO_VALU,
+                   LQ_BF16, LQ_F32, LQ_MAX_D, LQ_MAX_HB, LQError, LQLayer)
+
+__all__ = [
+    "lq_version", "lq_packed_size", "lq_pack_signs", "lq_unpack_signs", "lq_hadamard_scale",
+    "lq_lift_activations", "lq_sign_gemm_workspace_size", "lq_sign_gemm", "lq_sign_gemm_ex",
+    "lq_linear_workspace_size", "lq_linear", "lq_profile_events", "layer_struct", "LQError", "LQLayer",
+    "LQ_F32", "LQ_BF16", "LQ_ALGO_AUTO", "LQ_ALGO_VALU", "LQ_ALGO_MFMA_SMALL",
+    "LQ_ALGO_MFMA_LARGE", "LQ_MAX_D", "LQ_MAX_HB", "library_path",
+]
+
+_DTYPES = {torch.float32: LQ_F32, torch.bfloat16: LQ_BF16}
+
+
+def library_path() -> str:
+    return str(_lib.LIB_PATH)
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise LQError(status, where)
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous GPU tensor")
+    return t.data_ptr()
+
+
+def _opt(t, name):
+    return None if t is None else _dev(t, name)
+
+
+def _dtype(t: torch.Tensor, name: str) -> int:
+    if t.dtype not in _DTYPES:
+        raise ValueError(f"{name} must be float32 or bfloat16")
+    return _DTYPES[t.dtype]
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def lq_version() -> int:
+    return _lib.LIB.lq_version()
+
+
+def lq_packed_size(N: int, K: int, d: int, D: int) -> int:
+    out = ctypes.c_size_t()
+    _check(_lib.LIB.lq_packed_size(N, K, d, D, ctypes.byref(out)), "lq_packed_size")
+    return out.value
+
+
+def lq_pack_signs(signs, N, K, d, D, packed, stream=None) -> None:
+    _check(_lib.LIB.lq_pack_signs(_dev(signs, "signs"), N, K, d, D, _dev(packed, "packed"),
+                                  _stream(stream)), "lq_pack_signs")
+
+
+def lq_unpack_signs(packed, N, K, d, D, signs, stream=None) -> None:
+    _check(_lib.LIB.lq_unpack_signs(_dev(packed, "packed"), N, K, d, D, _dev(signs, "signs"),
+                                    _stream(stream)), "lq_unpack_signs")
+
+
+def lq_hadamard_scale(x, B, K, hb, c, xt, stream=None) -> None:
+    _check(_lib.LIB.lq_hadamard_scale(_dev(x, "x"), _dtype(x, "x"), B, K, hb, _dev(c, "c"),
+                                      _dev(xt, "xt"), _stream(stream)), "lq_hadamard_scale")
+
+
+def lq_lift_activations(xt, B, K, d, D, M, z, stream=None) -> None:
+    _check(_lib.LIB.lq_lift_activations(_dev(xt, "xt"), B, K, d, D, _dev(M, "M"), _dev(z, "z"),
+                                        _dtype(z, "z"), _stream(stream)), "lq_lift_activations")
+
+
+def lq_sign_gemm_workspace_size(B, N, L, ztype, algo=LQ_ALGO_AUTO) -> int:
+    out = ctypes.c_size_t()
+    zt = _DTYPES[ztype] if isinstance(ztype, torch.dtype) else int(ztype)
+    _check(_lib.LIB.lq_sign_gemm_workspace_size(B, N, L, zt, algo, ctypes.byref(out)),
+           "lq_sign_gemm_workspace_size")
+    return out.value
+
+
+def lq_sign_gemm_ex(packed, z, B, N, L, row_scale, y, algo, ws=None, stream=None) -> None:
+    ws_ptr = _opt(ws, "ws")
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.LIB.lq_sign_gemm_ex(_dev(packed, "packed"), _dev(z, "z"), _dtype(z, "z"), B, N, L,
+                                    _dev(row_scale, "row_scale"), _dev(y, "y"), _dtype(y, "y"),
+                                    algo, ws_ptr, ws_bytes, _stream(stream)), "lq_sign_gemm_ex")
+
+
+def lq_sign_gemm(packed, z, B, N, L, row_scale, y, ws=None, stream=None) -> None:
+    ws_ptr = _opt(ws, "ws")
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.LIB.lq_sign_gemm(_dev(packed, "packed"), _dev(z, "z"), _dtype(z, "z"), B, N, L,
+                                 _dev(row_scale, "row_scale"), _dev(y, "y"), _dtype(y, "y"),
+                                 ws_ptr, ws_bytes, _stream(stream)), "lq_sign_gemm")
+
+
+def layer_struct(N, K, d, D, hb, packed, M, c, row_scale) -> LQLayer:
+    """Fill a ``struct lq_layer`` from device tensors (the caller keeps the
+    tensors alive while the struct is used)."""
+    return LQLayer(N, K, d, D, hb, 0, _dev(packed, "packed"), _dev(M, "M"), _dev(c, "c"),
+                   _dev(row_scale, "row_scale"))
+
+
+def lq_linear_workspace_size(layer: LQLayer, B, xtype) -> int:
+    out = ctypes.c_size_t()
+    xt = _DTYPES[xtype] if isinstance(xtype, torch.dtype) else int(xtype)
+    _check(_lib.LIB.lq_linear_workspace_size(ctypes.byref(layer), B, xt, ctypes.byref(out)),
+           "lq_linear_workspace_size")
+    return out.value
+
+
+def lq_linear(layer: LQLayer, x, B, y, ws=None, stream=None) -> None:
+    ws_ptr = _opt(ws, "ws")
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.LIB.lq_linear(ctypes.byref(layer), _dev(x, "x"), _dtype(x, "x"), B, _dev(y, "y"),
+                              _dtype(y, "y"), ws_ptr, ws_bytes, _stream(stream)), "lq_linear")
+
+
+def lq_profile_events(starts, stops) -> None:
+    """Bracket every sign-product kernel launch with the given hipEvent_t
+    handles (sequences of ints, used round-robin); empty sequences clear it."""
+    n = len(starts)
+    if len(stops) != n:
+        raise ValueError("starts and stops must have the same length")
+    arr = ctypes.c_void_p * max(n, 1)
+    _check(_lib.LIB.lq_profile_events(arr(*starts), arr(*stops), n), "lq_profile_events")

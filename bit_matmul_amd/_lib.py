@@ -1,0 +1,73 @@
+"""ctypes loader and prototypes for liblq.so (the C ABI in include/lq.h)."""
+from __future__ import annotations
+
+import ctypes
+from ctypes import POINTER, c_char_p, c_int, c_int32, c_int64, c_size_t, c_void_p
+from pathlib import Path
+
+LIB_PATH = Path(__file__).resolve().parent / "liblq.so"
+
+LQ_OK, LQ_ERR_INVALID_ARG, LQ_ERR_UNSUPPORTED, LQ_ERR_WORKSPACE, LQ_ERR_HIP = range(5)
+LQ_F32, LQ_BF16 = 0, 1
+LQ_ALGO_AUTO, LQ_ALGO_VALU, LQ_ALGO_MFMA_SMALL, LQ_ALGO_MFMA_LARGE = range(4)
+LQ_MAX_D = 64
+LQ_MAX_HB = 1024
+
+# Every symbol include/lq.h declares.
+EXPORTS = [
+    "lq_version", "lq_status_string", "lq_last_hip_error", "lq_packed_size",
+    "lq_pack_signs", "lq_unpack_signs", "lq_hadamard_scale", "lq_lift_activations",
+    "lq_sign_gemm_workspace_size", "lq_sign_gemm", "lq_sign_gemm_ex",
+    "lq_linear_workspace_size", "lq_linear", "lq_profile_events",
+]
+
+
+class LQLayer(ctypes.Structure):
+    """Mirror of ``struct lq_layer``."""
+    _fields_ = [
+        ("N", c_int64), ("K", c_int64), ("d", c_int32), ("D", c_int32),
+        ("hb", c_int32), ("reserved", c_int32),
+        ("packed", c_void_p), ("M", c_void_p), ("c", c_void_p), ("row_scale", c_void_p),
+    ]
+
+
+class LQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = LIB.lq_status_string(status).decode() if LIB is not None else str(status)
+        if status == LQ_ERR_HIP and LIB is not None:
+            msg += f" (hipError {LIB.lq_last_hip_error()})"
+        super().__init__(f"{where}: {msg}")
+
+
+def _load():
+    if not LIB_PATH.exists():
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m bit_matmul_amd.build` "
+            "(the HIP library is required, there is no fallback)")
+    lib = ctypes.CDLL(str(LIB_PATH))
+    i64, i32, sz, vp = c_int64, c_int32, c_size_t, c_void_p
+    protos = {
+        "lq_version": (c_int, []),
+        "lq_status_string": (c_char_p, [c_int]),
+        "lq_last_hip_error": (c_int, []),
+        "lq_packed_size": (c_int, [i64, i64, i32, i32, POINTER(sz)]),
+        "lq_pack_signs": (c_int, [vp, i64, i64, i32, i32, vp, vp]),
+        "lq_unpack_signs": (c_int, [vp, i64, i64, i32, i32, vp, vp]),
+        "lq_hadamard_scale": (c_int, [vp, c_int, i64, i64, i32, vp, vp, vp]),
+        "lq_lift_activations": (c_int, [vp, i64, i64, i32, i32, vp, vp, c_int, vp]),
+        "lq_sign_gemm_workspace_size": (c_int, [i64, i64, i64, c_int, c_int, POINTER(sz)]),
+        "lq_sign_gemm": (c_int, [vp, vp, c_int, i64, i64, i64, vp, vp, c_int, vp, sz, vp]),
+        "lq_sign_gemm_ex": (c_int, [vp, vp, c_int, i64, i64, i64, vp, vp, c_int, c_int, vp, sz, vp]),
+        "lq_linear_workspace_size": (c_int, [POINTER(LQLayer), i64, c_int, POINTER(sz)]),
+        "lq_linear": (c_int, [POINTER(LQLayer), vp, c_int, i64, vp, c_int, vp, sz, vp]),
+        "lq_profile_events": (c_int, [POINTER(vp), POINTER(vp), i32]),
+    }
+    for name, (res, args) in protos.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+LIB = _load()

@@ -1,0 +1,210 @@
+/*
+ * liblq: the LiftQuant lift-then-project decode operator on AMD Instinct
+ * MI355X (gfx950), behind a plain C ABI.
+ *
+ * The operator (LiftQuant, arXiv 2606.04050, "LiftQuant: Continuous Bit-Width
+ * LLM via Dimensional Lifting and Projection"; §3 introduction and §3.1 of
+ * the paper, and the Method paragraph of the paper review of the same title):
+ *
+ *   A weight row of length K is cut into Kb = ceil(K/d) blocks of d weights.
+ *   Block b is stored as D one-bit signs w_q in {+1,-1}^D and decoded as
+ *   w = M w_q with one shared d x D mapping matrix M, so a layer costs
+ *   N * Kb * D bits (D/d bits per weight). The decode computes
+ *
+ *       y = diag(s) W (M T a)
+ *
+ *   for activations a: T is a whitening transform (Hadamard mixing plus
+ *   per-channel scaling), M lifts each d-block of T a into D-space,
+ *   z_b = M^T (T a)_b, W is the N x L sign matrix (L = Kb * D) and s is a
+ *   per-row scale. In this library:
+ *
+ *       xt = T x,   T = blockdiag_q(H_hb diag(c_q)),  H_hb orthonormal
+ *                       Sylvester-ordered Hadamard of order hb
+ *       z[b*D + e] = sum_i M[i][e] * xt[b*d + i]   (xt zero for k >= K)
+ *       y[n] = row_scale[n] * sum_j S[n][j] * z[j]
+ *
+ * Conventions shared by every entry point:
+ *
+ *   - Pointers to tensors are DEVICE pointers owned by the caller, unless the
+ *     argument says "host". The library allocates no memory and keeps no
+ *     pointer after a call returns. Tensors are dense, row-major, and must be
+ *     16-byte aligned.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued on it asynchronously; results are valid once the
+ *     stream has reached that point. Inputs must stay unchanged until then.
+ *   - Every argument is validated on the host before anything is enqueued.
+ *     On any error the call returns a non-zero lq_status, enqueues nothing
+ *     and writes nothing. B == 0 (or N == 0) is a valid empty call that
+ *     enqueues nothing.
+ *   - Results are deterministic: equal inputs give bitwise equal outputs on
+ *     the same GPU (no floating-point atomics).
+ *   - Functions never throw; they are thread-safe. Calls that share a
+ *     workspace buffer must be ordered by the caller.
+ *
+ * Packed sign layout (this library's format; the pages give none). S is
+ * N x L, N % 16 == 0, L % 8 == 0, total exactly N * L / 8 bytes:
+ *   - panel p = rows 16p..16p+15 occupies bytes [p*2L, (p+1)*2L);
+ *   - the first L/512 column tiles of a panel are 1024-byte full tiles; in
+ *     tile q the 16-byte slot l = 16*g + r (g < 4, r < 16) belongs to row
+ *     16p + r and its little-endian 32-bit word u (u < 4) holds, in bit b,
+ *     column q*512 + 128*u + 32*g + b;
+ *   - the remaining L % 512 columns (m = (L % 512) / 8 bytes per row) follow
+ *     as a row-major tail: byte t of row r at r*m + t, bit e = column
+ *     (L/512)*512 + 8t + e;
+ *   - a set bit is the sign -1.
+ */
+#ifndef LIFTQUANT_LQ_H
+#define LIFTQUANT_LQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lq_status {
+  LQ_OK = 0,
+  LQ_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, negative size, d > D, ... */
+  LQ_ERR_UNSUPPORTED = 2,   /* valid maths but outside this library's limits */
+  LQ_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
+  LQ_ERR_HIP = 4            /* a HIP runtime call failed; see lq_last_hip_error */
+} lq_status;
+
+typedef enum lq_dtype {
+  LQ_F32 = 0,               /* IEEE binary32 */
+  LQ_BF16 = 1               /* bfloat16 (upper half of binary32), RNE conversion */
+} lq_dtype;
+
+/* Sign-product algorithm for lq_sign_gemm_ex. */
+typedef enum lq_algo {
+  LQ_ALGO_AUTO = 0,         /* the library's choice (what lq_sign_gemm does) */
+  LQ_ALGO_VALU = 1,         /* fp32 sign-select on the vector ALUs; any z dtype,
+                               B <= 16 per pass; exact fp32 accumulation */
+  LQ_ALGO_MFMA_SMALL = 2,   /* B <= 16: signs expanded in registers to bf16 +-1,
+                               z as bf16, matrix-core products, fp32 accumulate */
+  LQ_ALGO_MFMA_LARGE = 3    /* any B: tiled GEMM on bf16 matrix cores, z as bf16
+                               (bf16 z) or as a bf16 hi+lo pair (fp32 z) */
+} lq_algo;
+
+/* Limits. d and D are runtime parameters: one operator for every rate. */
+#define LQ_MAX_D 64          /* 1 <= d <= D <= LQ_MAX_D */
+#define LQ_MAX_HB 1024       /* hb a power of two, 1 <= hb <= 1024, hb | K */
+
+/* One quantized linear layer (all pointers device, caller-owned). */
+typedef struct lq_layer {
+  int64_t N;                 /* output features, N % 16 == 0 */
+  int64_t K;                 /* input features, K % hb == 0 */
+  int32_t d;                 /* block length */
+  int32_t D;                 /* lifted dimension, ceil(K/d)*D % 8 == 0 */
+  int32_t hb;                /* Hadamard block of T */
+  int32_t reserved;          /* must be 0 */
+  const uint8_t* packed;     /* N*ceil(K/d)*D/8 bytes, layout above */
+  const float* M;            /* d x D, row-major */
+  const float* c;            /* K channel scales of T */
+  const float* row_scale;    /* N row scales (the paper's diag(s)) */
+} lq_layer;
+
+/* Library version, major*10000 + minor*100 + patch. Host only. */
+int lq_version(void);
+
+/* Human-readable name of a status code (static string). Host only. */
+const char* lq_status_string(lq_status status);
+
+/* hipError_t of the last LQ_ERR_HIP returned on this thread (0 if none). */
+int lq_last_hip_error(void);
+
+/*
+ * Storage of one layer: *bytes = N * ceil(K/d) * D / 8 (every weight block
+ * costs exactly D bits; paper §3 introduction and §3.1). Host only; `bytes`
+ * is a host pointer. Errors: INVALID_ARG for N < 0, K < 1, d < 1, D < d,
+ * null bytes; UNSUPPORTED for D > LQ_MAX_D, N % 16 != 0 or L % 8 != 0.
+ */
+lq_status lq_packed_size(int64_t N, int64_t K, int32_t d, int32_t D, size_t* bytes);
+
+/*
+ * Pack signs into the layout above.
+ * signs:  int8, N x Kb x D (= N x L row-major), every entry +1 or -1
+ *         (any negative value packs as -1, anything else as +1).
+ * packed: lq_packed_size bytes, fully overwritten.
+ * The signs are the w_q of every block (paper §3.1; one-bit weights of the
+ * INT1 GEMM, review Method and Released resources).
+ */
+lq_status lq_pack_signs(const int8_t* signs, int64_t N, int64_t K, int32_t d, int32_t D,
+                        uint8_t* packed, void* stream);
+
+/* Inverse of lq_pack_signs: writes N x L int8 values +1/-1. */
+lq_status lq_unpack_signs(const uint8_t* packed, int64_t N, int64_t K, int32_t d, int32_t D,
+                          int8_t* signs, void* stream);
+
+/*
+ * Whitening xt = T x (paper §3 introduction, the layer-wise whitening T;
+ * review Method: Hadamard mixing plus scalings), with
+ * T = blockdiag_q(H_hb diag(c_q)): for every batch row and every run of hb
+ * channels, xt = H_hb (c .* x) with H_hb[i][j] = (-1)^popcount(i&j)/sqrt(hb).
+ * x: B x K in xtype (F32 or BF16); c: K floats; xt: B x K floats.
+ * hb == 1 applies only the channel scales. Computed in fp32.
+ */
+lq_status lq_hadamard_scale(const void* x, lq_dtype xtype, int64_t B, int64_t K, int32_t hb,
+                            const float* c, float* xt, void* stream);
+
+/*
+ * Lift: z[b][j*D + e] = sum_{i<d} M[i][e] * xt[b][j*d + i], with xt taken as
+ * zero for columns k >= K (the virtual zero pad to Kb*d). This is the M T a
+ * factor of the fused operator (paper §3 introduction). xt: B x K floats;
+ * M: d x D floats; z: B x L in ztype (F32 or BF16, RNE). fp32 arithmetic.
+ */
+lq_status lq_lift_activations(const float* xt, int64_t B, int64_t K, int32_t d, int32_t D,
+                              const float* M, void* z, lq_dtype ztype, void* stream);
+
+/*
+ * Sign product with row scale: y[b][n] = row_scale[n] * sum_j S[n][j] z[b][j]
+ * (the INT1 x FP GEMM of the decode path, review Method; diag(s) of the
+ * paper's fused operator, §3 introduction).
+ * packed: N x L signs, layout above; z: B x L in ztype; row_scale: N floats;
+ * y: B x N in ytype. ws: device workspace of at least
+ * lq_sign_gemm_workspace_size bytes (may be NULL when that size is 0).
+ * lq_sign_gemm uses LQ_ALGO_AUTO. Accumulation is fp32 on every algorithm.
+ */
+lq_status lq_sign_gemm_workspace_size(int64_t B, int64_t N, int64_t L, lq_dtype ztype,
+                                      lq_algo algo, size_t* bytes);
+lq_status lq_sign_gemm(const uint8_t* packed, const void* z, lq_dtype ztype, int64_t B,
+                       int64_t N, int64_t L, const float* row_scale, void* y, lq_dtype ytype,
+                       void* ws, size_t ws_bytes, void* stream);
+lq_status lq_sign_gemm_ex(const uint8_t* packed, const void* z, lq_dtype ztype, int64_t B,
+                          int64_t N, int64_t L, const float* row_scale, void* y, lq_dtype ytype,
+                          lq_algo algo, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The whole decode operator y = diag(s) W (M T x) (paper §3 introduction):
+ * whitening, lift and sign product in sequence on `stream`.
+ * x: B x K in xtype; y: B x N in ytype. fp32 activations keep fp32 lifted
+ * values end to end; bf16 activations use bf16 lifted values on the matrix
+ * cores. ws: device workspace of at least lq_linear_workspace_size bytes.
+ */
+lq_status lq_linear_workspace_size(const lq_layer* layer, int64_t B, lq_dtype xtype,
+                                   size_t* bytes);
+lq_status lq_linear(const lq_layer* layer, const void* x, lq_dtype xtype, int64_t B, void* y,
+                    lq_dtype ytype, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Profiling aid: time the sign-product kernel itself. `starts` and `stops`
+ * are host arrays of `count` hipEvent_t handles (passed as void*) created by
+ * the caller. While set, every sign-product kernel launched by lq_sign_gemm,
+ * lq_sign_gemm_ex or lq_linear is bracketed by hipEventRecord(starts[i]) and
+ * hipEventRecord(stops[i]) on the call's stream, i = 0, 1, 2, ... wrapping
+ * modulo `count` (the split-K epilogue and the whitening/lift kernels are
+ * outside the brackets). Events recorded while a stream is being captured
+ * become event-record nodes of the graph. count == 0 clears the ring (the
+ * arrays may then be NULL); calling again restarts at slot 0. The ring is
+ * process-wide and guarded by a lock; the caller keeps the events alive
+ * while it is set. Errors: INVALID_ARG for count < 0 or NULL arrays with
+ * count > 0.
+ */
+lq_status lq_profile_events(void* const* starts, void* const* stops, int32_t count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIFTQUANT_LQ_H */

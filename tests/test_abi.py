@@ -1,0 +1,161 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+computes storage sizes, and rejects invalid calls before enqueueing anything.
+
+Pointer arguments here are fake (aligned integers that are never
+dereferenced): each call is chosen so that host-side validation rejects it,
+or so that it is an empty call that returns without touching the device.
+"""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+from bit_matmul_amd import _lib
+from bit_matmul_amd._lib import (LIB, LQ_BF16, LQ_ERR_INVALID_ARG, LQ_ERR_UNSUPPORTED,
+                                 LQ_ERR_WORKSPACE, LQ_F32, LQ_OK, LQLayer)
+from oracle import liftquant_ref as ref
+from workloads import WORKLOADS
+
+HEADER = Path(__file__).resolve().parent.parent / "include" / "lq.h"
+P = 0x100000            # fake, 16-byte aligned device address (never dereferenced)
+MIS = P + 4             # misaligned
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(LIB, n), f"liblq.so does not export {n}"
+    assert sorted(_lib.EXPORTS) == names
+
+
+def test_version_and_status_strings():
+    assert LIB.lq_version() == 100
+    for s in range(5):
+        assert LIB.lq_status_string(s).decode().startswith("LQ_")
+    assert LIB.lq_last_hip_error() == 0
+
+
+def size(N, K, d, D):
+    out = ctypes.c_size_t()
+    st = LIB.lq_packed_size(N, K, d, D, ctypes.byref(out))
+    return st, out.value
+
+
+def test_packed_size_matches_storage_formula():
+    for wl in WORKLOADS.values():
+        for l in wl.layers:
+            st, b = size(l.N, l.K, l.d, l.D)
+            assert st == LQ_OK
+            assert b * 8 == ref.packed_bits(l.N, l.K, l.d, l.D)
+    # values quoted for the Llama-3-8B gate/up and the 70B QKV shapes
+    assert size(14336, 4096, 10, 24) == (LQ_OK, 17633280)
+    assert size(10240, 8192, 10, 24) == (LQ_OK, 25190400)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((-16, 64, 2, 5), LQ_ERR_INVALID_ARG),
+    ((16, 0, 2, 5), LQ_ERR_INVALID_ARG),
+    ((16, 64, 0, 5), LQ_ERR_INVALID_ARG),
+    ((16, 64, 6, 5), LQ_ERR_INVALID_ARG),       # D < d
+    ((16, 64, 2, 65), LQ_ERR_UNSUPPORTED),      # D > LQ_MAX_D
+    ((15, 64, 2, 8), LQ_ERR_UNSUPPORTED),       # N % 16
+    ((16, 6, 2, 5), LQ_ERR_UNSUPPORTED),        # L = 15, not a multiple of 8
+])
+def test_packed_size_rejects(args, status):
+    assert size(*args)[0] == status
+
+
+def test_packed_size_null_output():
+    assert LIB.lq_packed_size(16, 64, 2, 8, None) == LQ_ERR_INVALID_ARG
+
+
+def test_pack_validation():
+    f = LIB.lq_pack_signs
+    assert f(None, 16, 64, 2, 8, P, None) == LQ_ERR_INVALID_ARG
+    assert f(P, 16, 64, 2, 8, MIS, None) == LQ_ERR_INVALID_ARG
+    assert f(P, 17, 64, 2, 8, P, None) == LQ_ERR_UNSUPPORTED
+    assert f(P, 0, 64, 2, 8, P, None) == LQ_OK                # empty: nothing enqueued
+    assert LIB.lq_unpack_signs(None, 16, 64, 2, 8, P, None) == LQ_ERR_INVALID_ARG
+
+
+def test_hadamard_validation():
+    f = LIB.lq_hadamard_scale
+    assert f(P, LQ_F32, 1, 96, 3, P, P, None) == LQ_ERR_INVALID_ARG     # hb not a power of 2
+    assert f(P, LQ_F32, 1, 4096, 2048, P, P, None) == LQ_ERR_UNSUPPORTED
+    assert f(P, LQ_F32, 1, 96, 64, P, P, None) == LQ_ERR_INVALID_ARG    # hb does not divide K
+    assert f(P, 7, 1, 64, 64, P, P, None) == LQ_ERR_INVALID_ARG         # bad dtype
+    assert f(MIS, LQ_F32, 1, 64, 64, P, P, None) == LQ_ERR_INVALID_ARG
+    assert f(P, LQ_F32, 1, 64, 64, None, P, None) == LQ_ERR_INVALID_ARG
+    assert f(P, LQ_F32, -1, 64, 64, P, P, None) == LQ_ERR_INVALID_ARG
+    assert f(P, LQ_F32, 0, 64, 64, P, P, None) == LQ_OK
+
+
+def test_lift_validation():
+    f = LIB.lq_lift_activations
+    assert f(P, 1, 64, 5, 2, P, P, LQ_F32, None) == LQ_ERR_INVALID_ARG   # D < d
+    assert f(P, 1, 64, 2, 100, P, P, LQ_F32, None) == LQ_ERR_UNSUPPORTED
+    assert f(P, 1, 64, 2, 5, None, P, LQ_F32, None) == LQ_ERR_INVALID_ARG
+    assert f(P, 1, 64, 2, 5, P, P, 3, None) == LQ_ERR_INVALID_ARG
+    assert f(P, 0, 64, 2, 5, P, P, LQ_BF16, None) == LQ_OK
+
+
+def ws_size(B, N, L, zt, algo):
+    out = ctypes.c_size_t()
+    st = LIB.lq_sign_gemm_workspace_size(B, N, L, zt, algo, ctypes.byref(out))
+    return st, out.value
+
+
+def test_sign_gemm_validation_and_workspace():
+    f = LIB.lq_sign_gemm_ex
+    st, need = ws_size(1, 4096, 34416, LQ_F32, 1)
+    assert st == LQ_OK and need > 0
+    assert ws_size(1, 4096, 34416, LQ_BF16, 3) == (LQ_OK, 0)
+    assert ws_size(17, 4096, 34416, LQ_BF16, 2)[0] == LQ_ERR_UNSUPPORTED   # small MFMA: B <= 16
+    assert ws_size(1, 4096, 34416, LQ_BF16, 9)[0] == LQ_ERR_INVALID_ARG
+    assert ws_size(1, 4095, 34416, LQ_BF16, 0)[0] == LQ_ERR_UNSUPPORTED
+    assert ws_size(1, 4096, 34415, LQ_BF16, 0)[0] == LQ_ERR_UNSUPPORTED
+    # too small / missing workspace
+    assert f(P, P, LQ_F32, 1, 4096, 34416, P, P, LQ_F32, 1, P, need - 1, None) == LQ_ERR_WORKSPACE
+    assert f(P, P, LQ_F32, 1, 4096, 34416, P, P, LQ_F32, 1, None, 0, None) == LQ_ERR_WORKSPACE
+    # misaligned / null operands
+    assert f(MIS, P, LQ_F32, 1, 4096, 34416, P, P, LQ_F32, 1, P, need, None) == LQ_ERR_INVALID_ARG
+    assert f(P, P, LQ_F32, 1, 4096, 34416, None, P, LQ_F32, 1, P, need, None) == LQ_ERR_INVALID_ARG
+    assert f(P, P, LQ_F32, 1, 4096, 34416, P, P, 5, 1, P, need, None) == LQ_ERR_INVALID_ARG
+    # empty batch: valid, enqueues nothing
+    assert f(None, None, LQ_F32, 0, 4096, 34416, None, None, LQ_F32, 0, None, 0, None) == LQ_OK
+
+
+def test_linear_validation():
+    lay = LQLayer(4096, 14336, 10, 24, 1024, 0, P, P, P, P)
+    out = ctypes.c_size_t()
+    assert LIB.lq_linear_workspace_size(ctypes.byref(lay), 1, LQ_BF16, ctypes.byref(out)) == LQ_OK
+    need = out.value
+    assert need >= 14336 * 4 + 34416 * 2
+    f = LIB.lq_linear
+    assert f(ctypes.byref(lay), P, LQ_BF16, 1, P, LQ_BF16, P, need - 1, None) == LQ_ERR_WORKSPACE
+    bad = LQLayer(4096, 14336, 10, 24, 1000, 0, P, P, P, P)
+    assert f(ctypes.byref(bad), P, LQ_BF16, 1, P, LQ_BF16, P, need, None) == LQ_ERR_INVALID_ARG
+    bad = LQLayer(4096, 14336, 10, 24, 1024, 1, P, P, P, P)       # reserved != 0
+    assert f(ctypes.byref(bad), P, LQ_BF16, 1, P, LQ_BF16, P, need, None) == LQ_ERR_INVALID_ARG
+    bad = LQLayer(4096, 14336, 10, 24, 1024, 0, P, MIS, P, P)
+    assert f(ctypes.byref(bad), P, LQ_BF16, 1, P, LQ_BF16, P, need, None) == LQ_ERR_INVALID_ARG
+    assert f(None, P, LQ_BF16, 1, P, LQ_BF16, P, need, None) == LQ_ERR_INVALID_ARG
+    assert f(ctypes.byref(lay), P, LQ_BF16, 0, P, LQ_BF16, None, 0, None) == LQ_OK
+
+
+def test_profile_events_validation():
+    f = LIB.lq_profile_events
+    arr = (ctypes.c_void_p * 2)(P, P)
+    assert f(None, None, -1) == LQ_ERR_INVALID_ARG
+    assert f(None, arr, 2) == LQ_ERR_INVALID_ARG
+    nulls = (ctypes.c_void_p * 2)(P, None)
+    assert f(arr, nulls, 2) == LQ_ERR_INVALID_ARG
+    assert f(None, None, 0) == LQ_OK
