@@ -39,14 +39,14 @@ lq_status check_layer_dims(int64_t N, int64_t K, int32_t d, int32_t D, int64_t* 
   if (D > LQ_MAX_D || N > kMaxDim || K > kMaxDim) return LQ_ERR_UNSUPPORTED;
   const int64_t Kb = (K + d - 1) / d;
   *L = Kb * D;
-  if (N % lq::kPanelRows != 0 || *L % 8 != 0) return LQ_ERR_UNSUPPORTED;
+  if (N % lq::kPanelRows != 0 || *L % 8 != 0 || *L > kMaxDim) return LQ_ERR_UNSUPPORTED;
   if (!mul_ok(N, *L, kMaxElems * 64)) return LQ_ERR_UNSUPPORTED;
   return LQ_OK;
 }
 
 lq_status check_sign_dims(int64_t B, int64_t N, int64_t L) {
   if (B < 0 || N < 0 || L < 1) return LQ_ERR_INVALID_ARG;
-  if (B > kMaxBatch || N > kMaxDim || L > kMaxDim * LQ_MAX_D) return LQ_ERR_UNSUPPORTED;
+  if (B > kMaxBatch || N > kMaxDim || L > kMaxDim) return LQ_ERR_UNSUPPORTED;
   if (N % lq::kPanelRows != 0 || L % 8 != 0) return LQ_ERR_UNSUPPORTED;
   if (!mul_ok(B, L, kMaxElems) || !mul_ok(B, N, kMaxElems)) return LQ_ERR_UNSUPPORTED;
   return LQ_OK;
@@ -87,49 +87,123 @@ lq_algo resolve_algo(lq_algo algo, lq_dtype ztype, int64_t B) {
   return ztype == LQ_F32 ? LQ_ALGO_VALU : LQ_ALGO_MFMA_SMALL;
 }
 
-// Workspace of the sign product; also validates the algorithm choice.
-lq_status sign_ws(int64_t B, int64_t N, int64_t L, lq_dtype ztype, lq_algo algo, size_t* bytes) {
-  const lq::PackedGeom g = lq::make_geom(N, L);
-  switch (resolve_algo(algo, ztype, B)) {
-    case LQ_ALGO_VALU: *bytes = lq::plan_valu(B, g).ws_bytes; return LQ_OK;
+// Everything one sign product (or one whole lq_linear) needs: algorithm,
+// geometry, plans and the byte offsets of its pieces in the workspace.
+struct Exec {
+  lq_algo algo;
+  lq::PackedGeom g;
+  lq::ValuPlan vp;
+  lq::Fp4Plan fp;
+  lq::OperandShape os;
+  int tickets;
+  size_t off_tickets, off_zop, off_inv, off_tp, off_partial, off_zf32, off_xt, off_z, total;
+};
+
+// Plans a sign product of z (ztype) or, when `linear`, the whole operator
+// for activations of type ztype with K input features.
+lq_status plan_exec(int64_t B, int64_t N, int64_t L, int64_t K, lq_dtype ztype, lq_algo algo,
+                    bool linear, Exec* e) {
+  e->algo = resolve_algo(algo, ztype, B);
+  e->g = lq::make_geom(N, L);
+  e->tickets = 0;
+  e->off_tickets = e->off_zop = e->off_inv = e->off_tp = e->off_partial = 0;
+  e->off_zf32 = e->off_xt = e->off_z = 0;
+  size_t at = 0;
+  auto take = [&](size_t bytes) { const size_t o = at; at += align_up(bytes); return o; };
+  switch (e->algo) {
+    case LQ_ALGO_VALU:
+      if (B > 16 && linear) return LQ_ERR_UNSUPPORTED;
+      e->vp = lq::plan_valu(B, e->g);
+      e->tickets = e->vp.ksplit > 1 ? e->vp.groups : 0;
+      e->off_tickets = take((size_t)e->tickets * 4);
+      e->off_partial = take(e->vp.partial_bytes);
+      if (linear) e->off_zf32 = take((size_t)B * L * sizeof(float));
+      break;
     case LQ_ALGO_MFMA_SMALL:
       if (B > 16) return LQ_ERR_UNSUPPORTED;
-      *bytes = lq::plan_mfma_small(B, g, ztype == LQ_BF16).ws_bytes;
-      return LQ_OK;
-    case LQ_ALGO_MFMA_LARGE: *bytes = 0; return LQ_OK;
-    default: return LQ_ERR_INVALID_ARG;
+      e->os = lq::operand_shape(B, ztype == LQ_BF16);
+      e->fp = lq::plan_fp4(B, e->g, e->os);
+      e->off_zop = take(lq::operand_bytes(B, L, e->os));
+      e->off_inv = take((size_t)e->g.ext_tiles * B * sizeof(float));
+      e->off_tp = take((size_t)e->g.ext_tiles * B * sizeof(float));
+      break;
+    case LQ_ALGO_MFMA_LARGE:
+      if (linear) {
+        e->off_xt = take((size_t)B * K * sizeof(float));
+        e->off_z = take((size_t)B * L * dtype_size(ztype));
+      }
+      break;
+    default:
+      return LQ_ERR_INVALID_ARG;
   }
+  e->total = at;
+  return LQ_OK;
 }
 
-lq_status run_sign(const uint8_t* packed, const void* z, lq_dtype ztype, int64_t B, int64_t N,
-                   int64_t L, const float* row_scale, void* y, lq_dtype ytype, lq_algo algo,
-                   void* ws, hipStream_t stream) {
-  const lq::PackedGeom g = lq::make_geom(N, L);
+// Sign product of a prepared input. `zin` is z (sign_gemm) or the raw
+// activations x (linear, whitened and lifted by the preparation launch).
+lq_status run_exec(const Exec& e, const uint8_t* packed, const void* zin, lq_dtype ztype,
+                   int64_t B, int64_t N, int64_t L, const float* row_scale, void* y,
+                   lq_dtype ytype, void* ws, hipStream_t st, const lq_layer* layer) {
+  char* base = static_cast<char*>(ws);
   const bool zb = ztype == LQ_BF16, yb = ytype == LQ_BF16;
-  switch (resolve_algo(algo, ztype, B)) {
+  unsigned* tickets = reinterpret_cast<unsigned*>(base + e.off_tickets);
+  float* partial = reinterpret_cast<float*>(base + e.off_partial);
+  lq_status s = LQ_OK;
+  switch (e.algo) {
     case LQ_ALGO_VALU: {
-      const lq::SplitPlan plan = lq::plan_valu(B, g);
-      float* partial = static_cast<float*>(ws);
-      float* colsum = partial + (size_t)plan.ksplit * B * N;
-      lq_status s = hip_status(profiled(stream, [&] {
-        return lq::launch_sign_valu(packed, g, z, zb, B, plan, partial, colsum, stream);
-      }));
+      const void* z = zin;
+      bool z_bf16 = zb;
+      if (layer) {
+        float* zf = reinterpret_cast<float*>(base + e.off_zf32);
+        s = hip_status(lq::launch_prep(zin, zb ? 1 : 0, B, layer->K, layer->d, layer->D, layer->hb,
+                                       layer->c, layer->M, L, zf, nullptr, tickets, e.tickets, st));
+        z = zf;
+        z_bf16 = false;
+      } else if (e.tickets > 0) {
+        s = hip_status(lq::launch_zero_u32(tickets, e.tickets, st));
+      }
       if (s != LQ_OK) return s;
-      return hip_status(lq::launch_split_epilogue(partial, colsum, plan.ksplit, B, N, row_scale, y, yb, stream));
+      return hip_status(profiled(st, [&] {
+        return lq::launch_sign_valu(packed, e.g, z, z_bf16, B, row_scale, y, yb, e.vp, partial,
+                                    tickets, st);
+      }));
     }
     case LQ_ALGO_MFMA_SMALL: {
-      const lq::SplitPlan plan = lq::plan_mfma_small(B, g, zb);
-      float* partial = static_cast<float*>(ws);
-      lq_status s = hip_status(profiled(stream, [&] {
-        return lq::launch_sign_mfma_small(packed, g, z, zb, B, plan, partial, stream);
-      }));
+      lq::OperandPlan op;
+      op.nt = e.os.nt;
+      op.rp = e.os.rp;
+      op.cs = e.os.cs;
+      op.ncv = e.os.ncv;
+      op.zop = reinterpret_cast<uint4*>(base + e.off_zop);
+      op.invscale = reinterpret_cast<float*>(base + e.off_inv);
+      op.tpart = reinterpret_cast<float*>(base + e.off_tp);
+      if (layer)
+        s = hip_status(lq::launch_prep(zin, zb ? 1 : 0, B, layer->K, layer->d, layer->D, layer->hb,
+                                       layer->c, layer->M, L, nullptr, &op, tickets, e.tickets, st));
+      else
+        s = hip_status(lq::launch_prep(zin, zb ? 3 : 2, B, 1, 1, 1, 1, nullptr, nullptr, L, nullptr,
+                                       &op, tickets, e.tickets, st));
       if (s != LQ_OK) return s;
-      return hip_status(lq::launch_split_epilogue(partial, nullptr, plan.ksplit, B, N, row_scale, y, yb, stream));
-    }
-    case LQ_ALGO_MFMA_LARGE:
-      return hip_status(profiled(stream, [&] {
-        return lq::launch_sign_mfma_large(packed, g, z, zb, B, row_scale, y, yb, stream);
+      return hip_status(profiled(st, [&] {
+        return lq::launch_sign_fp4(packed, e.g, op, B, row_scale, y, yb, e.fp, st);
       }));
+    }
+    case LQ_ALGO_MFMA_LARGE: {
+      const void* z = zin;
+      if (layer) {
+        float* xt = reinterpret_cast<float*>(base + e.off_xt);
+        void* zl = base + e.off_z;
+        s = hip_status(lq::launch_hadamard_scale(zin, zb, B, layer->K, layer->hb, layer->c, xt, st));
+        if (s != LQ_OK) return s;
+        s = hip_status(lq::launch_lift(xt, B, layer->K, layer->d, layer->D, layer->M, zl, zb, st));
+        if (s != LQ_OK) return s;
+        z = zl;
+      }
+      return hip_status(profiled(st, [&] {
+        return lq::launch_sign_mfma_large(packed, e.g, z, zb, B, row_scale, y, yb, st);
+      }));
+    }
     default:
       return LQ_ERR_INVALID_ARG;
   }
@@ -139,20 +213,6 @@ lq_status check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (need == 0) return LQ_OK;
   if (ws == nullptr || ws_bytes < need) return LQ_ERR_WORKSPACE;
   if (!aligned16(ws)) return LQ_ERR_INVALID_ARG;
-  return LQ_OK;
-}
-
-lq_status linear_ws(const lq_layer* layer, int64_t B, lq_dtype xtype, int64_t L, size_t* total,
-                    size_t* off_z, size_t* off_sign) {
-  const lq_dtype zt = xtype;   // lifted values keep the activation dtype
-  size_t sbytes = 0;
-  lq_status s = sign_ws(B, layer->N, L, zt, LQ_ALGO_AUTO, &sbytes);
-  if (s != LQ_OK) return s;
-  const size_t xt_bytes = align_up((size_t)B * layer->K * sizeof(float));
-  const size_t z_bytes = align_up((size_t)B * L * dtype_size(zt));
-  *off_z = xt_bytes;
-  *off_sign = xt_bytes + z_bytes;
-  *total = xt_bytes + z_bytes + align_up(sbytes);
   return LQ_OK;
 }
 
@@ -240,10 +300,15 @@ lq_status lq_lift_activations(const float* xt, int64_t B, int64_t K, int32_t d, 
 lq_status lq_sign_gemm_workspace_size(int64_t B, int64_t N, int64_t L, lq_dtype ztype,
                                       lq_algo algo, size_t* bytes) {
   if (bytes == nullptr || !valid_dtype(ztype)) return LQ_ERR_INVALID_ARG;
+  if (algo < LQ_ALGO_AUTO || algo > LQ_ALGO_MFMA_LARGE) return LQ_ERR_INVALID_ARG;
   lq_status s = check_sign_dims(B, N, L);
   if (s != LQ_OK) return s;
   if (B == 0 || N == 0) { *bytes = 0; return LQ_OK; }
-  return sign_ws(B, N, L, ztype, algo, bytes);
+  Exec e;
+  s = plan_exec(B, N, L, 0, ztype, algo, false, &e);
+  if (s != LQ_OK) return s;
+  *bytes = e.total;
+  return LQ_OK;
 }
 
 lq_status lq_sign_gemm_ex(const uint8_t* packed, const void* z, lq_dtype ztype, int64_t B,
@@ -254,14 +319,14 @@ lq_status lq_sign_gemm_ex(const uint8_t* packed, const void* z, lq_dtype ztype, 
   lq_status s = check_sign_dims(B, N, L);
   if (s != LQ_OK) return s;
   if (B == 0 || N == 0) return LQ_OK;
-  size_t need = 0;
-  s = sign_ws(B, N, L, ztype, algo, &need);
+  Exec e;
+  s = plan_exec(B, N, L, 0, ztype, algo, false, &e);
   if (s != LQ_OK) return s;
   if (!aligned16(packed) || !aligned16(z) || !aligned16(row_scale) || !aligned16(y))
     return LQ_ERR_INVALID_ARG;
-  s = check_ws(ws, ws_bytes, need);
+  s = check_ws(ws, ws_bytes, e.total);
   if (s != LQ_OK) return s;
-  return run_sign(packed, z, ztype, B, N, L, row_scale, y, ytype, algo, ws, (hipStream_t)stream);
+  return run_exec(e, packed, z, ztype, B, N, L, row_scale, y, ytype, ws, (hipStream_t)stream, nullptr);
 }
 
 lq_status lq_sign_gemm(const uint8_t* packed, const void* z, lq_dtype ztype, int64_t B, int64_t N,
@@ -279,9 +344,13 @@ lq_status lq_linear_workspace_size(const lq_layer* layer, int64_t B, lq_dtype xt
   if (s != LQ_OK) return s;
   s = check_sign_dims(B, layer->N, L);
   if (s != LQ_OK) return s;
+  if (!mul_ok(B, layer->K, kMaxElems)) return LQ_ERR_UNSUPPORTED;
   if (B == 0 || layer->N == 0) { *bytes = 0; return LQ_OK; }
-  size_t oz = 0, os = 0;
-  return linear_ws(layer, B, xtype, L, bytes, &oz, &os);
+  Exec e;
+  s = plan_exec(B, layer->N, L, layer->K, xtype, LQ_ALGO_AUTO, true, &e);
+  if (s != LQ_OK) return s;
+  *bytes = e.total;
+  return LQ_OK;
 }
 
 lq_status lq_linear(const lq_layer* layer, const void* x, lq_dtype xtype, int64_t B, void* y,
@@ -292,29 +361,18 @@ lq_status lq_linear(const lq_layer* layer, const void* x, lq_dtype xtype, int64_
   if (s != LQ_OK) return s;
   s = check_sign_dims(B, layer->N, L);
   if (s != LQ_OK) return s;
-  if (B > kMaxBatch || !mul_ok(B, layer->K, kMaxElems)) return LQ_ERR_UNSUPPORTED;
+  if (!mul_ok(B, layer->K, kMaxElems)) return LQ_ERR_UNSUPPORTED;
   if (B == 0 || layer->N == 0) return LQ_OK;
   if (!aligned16(x) || !aligned16(y) || !aligned16(layer->packed) || !aligned16(layer->M) ||
       !aligned16(layer->c) || !aligned16(layer->row_scale))
     return LQ_ERR_INVALID_ARG;
-  size_t need = 0, off_z = 0, off_sign = 0;
-  s = linear_ws(layer, B, xtype, L, &need, &off_z, &off_sign);
+  Exec e;
+  s = plan_exec(B, layer->N, L, layer->K, xtype, LQ_ALGO_AUTO, true, &e);
   if (s != LQ_OK) return s;
-  s = check_ws(ws, ws_bytes, need);
+  s = check_ws(ws, ws_bytes, e.total);
   if (s != LQ_OK) return s;
-
-  hipStream_t st = (hipStream_t)stream;
-  char* base = static_cast<char*>(ws);
-  float* xt = reinterpret_cast<float*>(base);
-  void* z = base + off_z;
-  void* sws = base + off_sign;
-  const lq_dtype zt = xtype;
-  s = hip_status(lq::launch_hadamard_scale(x, xtype == LQ_BF16, B, layer->K, layer->hb, layer->c, xt, st));
-  if (s != LQ_OK) return s;
-  s = hip_status(lq::launch_lift(xt, B, layer->K, layer->d, layer->D, layer->M, z, zt == LQ_BF16, st));
-  if (s != LQ_OK) return s;
-  return run_sign(layer->packed, z, zt, B, layer->N, L, layer->row_scale, y, ytype, LQ_ALGO_AUTO,
-                  sws, st);
+  return run_exec(e, layer->packed, x, xtype, B, layer->N, L, layer->row_scale, y, ytype, ws,
+                  (hipStream_t)stream, layer);
 }
 
 lq_status lq_profile_events(void* const* starts, void* const* stops, int32_t count) {

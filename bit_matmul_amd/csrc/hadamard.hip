@@ -80,6 +80,7 @@ __global__ __launch_bounds__(256) void hadamard_scale_kernel(const void* __restr
 
 hipError_t launch_hadamard_scale(const void* x, bool x_bf16, int64_t B, int64_t K, int hb,
                                  const float* c, float* xt, hipStream_t stream) {
+  (void)hipGetLastError();   // clear a stale error of an earlier runtime call
   const int64_t total = B * K;
   const int64_t blocks = (total + 1023) / 1024;
   // 1/sqrt(hb) for hb = 2^k: exact when k is even, correctly rounded otherwise.

@@ -45,15 +45,18 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
   return __uint_as_float(h << 16);
 }
 
-// The 16-byte slot (g, r) of tile q of one panel, as four 32-bit words:
+// The 16-byte slot (g, r) of full tile q of one panel, as four 32-bit words:
 // word u, bit b = sign bit of row r at tile column 128u + 32g + b.
-// For the tail tile (q == full_tiles) the words are assembled from the
-// row-major tail bytes; columns beyond L read as 0 (sign +1).
-__device__ __forceinline__ uint4 load_slot(const uint8_t* __restrict__ panel, int q,
-                                           int full_tiles, int tail_bytes, int g, int r) {
-  if (q < full_tiles) {
-    return *reinterpret_cast<const uint4*>(panel + (int64_t)q * kTileBytes + 16 * (16 * g + r));
-  }
+__device__ __forceinline__ uint4 load_full_slot(const uint8_t* __restrict__ panel, int q, int g,
+                                                int r) {
+  return *reinterpret_cast<const uint4*>(panel + (int64_t)q * kTileBytes + 16 * (16 * g + r));
+}
+
+// The same slot of the partial tail tile, assembled from the row-major tail
+// bytes (columns beyond L read as 0, sign +1). Branch-free: every lane loads
+// 16 bytes at clamped in-bounds offsets and masks the ones past the row.
+__device__ __forceinline__ uint4 load_tail_slot(const uint8_t* __restrict__ panel, int full_tiles,
+                                                int tail_bytes, int g, int r) {
   const uint8_t* row = panel + (int64_t)full_tiles * kTileBytes + r * tail_bytes;
   uint32_t w[4];
 #pragma unroll
@@ -61,12 +64,78 @@ __device__ __forceinline__ uint4 load_slot(const uint8_t* __restrict__ panel, in
     uint32_t v = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      int t = 16 * u + 4 * g + k;
-      if (t < tail_bytes) v |= (uint32_t)row[t] << (8 * k);
+      const int t = 16 * u + 4 * g + k;
+      const uint32_t byte = row[t < tail_bytes ? t : tail_bytes - 1];
+      v |= (t < tail_bytes ? byte : 0u) << (8 * k);
     }
     w[u] = v;
   }
   return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Slot of tile q (full or tail); `q`, `full_tiles` and `tail_bytes` are
+// uniform across the wavefront, so the choice is a scalar branch.
+__device__ __forceinline__ uint4 load_slot(const uint8_t* __restrict__ panel, int q,
+                                           int full_tiles, int tail_bytes, int g, int r) {
+  if (q < full_tiles) return load_full_slot(panel, q, g, r);
+  return load_tail_slot(panel, full_tiles, tail_bytes, g, r);
+}
+
+// Index of the calling thread's wavefront as a wave-uniform (scalar) value,
+// so that branches on it are scalar and do not make the compiler wait for
+// outstanding loads at their joins.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
+// Copy n (>= 1) elements from global memory to LDS with all of a thread's
+// loads in flight before its first LDS store (PER loads per thread per
+// round). The stores are unconditional: out-of-range ones go to dst[n],
+// which must exist (one spare element).
+template <int PER, typename T>
+__device__ __forceinline__ void copy_to_lds(T* __restrict__ dst, const T* __restrict__ src, int n) {
+  for (int base = 0; base < n; base += PER * (int)blockDim.x) {
+    T v[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = base + j * (int)blockDim.x + (int)threadIdx.x;
+      v[j] = src[i < n ? i : n - 1];
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = base + j * (int)blockDim.x + (int)threadIdx.x;
+      dst[i < n ? i : n] = v[j];
+    }
+  }
+}
+
+// Cross-workgroup hand-off of split-K partial sums without whole-cache
+// maintenance (an agent-scope fence would write back and invalidate the
+// XCD's entire L2): the partials are written and read with device-coherent
+// (agent-scope) relaxed atomic stores and loads, which go to the device
+// coherence point instead of an XCD's L2. Every wave waits for its stores to
+// complete (vmcnt 0) before the ticket is taken; compiler-level fences keep
+// the loads after it.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Returns true in every thread of the workgroup that takes the last of
+// `count` tickets of `ticket`. All partial stores of the workgroup must be
+// issued before the call.
+__device__ __forceinline__ bool last_ticket(unsigned* ticket, int count, int* flag) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // gfx9 encoding: vmcnt(0), expcnt(7), lgkmcnt(15)
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *flag = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            (unsigned)(count - 1);
+  __syncthreads();
+  const bool last = *flag != 0;
+  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  return last;
 }
 
 // ---------------------------------------------------------------- launchers
@@ -81,27 +150,56 @@ hipError_t launch_hadamard_scale(const void* x, bool x_bf16, int64_t B, int64_t 
 hipError_t launch_lift(const float* xt, int64_t B, int64_t K, int d, int D, const float* M,
                        void* z, bool z_bf16, hipStream_t stream);
 
-// Split-K plan shared by the panel-parallel sign products (VALU and small
-// MFMA). Workspace: partial[ksplit][B][N] and colsum[ksplit][B] floats.
-struct SplitPlan {
-  int ksplit;           // number of column ranges
-  int tiles_per_split;  // packed tiles per range
-  int batch_tile;       // batch columns per workgroup (VALU) or 16 (MFMA)
-  size_t ws_bytes;
-};
-SplitPlan plan_valu(int64_t B, const PackedGeom& g);
-SplitPlan plan_mfma_small(int64_t B, const PackedGeom& g, bool z_bf16);
+// ---- small batch (B <= 16): activation preparation and sign products.
+// VALU product: column ranges of a panel group are combined through a ticket
+// counter per group (every workgroup writes partial sums, the last to take a
+// ticket adds them); the tickets are cleared by the launch before it.
 
+// FP8 operand of the FP4 x FP8 product: each batch row takes nt MFMA columns
+// (one per fp8 term); rp batch rows per 16-column set; cs sets; ncv columns
+// stored per set.
+struct OperandShape {
+  int nt, rp, cs, ncv;
+};
+struct OperandPlan {
+  int nt, rp, cs, ncv;
+  uint4* zop;         // ext_tiles x 4 x cs x 2 x 4 x ncv 16-byte slices
+  float* invscale;    // ext_tiles x B
+  float* tpart;       // ext_tiles x B
+};
+OperandShape operand_shape(int64_t B, bool z_bf16);
+size_t operand_bytes(int64_t B, int64_t L, const OperandShape& s);
+
+struct Fp4Plan {
+  int ppw;      // panels per workgroup
+  int waves;    // wavefronts per workgroup (split the reduction length)
+  int tpw;      // tiles per wavefront
+  int groups;   // workgroups
+};
+Fp4Plan plan_fp4(int64_t B, const PackedGeom& g, const OperandShape& s);
+
+struct ValuPlan {
+  int bt, tps, ksplit, groups;
+  size_t partial_bytes;
+};
+ValuPlan plan_valu(int64_t B, const PackedGeom& g);
+
+// xkind: 0 x fp32, 1 x bf16 (whiten + lift), 2 z fp32, 3 z bf16 (as given).
+// op == nullptr: write fp32 z to zf32 (B x L); else the FP8 operand.
+hipError_t launch_prep(const void* x, int xkind, int64_t B, int64_t K, int d, int D, int hb,
+                       const float* c, const float* M, int64_t L, float* zf32,
+                       const OperandPlan* op, unsigned* tickets, int n_tickets,
+                       hipStream_t stream);
+hipError_t launch_sign_fp4(const uint8_t* packed, const PackedGeom& g, const OperandPlan& op,
+                           int64_t B, const float* row_scale, void* y, bool y_bf16,
+                           const Fp4Plan& plan, hipStream_t stream);
 hipError_t launch_sign_valu(const uint8_t* packed, const PackedGeom& g, const void* z,
-                            bool z_bf16, int64_t B, const SplitPlan& plan, float* partial,
-                            float* colsum, hipStream_t stream);
-hipError_t launch_sign_mfma_small(const uint8_t* packed, const PackedGeom& g, const void* z,
-                                  bool z_bf16, int64_t B, const SplitPlan& plan, float* partial,
-                                  hipStream_t stream);
-// y[b][n] = row_scale[n] * (sum_k colsum[k][b] (if colsum) + sum_k partial[k][b][n])
-hipError_t launch_split_epilogue(const float* partial, const float* colsum, int ksplit,
-                                 int64_t B, int64_t N, const float* row_scale, void* y,
-                                 bool y_bf16, hipStream_t stream);
+                            bool z_bf16, int64_t B, const float* row_scale, void* y, bool y_bf16,
+                            const ValuPlan& plan, float* partial, unsigned* tickets,
+                            hipStream_t stream);
+hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t stream);
+
+// ---- large batch: bf16 matrix-core GEMM (z bf16, or fp32 as a hi + lo pair).
 hipError_t launch_sign_mfma_large(const uint8_t* packed, const PackedGeom& g, const void* z,
                                   bool z_bf16, int64_t B, const float* row_scale, void* y,
                                   bool y_bf16, hipStream_t stream);

@@ -67,6 +67,7 @@ int grid_for(int64_t total) {
 
 hipError_t launch_pack(const int8_t* signs, int64_t N, int64_t L, uint8_t* packed,
                        hipStream_t stream) {
+  (void)hipGetLastError();   // clear a stale error of an earlier runtime call
   const PackedGeom g = make_geom(N, L);
   const int64_t total = N * L / 8;
   hipLaunchKernelGGL(pack_kernel, dim3(grid_for(total)), dim3(256), 0, stream, signs, L,
@@ -76,6 +77,7 @@ hipError_t launch_pack(const int8_t* signs, int64_t N, int64_t L, uint8_t* packe
 
 hipError_t launch_unpack(const uint8_t* packed, int64_t N, int64_t L, int8_t* signs,
                          hipStream_t stream) {
+  (void)hipGetLastError();   // clear a stale error of an earlier runtime call
   const PackedGeom g = make_geom(N, L);
   const int64_t total = N * L / 8;
   hipLaunchKernelGGL(unpack_kernel, dim3(grid_for(total)), dim3(256), 0, stream, packed, L,

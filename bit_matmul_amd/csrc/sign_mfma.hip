@@ -1,4 +1,5 @@
-// Sign products on the bf16 matrix cores (gfx950 v_mfma_f32_16x16x32_bf16).
+// Large-batch sign product on the bf16 matrix cores (gfx950
+// v_mfma_f32_16x16x32_bf16): a tiled GEMM for B > 16.
 //
 // Operand construction. In a 16x16x32 MFMA, lane l = 16*g + r supplies row r
 // of the A tile and column r of the B tile, each for the 8 reduction indices
@@ -59,69 +60,6 @@ __device__ __forceinline__ uint32_t zpair(const void* z, int64_t b, int64_t col,
     h1 = f32_to_bf16_bits(v1 - bf16_bits_to_f32(h1));
   }
   return h0 | (h1 << 16);
-}
-
-// ------------------------------------------------------------ small batch
-// B <= 16. One wavefront per 16-row panel and column range; the 16 MFMA
-// columns are the batch rows. LDS holds the range's z as bf16 pairs:
-// zl[term][b][G*16 + p] (b < B) with a per-row stride of groups*16 + 4 dwords
-// (padding that spreads the 16 batch rows over distinct LDS banks).
-template <bool kZBF16, int NTERM>
-__global__ __launch_bounds__(256) void sign_mfma_small_kernel(
-    const uint8_t* __restrict__ packed, int64_t panels, int64_t panel_bytes, int full_tiles,
-    int tail_bytes, int ext_tiles, const void* __restrict__ z, int64_t B, int64_t L, int tps,
-    float* __restrict__ partial, int64_t N) {
-  extern __shared__ uint32_t zl[];
-  const int ks = blockIdx.y;
-  const int q0 = ks * tps;
-  const int q1 = min(q0 + tps, ext_tiles);
-  const int groups = (q1 - q0) * (kTileCols / 32);
-  const int cs = groups * 16 + 4;
-  const int bn = (int)B;                       // <= 16
-  const int64_t c0 = (int64_t)q0 * kTileCols;
-
-  const int per_term = bn * groups * 16;
-  for (int idx = threadIdx.x; idx < NTERM * per_term; idx += blockDim.x) {
-    const int term = idx / per_term;
-    const int rem = idx - term * per_term;
-    const int b = rem / (groups * 16);
-    const int gp = rem - b * (groups * 16);
-    const int G = gp >> 4, p = gp & 15;
-    zl[(term * bn + b) * cs + gp] = zpair<kZBF16>(z, b, c0 + 32 * G + p, B, L, term);
-  }
-  __syncthreads();
-
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g = lane >> 4, r = lane & 15;
-  const int64_t pnl = (int64_t)blockIdx.x * 4 + wave;
-  if (pnl >= panels) return;
-  const uint8_t* panel = packed + pnl * panel_bytes;
-  const bool has_col = r < bn;
-
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int q = q0; q < q1; ++q) {
-    const uint4 sl = load_slot(panel, q, full_tiles, tail_bytes, g, r);
-    const uint32_t w4[4] = {sl.x, sl.y, sl.z, sl.w};
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int G = (q - q0) * 16 + 4 * u + g;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const u32x4 a = sign_operand(w4[u], s);
-#pragma unroll
-        for (int term = 0; term < NTERM; ++term) {
-          u32x4 bop = {0u, 0u, 0u, 0u};
-          if (has_col) bop = *reinterpret_cast<const u32x4*>(zl + (term * bn + r) * cs + G * 16 + 4 * s);
-          acc = mfma_bf16(a, bop, acc);
-        }
-      }
-    }
-  }
-  // Lane (g, r) holds rows 4g..4g+3 of the panel for batch row r.
-  if (has_col) {
-    float* dst = partial + ((int64_t)ks * B + r) * N + pnl * kPanelRows + 4 * g;
-    *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-  }
 }
 
 // ------------------------------------------------------------ large batch
@@ -218,11 +156,10 @@ __global__ __launch_bounds__(256) void sign_mfma_large_kernel(
   }
 }
 
-constexpr int kSmallLdsDwords = 16384;   // 64 KiB
-
 template <int PPW, bool kYBF16>
 hipError_t launch_large_ppw(const uint8_t* packed, const PackedGeom& g, const void* z, bool z_bf16,
                             int64_t B, const float* row_scale, void* y, hipStream_t stream) {
+  (void)hipGetLastError();   // clear a stale error of an earlier runtime call
   const dim3 grid((unsigned)((g.panels + 4 * PPW - 1) / (4 * PPW)), (unsigned)((B + 63) / 64));
   if (z_bf16)
     hipLaunchKernelGGL((sign_mfma_large_kernel<true, 1, PPW, kYBF16>), grid, dim3(256), 0, stream,
@@ -237,48 +174,10 @@ hipError_t launch_large_ppw(const uint8_t* packed, const PackedGeom& g, const vo
 
 }  // namespace
 
-SplitPlan plan_mfma_small(int64_t B, const PackedGeom& g, bool z_bf16) {
-  SplitPlan p;
-  p.batch_tile = 16;
-  const int64_t wgx = (g.panels + 3) / 4;
-  int64_t ks = (1024 + wgx - 1) / wgx;
-  // LDS: nterm x B rows x (tps * 256 + 4) dwords <= 16384.
-  const int bn = (int)(B < 1 ? 1 : B);
-  const int nterm = z_bf16 ? 1 : 2;
-  int max_tps = (kSmallLdsDwords / (nterm * bn) - 4) / 256;
-  if (max_tps < 1) max_tps = 1;
-  const int64_t ks_lds = (g.ext_tiles + max_tps - 1) / max_tps;
-  if (ks < ks_lds) ks = ks_lds;
-  if (ks > g.ext_tiles) ks = g.ext_tiles;
-  if (ks < 1) ks = 1;
-  int tps = (int)((g.ext_tiles + ks - 1) / ks);
-  if (tps > max_tps) tps = max_tps;
-  p.tiles_per_split = tps;
-  p.ksplit = (g.ext_tiles + tps - 1) / tps;
-  p.ws_bytes = (size_t)p.ksplit * B * g.N * sizeof(float);
-  return p;
-}
-
-hipError_t launch_sign_mfma_small(const uint8_t* packed, const PackedGeom& g, const void* z,
-                                  bool z_bf16, int64_t B, const SplitPlan& plan, float* partial,
-                                  hipStream_t stream) {
-  const dim3 grid((unsigned)((g.panels + 3) / 4), (unsigned)plan.ksplit);
-  const int nterm = z_bf16 ? 1 : 2;
-  const size_t lds = (size_t)nterm * B * (plan.tiles_per_split * 256 + 4) * sizeof(uint32_t);
-  if (z_bf16)
-    hipLaunchKernelGGL((sign_mfma_small_kernel<true, 1>), grid, dim3(256), lds, stream, packed,
-                       g.panels, g.panel_bytes, g.full_tiles, g.tail_bytes, g.ext_tiles, z, B, g.L,
-                       plan.tiles_per_split, partial, g.N);
-  else
-    hipLaunchKernelGGL((sign_mfma_small_kernel<false, 2>), grid, dim3(256), lds, stream, packed,
-                       g.panels, g.panel_bytes, g.full_tiles, g.tail_bytes, g.ext_tiles, z, B, g.L,
-                       plan.tiles_per_split, partial, g.N);
-  return hipGetLastError();
-}
-
 hipError_t launch_sign_mfma_large(const uint8_t* packed, const PackedGeom& g, const void* z,
                                   bool z_bf16, int64_t B, const float* row_scale, void* y,
                                   bool y_bf16, hipStream_t stream) {
+  (void)hipGetLastError();   // clear a stale error of an earlier runtime call
   // Four panels per wavefront when that still gives >= 512 workgroups.
   const int64_t bch = (B + 63) / 64;
   const bool big = ((g.panels + 15) / 16) * bch >= 512;

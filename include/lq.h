@@ -81,8 +81,12 @@ typedef enum lq_algo {
   LQ_ALGO_AUTO = 0,         /* the library's choice (what lq_sign_gemm does) */
   LQ_ALGO_VALU = 1,         /* fp32 sign-select on the vector ALUs; any z dtype,
                                B <= 16 per pass; exact fp32 accumulation */
-  LQ_ALGO_MFMA_SMALL = 2,   /* B <= 16: signs expanded in registers to bf16 +-1,
-                               z as bf16, matrix-core products, fp32 accumulate */
+  LQ_ALGO_MFMA_SMALL = 2,   /* B <= 16: packed signs fed to the FP4 x FP8
+                               matrix cores as bit planes; z carried as a sum of
+                               power-of-two-scaled fp8 terms (4 terms for fp32 z,
+                               3 for bf16 z and B <= 10, 2 for B = 11..16; worst
+                               relative error per value about 2^-16 / 2^-12 /
+                               2^-8); fp32 accumulate */
   LQ_ALGO_MFMA_LARGE = 3    /* any B: tiled GEMM on bf16 matrix cores, z as bf16
                                (bf16 z) or as a bf16 hi+lo pair (fp32 z) */
 } lq_algo;
@@ -194,8 +198,8 @@ lq_status lq_linear(const lq_layer* layer, const void* x, lq_dtype xtype, int64_
  * lq_sign_gemm_ex or lq_linear is bracketed by hipEventRecord(starts[i]) and
  * hipEventRecord(stops[i]) on the call's stream, i = 0, 1, 2, ... wrapping
  * modulo `count` (the split-K epilogue and the whitening/lift kernels are
- * outside the brackets). Events recorded while a stream is being captured
- * become event-record nodes of the graph. count == 0 clears the ring (the
+ * outside the brackets). Do not set the ring while capturing a stream into a
+ * graph: such event records cannot be timed. count == 0 clears the ring (the
  * arrays may then be NULL); calling again restarts at slot 0. The ring is
  * process-wide and guarded by a lock; the caller keeps the events alive
  * while it is set. Errors: INVALID_ARG for count < 0 or NULL arrays with

@@ -138,7 +138,7 @@ def test_linear_validation():
     out = ctypes.c_size_t()
     assert LIB.lq_linear_workspace_size(ctypes.byref(lay), 1, LQ_BF16, ctypes.byref(out)) == LQ_OK
     need = out.value
-    assert need >= 14336 * 4 + 34416 * 2
+    assert need >= 34416 * 3          # at least three fp8 terms per lifted column
     f = LIB.lq_linear
     assert f(ctypes.byref(lay), P, LQ_BF16, 1, P, LQ_BF16, P, need - 1, None) == LQ_ERR_WORKSPACE
     bad = LQLayer(4096, 14336, 10, 24, 1000, 0, P, P, P, P)
