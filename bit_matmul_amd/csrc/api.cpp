@@ -93,10 +93,10 @@ struct Exec {
   lq_algo algo;
   lq::PackedGeom g;
   lq::ValuPlan vp;
-  lq::Fp4Plan fp;
+  lq::Fp6Plan fp;
   lq::OperandShape os;
   int tickets;
-  size_t off_tickets, off_zop, off_inv, off_tp, off_partial, off_zf32, off_xt, off_z, total;
+  size_t off_tickets, off_aop, off_partial, off_zf32, off_xt, off_z, total;
 };
 
 // Plans a sign product of z (ztype) or, when `linear`, the whole operator
@@ -106,7 +106,7 @@ lq_status plan_exec(int64_t B, int64_t N, int64_t L, int64_t K, lq_dtype ztype, 
   e->algo = resolve_algo(algo, ztype, B);
   e->g = lq::make_geom(N, L);
   e->tickets = 0;
-  e->off_tickets = e->off_zop = e->off_inv = e->off_tp = e->off_partial = 0;
+  e->off_tickets = e->off_aop = e->off_partial = 0;
   e->off_zf32 = e->off_xt = e->off_z = 0;
   size_t at = 0;
   auto take = [&](size_t bytes) { const size_t o = at; at += align_up(bytes); return o; };
@@ -122,10 +122,8 @@ lq_status plan_exec(int64_t B, int64_t N, int64_t L, int64_t K, lq_dtype ztype, 
     case LQ_ALGO_MFMA_SMALL:
       if (B > 16) return LQ_ERR_UNSUPPORTED;
       e->os = lq::operand_shape(B, ztype == LQ_BF16);
-      e->fp = lq::plan_fp4(B, e->g, e->os);
-      e->off_zop = take(lq::operand_bytes(B, L, e->os));
-      e->off_inv = take((size_t)e->g.ext_tiles * B * sizeof(float));
-      e->off_tp = take((size_t)e->g.ext_tiles * B * sizeof(float));
+      e->fp = lq::plan_fp6(B, e->g, e->os);
+      e->off_aop = take(lq::operand_bytes(L, e->os));
       break;
     case LQ_ALGO_MFMA_LARGE:
       if (linear) {
@@ -171,13 +169,8 @@ lq_status run_exec(const Exec& e, const uint8_t* packed, const void* zin, lq_dty
     }
     case LQ_ALGO_MFMA_SMALL: {
       lq::OperandPlan op;
-      op.nt = e.os.nt;
-      op.rp = e.os.rp;
-      op.cs = e.os.cs;
-      op.ncv = e.os.ncv;
-      op.zop = reinterpret_cast<uint4*>(base + e.off_zop);
-      op.invscale = reinterpret_cast<float*>(base + e.off_inv);
-      op.tpart = reinterpret_cast<float*>(base + e.off_tp);
+      op.s = e.os;
+      op.aop = reinterpret_cast<uint8_t*>(base + e.off_aop);
       if (layer)
         s = hip_status(lq::launch_prep(zin, zb ? 1 : 0, B, layer->K, layer->d, layer->D, layer->hb,
                                        layer->c, layer->M, L, nullptr, &op, tickets, e.tickets, st));
@@ -186,7 +179,7 @@ lq_status run_exec(const Exec& e, const uint8_t* packed, const void* zin, lq_dty
                                        &op, tickets, e.tickets, st));
       if (s != LQ_OK) return s;
       return hip_status(profiled(st, [&] {
-        return lq::launch_sign_fp4(packed, e.g, op, B, row_scale, y, yb, e.fp, st);
+        return lq::launch_sign_fp6(packed, e.g, op, B, row_scale, y, yb, e.fp, st);
       }));
     }
     case LQ_ALGO_MFMA_LARGE: {

@@ -155,28 +155,48 @@ hipError_t launch_lift(const float* xt, int64_t B, int64_t K, int d, int D, cons
 // counter per group (every workgroup writes partial sums, the last to take a
 // ticket adds them); the tickets are cleared by the launch before it.
 
-// FP8 operand of the FP4 x FP8 product: each batch row takes nt MFMA columns
-// (one per fp8 term); rp batch rows per 16-column set; cs sets; ncv columns
-// stored per set.
+// Activation operand of the FP4 x FP6 product. Batch row b takes nt MFMA
+// columns cc = b * nt + t (term t), grouped in sets of 16 (cs = cc / 16,
+// c = cc % 16, ncs = columns in the set). Per full or tail tile one record
+// of `rec` bytes:
+//   data   [cs][u][g][c] 32 bytes: 6 dwords of FP6 E2M3 codes (code m at bit
+//          6m, the value meeting reduction index k = 32g + m of MFMA u) and
+//          2 zero dwords; set cs starts at 512 * 16 * cs
+//   scales [cs][g][c] dword at 512 * ncv + 256 * cs: byte u is the E8M0
+//          scale of that 32-value block
+//   tpart  [b] float at 528 * ncv: sum over the tile's plane-0..2 columns of
+//          the values the terms represent
 struct OperandShape {
-  int nt, rp, cs, ncv;
+  int nt;     // terms per batch row
+  int ncv;    // columns (B * nt)
+  int cs;     // 16-column sets
+  int rec;    // bytes per tile record (multiple of 16)
 };
+__host__ __device__ __forceinline__ int aop_data_offset(int cs, int u, int g, int c, int ncs) {
+  return 512 * 16 * cs + ((u * 4 + g) * ncs + c) * 32;
+}
+__host__ __device__ __forceinline__ int aop_scale_offset(int ncv, int cs, int g, int c, int ncs) {
+  return 512 * ncv + 256 * cs + (g * ncs + c) * 4;
+}
+__host__ __device__ __forceinline__ int aop_tpart_offset(int ncv) { return 528 * ncv; }
+
 struct OperandPlan {
-  int nt, rp, cs, ncv;
-  uint4* zop;         // ext_tiles x 4 x cs x 2 x 4 x ncv 16-byte slices
-  float* invscale;    // ext_tiles x B
-  float* tpart;       // ext_tiles x B
+  OperandShape s;
+  uint8_t* aop;   // ext_tiles records, then 1024 bytes of slack for chunked copies
 };
 OperandShape operand_shape(int64_t B, bool z_bf16);
-size_t operand_bytes(int64_t B, int64_t L, const OperandShape& s);
+size_t operand_bytes(int64_t L, const OperandShape& s);
 
-struct Fp4Plan {
-  int ppw;      // panels per workgroup
-  int waves;    // wavefronts per workgroup (split the reduction length)
-  int tpw;      // tiles per wavefront
-  int groups;   // workgroups
+struct Fp6Plan {
+  int p;            // panels per workgroup
+  int w;            // compute wavefronts per workgroup (plus one loader)
+  int tpc;          // tiles per compute wavefront per chunk
+  int nch;          // chunks of full tiles
+  int chunk_bytes;  // LDS bytes per chunk buffer
+  size_t lds_bytes; // dynamic LDS per workgroup
+  int groups;       // workgroups
 };
-Fp4Plan plan_fp4(int64_t B, const PackedGeom& g, const OperandShape& s);
+Fp6Plan plan_fp6(int64_t B, const PackedGeom& g, const OperandShape& s);
 
 struct ValuPlan {
   int bt, tps, ksplit, groups;
@@ -185,14 +205,14 @@ struct ValuPlan {
 ValuPlan plan_valu(int64_t B, const PackedGeom& g);
 
 // xkind: 0 x fp32, 1 x bf16 (whiten + lift), 2 z fp32, 3 z bf16 (as given).
-// op == nullptr: write fp32 z to zf32 (B x L); else the FP8 operand.
+// op == nullptr: write fp32 z to zf32 (B x L); else the FP6 operand.
 hipError_t launch_prep(const void* x, int xkind, int64_t B, int64_t K, int d, int D, int hb,
                        const float* c, const float* M, int64_t L, float* zf32,
                        const OperandPlan* op, unsigned* tickets, int n_tickets,
                        hipStream_t stream);
-hipError_t launch_sign_fp4(const uint8_t* packed, const PackedGeom& g, const OperandPlan& op,
+hipError_t launch_sign_fp6(const uint8_t* packed, const PackedGeom& g, const OperandPlan& op,
                            int64_t B, const float* row_scale, void* y, bool y_bf16,
-                           const Fp4Plan& plan, hipStream_t stream);
+                           const Fp6Plan& plan, hipStream_t stream);
 hipError_t launch_sign_valu(const uint8_t* packed, const PackedGeom& g, const void* z,
                             bool z_bf16, int64_t B, const float* row_scale, void* y, bool y_bf16,
                             const ValuPlan& plan, float* partial, unsigned* tickets,

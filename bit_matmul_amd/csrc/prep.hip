@@ -3,23 +3,25 @@
 // z[j*D + e] = sum_i M[i][e] xt[j*d + i], and the operand format the sign
 // product reads.
 //
-// One workgroup per (512-column lifted tile q, batch row b). The tile's
+// One 512-thread workgroup per (512-column lifted tile q, batch row b). The tile's
 // lifted columns need the original columns [k_lo, k_hi) of its d-blocks;
 // the workgroup loads the whole Hadamard blocks covering them into LDS,
 // transforms them in place (at most 2048 values: a tile spans at most 640
 // original columns), lifts, and writes either
 //   - fp32 z (the VALU product's input), or
-//   - the FP8 operand of the FP4 x FP8 matrix-core product: z is split into
-//     NT fp8 (e4m3) terms, each 16x finer than the previous, after scaling the
-//     tile by a power of two so that the largest |4 z| fits fp8's range. The
-//     bytes are laid out exactly as the product's B operand (see sign_fp4.hip)
-//     and pre-multiplied by the factor of the sign-bit plane they meet
-//     (-4, -2, -1 or +1). Per tile and batch row it also stores the inverse
-//     scale and the sum of z over the columns of planes 0..2.
-// Workgroup (0, 0) also clears the split-K tickets of the product that
+//   - the FP6 operand of the FP4 x FP6 matrix-core product (record layout in
+//     lq_internal.h): each 32-value block of the operand (the values one
+//     MFMA lane supplies: MFMA u, lane group g) is pre-multiplied by the
+//     factor of the sign-bit plane it meets (-4, -2, -1 or +1), then cut into
+//     nt terms; term t is the E2M3 rounding of the residual left by terms
+//     < t under its own power-of-two block scale (the largest that keeps the
+//     block's residual within E2M3's range). One 32-lane half-wavefront
+//     handles one block. The record also gets the sum over the tile's
+//     plane-0..2 columns of the values the terms represent.
+// Workgroup (0, 0) also clears the split-K tickets of the VALU product that
 // follows on the same stream.
+#include "lq_fp6.h"
 #include "lq_internal.h"
-#include "lq_fp8.h"
 
 namespace lq {
 namespace {
@@ -29,44 +31,77 @@ namespace {
 // 3 of 512, 4 of 256, ...: never more than 2048 values.
 constexpr int kSpanMax = 2048;
 
-__device__ __forceinline__ float block_reduce_sum(float v, float* red) {
-  // Fixed-order reduction: within waves by xor shuffles, then the 4 waves.
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
-  __syncthreads();
-  const float s = (red[0] + red[1]) + (red[2] + red[3]);
-  __syncthreads();
-  return s;
+constexpr int kThreads = 512;
+
+// Maximum over each 32-lane half of the wavefront: DPP within quads (lane
+// xor 1, xor 2), half-row and row mirrors (8, 16 lanes), then a swizzle
+// with lane xor 16.
+__device__ __forceinline__ float half_wave_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));
+  return v;
 }
 
-__device__ __forceinline__ float block_reduce_max(float v, float* red) {
+// In-place fast Walsh-Hadamard transform (unnormalised) of every 2^lhb-value
+// block of the 1024 values xs[0..1023], by one wavefront: lane l holds
+// xs[16l + k] (k = 0..15); stages with stride below 16 pair registers, the
+// others pair lanes l and l ^ (stride / 16).
+__device__ __forceinline__ void wave_fwht_1024(float* xs, int lhb, int lane) {
+  float a[16];
+  const float4* src = reinterpret_cast<const float4*>(xs + 16 * lane);
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
-  __syncthreads();
-  const float s = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  return s;
+  for (int i = 0; i < 4; ++i) {
+    const float4 v = src[i];
+    a[4 * i] = v.x; a[4 * i + 1] = v.y; a[4 * i + 2] = v.z; a[4 * i + 3] = v.w;
+  }
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    if (s < lhb) {
+      const int h = 1 << s;
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if ((k & h) == 0) {
+          const float x0 = a[k], x1 = a[k | h];
+          a[k] = x0 + x1;
+          a[k | h] = x0 - x1;
+        }
+    }
+  }
+#pragma unroll
+  for (int s = 4; s < 10; ++s) {
+    if (s < lhb) {
+      const int lb = 1 << (s - 4);
+      const bool upper = (lane & lb) != 0;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float p = __shfl_xor(a[k], lb, 64);
+        a[k] = upper ? p - a[k] : a[k] + p;
+      }
+    }
+  }
+  float4* dst = reinterpret_cast<float4*>(xs + 16 * lane);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[i] = make_float4(a[4 * i], a[4 * i + 1], a[4 * i + 2], a[4 * i + 3]);
 }
 
-// kMode 0: write fp32 z. kMode 1: write the FP8 operand (NT terms).
+// kMode 0: write fp32 z. kMode 1: write the FP6 operand.
 // kXKind 0: x fp32, 1: x bf16, 2: input is already-lifted z in fp32,
 // 3: already-lifted z in bf16 (whitening and lift skipped).
 // Index arithmetic is 32-bit (K, L < 2^31 is checked on the host).
 template <int kMode, int kXKind>
-__global__ __launch_bounds__(256) void prep_kernel(
-    const void* __restrict__ x, int B, int K, int d, int D, int hb, float norm,
+__global__ __launch_bounds__(kThreads) void prep_kernel(
+    const void* __restrict__ x, int B, int K, int d, int D, int lhb, float norm,
     const float* __restrict__ c, const float* __restrict__ M, int L,
     float* __restrict__ zf32,                      // kMode 0: B x L
-    uint4* __restrict__ zop, float* __restrict__ invscale, float* __restrict__ tpart,
-    int nt, int rp, int cs_count, int ncv, unsigned* __restrict__ tickets, int n_tickets) {
-  __shared__ float xs[kSpanMax];
+    uint8_t* __restrict__ aop, int nt, int ncv, int rec,
+    unsigned* __restrict__ tickets, int n_tickets) {
+  __shared__ __align__(16) float xs[kSpanMax];
   __shared__ float zt[kTileCols];
   __shared__ float Ms[64 * 64];
-  __shared__ float red[4];
+  __shared__ float red[8];
   const int q = blockIdx.x;
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
@@ -80,64 +115,61 @@ __global__ __launch_bounds__(256) void prep_kernel(
   if (kXKind <= 1) {
     // Original columns [k_lo, k_hi) feed this tile's d-blocks; load the
     // whole Hadamard blocks that cover them.
+    const int hb = 1 << lhb;
     const int j_lo = c_lo / D, j_hi = (c_lo + width - 1) / D + 1;
     const int k_lo = j_lo * d;
     const int k_hi = min(j_hi * d, K);
-    const int h_lo = k_lo < K ? (k_lo / hb) * hb : 0;
-    const int span = k_lo < K ? ((k_hi - 1) / hb + 1) * hb - h_lo : 0;
+    const int h_lo = k_lo < K ? (k_lo >> lhb) << lhb : 0;
+    const int span = k_lo < K ? (((k_hi - 1) >> lhb) + 1) * hb - h_lo : 0;
     const int64_t xrow = (int64_t)b * K;
     // Every global load of the thread first (x, c and M), then the LDS stores.
-    float xv[kSpanMax / 256], cv[kSpanMax / 256], mv[16];
+    float xv[kSpanMax / kThreads], cv[kSpanMax / kThreads], mv[4096 / kThreads];
 #pragma unroll
-    for (int j = 0; j < kSpanMax / 256; ++j) {
-      const int i = tid + 256 * j;
+    for (int j = 0; j < kSpanMax / kThreads; ++j) {
+      const int i = tid + kThreads * j;
       const int k = h_lo + (i < span ? i : 0);
       if (kXKind == 1) xv[j] = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(x)[xrow + k]);
       else xv[j] = reinterpret_cast<const float*>(x)[xrow + k];
       cv[j] = c[k];
     }
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int i = tid + 256 * j;
+    for (int j = 0; j < 4096 / kThreads; ++j) {
+      const int i = tid + kThreads * j;
       mv[j] = M[i < d * D ? i : 0];
     }
     // Unconditional stores (entries past span and d*D are never read).
 #pragma unroll
-    for (int j = 0; j < kSpanMax / 256; ++j) xs[tid + 256 * j] = xv[j] * cv[j];
+    for (int j = 0; j < kSpanMax / kThreads; ++j) xs[tid + kThreads * j] = xv[j] * cv[j];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) Ms[tid + 256 * j] = mv[j] * norm;   // fold 1/sqrt(hb) into M
+    for (int j = 0; j < 4096 / kThreads; ++j) Ms[tid + kThreads * j] = mv[j] * norm;   // fold 1/sqrt(hb) into M
     __syncthreads();
-    // In-place fast Walsh-Hadamard transform of each hb-block of the span.
-    for (int h = 1; h < hb; h <<= 1) {
-      for (int idx = tid; idx < span / 2; idx += 256) {
-        const int i = (idx / h) * 2 * h + (idx % h);
-        const float a0 = xs[i], a1 = xs[i + h];
-        xs[i] = a0 + a1;
-        xs[i + h] = a0 - a1;
-      }
-      __syncthreads();
-    }
-    // Lift the tile: 2 columns per thread, d multiply-adds each.
+    // Fast Walsh-Hadamard transform of each hb-block of the span, 1024
+    // values per wavefront (hb divides 1024; values past the span are
+    // transformed too and never read).
+    const int wave = tid >> 6;
+    if (1024 * wave < span) wave_fwht_1024(xs + 1024 * wave, lhb, tid & 63);
+    __syncthreads();
+    // Lift the tile: one column per thread, d multiply-adds.
 #pragma unroll
-    for (int jr = 0; jr < kTileCols / 256; ++jr) {
-      const int jj = tid + 256 * jr;
+    for (int jr = 0; jr < kTileCols / kThreads; ++jr) {
+      const int jj = tid + kThreads * jr;
       float acc = 0.0f;
       if (jj < width) {
         const int col = c_lo + jj;
         const int blk = col / D;
         const int e = col - blk * D;
         const int kb = blk * d;
-        for (int i = 0; i < d; ++i)
-          if (kb + i < K) acc = fmaf(Ms[i * D + e], xs[kb + i - h_lo], acc);
+        const int nk = min(d, K - kb);
+        for (int i = 0; i < nk; ++i) acc = fmaf(Ms[i * D + e], xs[kb + i - h_lo], acc);
       }
       zt[jj] = acc;
     }
   } else {
     const int64_t zrow = (int64_t)b * L + c_lo;
-    float v[kTileCols / 256];
+    float v[kTileCols / kThreads];
 #pragma unroll
-    for (int jr = 0; jr < kTileCols / 256; ++jr) {
-      const int jj = tid + 256 * jr;
+    for (int jr = 0; jr < kTileCols / kThreads; ++jr) {
+      const int jj = tid + kThreads * jr;
       const int jc = jj < width ? jj : 0;
       float t;
       if (kXKind == 3) t = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(x)[zrow + jc]);
@@ -145,81 +177,82 @@ __global__ __launch_bounds__(256) void prep_kernel(
       v[jr] = jj < width ? t : 0.0f;
     }
 #pragma unroll
-    for (int jr = 0; jr < kTileCols / 256; ++jr) zt[tid + 256 * jr] = v[jr];
+    for (int jr = 0; jr < kTileCols / kThreads; ++jr) zt[tid + kThreads * jr] = v[jr];
   }
   __syncthreads();
 
   if (kMode == 0) {
     const int64_t zrow = (int64_t)b * L + c_lo;
 #pragma unroll
-    for (int jr = 0; jr < kTileCols / 256; ++jr) {
-      const int jj = tid + 256 * jr;
+    for (int jr = 0; jr < kTileCols / kThreads; ++jr) {
+      const int jj = tid + kThreads * jr;
       if (jj < width) zf32[zrow + jj] = zt[jj];
     }
     return;
   }
 
-  // ---- FP8 operand (kMode 1)
-  float amax = 0.0f, tp = 0.0f;
+  // ---- FP6 operand (kMode 1). Half-wavefront h (0..15) takes block h
+  // of the tile's 16 blocks (u, g); lane m of the half holds
+  // the value meeting reduction index k = 32g + m, i.e. plane j = m / 8 of
+  // packed column 128u + 32g + 4(m % 8) + j.
+  uint8_t* recp = aop + (int64_t)q * rec;
+  const int m = tid & 31, half = tid >> 5;
+  const int j = m >> 3, i8 = m & 7;
+  const float f = j == 3 ? 1.0f : (j == 2 ? -1.0f : (j == 1 ? -2.0f : -4.0f));
+  float tp = 0.0f;
+  // Lane L < 6 of a half assembles dword L of a block's 192 code bits from
+  // the codes of lanes first(L) .. first(L) + 5 (code n sits at bit 6n).
+  const int L6 = m < 6 ? m : 5;
+  const int first = (32 * L6) / 6;
+  {
+    const int blk = half;
+    const int u = blk >> 2, g = blk & 3;
+    const float orig = f * zt[128 * u + 32 * g + 4 * i8 + j];
+    float v = orig;
+    for (int t = 0; t < nt; ++t) {
+      const int e = e2m3_block_exponent(half_wave_max(fabsf(v)));
+      const uint32_t code = e2m3_encode(ldexpf(v, -e));
+      v -= ldexpf(e2m3_decode(code), e);
+      uint32_t dw = 0u;
 #pragma unroll
-  for (int jr = 0; jr < kTileCols / 256; ++jr) {
-    const int jj = tid + 256 * jr;
-    const float v = zt[jj];
-    amax = fmaxf(amax, fabsf(v));
-    if ((jj & 3) != 3) tp += v;
-  }
-  amax = block_reduce_max(amax, red);
-  tp = block_reduce_sum(tp, red);
-  // Scale 2^e with 32 <= amax * 2^e < 64, so |4 z| * 2^e < 256 <= 448.
-  int e = 0;
-  if (amax > 0.0f) {
-    e = 5 - ilogbf(amax);
-    e = e > 100 ? 100 : (e < -100 ? -100 : e);
-  }
-  const float s = ldexpf(1.0f, e);
-  if (tid == 0) {
-    invscale[q * B + b] = ldexpf(1.0f, -e);
-    tpart[q * B + b] = tp;
-  }
-  // This (tile, batch row) owns MFMA columns cidx = (b % rp) * nt + t of
-  // column set b / rp. Work item = one dword (4 bytes) of one 16-byte
-  // operand slice: (t, u, h, gb, dw).
-  const int cset = b / rp;
-  const int cbase = (b % rp) * nt;
-  uint32_t* zop32 = reinterpret_cast<uint32_t*>(zop);
-  for (int item = tid; item < 128 * nt; item += 256) {
-    const int t = item >> 7, rest = item & 127;
-    const int u = rest >> 5, h = (rest >> 4) & 1, gb = (rest >> 2) & 3, dw = rest & 3;
-    uint32_t word = 0u;
-#pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      // Reduction index k of byte (h*16 + e16) of lane group gb; the sign
-      // operand holds k = 32*gA + n at nibble n = 8*plane + i, which is
-      // packed column 128u + 32*gA + 4*i + plane of the word.
-      const int e16 = 4 * dw + e4;
-      const int k = 64 * h + 16 * gb + e16;
-      const int gA = k >> 5, n = k & 31;
-      const int plane = n >> 3, i = n & 7;
-      const float f = (plane == 3) ? 1.0f : (plane == 2 ? -1.0f : (plane == 1 ? -2.0f : -4.0f));
-      const float v = zt[128 * u + 32 * gA + 4 * i + plane] * s * f;
-      word |= fp8_term(v, t) << (8 * e4);
+      for (int s = 0; s < 6; ++s) {
+        const int src = min(first + s, 31);
+        const uint32_t cv = __shfl(code & 63u, src, 32);
+        const int pos = 6 * src - 32 * L6;
+        if (first + s <= 31 && pos > -6 && pos < 32) dw |= pos >= 0 ? (cv << pos) : (cv >> -pos);
+      }
+      const int cc = b * nt + t, cs = cc >> 4, cl = cc & 15;
+      const int ncs = min(16, ncv - 16 * cs);
+      if (m < 8)
+        *reinterpret_cast<uint32_t*>(recp + aop_data_offset(cs, u, g, cl, ncs) + 4 * m) =
+            m < 6 ? dw : 0u;
+      if (m == 0) recp[aop_scale_offset(ncv, cs, g, cl, ncs) + u] = (uint8_t)(127 + e);
     }
-    const int slot = (((q * 4 + u) * cs_count + cset) * 2 + h) * 4 + gb;
-    zop32[(slot * ncv + cbase + t) * 4 + dw] = word;
+    if (j < 3) tp += (orig - v) / f;          // the value the terms represent
   }
+  // Plane-0..2 sum over the tile (fixed-order reduction).
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) tp += __shfl_xor(tp, o, 64);
+  if ((tid & 63) == 0) red[tid >> 6] = tp;
+  __syncthreads();
+  if (tid == 0)
+    *reinterpret_cast<float*>(recp + aop_tpart_offset(ncv) + 4 * b) =
+        ((red[0] + red[1]) + (red[2] + red[3])) + ((red[4] + red[5]) + (red[6] + red[7]));
 }
 
 template <int kMode, int kXKind>
 hipError_t launch_prep_t(const void* x, int64_t B, int64_t K, int d, int D, int hb, const float* c,
-                         const float* M, int64_t L, float* zf32, const OperandPlan& op,
+                         const float* M, int64_t L, float* zf32, const OperandPlan* op,
                          unsigned* tickets, int n_tickets, hipStream_t stream) {
   int k = 0;
   while ((1 << k) < hb) ++k;
   const float norm = (k % 2 == 0) ? ldexpf(1.0f, -k / 2) : (float)(1.0 / sqrt((double)hb));
   const int ext = (int)((L + kTileCols - 1) / kTileCols);
-  hipLaunchKernelGGL((prep_kernel<kMode, kXKind>), dim3((unsigned)ext, (unsigned)B), dim3(256), 0,
-                     stream, x, (int)B, (int)K, d, D, hb, norm, c, M, (int)L, zf32, op.zop,
-                     op.invscale, op.tpart, op.nt, op.rp, op.cs, op.ncv, tickets, n_tickets);
+  uint8_t* aop = op ? op->aop : nullptr;
+  const int nt = op ? op->s.nt : 0, ncv = op ? op->s.ncv : 0, rec = op ? op->s.rec : 0;
+  hipLaunchKernelGGL((prep_kernel<kMode, kXKind>), dim3((unsigned)ext, (unsigned)B), dim3(kThreads), 0,
+                     stream, x, (int)B, (int)K, d, D, k, norm, c, M, (int)L, zf32, aop, nt, ncv,
+                     rec, tickets, n_tickets);
   return hipGetLastError();
 }
 
@@ -227,17 +260,18 @@ hipError_t launch_prep_t(const void* x, int64_t B, int64_t K, int d, int D, int 
 
 OperandShape operand_shape(int64_t B, bool z_bf16) {
   OperandShape s;
-  if (!z_bf16) { s.nt = 4; s.rp = 4; }
-  else if (B <= 10) { s.nt = 3; s.rp = 5; }
-  else { s.nt = 2; s.rp = 8; }
-  s.cs = (int)((B + s.rp - 1) / s.rp);
-  s.ncv = (s.cs == 1) ? (int)B * s.nt : s.rp * s.nt;
+  // 4 terms for fp32 z (3 beyond B = 12, where 4 would need a fourth
+  // 16-column set), 3 for bf16 z: at most 48 columns.
+  s.nt = (z_bf16 || 4 * B > 48) ? 3 : 4;
+  s.ncv = (int)B * s.nt;
+  s.cs = (s.ncv + 15) / 16;
+  s.rec = ((528 * s.ncv + 4 * (int)B) + 15) / 16 * 16;
   return s;
 }
 
-size_t operand_bytes(int64_t B, int64_t L, const OperandShape& s) {
+size_t operand_bytes(int64_t L, const OperandShape& s) {
   const int64_t ext = (L + kTileCols - 1) / kTileCols;
-  return (size_t)ext * 4 * s.cs * 2 * 4 * s.ncv * 16;
+  return (size_t)ext * s.rec + 1024;
 }
 
 hipError_t launch_prep(const void* x, int xkind, int64_t B, int64_t K, int d, int D, int hb,
@@ -245,21 +279,19 @@ hipError_t launch_prep(const void* x, int xkind, int64_t B, int64_t K, int d, in
                        const OperandPlan* op, unsigned* tickets, int n_tickets,
                        hipStream_t stream) {
   (void)hipGetLastError();   // clear a stale error of an earlier runtime call
-  OperandPlan none{};
-  const OperandPlan& o = op ? *op : none;
   if (op == nullptr) {
     switch (xkind) {
-      case 0: return launch_prep_t<0, 0>(x, B, K, d, D, hb, c, M, L, zf32, o, tickets, n_tickets, stream);
-      case 1: return launch_prep_t<0, 1>(x, B, K, d, D, hb, c, M, L, zf32, o, tickets, n_tickets, stream);
-      case 2: return launch_prep_t<0, 2>(x, B, K, d, D, hb, c, M, L, zf32, o, tickets, n_tickets, stream);
-      default: return launch_prep_t<0, 3>(x, B, K, d, D, hb, c, M, L, zf32, o, tickets, n_tickets, stream);
+      case 0: return launch_prep_t<0, 0>(x, B, K, d, D, hb, c, M, L, zf32, op, tickets, n_tickets, stream);
+      case 1: return launch_prep_t<0, 1>(x, B, K, d, D, hb, c, M, L, zf32, op, tickets, n_tickets, stream);
+      case 2: return launch_prep_t<0, 2>(x, B, K, d, D, hb, c, M, L, zf32, op, tickets, n_tickets, stream);
+      default: return launch_prep_t<0, 3>(x, B, K, d, D, hb, c, M, L, zf32, op, tickets, n_tickets, stream);
     }
   }
   switch (xkind) {
-    case 0: return launch_prep_t<1, 0>(x, B, K, d, D, hb, c, M, L, zf32, o, tickets, n_tickets, stream);
-    case 1: return launch_prep_t<1, 1>(x, B, K, d, D, hb, c, M, L, zf32, o, tickets, n_tickets, stream);
-    case 2: return launch_prep_t<1, 2>(x, B, K, d, D, hb, c, M, L, zf32, o, tickets, n_tickets, stream);
-    default: return launch_prep_t<1, 3>(x, B, K, d, D, hb, c, M, L, zf32, o, tickets, n_tickets, stream);
+    case 0: return launch_prep_t<1, 0>(x, B, K, d, D, hb, c, M, L, zf32, op, tickets, n_tickets, stream);
+    case 1: return launch_prep_t<1, 1>(x, B, K, d, D, hb, c, M, L, zf32, op, tickets, n_tickets, stream);
+    case 2: return launch_prep_t<1, 2>(x, B, K, d, D, hb, c, M, L, zf32, op, tickets, n_tickets, stream);
+    default: return launch_prep_t<1, 3>(x, B, K, d, D, hb, c, M, L, zf32, op, tickets, n_tickets, stream);
   }
 }
 

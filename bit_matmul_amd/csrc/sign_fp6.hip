@@ -1,0 +1,395 @@
+// Small-batch sign product (B <= 16) on the gfx950 matrix cores:
+// v_mfma_scale_f32_16x16x128_f8f6f4 with the signs as the FP4 (E2M1) A
+// operand and the lifted activations as the FP6 (E2M3) B operand, whose
+// per-32-value E8M0 block scales ride in the instruction's scale operand.
+//
+// Sign operand. A lane of a 16x16x128 MFMA supplies 32 reduction indices of
+// one row: k = 32g + n for lane group g, in nibble n = 8j + i of its 4-dword
+// A operand. A packed word u of slot (g, r) holds row r's signs for tile
+// columns 128u + 32g + b. One word becomes one whole A operand with four
+// bit operations and no shifts, by splitting its bits into the four planes
+// b = 4i + j:
+//   dword 0 = w & 0x11111111   nibble 0x1 = 0.5 where the bit is set, else 0
+//   dword 1 = w & 0x22222222   nibble 0x2 = 1.0
+//   dword 2 = w & 0x44444444   nibble 0x4 = 2.0
+//   dword 3 = (w & 0x88888888) | 0x22222222   nibble = +1.0 or -1.0 (0xA)
+// so nibble 8j + i meets packed column 128u + 32g + 4i + j. With the sign
+// s = 1 - 2*bit, sum_j s_j z_j = sum_{plane 3} s z + sum_{planes 0-2} z
+// - 2 sum_{planes 0-2} bit z: the activation operand carries z on plane 3
+// and -4z, -2z, -z on planes 0, 1, 2, and the plane-0..2 column sums of z
+// (stored with the operand) are added once per batch row.
+//
+// Activation operand (written by the preparation kernel, layout in
+// lq_internal.h): per tile one record holding, for every MFMA column
+// (batch row b, term t), the FP6 codes of the t-th residual term of
+// 32-value blocks, the blocks' E8M0 scales, and the per-row plane sums.
+//
+// Work split: a workgroup owns P 16-row panels over the whole reduction
+// length (no communication between workgroups). Its W compute wavefronts
+// take the full tiles in chunks of W*TPC tiles, TPC consecutive tiles each,
+// all P panels per tile, so one activation-operand read from LDS feeds P
+// MFMAs. An extra loader wavefront copies each chunk's activation records
+// into LDS with global_load_lds (double-buffered, one chunk ahead) and
+// computes the partial tail tile from registers. The compute wavefronts
+// keep the packed slots of two chunks in flight; since a wavefront waits for
+// its loads in issue order and it issues nothing else, every tile's MFMAs
+// start as soon as that tile's 16-byte slots have arrived.
+// The wavefronts' accumulators are added in LDS in a fixed order, the terms
+// and plane sums combined, and y written: deterministic, no atomics.
+#include <algorithm>
+
+#include "lq_internal.h"
+
+namespace lq {
+namespace {
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+
+template <int U>
+__device__ __forceinline__ f32x4 mfma_fp4_fp6(uint32_t w, const i32x8& b, uint32_t scale, f32x4 c) {
+  i32x8 a;
+  a[0] = (int)(w & 0x11111111u);
+  a[1] = (int)(w & 0x22222222u);
+  a[2] = (int)(w & 0x44444444u);
+  a[3] = (int)((w & 0x88888888u) | 0x22222222u);
+  a[4] = a[5] = a[6] = a[7] = 0;   // unused by an FP4 operand
+  // cbsz = 4: A is FP4 E2M1 (scale 2^0); blgp = 2: B is FP6 E2M3, its block
+  // scale is byte U of `scale`.
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 2, 0, 127, U, (int)scale);
+}
+
+// Workgroup barrier without a memory fence: this wavefront's LDS accesses
+// complete, then s_barrier; the memory clobber keeps the compiler from moving
+// memory accesses across it. (__syncthreads would also wait for every global
+// load in flight, since the loader's LDS copies count as global loads.) LDS
+// copies (global_load_lds) are waited for explicitly by the loader before
+// the barrier that publishes them.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ i32x8 lds_b_operand(const uint8_t* p) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(p);
+  const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
+  i32x8 b;
+  b[0] = (int)lo.x; b[1] = (int)lo.y; b[2] = (int)lo.z; b[3] = (int)lo.w;
+  b[4] = (int)hi.x; b[5] = (int)hi.y; b[6] = 0; b[7] = 0;
+  return b;
+}
+
+template <int P, int CS, int W, int TPC>
+__global__ __launch_bounds__(64 * (W + 1)) void sign_fp6_kernel(
+    const uint8_t* __restrict__ packed, int panels, int64_t panel_bytes, int full_tiles,
+    int tail_bytes, const uint8_t* __restrict__ aop, int rec, int ncv, int B, int nch,
+    int chunk_bytes, const float* __restrict__ row_scale, void* __restrict__ y, int y_bf16, int N) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  constexpr int CT = W * TPC;                       // full tiles per chunk
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int g = lane >> 4, r = lane & 15;
+  const bool loader = wave == W;
+  const int pbase = blockIdx.x * P;
+
+  // This lane's MFMA column in each column set; unused columns read the
+  // set's last column (their products are never read).
+  int boff[CS], soff[CS];
+#pragma unroll
+  for (int cs = 0; cs < CS; ++cs) {
+    const int ncs = max(1, min(16, ncv - 16 * cs));
+    const int col = min(r, ncs - 1);
+    boff[cs] = aop_data_offset(cs, 0, g, col, ncs);
+    soff[cs] = aop_scale_offset(ncv, cs, g, col, ncs);
+  }
+  int u_str[CS];                                    // bytes between the u blocks of a set
+#pragma unroll
+  for (int cs = 0; cs < CS; ++cs) u_str[cs] = 4 * 32 * max(1, min(16, ncv - 16 * cs));
+  const int tpoff = aop_tpart_offset(ncv) + 4 * min(lane, B - 1);
+
+  const uint8_t* prow[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) prow[p] = packed + (int64_t)min(pbase + p, panels - 1) * panel_bytes;
+
+  f32x4 acc[P][CS];
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+#pragma unroll
+    for (int cs = 0; cs < CS; ++cs) acc[p][cs] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+  float tacc = 0.0f;
+
+  uint4 A0[TPC][P], A1[TPC][P];
+  const int last_full = max(full_tiles - 1, 0);
+  // Packed slots of chunk c. Past the last chunk every lane reads the same
+  // 16 bytes instead (one cache line; the registers are not used): the loads
+  // are issued on every path, so that no register ever merges two values (a
+  // merge would make the compiler wait for the loads in flight).
+  auto issue_A = [&](int c, uint4 (&A)[TPC][P]) {
+    const bool live = c < nch;
+#pragma unroll
+    for (int q = 0; q < TPC; ++q) {
+      const int t = min(c * CT + wave * TPC + q, last_full);
+      const int off = live ? t * kTileBytes + 16 * lane : 0;
+#pragma unroll
+      for (int p = 0; p < P; ++p) A[q][p] = *reinterpret_cast<const uint4*>(prow[p] + off);
+    }
+  };
+  // The MFMAs of one tile whose activation record starts at `recp` (LDS).
+  auto tile_mfma = [&](const uint8_t* recp, const uint4 (&S)[P]) {
+    i32x8 bop[CS][4];
+    uint32_t sc[CS];
+#pragma unroll
+    for (int cs = 0; cs < CS; ++cs) {
+      sc[cs] = *reinterpret_cast<const uint32_t*>(recp + soff[cs]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) bop[cs][u] = lds_b_operand(recp + boff[cs] + u * u_str[cs]);
+    }
+    tacc += *reinterpret_cast<const float*>(recp + tpoff);
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+#pragma unroll
+      for (int cs = 0; cs < CS; ++cs) {
+        acc[p][cs] = mfma_fp4_fp6<0>(S[p].x, bop[cs][0], sc[cs], acc[p][cs]);
+        acc[p][cs] = mfma_fp4_fp6<1>(S[p].y, bop[cs][1], sc[cs], acc[p][cs]);
+        acc[p][cs] = mfma_fp4_fp6<2>(S[p].z, bop[cs][2], sc[cs], acc[p][cs]);
+        acc[p][cs] = mfma_fp4_fp6<3>(S[p].w, bop[cs][3], sc[cs], acc[p][cs]);
+      }
+    }
+  };
+  auto dma_chunk = [&](int c, uint8_t* dst) {
+    const int t0 = c * CT;
+    const int bytes = min(CT, full_tiles - t0) * rec;
+    const uint8_t* src = aop + (int64_t)t0 * rec + 16 * lane;
+    for (int off = 0; off < bytes; off += 1024)
+      __builtin_amdgcn_global_load_lds((const void*)(src + off),
+                                       (__attribute__((address_space(3))) void*)(dst + off), 16, 0, 0);
+  };
+
+  // LDS: row scales (1 KB), chunk buffers 0 and 1, the tail tile's record
+  // and slots; the final reduction reuses everything after the row scales.
+  float* rs_lds = reinterpret_cast<float*>(smem);
+  uint8_t* buf0 = smem + 1024;
+  uint8_t* buf1 = buf0 + chunk_bytes;
+
+  // ---- Pipeline. A compute unit serves its vector-memory requests roughly
+  // in order, so the activation records (L2 hits) must be requested before
+  // the HBM traffic that would otherwise delay them: the loader requests
+  // chunks 0 and 1, the tail tile and the row scales first; a barrier then
+  // releases the compute wavefronts' requests for the packed slots of chunks
+  // 0 and 1. After multiplying chunk c, the loader requests chunk c + 2 into
+  // the freed buffer before a barrier that releases the slot requests of
+  // chunk c + 2, so each compute wavefront keeps two chunks of slots
+  // requested and each copy lands a chunk ahead of its use.
+  // The two roles run separate code with the same sequence of barriers, so
+  // the compute wavefronts' waits on their slot loads never include the
+  // loader's copies (which the compiler would otherwise have to assume may
+  // still be in flight). The tail tile (its record and the P panels'
+  // row-major tail bytes) is multiplied by the loader at the end.
+  const bool tail = tail_bytes > 0;
+  uint8_t* trec_lds = buf1 + chunk_bytes;
+  uint8_t* tslot_lds = trec_lds + ((rec + 1023) / 1024) * 1024;
+
+  if (loader) {
+    // Row scales of the workgroup's rows (16 bytes per lane, clamped to N).
+    const int n4 = min(pbase * kPanelRows + 4 * lane, N - 4);
+    __builtin_amdgcn_global_load_lds((const void*)(row_scale + n4),
+                                     (__attribute__((address_space(3))) void*)rs_lds, 16, 0, 0);
+    if (nch > 0) dma_chunk(0, buf0);
+    if (nch > 1) dma_chunk(1, buf1);
+    if (tail) {
+      const uint8_t* trec = aop + (int64_t)full_tiles * rec + 16 * lane;
+      for (int off = 0; off < rec; off += 1024)
+        __builtin_amdgcn_global_load_lds((const void*)(trec + off),
+                                         (__attribute__((address_space(3))) void*)(trec_lds + off), 16, 0, 0);
+      const int tb = kPanelRows * tail_bytes;         // a multiple of 16, at most 1008
+      const int o = min(16 * lane, tb - 16);
+#pragma unroll
+      for (int p = 0; p < P; ++p)
+        __builtin_amdgcn_global_load_lds((const void*)(prow[p] + (int64_t)full_tiles * kTileBytes + o),
+                                         (__attribute__((address_space(3))) void*)(tslot_lds + 1024 * p), 16, 0, 0);
+    }
+    wg_barrier();
+    __builtin_amdgcn_s_waitcnt(0);                    // chunks 0, 1, the tail, the row scales
+    wg_barrier();
+    for (int c = 0; c < nch; c += 2) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {                   // step c + k
+        __builtin_amdgcn_s_waitcnt(0);                // chunk c + k + 1 is in LDS
+        wg_barrier();
+        if (c + k + 2 < nch) dma_chunk(c + k + 2, k == 0 ? buf0 : buf1);
+        wg_barrier();
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    if (tail) {
+      // Slot (g, r) of the tail: bytes 16u + 4g .. + 3 of row r (zero past
+      // the row's tail_bytes), as in load_tail_slot.
+      uint4 TS[P];
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const uint8_t* row = tslot_lds + 1024 * p + r * tail_bytes;
+        uint32_t w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          uint32_t v = 0;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int t = 16 * u + 4 * g + k;
+            const uint32_t byte = row[min(t, tail_bytes - 1)];       // unconditional read
+            v |= (byte & (t < tail_bytes ? 0xFFu : 0u)) << (8 * k);
+          }
+          w[u] = v;
+        }
+        TS[p] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+      tile_mfma(trec_lds, TS);
+    }
+  } else {
+    wg_barrier();
+    issue_A(0, A0);
+    issue_A(1, A1);
+    wg_barrier();
+    // Step c: chunk c is in LDS (`cur`), its slots (A) are requested.
+    auto step = [&](int c, uint4 (&A)[TPC][P], uint8_t* cur) {
+#pragma unroll
+      for (int q = 0; q < TPC; ++q) {
+        const int j = wave * TPC + q;                 // tile within the chunk
+        if (c * CT + j < full_tiles) tile_mfma(cur + j * rec, A[q]);
+      }
+      wg_barrier();                                   // `cur` and A are free
+      wg_barrier();                                   // chunk c + 2 requested
+      issue_A(c + 2, A);
+    };
+    // Unrolled by two for the two register sets; an odd chunk count ends
+    // with one empty step (no tiles).
+    for (int c = 0; c < nch; c += 2) {
+      step(c, A0, buf0);
+      step(c + 1, A1, buf1);
+    }
+  }
+  wg_barrier();                                      // LDS past the row scales is reused below
+
+  // ---- add the wavefronts' accumulators in a fixed order and write y.
+  uint8_t* red_base = buf0;
+  f32x4* red = reinterpret_cast<f32x4*>(red_base);                   // [W+1][P][CS][64]
+  float* tred = reinterpret_cast<float*>(red_base + (W + 1) * P * CS * 64 * 16);   // [W+1][16]
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+#pragma unroll
+    for (int cs = 0; cs < CS; ++cs) red[((wave * P + p) * CS + cs) * 64 + lane] = acc[p][cs];
+  if (lane < 16) tred[wave * 16 + lane] = tacc;
+  wg_barrier();
+
+  // One output (panel p, row, batch row b) per thread and pass: every LDS
+  // read is issued before the sums (fixed order: terms, then wavefronts).
+  const int nt = ncv / B;                           // 1..4
+  const int items = P * B * 16;
+  for (int item = threadIdx.x; item < items; item += 64 * (W + 1)) {
+    const int row = item & 15;
+    const int b = (item >> 4) % B;
+    const int p = (item >> 4) / B;
+    float v[W + 1][4], tv[W + 1];
+#pragma unroll
+    for (int w = 0; w <= W; ++w) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int cc = b * nt + min(t, nt - 1);
+        const int l = 16 * (row >> 2) + (cc & 15);
+        v[w][t] = red[((w * P + p) * CS + (cc >> 4)) * 64 + l][row & 3];
+      }
+      tv[w] = tred[w * 16 + b];
+    }
+    const float rs = rs_lds[p * kPanelRows + row];
+    float acc_s = 0.0f, tp = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t < nt) {
+#pragma unroll
+        for (int w = 0; w <= W; ++w) acc_s += v[w][t];
+      }
+    }
+#pragma unroll
+    for (int w = 0; w <= W; ++w) tp += tv[w];
+    const float out = rs * (acc_s + tp);
+    const int n = (pbase + p) * kPanelRows + row;
+    if (pbase + p < panels) {
+      if (y_bf16)
+        reinterpret_cast<uint16_t*>(y)[(int64_t)b * N + n] = (uint16_t)f32_to_bf16_bits(out);
+      else
+        reinterpret_cast<float*>(y)[(int64_t)b * N + n] = out;
+    }
+  }
+}
+
+template <int P, int CS, int W, int TPC>
+hipError_t launch_fp6_t(const uint8_t* packed, const PackedGeom& g, const OperandPlan& op,
+                        int64_t B, const float* row_scale, void* y, bool y_bf16,
+                        const Fp6Plan& plan, hipStream_t stream) {
+  const dim3 grid((unsigned)plan.groups);
+  const dim3 block(64 * (W + 1));
+  if (plan.lds_bytes > 160 * 1024) return hipErrorInvalidValue;   // a compute unit's LDS
+  // Dynamic LDS beyond the default 64 KB limit has to be allowed per kernel.
+  static size_t allowed = 0;
+  if (plan.lds_bytes > allowed) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&sign_fp6_kernel<P, CS, W, TPC>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)plan.lds_bytes);
+    if (e != hipSuccess) return e;
+    allowed = plan.lds_bytes;
+  }
+  hipLaunchKernelGGL((sign_fp6_kernel<P, CS, W, TPC>), grid, block, plan.lds_bytes, stream,
+                     packed, (int)g.panels, g.panel_bytes, g.full_tiles, g.tail_bytes, op.aop,
+                     op.s.rec, op.s.ncv, (int)B, plan.nch, plan.chunk_bytes, row_scale, y,
+                     y_bf16 ? 1 : 0, (int)g.N);
+  return hipGetLastError();
+}
+
+// Compute wavefronts and tiles per wavefront per chunk for each column-set
+// count: wider operands take fewer tiles per chunk so that two chunks of
+// activation records fit in LDS.
+// (Registers: with W + 1 wavefronts a SIMD runs up to ceil((W + 1) / 4) of
+// them, each with 512 / that many VGPRs.)
+constexpr int waves_for(int p, int cs) { return cs == 1 ? (p >= 4 ? 4 : 8) : (cs == 2 && p < 8 ? 4 : 2); }
+constexpr int tiles_for(int p, int cs) { return cs == 1 && p <= 4 ? 3 : 1; }
+
+}  // namespace
+
+Fp6Plan plan_fp6(int64_t B, const PackedGeom& g, const OperandShape& s) {
+  (void)B;
+  Fp6Plan p;
+  // Panels per workgroup: enough workgroups to cover the 256 compute units,
+  // as many panels as possible sharing each activation-operand read.
+  p.p = 1;
+  for (int cand : {8, 4, 2}) {
+    if (cand == 8 && s.cs >= 3) continue;      // register budget
+    if ((g.panels + cand - 1) / cand >= 200) { p.p = cand; break; }
+  }
+  p.w = waves_for(p.p, s.cs);
+  const int budget = 112 * 1024;   // two chunks of activation records
+  p.tpc = 1;
+  if (tiles_for(p.p, s.cs) == 3 && 2 * p.w * 3 * s.rec + 2048 <= budget) p.tpc = 3;
+  const int ct = p.w * p.tpc;
+  p.nch = (g.full_tiles + ct - 1) / ct;
+  p.chunk_bytes = ((ct * s.rec + 1023) / 1024) * 1024;
+  const size_t red = (size_t)(p.w + 1) * p.p * s.cs * 64 * 16 + (size_t)(p.w + 1) * 16 * 4;
+  const size_t tail = (size_t)((s.rec + 1023) / 1024) * 1024 + (size_t)1024 * p.p;
+  p.lds_bytes = 1024 + std::max((size_t)2 * p.chunk_bytes + tail, red);
+  p.groups = (int)((g.panels + p.p - 1) / p.p);
+  return p;
+}
+
+hipError_t launch_sign_fp6(const uint8_t* packed, const PackedGeom& g, const OperandPlan& op,
+                           int64_t B, const float* row_scale, void* y, bool y_bf16,
+                           const Fp6Plan& plan, hipStream_t stream) {
+  (void)hipGetLastError();   // clear a stale error of an earlier runtime call
+#define LQ_FP6_CASE(P_, CS_, TPC_)                                                          \
+  if (plan.p == P_ && op.s.cs == CS_ && plan.tpc == TPC_ && plan.w == waves_for(P_, CS_))   \
+    return launch_fp6_t<P_, CS_, waves_for(P_, CS_), TPC_>(packed, g, op, B, row_scale, y,  \
+                                                           y_bf16, plan, stream);
+  LQ_FP6_CASE(1, 1, 3) LQ_FP6_CASE(2, 1, 3) LQ_FP6_CASE(4, 1, 3)
+  LQ_FP6_CASE(1, 1, 1) LQ_FP6_CASE(2, 1, 1) LQ_FP6_CASE(4, 1, 1) LQ_FP6_CASE(8, 1, 1)
+  LQ_FP6_CASE(1, 2, 1) LQ_FP6_CASE(2, 2, 1) LQ_FP6_CASE(4, 2, 1) LQ_FP6_CASE(8, 2, 1)
+  LQ_FP6_CASE(1, 3, 1) LQ_FP6_CASE(2, 3, 1) LQ_FP6_CASE(4, 3, 1)
+#undef LQ_FP6_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lq

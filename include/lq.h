@@ -81,12 +81,12 @@ typedef enum lq_algo {
   LQ_ALGO_AUTO = 0,         /* the library's choice (what lq_sign_gemm does) */
   LQ_ALGO_VALU = 1,         /* fp32 sign-select on the vector ALUs; any z dtype,
                                B <= 16 per pass; exact fp32 accumulation */
-  LQ_ALGO_MFMA_SMALL = 2,   /* B <= 16: packed signs fed to the FP4 x FP8
+  LQ_ALGO_MFMA_SMALL = 2,   /* B <= 16: packed signs fed to the FP4 x FP6
                                matrix cores as bit planes; z carried as a sum of
-                               power-of-two-scaled fp8 terms (4 terms for fp32 z,
-                               3 for bf16 z and B <= 10, 2 for B = 11..16; worst
-                               relative error per value about 2^-16 / 2^-12 /
-                               2^-8); fp32 accumulate */
+                               FP6 (E2M3) residual terms with a power-of-two
+                               scale per 32-value block (4 terms for fp32 z,
+                               3 for bf16 z; about 2^-20 / 2^-15 relative);
+                               fp32 accumulate */
   LQ_ALGO_MFMA_LARGE = 3    /* any B: tiled GEMM on bf16 matrix cores, z as bf16
                                (bf16 z) or as a bf16 hi+lo pair (fp32 z) */
 } lq_algo;
