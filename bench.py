@@ -8,8 +8,10 @@ activations, each a full lq_linear call (whitening, lift, sign product).
 Every step uses the next of `--weight-sets` distinct copies of the packed
 weights, so the 52.9 MB of packed bits a step reads cannot stay in the
 256 MB Infinity Cache (like a real 32-layer model, whose weights are all
-different). The steps are captured once in a HIP graph and replayed, so the
-timing is the GPU's, not Python's launch rate.
+different). The K timed steps are captured once in a HIP graph and replayed;
+the sign-product kernel durations come from an eager replay of the same K
+steps right after, each launch timed by events its own dispatch records
+(recording them inside the timed region would slow it down).
 
 Printed (one JSON line): whole-step packed-weight throughput in GB/s
 (`value`), the roofline of the dominant kernel (the sign product), timed
@@ -20,6 +22,15 @@ CPU oracle's rate on a bounded sample of the same workload. With
 Synthetic data: packed weights are uniformly random bytes (i.e. independent
 fair signs), M ~ N(0, 1/D), row scales ~ U[0.5, 1.5], channel scales ~
 U[0.8, 1.2], activations ~ N(0, 1) rounded to bf16.
+
+Profiling helpers (the summaries under profiles/ are made with these):
+  --pmc-workload          a 256 MiB device copy (the counter calibration),
+                          then a few eager decode steps; run it under
+                          rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE
+  --summarize-pmc F W     per-kernel FETCH_SIZE / WRITE_SIZE of those two
+                          runs (their output directories), scaled by the copy
+  --summarize-stats DIR   per-kernel calls and durations of a
+                          rocprofv3 --kernel-trace --stats run
 """
 from __future__ import annotations
 
@@ -32,6 +43,10 @@ import time
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+ROOT = os.path.dirname(os.path.abspath(__file__))
+SIGN_KERNEL = "sign_fp6_kernel"
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_sign_fp6_llama3_8b_mlp_b1.txt")
+COPY_BYTES = 256 << 20         # the calibration copy of --pmc-workload
 
 
 def parse_args():
@@ -45,8 +60,179 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--prefill", action="store_true",
                    help="also time the 2048-token prefill layer (TFLOP/s)")
-    p.add_argument("--eager", action="store_true", help="launch eagerly instead of a HIP graph")
+    p.add_argument("--eager", action="store_true",
+                   help="launch the timed steps eagerly, each sign product timed by its own "
+                        "dispatch events (slows the launches down)")
+    p.add_argument("--pmc-workload", action="store_true",
+                   help="calibration copy plus a few eager decode steps, for rocprofv3 --pmc")
+    p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    p.add_argument("--summarize-stats", metavar="DIR")
+    p.add_argument("--profiled-steps", type=int, default=None,
+                   help="with --summarize-stats: the --steps of the profiled run")
     return p.parse_args()
+
+
+# ------------------------------------------------------------ profiling aids
+
+def kernel_sources_hash():
+    """Hash of the HIP sources of the decode path (a counter summary taken
+    on other sources is stale)."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bit_matmul_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def _read_rocprof_rows(d, kind):
+    """Rows of a rocprofv3 output directory: ('pmc') counter rows as dicts
+    with kernel, counter, value; ('trace') kernel dispatches with name and
+    duration in ns. Reads the CSV files if present, else the SQLite db."""
+    import csv
+    import glob
+    import sqlite3
+    rows = []
+    if kind == "pmc":
+        for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(fn) as f:
+                for r in csv.DictReader(f):
+                    rows.append(dict(kernel=r.get("Kernel_Name", ""), counter=r.get("Counter_Name", ""),
+                                     value=float(r.get("Counter_Value", "nan")),
+                                     dispatch=r.get("Dispatch_Id", "")))
+        if rows:
+            return rows
+        for fn in glob.glob(os.path.join(d, "**", "*results.db"), recursive=True):
+            db = sqlite3.connect(fn)
+            q = ("select k.name, p.counter_name, p.value, p.dispatch_id from pmc_events p "
+                 "join kernels k on k.dispatch_id = p.dispatch_id")
+            try:
+                for name, cn, v, did in db.execute(q):
+                    rows.append(dict(kernel=name, counter=cn, value=float(v), dispatch=did))
+            except sqlite3.Error:
+                pass
+        return rows
+    for fn in glob.glob(os.path.join(d, "**", "*results.db"), recursive=True):
+        db = sqlite3.connect(fn)
+        for name, dur in db.execute("select name, duration from kernels"):
+            rows.append(dict(kernel=name, duration=float(dur)))
+    for fn in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                rows.append(dict(kernel=r["Kernel_Name"],
+                                 duration=float(r["End_Timestamp"]) - float(r["Start_Timestamp"])))
+    return rows
+
+
+def _short(name):
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return name.split("(")[0].strip()
+
+
+def summarize_stats(d, steps=None):
+    """Per-kernel calls and durations. With `steps` (the --steps of the
+    profiled bench run), also the sign-product dispatches split by phase:
+    the graph's timed replay and the eager replay whose dispatch events give
+    bench.py's kernel durations (the last 3 * steps sign launches)."""
+    rows = _read_rocprof_rows(d, "trace")
+    agg = {}
+    for r in rows:
+        a = agg.setdefault(_short(r["kernel"]), [])
+        a.append(r["duration"])
+    lines = ["kernel | calls | avg us | min us | max us | total us"]
+    for k, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{k} | {len(v)} | {sum(v) / len(v) / 1e3:.3f} | {min(v) / 1e3:.3f} | "
+                     f"{max(v) / 1e3:.3f} | {sum(v) / 1e3:.1f}")
+    if steps:
+        import glob
+        import sqlite3
+        sign = []
+        for fn in glob.glob(os.path.join(d, "**", "*results.db"), recursive=True):
+            db = sqlite3.connect(fn)
+            sign += [(s0, e0) for n, s0, e0 in db.execute("select name, start, end from kernels")
+                     if SIGN_KERNEL in n]
+        sign.sort()
+        dur = [e0 - s0 for s0, e0 in sign]
+        n = 3 * steps
+        if len(dur) >= 2 * n:
+            timed, replay = dur[-2 * n:-n], dur[-n:]
+            lines.append("")
+            lines.append(f"{SIGN_KERNEL}, graph timed replay ({n} launches): avg "
+                         f"{sum(timed) / n / 1e3:.3f} us")
+            lines.append(f"{SIGN_KERNEL}, eager replay with dispatch events ({n} launches): avg "
+                         f"{sum(replay) / n / 1e3:.3f} us")
+    return "\n".join(lines)
+
+
+def summarize_pmc(fetch_dir, write_dir):
+    """Per-kernel average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) and the
+    calibration factors: the known size of the --pmc-workload copy over what
+    each counter reads for that copy (its largest copy dispatch)."""
+    out, copy = {}, {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = {}
+        for r in _read_rocprof_rows(d, "pmc"):
+            if r["counter"] != counter:
+                continue
+            k = _short(r["kernel"])
+            per.setdefault(k, []).append(r["value"])
+            if "copyBuffer" in k:
+                copy[counter] = max(copy.get(counter, 0.0), r["value"])
+        out[counter] = {k: sum(v) / len(v) for k, v in per.items() if "copyBuffer" not in k}
+    lines = [f"sources {kernel_sources_hash()}",
+             f"copy_bytes {COPY_BYTES}"]
+    if "FETCH_SIZE" in copy and "WRITE_SIZE" in copy:
+        lines.append(f"copy_fetch_kib {copy['FETCH_SIZE']:.1f}")
+        lines.append(f"copy_write_kib {copy['WRITE_SIZE']:.1f}")
+        lines.append(f"fetch_factor {COPY_BYTES / 1024.0 / copy['FETCH_SIZE']:.4f}")
+        lines.append(f"write_factor {COPY_BYTES / 1024.0 / copy['WRITE_SIZE']:.4f}")
+    for k in sorted(out["FETCH_SIZE"]):
+        lines.append(f"kernel {k} fetch_kib {out['FETCH_SIZE'][k]:.1f} "
+                     f"write_kib {out['WRITE_SIZE'].get(k, float('nan')):.1f}")
+    return "\n".join(lines)
+
+
+def traffic_from_summary():
+    """HBM bytes per launch of the sign product from the committed counter
+    summary, or None when there is none or it was taken on other sources."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            text = f.read()
+    except OSError:
+        return None
+    import re
+    kv, kern = {}, {}
+    for line in text.splitlines():
+        parts = line.split()
+        if len(parts) >= 2 and parts[0] in ("sources", "fetch_factor", "write_factor"):
+            kv[parts[0]] = parts[1]
+        m = re.match(r"^kernel (.*) fetch_kib ([0-9.]+) write_kib ([0-9.]+)$", line)
+        if m and SIGN_KERNEL in m.group(1):
+            kern[m.group(1)] = (float(m.group(2)), float(m.group(3)))
+    if kv.get("sources") != kernel_sources_hash() or not kern:
+        return None
+    ff, wf = float(kv["fetch_factor"]), float(kv["write_factor"])
+    f = sum(v[0] for v in kern.values()) / len(kern)
+    w = sum(v[1] for v in kern.values()) / len(kern)
+    return round((f * ff + w * wf) * 1024.0, 1)
+
+
+def pmc_workload(torch, lq):
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    specs, layers, x_in, ys, ws, M = build_decode_case(torch, lq, 4)
+    for i in range(3):
+        for l in layers[i % len(layers)]:
+            x = x_in["down"] if l["name"] == "down" else x_in["gate"]
+            lq.lq_linear(l["struct"], x, 1, ys[l["name"]], ws)
+    torch.cuda.synchronize()
+    print("pmc workload done", flush=True)
 
 
 class HipEvents:
@@ -147,13 +333,15 @@ def run_decode(args, torch, lq, ev):
         torch.cuda.synchronize()
         t1 = time.perf_counter()
     lq.lq_profile_events([], [])
-    timing = "hipEvents around every sign-product launch inside the timed region"
+    timing = ("hipEvents recorded by the dispatch of every sign-product launch inside the "
+              "timed region")
     try:
         durs = [ev.elapsed_ms(a, b) for a, b in zip(starts, stops)]
     except RuntimeError:
         # Fallback: the same K steps launched eagerly right after the timed
         # region, each sign-product kernel bracketed by events.
-        timing = "hipEvents around every sign-product launch of an eager replay of the K steps"
+        timing = ("hipEvents recorded by the dispatch of every sign-product launch of an eager "
+                  "replay of the K steps")
         lq.lq_profile_events(starts, stops)
         for i in range(K):
             step(i)
@@ -246,16 +434,28 @@ def cpu_baseline(budget_s):
 
     rows = 64
     nb, t = run(rows)
+    reps = 1
     if t < budget_s / 4:
-        rows = int(min(4096, max(64, rows * (budget_s / 2) / max(t, 1e-3))) // 16 * 16)
+        rows = int(min(4096, max(64, rows * budget_s / max(t, 1e-3))) // 16 * 16)
         nb, t = run(rows)
+        reps = max(1, int(budget_s / max(t, 1e-3)))        # repeat the sample up to the budget
+        for _ in range(reps - 1):
+            nb2, t2 = run(rows)
+            nb += nb2
+            t += t2
     return dict(value=round(nb / t / 1e9, 6), unit="GB/s", cores=threads, kind="oracle",
                 sample=f"oracle linear() on the first {rows} rows of each of gate, up and down "
-                       f"(B=1, d=10, D=24): {nb} packed bytes in {t:.2f} s")
+                       f"(B=1, d=10, D=24), {reps} times: {nb} packed bytes in {t:.2f} s")
 
 
 def main():
     args = parse_args()
+    if args.summarize_stats:
+        print(summarize_stats(args.summarize_stats, args.profiled_steps))
+        return
+    if args.summarize_pmc:
+        print(summarize_pmc(*args.summarize_pmc))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures a single GPU: this build has no multi-GPU path "
@@ -267,6 +467,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.pmc_workload:
+        pmc_workload(torch, lq)
+        return
     ev = HipEvents()
     dec = run_decode(args, torch, lq, ev)
     out = {
@@ -293,12 +496,12 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "sign product (lq sign_fp4_kernel)",
+            "kernel": f"sign product (lq {SIGN_KERNEL})",
             "achieved": round(dec["achieved"], 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dec["achieved"] / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic_from_summary(),
             "avg_launch_us": round(dec["kern_ms"] * 1e3, 3),
             "per_layer_avg_us": dec["per_proj_us"],
             "timing": dec["timing"],

@@ -11,6 +11,13 @@
 
 #include "lq_internal.h"
 
+namespace lq {
+LaunchEvents& launch_events() {
+  thread_local LaunchEvents ev;
+  return ev;
+}
+}  // namespace lq
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
@@ -63,9 +70,11 @@ ProfileRing& profile_ring() {
   return ring;
 }
 
-// Launch `fn` (which enqueues one kernel) between the ring's next event pair.
+// Launch `fn` (which enqueues one sign-product kernel) with the ring's next
+// event pair pending: the kernel's dispatch records them at its start and end.
 template <typename Fn>
 hipError_t profiled(hipStream_t stream, Fn fn) {
+  (void)stream;
   ProfileRing& ring = profile_ring();
   std::unique_lock<std::mutex> lock(ring.mu);
   if (ring.starts.empty()) {
@@ -74,11 +83,12 @@ hipError_t profiled(hipStream_t stream, Fn fn) {
   }
   const size_t i = ring.next;
   ring.next = (ring.next + 1) % ring.starts.size();
-  hipError_t e = hipEventRecord(ring.starts[i], stream);
-  if (e != hipSuccess) return e;
-  e = fn();
-  if (e != hipSuccess) return e;
-  return hipEventRecord(ring.stops[i], stream);
+  lq::LaunchEvents& ev = lq::launch_events();
+  ev.start = ring.starts[i];
+  ev.stop = ring.stops[i];
+  const hipError_t e = fn();
+  ev = lq::LaunchEvents{};
+  return e;
 }
 
 lq_algo resolve_algo(lq_algo algo, lq_dtype ztype, int64_t B) {

@@ -2,6 +2,7 @@
 // launchers that the C ABI (api.cpp) calls. Not installed, not part of the ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -136,6 +137,28 @@ __device__ __forceinline__ bool last_ticket(unsigned* ticket, int count, int* fl
   const bool last = *flag != 0;
   if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   return last;
+}
+
+// Timing of the sign-product kernels (the C ABI's lq_profile_events): when
+// a pair of events is pending for the calling thread, the next sign-product
+// launch takes it, and the events are recorded by the dispatch itself at the
+// kernel's start and end (hipExtLaunchKernelGGL), as a profiler times it.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents& launch_events();   // thread-local, defined with the C ABI
+
+template <typename Kernel, typename... Args>
+hipError_t launch_timed(Kernel kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                        Args... args) {
+  LaunchEvents& ev = launch_events();
+  if (ev.start != nullptr) {
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, stream, ev.start, ev.stop, 0u, args...);
+    ev = LaunchEvents{};
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, lds, stream, args...);
+  }
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- launchers

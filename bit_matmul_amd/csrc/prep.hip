@@ -45,6 +45,29 @@ __device__ __forceinline__ float half_wave_max(float v) {
   return v;
 }
 
+// Value of lane ^ X (X a power of two up to 32): DPP for 1 and 2, a
+// swizzle for 4..16 (within 32 lanes), a permute for 32.
+template <int X>
+__device__ __forceinline__ float lane_xor(float v) {
+  const int i = __float_as_int(v);
+  if constexpr (X == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, i, 0xB1, 0xF, 0xF, false));
+  else if constexpr (X == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, i, 0x4E, 0xF, 0xF, false));
+  else if constexpr (X <= 16) return __int_as_float(__builtin_amdgcn_ds_swizzle(i, 0x1F | (X << 10)));
+  else return __shfl_xor(v, X, 64);
+}
+
+// One cross-lane butterfly stage over the 16 registers: all exchanges are
+// issued before any is used.
+template <int X>
+__device__ __forceinline__ void lane_stage(float (&a)[16], int lane) {
+  float p[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) p[k] = lane_xor<X>(a[k]);
+  const bool upper = (lane & X) != 0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) a[k] = upper ? p[k] - a[k] : a[k] + p[k];
+}
+
 // In-place fast Walsh-Hadamard transform (unnormalised) of every 2^lhb-value
 // block of the 1024 values xs[0..1023], by one wavefront: lane l holds
 // xs[16l + k] (k = 0..15); stages with stride below 16 pair registers, the
@@ -70,18 +93,12 @@ __device__ __forceinline__ void wave_fwht_1024(float* xs, int lhb, int lane) {
         }
     }
   }
-#pragma unroll
-  for (int s = 4; s < 10; ++s) {
-    if (s < lhb) {
-      const int lb = 1 << (s - 4);
-      const bool upper = (lane & lb) != 0;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const float p = __shfl_xor(a[k], lb, 64);
-        a[k] = upper ? p - a[k] : a[k] + p;
-      }
-    }
-  }
+  if (lhb > 4) lane_stage<1>(a, lane);
+  if (lhb > 5) lane_stage<2>(a, lane);
+  if (lhb > 6) lane_stage<4>(a, lane);
+  if (lhb > 7) lane_stage<8>(a, lane);
+  if (lhb > 8) lane_stage<16>(a, lane);
+  if (lhb > 9) lane_stage<32>(a, lane);
   float4* dst = reinterpret_cast<float4*>(xs + 16 * lane);
 #pragma unroll
   for (int i = 0; i < 4; ++i) dst[i] = make_float4(a[4 * i], a[4 * i + 1], a[4 * i + 2], a[4 * i + 3]);
@@ -213,13 +230,16 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
       const int e = e2m3_block_exponent(half_wave_max(fabsf(v)));
       const uint32_t code = e2m3_encode(ldexpf(v, -e));
       v -= ldexpf(e2m3_decode(code), e);
+      // All six exchanges first, then the (branch-free) assembly.
+      uint32_t cv[6];
+#pragma unroll
+      for (int s6 = 0; s6 < 6; ++s6) cv[s6] = __shfl(code & 63u, min(first + s6, 31), 32);
       uint32_t dw = 0u;
 #pragma unroll
-      for (int s = 0; s < 6; ++s) {
-        const int src = min(first + s, 31);
-        const uint32_t cv = __shfl(code & 63u, src, 32);
-        const int pos = 6 * src - 32 * L6;
-        if (first + s <= 31 && pos > -6 && pos < 32) dw |= pos >= 0 ? (cv << pos) : (cv >> -pos);
+      for (int s6 = 0; s6 < 6; ++s6) {
+        const int pos = 6 * (first + s6) - 32 * L6;    // bit of the code within dword L6
+        const uint32_t lo = pos >= 0 ? (cv[s6] << (pos & 31)) : (cv[s6] >> ((-pos) & 31));
+        dw |= (first + s6 <= 31 && pos < 32) ? lo : 0u;
       }
       const int cc = b * nt + t, cs = cc >> 4, cl = cc & 15;
       const int ncs = min(16, ncv - 16 * cs);

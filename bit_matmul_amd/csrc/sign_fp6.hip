@@ -335,11 +335,10 @@ hipError_t launch_fp6_t(const uint8_t* packed, const PackedGeom& g, const Operan
     if (e != hipSuccess) return e;
     allowed = plan.lds_bytes;
   }
-  hipLaunchKernelGGL((sign_fp6_kernel<P, CS, W, TPC>), grid, block, plan.lds_bytes, stream,
-                     packed, (int)g.panels, g.panel_bytes, g.full_tiles, g.tail_bytes, op.aop,
-                     op.s.rec, op.s.ncv, (int)B, plan.nch, plan.chunk_bytes, row_scale, y,
-                     y_bf16 ? 1 : 0, (int)g.N);
-  return hipGetLastError();
+  return launch_timed(sign_fp6_kernel<P, CS, W, TPC>, grid, block, plan.lds_bytes, stream,
+                      packed, (int)g.panels, g.panel_bytes, g.full_tiles, g.tail_bytes, op.aop,
+                      op.s.rec, op.s.ncv, (int)B, plan.nch, plan.chunk_bytes, row_scale, y,
+                      y_bf16 ? 1 : 0, (int)g.N);
 }
 
 // Compute wavefronts and tiles per wavefront per chunk for each column-set

@@ -162,14 +162,12 @@ hipError_t launch_large_ppw(const uint8_t* packed, const PackedGeom& g, const vo
   (void)hipGetLastError();   // clear a stale error of an earlier runtime call
   const dim3 grid((unsigned)((g.panels + 4 * PPW - 1) / (4 * PPW)), (unsigned)((B + 63) / 64));
   if (z_bf16)
-    hipLaunchKernelGGL((sign_mfma_large_kernel<true, 1, PPW, kYBF16>), grid, dim3(256), 0, stream,
-                       packed, g.panels, g.panel_bytes, g.full_tiles, g.tail_bytes, g.ext_tiles, z,
-                       B, g.L, row_scale, y, g.N);
-  else
-    hipLaunchKernelGGL((sign_mfma_large_kernel<false, 2, PPW, kYBF16>), grid, dim3(256), 0, stream,
-                       packed, g.panels, g.panel_bytes, g.full_tiles, g.tail_bytes, g.ext_tiles, z,
-                       B, g.L, row_scale, y, g.N);
-  return hipGetLastError();
+    return launch_timed(sign_mfma_large_kernel<true, 1, PPW, kYBF16>, grid, dim3(256), 0, stream,
+                        packed, g.panels, g.panel_bytes, g.full_tiles, g.tail_bytes, g.ext_tiles, z,
+                        B, g.L, row_scale, y, g.N);
+  return launch_timed(sign_mfma_large_kernel<false, 2, PPW, kYBF16>, grid, dim3(256), 0, stream,
+                      packed, g.panels, g.panel_bytes, g.full_tiles, g.tail_bytes, g.ext_tiles, z,
+                      B, g.L, row_scale, y, g.N);
 }
 
 }  // namespace

@@ -173,14 +173,12 @@ hipError_t launch_valu_bt(const uint8_t* packed, const PackedGeom& g, const void
   const dim3 grid((unsigned)((g.panels + 3) / 4), (unsigned)plan.ksplit, (unsigned)((B + BT - 1) / BT));
   const size_t lds = ((size_t)BT * TPS * 576 + 1) * sizeof(float);
   if (z_bf16)
-    hipLaunchKernelGGL((sign_valu_kernel<BT, TPS, true>), grid, dim3(256), lds, stream, packed,
-                       g.panels, g.panel_bytes, g.full_tiles, g.tail_bytes, g.ext_tiles, z, B, g.L,
-                       row_scale, y, y_bf16 ? 1 : 0, g.N, partial, tickets, plan.ksplit);
-  else
-    hipLaunchKernelGGL((sign_valu_kernel<BT, TPS, false>), grid, dim3(256), lds, stream, packed,
-                       g.panels, g.panel_bytes, g.full_tiles, g.tail_bytes, g.ext_tiles, z, B, g.L,
-                       row_scale, y, y_bf16 ? 1 : 0, g.N, partial, tickets, plan.ksplit);
-  return hipGetLastError();
+    return launch_timed(sign_valu_kernel<BT, TPS, true>, grid, dim3(256), lds, stream, packed,
+                        g.panels, g.panel_bytes, g.full_tiles, g.tail_bytes, g.ext_tiles, z, B, g.L,
+                        row_scale, y, y_bf16 ? 1 : 0, g.N, partial, tickets, plan.ksplit);
+  return launch_timed(sign_valu_kernel<BT, TPS, false>, grid, dim3(256), lds, stream, packed,
+                      g.panels, g.panel_bytes, g.full_tiles, g.tail_bytes, g.ext_tiles, z, B, g.L,
+                      row_scale, y, y_bf16 ? 1 : 0, g.N, partial, tickets, plan.ksplit);
 }
 
 }  // namespace

@@ -195,11 +195,11 @@ lq_status lq_linear(const lq_layer* layer, const void* x, lq_dtype xtype, int64_
  * Profiling aid: time the sign-product kernel itself. `starts` and `stops`
  * are host arrays of `count` hipEvent_t handles (passed as void*) created by
  * the caller. While set, every sign-product kernel launched by lq_sign_gemm,
- * lq_sign_gemm_ex or lq_linear is bracketed by hipEventRecord(starts[i]) and
- * hipEventRecord(stops[i]) on the call's stream, i = 0, 1, 2, ... wrapping
- * modulo `count` (the split-K epilogue and the whitening/lift kernels are
- * outside the brackets). Do not set the ring while capturing a stream into a
- * graph: such event records cannot be timed. count == 0 clears the ring (the
+ * lq_sign_gemm_ex or lq_linear records starts[i] and stops[i] at its own
+ * start and end (the events ride on the kernel's dispatch, as in
+ * hipExtLaunchKernelGGL, so they time the kernel alone, as a profiler does),
+ * i = 0, 1, 2, ... wrapping modulo `count` (the preparation kernels are not
+ * timed). Do not set the ring while capturing a stream into a graph. count == 0 clears the ring (the
  * arrays may then be NULL); calling again restarts at slot 0. The ring is
  * process-wide and guarded by a lock; the caller keeps the events alive
  * while it is set. Errors: INVALID_ARG for count < 0 or NULL arrays with
