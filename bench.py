@@ -292,7 +292,7 @@ def build_decode_case(torch, lq, n_sets, seed=0):
     }
     ys = {p: torch.empty((1, s.N), dtype=torch.bfloat16, device=dev) for p, s in specs}
     ws_bytes = max(lq.lq_linear_workspace_size(layers[0][i]["struct"], 1, torch.bfloat16) for i in range(3))
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)      # zeroed control area
     return specs, layers, x_in, ys, ws, M
 
 
@@ -381,7 +381,7 @@ def run_prefill(args, torch, lq, ev, steps=10):
     st = lq.layer_struct(s.N, s.K, s.d, s.D, s.hb, packed, M, c, r)
     x = torch.randn(B, s.K, device=dev, generator=gen).to(torch.bfloat16)
     y = torch.empty(B, s.N, dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(lq.lq_linear_workspace_size(st, B, torch.bfloat16), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(lq.lq_linear_workspace_size(st, B, torch.bfloat16), dtype=torch.uint8, device=dev)
     for _ in range(2):
         lq.lq_linear(st, x, B, y, ws)
     torch.cuda.synchronize()

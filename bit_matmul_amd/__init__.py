@@ -14,15 +14,18 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import (LQ_ALGO_AUTO, LQ_ALGO_MFMA_LARGE, LQ_ALGO_MFMA_SMALL, LQ_ALGO_VALU,
-                   LQ_BF16, LQ_F32, LQ_MAX_D, LQ_MAX_HB, LQError, LQLayer)
+from ._lib import (LQ_ALGO_AUTO, LQ_ALGO_FUSED, LQ_ALGO_MFMA_LARGE, LQ_ALGO_MFMA_SMALL,
+                   LQ_ALGO_VALU, LQ_BF16, LQ_F32, LQ_MAX_D, LQ_MAX_HB, LQ_WS_CONTROL_BYTES,
+                   LQ_WS_ERROR_WORD, LQError, LQLayer)
 
 __all__ = [
     "lq_version", "lq_packed_size", "lq_pack_signs", "lq_unpack_signs", "lq_hadamard_scale",
     "lq_lift_activations", "lq_sign_gemm_workspace_size", "lq_sign_gemm", "lq_sign_gemm_ex",
-    "lq_linear_workspace_size", "lq_linear", "lq_profile_events", "layer_struct", "LQError", "LQLayer",
+    "lq_linear_workspace_size", "lq_linear", "lq_linear_workspace_size_ex", "lq_linear_ex",
+    "lq_workspace_init", "lq_profile_events", "layer_struct", "LQError", "LQLayer",
     "LQ_F32", "LQ_BF16", "LQ_ALGO_AUTO", "LQ_ALGO_VALU", "LQ_ALGO_MFMA_SMALL",
-    "LQ_ALGO_MFMA_LARGE", "LQ_MAX_D", "LQ_MAX_HB", "library_path",
+    "LQ_ALGO_MFMA_LARGE", "LQ_ALGO_FUSED", "LQ_MAX_D", "LQ_MAX_HB", "LQ_WS_CONTROL_BYTES",
+    "LQ_WS_ERROR_WORD", "library_path",
 ]
 
 _DTYPES = {torch.float32: LQ_F32, torch.bfloat16: LQ_BF16}
@@ -133,6 +136,28 @@ def lq_linear(layer: LQLayer, x, B, y, ws=None, stream=None) -> None:
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(_lib.LIB.lq_linear(ctypes.byref(layer), _dev(x, "x"), _dtype(x, "x"), B, _dev(y, "y"),
                               _dtype(y, "y"), ws_ptr, ws_bytes, _stream(stream)), "lq_linear")
+
+
+def lq_linear_workspace_size_ex(layer: LQLayer, B, xtype, algo) -> int:
+    out = ctypes.c_size_t()
+    xt = _DTYPES[xtype] if isinstance(xtype, torch.dtype) else int(xtype)
+    _check(_lib.LIB.lq_linear_workspace_size_ex(ctypes.byref(layer), B, xt, algo, ctypes.byref(out)),
+           "lq_linear_workspace_size_ex")
+    return out.value
+
+
+def lq_linear_ex(layer: LQLayer, x, B, y, algo, ws=None, stream=None) -> None:
+    ws_ptr = _opt(ws, "ws")
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.LIB.lq_linear_ex(ctypes.byref(layer), _dev(x, "x"), _dtype(x, "x"), B, _dev(y, "y"),
+                                 _dtype(y, "y"), algo, ws_ptr, ws_bytes, _stream(stream)),
+           "lq_linear_ex")
+
+
+def lq_workspace_init(ws, stream=None) -> None:
+    """Zero the control area of a workspace before its first use."""
+    _check(_lib.LIB.lq_workspace_init(_dev(ws, "ws"), ws.numel() * ws.element_size(),
+                                      _stream(stream)), "lq_workspace_init")
 
 
 def lq_profile_events(starts, stops) -> None:

@@ -9,16 +9,19 @@ LIB_PATH = Path(__file__).resolve().parent / "liblq.so"
 
 LQ_OK, LQ_ERR_INVALID_ARG, LQ_ERR_UNSUPPORTED, LQ_ERR_WORKSPACE, LQ_ERR_HIP = range(5)
 LQ_F32, LQ_BF16 = 0, 1
-LQ_ALGO_AUTO, LQ_ALGO_VALU, LQ_ALGO_MFMA_SMALL, LQ_ALGO_MFMA_LARGE = range(4)
+LQ_ALGO_AUTO, LQ_ALGO_VALU, LQ_ALGO_MFMA_SMALL, LQ_ALGO_MFMA_LARGE, LQ_ALGO_FUSED = range(5)
 LQ_MAX_D = 64
 LQ_MAX_HB = 1024
+LQ_WS_CONTROL_BYTES = 16896
+LQ_WS_ERROR_WORD = 96
 
 # Every symbol include/lq.h declares.
 EXPORTS = [
     "lq_version", "lq_status_string", "lq_last_hip_error", "lq_packed_size",
     "lq_pack_signs", "lq_unpack_signs", "lq_hadamard_scale", "lq_lift_activations",
     "lq_sign_gemm_workspace_size", "lq_sign_gemm", "lq_sign_gemm_ex",
-    "lq_linear_workspace_size", "lq_linear", "lq_profile_events",
+    "lq_linear_workspace_size", "lq_linear", "lq_linear_workspace_size_ex", "lq_linear_ex",
+    "lq_workspace_init", "lq_profile_events",
 ]
 
 
@@ -61,6 +64,9 @@ def _load():
         "lq_sign_gemm_ex": (c_int, [vp, vp, c_int, i64, i64, i64, vp, vp, c_int, c_int, vp, sz, vp]),
         "lq_linear_workspace_size": (c_int, [POINTER(LQLayer), i64, c_int, POINTER(sz)]),
         "lq_linear": (c_int, [POINTER(LQLayer), vp, c_int, i64, vp, c_int, vp, sz, vp]),
+        "lq_linear_workspace_size_ex": (c_int, [POINTER(LQLayer), i64, c_int, c_int, POINTER(sz)]),
+        "lq_linear_ex": (c_int, [POINTER(LQLayer), vp, c_int, i64, vp, c_int, c_int, vp, sz, vp]),
+        "lq_workspace_init": (c_int, [vp, sz, vp]),
         "lq_profile_events": (c_int, [POINTER(vp), POINTER(vp), i32]),
     }
     for name, (res, args) in protos.items():

@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <mutex>
 #include <vector>
@@ -91,10 +93,34 @@ hipError_t profiled(hipStream_t stream, Fn fn) {
   return e;
 }
 
-lq_algo resolve_algo(lq_algo algo, lq_dtype ztype, int64_t B) {
-  if (algo != LQ_ALGO_AUTO) return algo;
-  if (B > 16) return LQ_ALGO_MFMA_LARGE;
-  return ztype == LQ_F32 ? LQ_ALGO_VALU : LQ_ALGO_MFMA_SMALL;
+
+static_assert(lq::kFusedControlBytes == LQ_WS_CONTROL_BYTES, "control area size");
+static_assert(lq::kFusedErrorWord == LQ_WS_ERROR_WORD, "error word");
+
+// Compute units of the current device (0 when there is none), cached.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  const bool cached = dev >= 0 && dev < 64;
+  if (cached) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  if (cached) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+bool valid_algo(lq_algo algo, bool linear) {
+  return algo >= LQ_ALGO_AUTO && algo <= (linear ? LQ_ALGO_FUSED : LQ_ALGO_MFMA_LARGE);
 }
 
 // Everything one sign product (or one whole lq_linear) needs: algorithm,
@@ -105,20 +131,38 @@ struct Exec {
   lq::ValuPlan vp;
   lq::Fp6Plan fp;
   lq::OperandShape os;
+  lq::FusedPlan fu;
   int tickets;
   size_t off_tickets, off_aop, off_partial, off_zf32, off_xt, off_z, total;
 };
 
 // Plans a sign product of z (ztype) or, when `linear`, the whole operator
 // for activations of type ztype with K input features.
+// Every workspace that is used at all starts with the control area of the
+// one-launch decode (only that kernel writes it), so one workspace can serve
+// calls of every algorithm in turn.
 lq_status plan_exec(int64_t B, int64_t N, int64_t L, int64_t K, lq_dtype ztype, lq_algo algo,
                     bool linear, Exec* e) {
-  e->algo = resolve_algo(algo, ztype, B);
   e->g = lq::make_geom(N, L);
+  e->algo = algo;
+  if (algo == LQ_ALGO_AUTO) {
+    if (B > 16) {
+      e->algo = LQ_ALGO_MFMA_LARGE;
+    } else if (ztype == LQ_F32) {
+      e->algo = LQ_ALGO_VALU;
+    } else {
+      // The one-launch decode is correct but, as measured so far, slower
+      // than the preparation launch plus the product launch: its chain of
+      // dependent memory round trips (load x, publish, poll, copy the
+      // operand) outweighs the launch it saves. It is chosen explicitly.
+      e->algo = LQ_ALGO_MFMA_SMALL;
+    }
+  }
   e->tickets = 0;
   e->off_tickets = e->off_aop = e->off_partial = 0;
   e->off_zf32 = e->off_xt = e->off_z = 0;
-  size_t at = 0;
+  const size_t ctl = align_up(lq::kFusedControlBytes);
+  size_t at = ctl;
   auto take = [&](size_t bytes) { const size_t o = at; at += align_up(bytes); return o; };
   switch (e->algo) {
     case LQ_ALGO_VALU:
@@ -135,6 +179,14 @@ lq_status plan_exec(int64_t B, int64_t N, int64_t L, int64_t K, lq_dtype ztype, 
       e->fp = lq::plan_fp6(B, e->g, e->os);
       e->off_aop = take(lq::operand_bytes(L, e->os));
       break;
+    case LQ_ALGO_FUSED:
+      if (!linear) return LQ_ERR_INVALID_ARG;
+      if (B > 16) return LQ_ERR_UNSUPPORTED;
+      e->os = lq::operand_shape(B, ztype == LQ_BF16);
+      e->fu = lq::plan_fused(B, e->g, e->os, device_cus());
+      if (!e->fu.ok) return LQ_ERR_UNSUPPORTED;
+      e->off_aop = take(lq::operand_bytes(L, e->os));
+      break;
     case LQ_ALGO_MFMA_LARGE:
       if (linear) {
         e->off_xt = take((size_t)B * K * sizeof(float));
@@ -144,7 +196,7 @@ lq_status plan_exec(int64_t B, int64_t N, int64_t L, int64_t K, lq_dtype ztype, 
     default:
       return LQ_ERR_INVALID_ARG;
   }
-  e->total = at;
+  e->total = at == ctl ? 0 : at;
   return LQ_OK;
 }
 
@@ -190,6 +242,17 @@ lq_status run_exec(const Exec& e, const uint8_t* packed, const void* zin, lq_dty
       if (s != LQ_OK) return s;
       return hip_status(profiled(st, [&] {
         return lq::launch_sign_fp6(packed, e.g, op, B, row_scale, y, yb, e.fp, st);
+      }));
+    }
+    case LQ_ALGO_FUSED: {
+      lq::OperandPlan op;
+      op.s = e.os;
+      op.aop = reinterpret_cast<uint8_t*>(base + e.off_aop);
+      unsigned* ctl = reinterpret_cast<unsigned*>(base);
+      return hip_status(profiled(st, [&] {
+        return lq::launch_decode_fused(packed, e.g, zin, zb, B, layer->K, layer->d, layer->D,
+                                       layer->hb, layer->c, layer->M, op, ctl, row_scale, y, yb,
+                                       e.fu, st);
       }));
     }
     case LQ_ALGO_MFMA_LARGE: {
@@ -303,7 +366,7 @@ lq_status lq_lift_activations(const float* xt, int64_t B, int64_t K, int32_t d, 
 lq_status lq_sign_gemm_workspace_size(int64_t B, int64_t N, int64_t L, lq_dtype ztype,
                                       lq_algo algo, size_t* bytes) {
   if (bytes == nullptr || !valid_dtype(ztype)) return LQ_ERR_INVALID_ARG;
-  if (algo < LQ_ALGO_AUTO || algo > LQ_ALGO_MFMA_LARGE) return LQ_ERR_INVALID_ARG;
+  if (!valid_algo(algo, false)) return LQ_ERR_INVALID_ARG;
   lq_status s = check_sign_dims(B, N, L);
   if (s != LQ_OK) return s;
   if (B == 0 || N == 0) { *bytes = 0; return LQ_OK; }
@@ -318,7 +381,7 @@ lq_status lq_sign_gemm_ex(const uint8_t* packed, const void* z, lq_dtype ztype, 
                           int64_t N, int64_t L, const float* row_scale, void* y, lq_dtype ytype,
                           lq_algo algo, void* ws, size_t ws_bytes, void* stream) {
   if (!valid_dtype(ztype) || !valid_dtype(ytype)) return LQ_ERR_INVALID_ARG;
-  if (algo < LQ_ALGO_AUTO || algo > LQ_ALGO_MFMA_LARGE) return LQ_ERR_INVALID_ARG;
+  if (!valid_algo(algo, false)) return LQ_ERR_INVALID_ARG;
   lq_status s = check_sign_dims(B, N, L);
   if (s != LQ_OK) return s;
   if (B == 0 || N == 0) return LQ_OK;
@@ -339,9 +402,10 @@ lq_status lq_sign_gemm(const uint8_t* packed, const void* z, lq_dtype ztype, int
                          ws_bytes, stream);
 }
 
-lq_status lq_linear_workspace_size(const lq_layer* layer, int64_t B, lq_dtype xtype,
-                                   size_t* bytes) {
+lq_status lq_linear_workspace_size_ex(const lq_layer* layer, int64_t B, lq_dtype xtype,
+                                      lq_algo algo, size_t* bytes) {
   if (bytes == nullptr || !valid_dtype(xtype) || B < 0) return LQ_ERR_INVALID_ARG;
+  if (!valid_algo(algo, true)) return LQ_ERR_INVALID_ARG;
   int64_t L = 0;
   lq_status s = check_layer(layer, &L);
   if (s != LQ_OK) return s;
@@ -350,15 +414,21 @@ lq_status lq_linear_workspace_size(const lq_layer* layer, int64_t B, lq_dtype xt
   if (!mul_ok(B, layer->K, kMaxElems)) return LQ_ERR_UNSUPPORTED;
   if (B == 0 || layer->N == 0) { *bytes = 0; return LQ_OK; }
   Exec e;
-  s = plan_exec(B, layer->N, L, layer->K, xtype, LQ_ALGO_AUTO, true, &e);
+  s = plan_exec(B, layer->N, L, layer->K, xtype, algo, true, &e);
   if (s != LQ_OK) return s;
   *bytes = e.total;
   return LQ_OK;
 }
 
-lq_status lq_linear(const lq_layer* layer, const void* x, lq_dtype xtype, int64_t B, void* y,
-                    lq_dtype ytype, void* ws, size_t ws_bytes, void* stream) {
+lq_status lq_linear_workspace_size(const lq_layer* layer, int64_t B, lq_dtype xtype,
+                                   size_t* bytes) {
+  return lq_linear_workspace_size_ex(layer, B, xtype, LQ_ALGO_AUTO, bytes);
+}
+
+lq_status lq_linear_ex(const lq_layer* layer, const void* x, lq_dtype xtype, int64_t B, void* y,
+                       lq_dtype ytype, lq_algo algo, void* ws, size_t ws_bytes, void* stream) {
   if (!valid_dtype(xtype) || !valid_dtype(ytype) || B < 0) return LQ_ERR_INVALID_ARG;
+  if (!valid_algo(algo, true)) return LQ_ERR_INVALID_ARG;
   int64_t L = 0;
   lq_status s = check_layer(layer, &L);
   if (s != LQ_OK) return s;
@@ -370,12 +440,25 @@ lq_status lq_linear(const lq_layer* layer, const void* x, lq_dtype xtype, int64_
       !aligned16(layer->c) || !aligned16(layer->row_scale))
     return LQ_ERR_INVALID_ARG;
   Exec e;
-  s = plan_exec(B, layer->N, L, layer->K, xtype, LQ_ALGO_AUTO, true, &e);
+  s = plan_exec(B, layer->N, L, layer->K, xtype, algo, true, &e);
   if (s != LQ_OK) return s;
   s = check_ws(ws, ws_bytes, e.total);
   if (s != LQ_OK) return s;
   return run_exec(e, layer->packed, x, xtype, B, layer->N, L, layer->row_scale, y, ytype, ws,
                   (hipStream_t)stream, layer);
+}
+
+lq_status lq_linear(const lq_layer* layer, const void* x, lq_dtype xtype, int64_t B, void* y,
+                    lq_dtype ytype, void* ws, size_t ws_bytes, void* stream) {
+  return lq_linear_ex(layer, x, xtype, B, y, ytype, LQ_ALGO_AUTO, ws, ws_bytes, stream);
+}
+
+lq_status lq_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (ws_bytes == 0) return LQ_OK;
+  if (!aligned16(ws)) return LQ_ERR_INVALID_ARG;
+  const size_t n = std::min(ws_bytes, (size_t)LQ_WS_CONTROL_BYTES) / 4;
+  if (n == 0) return LQ_OK;
+  return hip_status(lq::launch_zero_u32(static_cast<unsigned*>(ws), (int)n, (hipStream_t)stream));
 }
 
 lq_status lq_profile_events(void* const* starts, void* const* stops, int32_t count) {

@@ -221,6 +221,26 @@ struct Fp6Plan {
 };
 Fp6Plan plan_fp6(int64_t B, const PackedGeom& g, const OperandShape& s);
 
+// Fused decode (whitening, lift, operand and product in one launch; the
+// operand record of each (tile, batch row) is produced by one workgroup and
+// published through per-tile flags in the workspace's control area).
+constexpr int kFusedCtlWords = 128;    // epoch, ticket, done, error words (128 B apart)
+constexpr int kFusedErrorWord = 96;
+constexpr int kMaxFusedTiles = 256;    // flags [tile][16] for at most this many column tiles
+constexpr size_t kFusedControlBytes = (size_t)(kFusedCtlWords + kMaxFusedTiles * 16) * 4;
+struct FusedPlan {
+  bool ok;          // applicable (one column set, producers <= workgroups, LDS fits)
+  int p, tpc, nch, chunk_bytes, groups, producers;
+  size_t lds_bytes;
+};
+// `cus`: compute units of the device (all producers must be co-resident).
+FusedPlan plan_fused(int64_t B, const PackedGeom& g, const OperandShape& s, int cus);
+hipError_t launch_decode_fused(const uint8_t* packed, const PackedGeom& g, const void* x,
+                               bool x_bf16, int64_t B, int64_t K, int d, int D, int hb,
+                               const float* c, const float* M, const OperandPlan& op,
+                               unsigned* ctl, const float* row_scale, void* y, bool y_bf16,
+                               const FusedPlan& plan, hipStream_t stream);
+
 struct ValuPlan {
   int bt, tps, ksplit, groups;
   size_t partial_bytes;

@@ -20,89 +20,12 @@
 //     plane-0..2 columns of the values the terms represent.
 // Workgroup (0, 0) also clears the split-K tickets of the VALU product that
 // follows on the same stream.
-#include "lq_fp6.h"
-#include "lq_internal.h"
+#include "lq_prep.h"
 
 namespace lq {
 namespace {
 
-// A tile's lifted columns come from at most 511/D + 2 d-blocks, i.e. at most
-// 511 + 2D <= 639 original columns, which lie in at most 2 blocks of 1024,
-// 3 of 512, 4 of 256, ...: never more than 2048 values.
-constexpr int kSpanMax = 2048;
-
 constexpr int kThreads = 512;
-
-// Maximum over each 32-lane half of the wavefront: DPP within quads (lane
-// xor 1, xor 2), half-row and row mirrors (8, 16 lanes), then a swizzle
-// with lane xor 16.
-__device__ __forceinline__ float half_wave_max(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));
-  return v;
-}
-
-// Value of lane ^ X (X a power of two up to 32): DPP for 1 and 2, a
-// swizzle for 4..16 (within 32 lanes), a permute for 32.
-template <int X>
-__device__ __forceinline__ float lane_xor(float v) {
-  const int i = __float_as_int(v);
-  if constexpr (X == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, i, 0xB1, 0xF, 0xF, false));
-  else if constexpr (X == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, i, 0x4E, 0xF, 0xF, false));
-  else if constexpr (X <= 16) return __int_as_float(__builtin_amdgcn_ds_swizzle(i, 0x1F | (X << 10)));
-  else return __shfl_xor(v, X, 64);
-}
-
-// One cross-lane butterfly stage over the 16 registers: all exchanges are
-// issued before any is used.
-template <int X>
-__device__ __forceinline__ void lane_stage(float (&a)[16], int lane) {
-  float p[16];
-#pragma unroll
-  for (int k = 0; k < 16; ++k) p[k] = lane_xor<X>(a[k]);
-  const bool upper = (lane & X) != 0;
-#pragma unroll
-  for (int k = 0; k < 16; ++k) a[k] = upper ? p[k] - a[k] : a[k] + p[k];
-}
-
-// In-place fast Walsh-Hadamard transform (unnormalised) of every 2^lhb-value
-// block of the 1024 values xs[0..1023], by one wavefront: lane l holds
-// xs[16l + k] (k = 0..15); stages with stride below 16 pair registers, the
-// others pair lanes l and l ^ (stride / 16).
-__device__ __forceinline__ void wave_fwht_1024(float* xs, int lhb, int lane) {
-  float a[16];
-  const float4* src = reinterpret_cast<const float4*>(xs + 16 * lane);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float4 v = src[i];
-    a[4 * i] = v.x; a[4 * i + 1] = v.y; a[4 * i + 2] = v.z; a[4 * i + 3] = v.w;
-  }
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    if (s < lhb) {
-      const int h = 1 << s;
-#pragma unroll
-      for (int k = 0; k < 16; ++k)
-        if ((k & h) == 0) {
-          const float x0 = a[k], x1 = a[k | h];
-          a[k] = x0 + x1;
-          a[k | h] = x0 - x1;
-        }
-    }
-  }
-  if (lhb > 4) lane_stage<1>(a, lane);
-  if (lhb > 5) lane_stage<2>(a, lane);
-  if (lhb > 6) lane_stage<4>(a, lane);
-  if (lhb > 7) lane_stage<8>(a, lane);
-  if (lhb > 8) lane_stage<16>(a, lane);
-  if (lhb > 9) lane_stage<32>(a, lane);
-  float4* dst = reinterpret_cast<float4*>(xs + 16 * lane);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) dst[i] = make_float4(a[4 * i], a[4 * i + 1], a[4 * i + 2], a[4 * i + 3]);
-}
 
 // kMode 0: write fp32 z. kMode 1: write the FP6 operand.
 // kXKind 0: x fp32, 1: x bf16, 2: input is already-lifted z in fp32,
@@ -285,7 +208,8 @@ OperandShape operand_shape(int64_t B, bool z_bf16) {
   s.nt = (z_bf16 || 4 * B > 48) ? 3 : 4;
   s.ncv = (int)B * s.nt;
   s.cs = (s.ncv + 15) / 16;
-  s.rec = ((528 * s.ncv + 4 * (int)B) + 15) / 16 * 16;
+  // Records are 128-byte aligned: a cache line never holds parts of two.
+  s.rec = ((528 * s.ncv + 4 * (int)B) + 127) / 128 * 128;
   return s;
 }
 

@@ -38,45 +38,10 @@
 // and plane sums combined, and y written: deterministic, no atomics.
 #include <algorithm>
 
-#include "lq_internal.h"
+#include "lq_fp6_mma.h"
 
 namespace lq {
 namespace {
-
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(8))) int i32x8;
-
-template <int U>
-__device__ __forceinline__ f32x4 mfma_fp4_fp6(uint32_t w, const i32x8& b, uint32_t scale, f32x4 c) {
-  i32x8 a;
-  a[0] = (int)(w & 0x11111111u);
-  a[1] = (int)(w & 0x22222222u);
-  a[2] = (int)(w & 0x44444444u);
-  a[3] = (int)((w & 0x88888888u) | 0x22222222u);
-  a[4] = a[5] = a[6] = a[7] = 0;   // unused by an FP4 operand
-  // cbsz = 4: A is FP4 E2M1 (scale 2^0); blgp = 2: B is FP6 E2M3, its block
-  // scale is byte U of `scale`.
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 2, 0, 127, U, (int)scale);
-}
-
-// Workgroup barrier without a memory fence: this wavefront's LDS accesses
-// complete, then s_barrier; the memory clobber keeps the compiler from moving
-// memory accesses across it. (__syncthreads would also wait for every global
-// load in flight, since the loader's LDS copies count as global loads.) LDS
-// copies (global_load_lds) are waited for explicitly by the loader before
-// the barrier that publishes them.
-__device__ __forceinline__ void wg_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-__device__ __forceinline__ i32x8 lds_b_operand(const uint8_t* p) {
-  const uint4 lo = *reinterpret_cast<const uint4*>(p);
-  const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
-  i32x8 b;
-  b[0] = (int)lo.x; b[1] = (int)lo.y; b[2] = (int)lo.z; b[3] = (int)lo.w;
-  b[4] = (int)hi.x; b[5] = (int)hi.y; b[6] = 0; b[7] = 0;
-  return b;
-}
 
 template <int P, int CS, int W, int TPC>
 __global__ __launch_bounds__(64 * (W + 1)) void sign_fp6_kernel(

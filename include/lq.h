@@ -40,6 +40,13 @@
  *     the same GPU (no floating-point atomics).
  *   - Functions never throw; they are thread-safe. Calls that share a
  *     workspace buffer must be ordered by the caller.
+ *   - Workspaces: the first LQ_WS_CONTROL_BYTES bytes of a workspace hold
+ *     control words through which the workgroups of the one-launch decode
+ *     (LQ_ALGO_FUSED) order themselves. Before its first use a workspace
+ *     must be zero-filled (allocate it zeroed, or call lq_workspace_init);
+ *     afterwards the library keeps those words consistent from call to call,
+ *     and the caller must not write them. After LQ_ERR_HIP or a device fault,
+ *     prepare the workspace again.
  *
  * Packed sign layout (this library's format; the pages give none). S is
  * N x L, N % 16 == 0, L % 8 == 0, total exactly N * L / 8 bytes:
@@ -87,13 +94,33 @@ typedef enum lq_algo {
                                scale per 32-value block (4 terms for fp32 z,
                                3 for bf16 z; about 2^-20 / 2^-15 relative);
                                fp32 accumulate */
-  LQ_ALGO_MFMA_LARGE = 3    /* any B: tiled GEMM on bf16 matrix cores, z as bf16
+  LQ_ALGO_MFMA_LARGE = 3,   /* any B: tiled GEMM on bf16 matrix cores, z as bf16
                                (bf16 z) or as a bf16 hi+lo pair (fp32 z) */
+  LQ_ALGO_FUSED = 4         /* lq_linear_ex only: the whole operator in ONE
+                               launch, the MFMA_SMALL arithmetic (same FP6
+                               terms, same results up to fp32 summation order):
+                               the first workgroups whiten and lift x and
+                               publish the activation operand, every workgroup
+                               streams its weight panels meanwhile. Applies
+                               when the operand fits one 16-column set
+                               (B <= 5 bf16 x, B <= 4 fp32 x) and
+                               ceil(L/512)*B is at most both the number of
+                               workgroups and of compute units; otherwise
+                               UNSUPPORTED */
+
 } lq_algo;
 
 /* Limits. d and D are runtime parameters: one operator for every rate. */
 #define LQ_MAX_D 64          /* 1 <= d <= D <= LQ_MAX_D */
 #define LQ_MAX_HB 1024       /* hb a power of two, 1 <= hb <= 1024, hb | K */
+
+/* Workspace control area (see the conventions above). */
+#define LQ_WS_CONTROL_BYTES 16896
+/* 32-bit word of the control area that the one-launch decode sets non-zero
+ * when a workgroup gave up waiting for the activation operand (about one
+ * second; possible only when other work holds the GPU's compute units): the
+ * output of that call is then wrong. lq_workspace_init clears it. */
+#define LQ_WS_ERROR_WORD 96
 
 /* One quantized linear layer (all pointers device, caller-owned). */
 typedef struct lq_layer {
@@ -192,10 +219,31 @@ lq_status lq_linear(const lq_layer* layer, const void* x, lq_dtype xtype, int64_
                     lq_dtype ytype, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * As lq_linear, with the algorithm chosen by the caller: LQ_ALGO_AUTO (what
+ * lq_linear does: B > 16 MFMA_LARGE; fp32 x VALU; bf16 x MFMA_SMALL),
+ * VALU (B <= 16), MFMA_SMALL (B <= 16; whitening,
+ * lift and operand in one preparation launch, then the product launch),
+ * MFMA_LARGE, or FUSED (one launch; UNSUPPORTED where it does not apply).
+ * The workspace size depends on the algorithm.
+ */
+lq_status lq_linear_workspace_size_ex(const lq_layer* layer, int64_t B, lq_dtype xtype,
+                                      lq_algo algo, size_t* bytes);
+lq_status lq_linear_ex(const lq_layer* layer, const void* x, lq_dtype xtype, int64_t B, void* y,
+                       lq_dtype ytype, lq_algo algo, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Prepare a workspace for first use: zero-fill its control area (the first
+ * min(ws_bytes, LQ_WS_CONTROL_BYTES) bytes, with a kernel on `stream`).
+ * Errors: INVALID_ARG for a NULL or unaligned ws with ws_bytes > 0.
+ */
+lq_status lq_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Profiling aid: time the sign-product kernel itself. `starts` and `stops`
  * are host arrays of `count` hipEvent_t handles (passed as void*) created by
  * the caller. While set, every sign-product kernel launched by lq_sign_gemm,
- * lq_sign_gemm_ex or lq_linear records starts[i] and stops[i] at its own
+ * lq_sign_gemm_ex, lq_linear or lq_linear_ex (for LQ_ALGO_FUSED, the one
+ * kernel of the call) records starts[i] and stops[i] at its own
  * start and end (the events ride on the kernel's dispatch, as in
  * hipExtLaunchKernelGGL, so they time the kernel alone, as a profiler does),
  * i = 0, 1, 2, ... wrapping modulo `count` (the preparation kernels are not

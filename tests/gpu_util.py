@@ -50,20 +50,41 @@ class DeviceLayer:
         self.r = dev(li.row_scale)
         self.struct = lq.layer_struct(s.N, s.K, s.d, s.D, s.hb, self.packed, self.M, self.c, self.r)
 
-    def linear(self, lq, x: torch.Tensor, B: int, ydtype) -> torch.Tensor:
+    def linear(self, lq, x: torch.Tensor, B: int, ydtype, algo=None) -> torch.Tensor:
+        """lq_linear (algo None) or lq_linear_ex on a fresh workspace whose
+        contents beyond the control area are garbage; checks the error word."""
         y = torch.empty((B, self.N), dtype=ydtype, device=DEV)
-        nbytes = lq.lq_linear_workspace_size(self.struct, B, x.dtype)
-        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=DEV)
-        note(f"lq_linear N={self.N} K={self.K} d={self.d} D={self.D} hb={self.hb} B={B} x={x.dtype}")
-        lq.lq_linear(self.struct, x, B, y, ws)
+        a = lq.LQ_ALGO_AUTO if algo is None else algo
+        nbytes = lq.lq_linear_workspace_size_ex(self.struct, B, x.dtype, a)
+        ws = workspace(lq, nbytes)
+        note(f"lq_linear N={self.N} K={self.K} d={self.d} D={self.D} hb={self.hb} B={B} "
+             f"x={x.dtype} algo={algo}")
+        if algo is None:
+            lq.lq_linear(self.struct, x, B, y, ws)
+        else:
+            lq.lq_linear_ex(self.struct, x, B, y, algo, ws)
         torch.cuda.synchronize()
+        assert control_error(lq, ws) == 0
         return y
+
+
+def workspace(lq, nbytes: int) -> torch.Tensor:
+    """A workspace with garbage contents and a zeroed control area."""
+    ws = torch.full((max(nbytes, 16),), 0xA5, dtype=torch.uint8, device=DEV)
+    lq.lq_workspace_init(ws)
+    return ws
+
+
+def control_error(lq, ws: torch.Tensor) -> int:
+    if ws.numel() < lq.LQ_WS_CONTROL_BYTES:
+        return 0
+    return int(ws[: lq.LQ_WS_CONTROL_BYTES].view(torch.int32)[lq.LQ_WS_ERROR_WORD].item())
 
 
 def sign_gemm(lq, packed, z: torch.Tensor, B, N, L, r, ydtype, algo):
     y = torch.empty((B, N), dtype=ydtype, device=DEV)
     nbytes = lq.lq_sign_gemm_workspace_size(B, N, L, z.dtype, algo)
-    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=DEV)
+    ws = workspace(lq, nbytes)
     note(f"lq_sign_gemm_ex algo={algo} B={B} N={N} L={L} z={z.dtype} y={ydtype}")
     lq.lq_sign_gemm_ex(packed, z, B, N, L, r, y, algo, ws)
     torch.cuda.synchronize()

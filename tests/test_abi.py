@@ -151,6 +151,41 @@ def test_linear_validation():
     assert f(ctypes.byref(lay), P, LQ_BF16, 0, P, LQ_BF16, None, 0, None) == LQ_OK
 
 
+def linear_ws_size(lay, B, xt, algo):
+    out = ctypes.c_size_t()
+    st = LIB.lq_linear_workspace_size_ex(ctypes.byref(lay), B, xt, algo, ctypes.byref(out))
+    return st, out.value
+
+
+def test_linear_ex_validation_and_control_area():
+    lay = LQLayer(4096, 14336, 10, 24, 1024, 0, P, P, P, P)
+    for algo in (0, 1, 2, 3):
+        st, need = linear_ws_size(lay, 1, LQ_BF16, algo)
+        assert st == LQ_OK
+        # every workspace that is used at all starts with the control area
+        assert need >= _lib.LQ_WS_CONTROL_BYTES + 34416 * 3 // 4
+    assert linear_ws_size(lay, 1, LQ_BF16, 5)[0] == LQ_ERR_INVALID_ARG
+    assert linear_ws_size(lay, 17, LQ_BF16, 4)[0] == LQ_ERR_UNSUPPORTED      # one launch: B <= 16
+    assert linear_ws_size(lay, 8, LQ_BF16, 4)[0] == LQ_ERR_UNSUPPORTED       # 24 operand columns
+    assert linear_ws_size(lay, 17, LQ_BF16, 1)[0] == LQ_ERR_UNSUPPORTED      # VALU linear: B <= 16
+    assert ws_size(1, 4096, 34416, LQ_BF16, 4)[0] == LQ_ERR_INVALID_ARG      # sign_gemm: no FUSED
+    assert linear_ws_size(lay, 0, LQ_BF16, 4) == (LQ_OK, 0)
+    f = LIB.lq_linear_ex
+    need = linear_ws_size(lay, 1, LQ_BF16, 2)[1]
+    assert f(ctypes.byref(lay), P, LQ_BF16, 1, P, LQ_BF16, 2, P, need - 1, None) == LQ_ERR_WORKSPACE
+    assert f(ctypes.byref(lay), P, LQ_BF16, 1, P, LQ_BF16, 7, P, need, None) == LQ_ERR_INVALID_ARG
+    assert f(ctypes.byref(lay), P, LQ_BF16, 17, P, LQ_BF16, 4, P, need, None) == LQ_ERR_UNSUPPORTED
+    assert f(ctypes.byref(lay), P, LQ_BF16, 0, P, LQ_BF16, 4, None, 0, None) == LQ_OK
+
+
+def test_workspace_init_validation():
+    f = LIB.lq_workspace_init
+    assert f(None, 0, None) == LQ_OK
+    assert f(P, 0, None) == LQ_OK
+    assert f(None, 64, None) == LQ_ERR_INVALID_ARG
+    assert f(MIS, 64, None) == LQ_ERR_INVALID_ARG
+
+
 def test_profile_events_validation():
     f = LIB.lq_profile_events
     arr = (ctypes.c_void_p * 2)(P, P)

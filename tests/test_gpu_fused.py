@@ -1,0 +1,205 @@
+"""Parity of the one-launch decode (lq_linear_ex with LQ_ALGO_FUSED) with the
+CPU oracle and with the two-launch small-batch path, through the C ABI.
+
+* Every layer of every workload at full size, at each batch size where the
+  one-launch decode applies, bf16 and fp32 activations: sampled output rows
+  recomputed by the oracle one by one.
+* Same results as the two-launch path (MFMA_SMALL) up to fp32 summation
+  order: both carry the lifted activations as the same FP6 terms.
+* Ragged shapes: only a tail tile (L < 512), no tail (L % 512 == 0), K not a
+  multiple of d, hb = 1, d = 1, D = d with M = I, one 16-row panel.
+* One zero-filled workspace reused by many calls of different layers (the
+  control words advance an epoch per launch), graph replays, determinism,
+  and the error word staying clear.
+Tolerances (relative L2): fp32 x 2e-5 (four FP6 terms), bf16 x 5e-4 (three).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import liftquant_ref as ref
+from tests.gpu_util import DEV, DeviceLayer, control_error, dev, host, note, rel_l2, workspace
+from workloads import WORKLOADS, make_layer, make_layer_small
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 2e-5, torch.bfloat16: 5e-4}
+
+
+@pytest.fixture(scope="module")
+def lq():
+    import bit_matmul_amd
+    assert torch.cuda.is_available()
+    return bit_matmul_amd
+
+
+def _fused_ok(lq, layer, B, xd):
+    try:
+        lq.lq_linear_workspace_size_ex(layer.struct, B, xd, lq.LQ_ALGO_FUSED)
+        return True
+    except lq.LQError as e:
+        assert e.status == 2, e          # UNSUPPORTED, nothing else
+        return False
+
+
+FULL = [(w, i) for w in WORKLOADS for i in range(len(WORKLOADS[w].layers)) if w != "tiny"]
+
+
+@pytest.mark.parametrize("wl_name,li", FULL, ids=[f"{w}-{WORKLOADS[w].layers[i].name}" for w, i in FULL])
+def test_fused_full_size_sampled_rows(lq, wl_name, li):
+    wl = WORKLOADS[wl_name]
+    spec = wl.layers[li]
+    inp = make_layer(spec, wl, B_max=5)
+    layer = DeviceLayer(inp, lq)
+    rng = np.random.default_rng(spec.seed + 1)
+    rows = np.sort(rng.choice(spec.N, size=48, replace=False))
+    rows[0], rows[-1] = 0, spec.N - 1
+    ran = 0
+    for B in (1, 2, 3, 4, 5):
+        x = inp.x(B)
+        for xd in (torch.bfloat16, torch.float32):
+            if not _fused_ok(lq, layer, B, xd):
+                continue
+            y = host(layer.linear(lq, dev(x, xd), B, torch.float32, algo=lq.LQ_ALGO_FUSED))
+            want = ref.linear(x, inp.c, spec.hb, inp.M, inp.signs_rows(rows), inp.row_scale[rows])
+            err = rel_l2(y[:, rows], want)
+            assert err < TOL[xd], (B, xd, err)
+            assert np.all(np.isfinite(y))
+            ran += 1
+    assert ran > 0 or spec.K * spec.D // spec.d > 512 * 256
+
+
+def test_fused_batch1_applies_on_every_full_size_layer(lq):
+    """Batch 1 with bf16 activations is the decode the one launch is for:
+    every full-size layer qualifies, with the same workspace size as the
+    two-launch path."""
+    for wl_name, li in FULL:
+        wl = WORKLOADS[wl_name]
+        s = wl.layers[li]
+        st = lq.layer_struct(s.N, s.K, s.d, s.D, s.hb, *(torch.empty(16, device=DEV),) * 4)
+        a = lq.lq_linear_workspace_size_ex(st, 1, torch.bfloat16, lq.LQ_ALGO_MFMA_SMALL)
+        f = lq.lq_linear_workspace_size_ex(st, 1, torch.bfloat16, lq.LQ_ALGO_FUSED)
+        assert a == f, (wl_name, s.name)
+
+
+@pytest.mark.parametrize("xd", [torch.bfloat16, torch.float32])
+def test_fused_matches_two_launch(lq, xd):
+    inp = make_layer_small(2048, 4096, 10, 24, 1024, seed=91, B_max=4,
+                           xdtype="bf16" if xd == torch.bfloat16 else "f32")
+    layer = DeviceLayer(inp, lq)
+    for B in (1, 2, 3, 4):
+        x = dev(inp.x(B), xd)
+        yf = host(layer.linear(lq, x, B, torch.float32, algo=lq.LQ_ALGO_FUSED))
+        ys = host(layer.linear(lq, x, B, torch.float32, algo=lq.LQ_ALGO_MFMA_SMALL))
+        assert rel_l2(yf, ys) < 2e-6, B
+        want = ref.linear(inp.x(B), inp.c, 1024, inp.M, inp.signs(), inp.row_scale)
+        assert rel_l2(yf, want) < TOL[xd]
+
+
+EDGE = [
+    # (N, K, d, D, hb, label)
+    (16, 64, 2, 8, 64, "single panel, tail only"),
+    (160, 1037, 10, 24, 1, "K not a multiple of d, hb=1"),
+    (48, 256, 4, 4, 256, "D = d, tail only"),
+    (512, 4096, 16, 32, 1024, "LQ-32/16, no tail"),
+    (320, 600, 1, 8, 8, "d = 1"),
+    (1024, 8192, 3, 8, 1024, "2.67 bit ragged pad"),
+    (80, 24, 8, 24, 8, "LQ-24/8 one block row"),
+    (1024, 2560, 5, 16, 512, "16 full tiles, no tail"),
+    (512, 2600, 10, 24, 8, "ragged tail after 12 tiles"),
+]
+
+
+@pytest.mark.parametrize("N,K,d,D,hb,label", EDGE, ids=[e[-1] for e in EDGE])
+@pytest.mark.parametrize("xd", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_fused_edge_shapes(lq, N, K, d, D, hb, label, xd):
+    inp = make_layer_small(N, K, d, D, hb, seed=N + K + d + D + 5, B_max=5,
+                           xdtype="f32" if xd == torch.float32 else "bf16")
+    if label.startswith("D = d"):
+        inp.M = np.eye(d, dtype=np.float32)
+    layer = DeviceLayer(inp, lq)
+    ran = 0
+    for B in (1, 2, 3, 4, 5):
+        if not _fused_ok(lq, layer, B, xd):
+            continue
+        x = inp.x(B)
+        y = layer.linear(lq, dev(x, xd), B, torch.float32, algo=lq.LQ_ALGO_FUSED)
+        want = ref.linear(x, inp.c, hb, inp.M, inp.signs(), inp.row_scale)
+        assert rel_l2(host(y), want) < TOL[xd], B
+        ran += 1
+    assert ran > 0
+
+
+def test_fused_shared_workspace_many_calls(lq):
+    """One workspace, zero-filled once, serving interleaved calls of three
+    layers of different geometry (and of the two-launch path) for several
+    rounds: every call must see only its own launch's published operand."""
+    shapes = [(512, 2048, 10, 24, 1024), (2048, 5120, 10, 24, 1024), (1024, 1024, 5, 16, 256)]
+    layers, inps = [], []
+    for i, (N, K, d, D, hb) in enumerate(shapes):
+        inp = make_layer_small(N, K, d, D, hb, seed=200 + i, B_max=3, xdtype="bf16")
+        inps.append(inp)
+        layers.append(DeviceLayer(inp, lq))
+    nbytes = max(lq.lq_linear_workspace_size_ex(l.struct, 3, torch.bfloat16, a)
+                 for l in layers for a in (lq.LQ_ALGO_FUSED, lq.LQ_ALGO_MFMA_SMALL))
+    ws = workspace(lq, nbytes)
+    rng = np.random.default_rng(5)
+    note("shared workspace: 3 layers x 4 rounds, fused and two-launch interleaved")
+    for rnd in range(4):
+        for li, (layer, inp) in enumerate(zip(layers, inps)):
+            B = 1 + (rnd + li) % 3
+            x = (rng.standard_normal((B, layer.K)).astype(np.float32))
+            xb = dev(x, torch.bfloat16)
+            algo = lq.LQ_ALGO_FUSED if (rnd + li) % 4 != 3 else lq.LQ_ALGO_MFMA_SMALL
+            y = torch.empty((B, layer.N), dtype=torch.float32, device=DEV)
+            lq.lq_linear_ex(layer.struct, xb, B, y, algo, ws)
+            torch.cuda.synchronize()
+            want = ref.linear(host(xb).astype(np.float32), inp.c, layer.hb, inp.M, inp.signs(),
+                              inp.row_scale)
+            assert rel_l2(host(y), want) < TOL[torch.bfloat16], (rnd, li, algo)
+    assert control_error(lq, ws) == 0
+
+
+def test_fused_graph_replay(lq):
+    """A captured one-launch decode replays correctly: the control words are
+    reset by the kernel itself (no memset node), each replay checked against
+    the eager result, with eager work of the same workspace in between."""
+    inp = make_layer_small(2048, 4096, 10, 24, 1024, seed=301, B_max=2, xdtype="bf16")
+    layer = DeviceLayer(inp, lq)
+    B = 2
+    nbytes = lq.lq_linear_workspace_size_ex(layer.struct, B, torch.bfloat16, lq.LQ_ALGO_FUSED)
+    ws = workspace(lq, nbytes)
+    x = dev(inp.x(B), torch.bfloat16)
+    y = torch.empty((B, layer.N), dtype=torch.float32, device=DEV)
+    lq.lq_linear_ex(layer.struct, x, B, y, lq.LQ_ALGO_FUSED, ws)      # warm (LDS attribute set)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    note("capture one-launch decode")
+    with torch.cuda.graph(g, stream=s):
+        lq.lq_linear_ex(layer.struct, x, B, y, lq.LQ_ALGO_FUSED, ws, stream=s)
+    rng = np.random.default_rng(9)
+    for rep in range(4):
+        xn = rng.standard_normal((B, layer.K)).astype(np.float32)
+        x.copy_(dev(xn, torch.bfloat16))
+        note(f"graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        got = y.clone()
+        y_eager = torch.empty_like(y)
+        lq.lq_linear_ex(layer.struct, x, B, y_eager, lq.LQ_ALGO_FUSED, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(got, y_eager), rep
+        want = ref.linear(host(x).astype(np.float32), inp.c, 1024, inp.M, inp.signs(), inp.row_scale)
+        assert rel_l2(host(got), want) < TOL[torch.bfloat16]
+    assert control_error(lq, ws) == 0
+
+
+def test_fused_deterministic(lq):
+    wl = WORKLOADS["llama3_8b_mlp"]
+    inp = make_layer(wl.layers[1], wl, B_max=1)
+    layer = DeviceLayer(inp, lq)
+    x = dev(inp.x(1), torch.bfloat16)
+    y1 = layer.linear(lq, x, 1, torch.bfloat16, algo=lq.LQ_ALGO_FUSED)
+    y2 = layer.linear(lq, x, 1, torch.bfloat16, algo=lq.LQ_ALGO_FUSED)
+    assert torch.equal(y1, y2)
