@@ -36,7 +36,7 @@ namespace {
 
 constexpr int kW = 7;                  // compute wavefronts (plus one loader)
 constexpr int kFusedThreads = 64 * (kW + 1);
-constexpr int kPrepThreads = 64 * kW;  // the compute wavefronts do the preparation
+static_assert(kFusedThreads == kTileCols, "the lift gives one column to every thread");
 constexpr unsigned kMaxPolls = 1u << 20;
 
 // Control words (separate 128-byte lines), then flags [tiles][16].
@@ -56,9 +56,7 @@ __device__ __forceinline__ unsigned load_coherent_u32(const unsigned* p) {
 struct PrepLds {
   float xs[kSpanMax];        // x * c, then its Hadamard transform
   float zt[kTileCols];       // the tile's lifted values
-  float Ms[64 * 64];         // M (not yet scaled by 1/sqrt(hb))
-  float red[8];
-  uint32_t sc[4 * 16];       // scale dwords [g][column]
+  float Ms[64 * 64];         // M / sqrt(hb)
 };
 
 template <int P, int TPC, int kXKind>
@@ -173,6 +171,38 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(
     }
   };
 
+  // ---- preparation phases of a producer: the lift (one column per thread
+  // of all 8 wavefronts, written in the FP6 conversion's slot order with the
+  // plane factors applied) and the FP6 blocks (lane h < 16 of wavefront 0
+  // converts block h of the tile into this producer's record columns).
+  auto lift_phase = [&](const TileSpan& ts) {
+    const int jj = tid;                               // kTileCols threads
+    const float z = jj < ts.width ? lift_column(pl.Ms, pl.xs, pq * kTileCols + jj, d, D, K, ts.h_lo)
+                                  : 0.0f;
+    float f;
+    const int slot = fp6_slot(jj, f);
+    pl.zt[slot] = f * z;
+  };
+  auto quant_phase = [&]() {
+    if (tid >= 16) return;
+    const int u = tid >> 2, gg = tid & 3;
+    Fp6LaneTerms rt;
+    float tp = fp6_lane_block(pl.zt, tid, nt, rt);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t < nt) {
+        const int cc = pb * nt + t;
+        uint4* dst = reinterpret_cast<uint4*>(prec + aop_data_offset(0, u, gg, cc, ncs));
+        dst[0] = make_uint4(rt.dw[t][0], rt.dw[t][1], rt.dw[t][2], rt.dw[t][3]);
+        dst[1] = make_uint4(rt.dw[t][4], rt.dw[t][5], 0u, 0u);
+        prec[aop_scale_offset(ncv, 0, gg, cc, ncs) + u] = (uint8_t)(127 + rt.e[t]);
+      }
+    }
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) tp += __shfl_xor(tp, o, 16);
+    if (tid == 0) *reinterpret_cast<float*>(prec + aop_tpart_offset(ncv) + 4 * pb) = tp;
+  };
+
   if (loader) {
     // ---- preparation inputs of a producer: x and c over the covering
     // Hadamard blocks, and M, into LDS
@@ -211,9 +241,10 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(
     }
     wg_barrier();                                     // B1: inputs in LDS
     if (producer) {
+      const TileSpan ts = tile_span(pq, K, d, D, lhb, L);
       wg_barrier();                                   // m1: transformed
+      lift_phase(ts);
       wg_barrier();                                   // m2: lifted
-      wg_barrier();                                   // m3: blocks done
     }
     wg_barrier();                                     // B2: record in LDS
     if (producer) {
@@ -304,63 +335,14 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(
     issue_A(1, A1);
     wg_barrier();                                     // B1
     if (producer) {
-      // ---- preparation of (tile pq, batch row pb) by the 7 compute wavefronts
+      // ---- preparation of (tile pq, batch row pb); the loader wavefront
+      // joins the lift
       const TileSpan ts = tile_span(pq, K, d, D, lhb, L);
       if (1024 * wave < ts.span) wave_fwht_1024(pl.xs + 1024 * wave, lhb, lane);
       wg_barrier();                                   // m1
-      const int c_lo = pq * kTileCols;
-      for (int jj = tid; jj < kTileCols; jj += kPrepThreads) {
-        float a = 0.0f;
-        if (jj < ts.width) {
-          const int colj = c_lo + jj;
-          const int blk = colj / D;
-          const int e = colj - blk * D;
-          const int kb = blk * d;
-          const int nk = min(d, K - kb);
-          for (int i = 0; i < nk; ++i) a = fmaf(pl.Ms[i * D + e], pl.xs[kb + i - ts.h_lo], a);
-        }
-        pl.zt[jj] = a;
-      }
+      lift_phase(ts);
       wg_barrier();                                   // m2
-      // 16 blocks (u, g) over 14 half-wavefronts; lane m holds the value
-      // meeting reduction index 32g + m (plane m / 8 of column 128u + 32g +
-      // 4 (m % 8) + m / 8).
-      const int m = tid & 31, half = tid >> 5;
-      const int j = m >> 3, i8 = m & 7;
-      const float f = j == 3 ? 1.0f : (j == 2 ? -1.0f : (j == 1 ? -2.0f : -4.0f));
-      float tp = 0.0f;
-      for (int blk = half; blk < 16; blk += 2 * kW) {
-        const int u = blk >> 2, gg = blk & 3;
-        const float orig = f * pl.zt[128 * u + 32 * gg + 4 * i8 + j];
-        float v = orig;
-        const Fp6Block fb = fp6_block_terms(v, nt, m);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          if (t < nt) {
-            const int cc = pb * nt + t;
-            if (m < 8)
-              *reinterpret_cast<uint32_t*>(prec + aop_data_offset(0, u, gg, cc, ncs) + 4 * m) =
-                  m < 6 ? fb.dw[t] : 0u;
-            if (m == 0) reinterpret_cast<uint8_t*>(pl.sc)[(gg * 16 + t) * 4 + u] = (uint8_t)(127 + fb.e[t]);
-          }
-        }
-        if (j < 3) tp += (orig - v) / f;
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) tp += __shfl_xor(tp, o, 64);
-      if (lane == 0) pl.red[wave] = tp;
-      wg_barrier();                                   // m3: blocks done
-      if (tid < 4 * nt) {
-        const int t = tid / 4, gg = tid % 4;
-        *reinterpret_cast<uint32_t*>(prec + aop_scale_offset(ncv, 0, gg, pb * nt + t, ncs)) =
-            pl.sc[gg * 16 + t];
-      }
-      if (tid == 0) {
-        float s = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kW; ++w) s += pl.red[w];
-        *reinterpret_cast<float*>(prec + aop_tpart_offset(ncv) + 4 * pb) = s;
-      }
+      quant_phase();
     }
     wg_barrier();                                     // B2
     wg_barrier();                                     // Y0

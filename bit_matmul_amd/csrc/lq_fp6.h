@@ -39,7 +39,7 @@ __device__ __forceinline__ float e2m3_decode(uint32_t code) {
 // clamped to the E8M0 range. amax == 0 gives 0.
 __device__ __forceinline__ int e2m3_block_exponent(float amax) {
   if (!(amax > 0.0f)) return 0;
-  const int E = ilogbf(amax);                          // 2^E <= amax < 2^(E+1)
+  const int E = __builtin_amdgcn_frexp_expf(amax) - 1;  // 2^E <= amax < 2^(E+1)
   int e = (amax <= ldexpf(kE2M3Max, E - 2)) ? E - 2 : E - 1;
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }

@@ -32,18 +32,6 @@ __device__ __forceinline__ TileSpan tile_span(int q, int K, int d, int D, int lh
   return t;
 }
 
-// Maximum over each 32-lane half of the wavefront: DPP within quads (lane
-// xor 1, xor 2), half-row and row mirrors (8, 16 lanes), then a swizzle
-// with lane xor 16.
-__device__ __forceinline__ float half_wave_max(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));
-  return v;
-}
-
 // Value of lane ^ X (X a power of two up to 32): DPP for 1 and 2, a
 // swizzle for 4..16 (within 32 lanes), a permute for 32.
 template <int X>
@@ -68,9 +56,11 @@ __device__ __forceinline__ void lane_stage(float (&a)[16], int lane) {
 }
 
 // In-place fast Walsh-Hadamard transform (unnormalised) of every 2^lhb-value
-// block of the 1024 values xs[0..1023], by one wavefront: lane l holds
-// xs[16l + k] (k = 0..15); stages with stride below 16 pair registers, the
-// others pair lanes l and l ^ (stride / 16).
+// block of the 1024 values xs[0..1023], by one wavefront. Index bit s of a
+// value is butterflied in stage s (s < lhb). Lane l first holds xs[16l + k]
+// (k = 0..15): bits 0..3 pair registers, bits 4 and 5 pair lanes l ^ 1 and
+// l ^ 2 (DPP). For bits 6..9 the values go through LDS once so that lane l
+// holds xs[l + 64k], where those bits pair registers again.
 __device__ __forceinline__ void wave_fwht_1024(float* xs, int lhb, int lane) {
   float a[16];
   const float4* src = reinterpret_cast<const float4*>(xs + 16 * lane);
@@ -94,55 +84,147 @@ __device__ __forceinline__ void wave_fwht_1024(float* xs, int lhb, int lane) {
   }
   if (lhb > 4) lane_stage<1>(a, lane);
   if (lhb > 5) lane_stage<2>(a, lane);
-  if (lhb > 6) lane_stage<4>(a, lane);
-  if (lhb > 7) lane_stage<8>(a, lane);
-  if (lhb > 8) lane_stage<16>(a, lane);
-  if (lhb > 9) lane_stage<32>(a, lane);
   float4* dst = reinterpret_cast<float4*>(xs + 16 * lane);
 #pragma unroll
   for (int i = 0; i < 4; ++i) dst[i] = make_float4(a[4 * i], a[4 * i + 1], a[4 * i + 2], a[4 * i + 3]);
+  if (lhb > 6) {
+    // The wavefront's own LDS writes are seen by its later reads.
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) a[k] = xs[lane + 64 * k];
+#pragma unroll
+    for (int s = 6; s < 10; ++s) {
+      if (s < lhb) {
+        const int h = 1 << (s - 6);
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          if ((k & h) == 0) {
+            const float x0 = a[k], x1 = a[k | h];
+            a[k] = x0 + x1;
+            a[k | h] = x0 - x1;
+          }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) xs[lane + 64 * k] = a[k];
+  }
 }
 
+// One lifted value z[col] = sum_{i < min(d, K - kb)} Ms[i * D + e] *
+// xs[kb + i - h_lo] with col = blk * D + e and kb = blk * d (the lift of
+// d-block blk; rows of the virtual zero pad are skipped). Products are added
+// in order of i; the LDS reads of 8 terms are issued before they are used.
+__device__ __forceinline__ float lift_column(const float* Ms, const float* xs, int col, int d,
+                                             int D, int K, int h_lo) {
+  const int blk = col / D;
+  const int e = col - blk * D;
+  const int kb = blk * d;
+  const int nk = min(d, K - kb);
+  float acc = 0.0f;
+  for (int i0 = 0; i0 < nk; i0 += 8) {
+    float mv[8], xv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = min(i0 + u, nk - 1);
+      mv[u] = Ms[i * D + e];
+      xv[u] = xs[kb + i - h_lo];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (i0 + u < nk) acc = fmaf(mv[u], xv[u], acc);
+  }
+  return acc;
+}
 
-// FP6 record of one 32-value block: lane m (0..31) of a half-wavefront holds
-// value v (already multiplied by its plane factor); cuts it into nt terms
-// and returns, per term t, the six code dwords in lanes 0..5 (dw[t]) and the
-// E8M0 scale byte (e[t] + 127, the same in every lane). `orig - v` after the
-// call is the value the terms represent.
-struct Fp6Block {
-  uint32_t dw[4];
+// FP6 terms of one 32-value block held by ONE lane, on the gfx950 packed
+// conversion instructions. The lane holds the value meeting reduction index
+// 32g + n in va[n / 2] (n even) or vb[n / 2] (n odd): the conversion puts
+// element i of its first source at code 2i and of its second at code 2i + 1,
+// so code n lands at bit 6n of the six dwords, the matrix-core operand
+// layout. Per term t: the block exponent e (the largest with
+// max|v| * 2^-e <= 7.5), the codes round-to-nearest-even(v / 2^e), then
+// v -= the decoded codes; va and vb end as the residual.
+typedef float lq_v16f __attribute__((ext_vector_type(16)));
+typedef float lq_v32f __attribute__((ext_vector_type(32)));
+typedef int lq_v6i __attribute__((ext_vector_type(6)));
+struct Fp6LaneTerms {
+  uint32_t dw[4][6];
   int e[4];
 };
-__device__ __forceinline__ Fp6Block fp6_block_terms(float& v, int nt, int m) {
-  Fp6Block r;
-  const int L6 = m < 6 ? m : 5;
-  const int first = (32 * L6) / 6;
+__device__ __forceinline__ void fp6_lane_block_terms(lq_v16f& va, lq_v16f& vb, int nt,
+                                                     Fp6LaneTerms& r) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    r.dw[t] = 0u;
-    r.e[t] = 0;
     if (t < nt) {
-      const int e = e2m3_block_exponent(half_wave_max(fabsf(v)));
-      const uint32_t code = e2m3_encode(ldexpf(v, -e));
-      v -= ldexpf(e2m3_decode(code), e);
-      // Lane L < 6 assembles dword L of the 192 code bits from the codes of
-      // lanes first(L) .. first(L) + 5 (code n sits at bit 6n); all six
-      // exchanges first, then the branch-free assembly.
-      uint32_t cv[6];
+      float m16[16];
 #pragma unroll
-      for (int s6 = 0; s6 < 6; ++s6) cv[s6] = __shfl(code & 63u, min(first + s6, 31), 32);
-      uint32_t dw = 0u;
+      for (int i = 0; i < 16; ++i) m16[i] = fmaxf(fabsf(va[i]), fabsf(vb[i]));
 #pragma unroll
-      for (int s6 = 0; s6 < 6; ++s6) {
-        const int pos = 6 * (first + s6) - 32 * L6;
-        const uint32_t lo = pos >= 0 ? (cv[s6] << (pos & 31)) : (cv[s6] >> ((-pos) & 31));
-        dw |= (first + s6 <= 31 && pos < 32) ? lo : 0u;
+      for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+        for (int i = 0; i < w; ++i) m16[i] = fmaxf(m16[i], m16[i + w]);
+      // (a normal scale: 2^-127 would be a subnormal fp32 operand)
+      const int e = max(e2m3_block_exponent(m16[0]), -126);
+      const float sc = ldexpf(1.0f, e);
+      const lq_v6i codes = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(va, vb, sc);
+      // The conversion must not write registers it still reads: keeping the
+      // sources live past it stops the register allocator from giving the
+      // destination any of their registers.
+      asm volatile("" ::"v"(va), "v"(vb));
+      const lq_v32f back = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(codes, sc);
+      asm volatile("" ::"v"(codes));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        va[i] -= back[2 * i];
+        vb[i] -= back[2 * i + 1];
       }
-      r.dw[t] = dw;
+#pragma unroll
+      for (int k = 0; k < 6; ++k) r.dw[t][k] = (uint32_t)codes[k];
       r.e[t] = e;
     }
   }
-  return r;
+}
+
+// Where the lane-per-block conversion wants lifted column jj of a tile (its
+// LDS slot) and the sign-plane factor the value is pre-multiplied by. Column
+// offset r = jj % 32 of block (u, g) = jj / 32 meets plane j = r % 4 (factor
+// -4, -2, -1, +1 for j = 0..3) at reduction index n = 8 j + r / 4; index n
+// goes to va[n / 2] (n even, slot n / 2) or vb[n / 2] (n odd, slot
+// 16 + n / 2) of the lane that converts the block.
+__device__ __forceinline__ int fp6_slot(int jj, float& f) {
+  const int r = jj & 31, j = r & 3, n = 8 * j + (r >> 2);
+  f = j == 3 ? 1.0f : (j == 2 ? -1.0f : (j == 1 ? -2.0f : -4.0f));
+  return (jj & ~31) + ((n & 1) ? 16 : 0) + (n >> 1);
+}
+
+// FP6 terms of block blk of a tile whose 512 values sit in LDS in the
+// fp6_slot layout, by one lane. Returns the sum over the block's plane 0..2
+// values (n < 24) of what the terms represent, divided by the plane factor:
+// the block's share of the plane-0..2 column sum the product adds back.
+__device__ __forceinline__ float fp6_lane_block(const float* zt, int blk, int nt, Fp6LaneTerms& r) {
+  lq_v16f va, vb;
+  const float4* p = reinterpret_cast<const float4*>(zt + 32 * blk);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 qa = p[i], qb = p[4 + i];
+    va[4 * i] = qa.x; va[4 * i + 1] = qa.y; va[4 * i + 2] = qa.z; va[4 * i + 3] = qa.w;
+    vb[4 * i] = qb.x; vb[4 * i + 1] = qb.y; vb[4 * i + 2] = qb.z; vb[4 * i + 3] = qb.w;
+  }
+  float oa[12], ob[12];
+#pragma unroll
+  for (int i = 0; i < 12; ++i) {
+    oa[i] = va[i];
+    ob[i] = vb[i];
+  }
+  fp6_lane_block_terms(va, vb, nt, r);
+  float tp = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 12; ++i) {
+    const float inv = i < 4 ? -0.25f : (i < 8 ? -0.5f : -1.0f);    // 1 / factor of plane i / 4
+    tp = fmaf(oa[i] - va[i], inv, tp);
+    tp = fmaf(ob[i] - vb[i], inv, tp);
+  }
+  return tp;
 }
 
 }  // namespace lq

@@ -15,9 +15,9 @@
 //     factor of the sign-bit plane it meets (-4, -2, -1 or +1), then cut into
 //     nt terms; term t is the E2M3 rounding of the residual left by terms
 //     < t under its own power-of-two block scale (the largest that keeps the
-//     block's residual within E2M3's range). One 32-lane half-wavefront
-//     handles one block. The record also gets the sum over the tile's
-//     plane-0..2 columns of the values the terms represent.
+//     block's residual within E2M3's range). One lane converts one block
+//     with the packed conversion instructions. The record also gets the sum
+//     over the tile's plane-0..2 columns of the values the terms represent.
 // Workgroup (0, 0) also clears the split-K tickets of the VALU product that
 // follows on the same stream.
 #include "lq_prep.h"
@@ -39,9 +39,8 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     uint8_t* __restrict__ aop, int nt, int ncv, int rec,
     unsigned* __restrict__ tickets, int n_tickets) {
   __shared__ __align__(16) float xs[kSpanMax];
-  __shared__ float zt[kTileCols];
+  __shared__ __align__(16) float zt[kTileCols];   // kMode 1: fp6_slot layout, plane factors applied
   __shared__ float Ms[64 * 64];
-  __shared__ float red[8];
   const int q = blockIdx.x;
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
@@ -93,16 +92,14 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
 #pragma unroll
     for (int jr = 0; jr < kTileCols / kThreads; ++jr) {
       const int jj = tid + kThreads * jr;
-      float acc = 0.0f;
-      if (jj < width) {
-        const int col = c_lo + jj;
-        const int blk = col / D;
-        const int e = col - blk * D;
-        const int kb = blk * d;
-        const int nk = min(d, K - kb);
-        for (int i = 0; i < nk; ++i) acc = fmaf(Ms[i * D + e], xs[kb + i - h_lo], acc);
+      const float z = jj < width ? lift_column(Ms, xs, c_lo + jj, d, D, K, h_lo) : 0.0f;
+      if (kMode == 1) {
+        float f;
+        const int slot = fp6_slot(jj, f);
+        zt[slot] = f * z;
+      } else {
+        zt[jj] = z;
       }
-      zt[jj] = acc;
     }
   } else {
     const int64_t zrow = (int64_t)b * L + c_lo;
@@ -117,7 +114,16 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
       v[jr] = jj < width ? t : 0.0f;
     }
 #pragma unroll
-    for (int jr = 0; jr < kTileCols / kThreads; ++jr) zt[tid + kThreads * jr] = v[jr];
+    for (int jr = 0; jr < kTileCols / kThreads; ++jr) {
+      const int jj = tid + kThreads * jr;
+      if (kMode == 1) {
+        float f;
+        const int slot = fp6_slot(jj, f);
+        zt[slot] = f * v[jr];
+      } else {
+        zt[jj] = v[jr];
+      }
+    }
   }
   __syncthreads();
 
@@ -131,56 +137,28 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     return;
   }
 
-  // ---- FP6 operand (kMode 1). Half-wavefront h (0..15) takes block h
-  // of the tile's 16 blocks (u, g); lane m of the half holds
-  // the value meeting reduction index k = 32g + m, i.e. plane j = m / 8 of
-  // packed column 128u + 32g + 4(m % 8) + j.
+  // ---- FP6 operand (kMode 1): lane h < 16 of the first wavefront converts
+  // block h = (u, g) = (h / 4, h % 4) of the tile.
+  if (tid >= 16) return;
   uint8_t* recp = aop + (int64_t)q * rec;
-  const int m = tid & 31, half = tid >> 5;
-  const int j = m >> 3, i8 = m & 7;
-  const float f = j == 3 ? 1.0f : (j == 2 ? -1.0f : (j == 1 ? -2.0f : -4.0f));
-  float tp = 0.0f;
-  // Lane L < 6 of a half assembles dword L of a block's 192 code bits from
-  // the codes of lanes first(L) .. first(L) + 5 (code n sits at bit 6n).
-  const int L6 = m < 6 ? m : 5;
-  const int first = (32 * L6) / 6;
-  {
-    const int blk = half;
-    const int u = blk >> 2, g = blk & 3;
-    const float orig = f * zt[128 * u + 32 * g + 4 * i8 + j];
-    float v = orig;
-    for (int t = 0; t < nt; ++t) {
-      const int e = e2m3_block_exponent(half_wave_max(fabsf(v)));
-      const uint32_t code = e2m3_encode(ldexpf(v, -e));
-      v -= ldexpf(e2m3_decode(code), e);
-      // All six exchanges first, then the (branch-free) assembly.
-      uint32_t cv[6];
+  const int u = tid >> 2, g = tid & 3;
+  Fp6LaneTerms r;
+  float tp = fp6_lane_block(zt, tid, nt, r);
 #pragma unroll
-      for (int s6 = 0; s6 < 6; ++s6) cv[s6] = __shfl(code & 63u, min(first + s6, 31), 32);
-      uint32_t dw = 0u;
-#pragma unroll
-      for (int s6 = 0; s6 < 6; ++s6) {
-        const int pos = 6 * (first + s6) - 32 * L6;    // bit of the code within dword L6
-        const uint32_t lo = pos >= 0 ? (cv[s6] << (pos & 31)) : (cv[s6] >> ((-pos) & 31));
-        dw |= (first + s6 <= 31 && pos < 32) ? lo : 0u;
-      }
+  for (int t = 0; t < 4; ++t) {
+    if (t < nt) {
       const int cc = b * nt + t, cs = cc >> 4, cl = cc & 15;
       const int ncs = min(16, ncv - 16 * cs);
-      if (m < 8)
-        *reinterpret_cast<uint32_t*>(recp + aop_data_offset(cs, u, g, cl, ncs) + 4 * m) =
-            m < 6 ? dw : 0u;
-      if (m == 0) recp[aop_scale_offset(ncv, cs, g, cl, ncs) + u] = (uint8_t)(127 + e);
+      uint4* dst = reinterpret_cast<uint4*>(recp + aop_data_offset(cs, u, g, cl, ncs));
+      dst[0] = make_uint4(r.dw[t][0], r.dw[t][1], r.dw[t][2], r.dw[t][3]);
+      dst[1] = make_uint4(r.dw[t][4], r.dw[t][5], 0u, 0u);
+      recp[aop_scale_offset(ncv, cs, g, cl, ncs) + u] = (uint8_t)(127 + r.e[t]);
     }
-    if (j < 3) tp += (orig - v) / f;          // the value the terms represent
   }
-  // Plane-0..2 sum over the tile (fixed-order reduction).
+  // Plane-0..2 sum over the tile's 16 blocks (fixed-order butterfly).
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) tp += __shfl_xor(tp, o, 64);
-  if ((tid & 63) == 0) red[tid >> 6] = tp;
-  __syncthreads();
-  if (tid == 0)
-    *reinterpret_cast<float*>(recp + aop_tpart_offset(ncv) + 4 * b) =
-        ((red[0] + red[1]) + (red[2] + red[3])) + ((red[4] + red[5]) + (red[6] + red[7]));
+  for (int o = 8; o >= 1; o >>= 1) tp += __shfl_xor(tp, o, 16);
+  if (tid == 0) *reinterpret_cast<float*>(recp + aop_tpart_offset(ncv) + 4 * b) = tp;
 }
 
 template <int kMode, int kXKind>
