@@ -133,7 +133,7 @@ struct Exec {
   lq::OperandShape os;
   lq::FusedPlan fu;
   int tickets;
-  size_t off_tickets, off_aop, off_partial, off_zf32, off_xt, off_z, total;
+  size_t off_tickets, off_aop, off_partial, off_zf32, off_xt, off_zp, total;
 };
 
 // Plans a sign product of z (ztype) or, when `linear`, the whole operator
@@ -160,7 +160,7 @@ lq_status plan_exec(int64_t B, int64_t N, int64_t L, int64_t K, lq_dtype ztype, 
   }
   e->tickets = 0;
   e->off_tickets = e->off_aop = e->off_partial = 0;
-  e->off_zf32 = e->off_xt = e->off_z = 0;
+  e->off_zf32 = e->off_xt = e->off_zp = 0;
   const size_t ctl = align_up(lq::kFusedControlBytes);
   size_t at = ctl;
   auto take = [&](size_t bytes) { const size_t o = at; at += align_up(bytes); return o; };
@@ -188,10 +188,8 @@ lq_status plan_exec(int64_t B, int64_t N, int64_t L, int64_t K, lq_dtype ztype, 
       e->off_aop = take(lq::operand_bytes(L, e->os));
       break;
     case LQ_ALGO_MFMA_LARGE:
-      if (linear) {
-        e->off_xt = take((size_t)B * K * sizeof(float));
-        e->off_z = take((size_t)B * L * dtype_size(ztype));
-      }
+      if (linear) e->off_xt = take((size_t)B * K * sizeof(float));
+      e->off_zp = take(lq::zp_geom(B, e->g, ztype == LQ_BF16).bytes);
       break;
     default:
       return LQ_ERR_INVALID_ARG;
@@ -256,18 +254,19 @@ lq_status run_exec(const Exec& e, const uint8_t* packed, const void* zin, lq_dty
       }));
     }
     case LQ_ALGO_MFMA_LARGE: {
-      const void* z = zin;
+      void* zp = base + e.off_zp;
       if (layer) {
         float* xt = reinterpret_cast<float*>(base + e.off_xt);
-        void* zl = base + e.off_z;
         s = hip_status(lq::launch_hadamard_scale(zin, zb, B, layer->K, layer->hb, layer->c, xt, st));
         if (s != LQ_OK) return s;
-        s = hip_status(lq::launch_lift(xt, B, layer->K, layer->d, layer->D, layer->M, zl, zb, st));
-        if (s != LQ_OK) return s;
-        z = zl;
+        s = hip_status(lq::launch_zp(xt, zb ? 3 : 2, B, L, layer->K, layer->d, layer->D, layer->M,
+                                     e.g, zp, st));
+      } else {
+        s = hip_status(lq::launch_zp(zin, zb ? 1 : 0, B, L, 0, 1, 1, nullptr, e.g, zp, st));
       }
+      if (s != LQ_OK) return s;
       return hip_status(profiled(st, [&] {
-        return lq::launch_sign_mfma_large(packed, e.g, z, zb, B, row_scale, y, yb, st);
+        return lq::launch_sign_mfma_large(packed, e.g, zp, zb, B, row_scale, y, yb, st);
       }));
     }
     default:

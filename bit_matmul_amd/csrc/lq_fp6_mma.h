@@ -23,16 +23,6 @@ __device__ __forceinline__ f32x4 mfma_fp4_fp6(uint32_t w, const i32x8& b, uint32
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 2, 0, 127, U, (int)scale);
 }
 
-// Workgroup barrier without a memory fence: this wavefront's LDS accesses
-// complete, then s_barrier; the memory clobber keeps the compiler from moving
-// memory accesses across it. (__syncthreads would also wait for every global
-// load in flight, since the loader's LDS copies count as global loads.) LDS
-// copies (global_load_lds) are waited for explicitly by the loader before
-// the barrier that publishes them.
-__device__ __forceinline__ void wg_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 __device__ __forceinline__ i32x8 lds_b_operand(const uint8_t* p) {
   const uint4 lo = *reinterpret_cast<const uint4*>(p);
   const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);

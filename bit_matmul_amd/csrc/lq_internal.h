@@ -82,6 +82,16 @@ __device__ __forceinline__ uint4 load_slot(const uint8_t* __restrict__ panel, in
   return load_tail_slot(panel, full_tiles, tail_bytes, g, r);
 }
 
+// Workgroup barrier without a memory fence: this wavefront's LDS accesses
+// complete, then s_barrier; the memory clobber keeps the compiler from moving
+// memory accesses across it. (__syncthreads would also wait for every global
+// load in flight, since the loader's LDS copies count as global loads.) LDS
+// copies (global_load_lds) are waited for explicitly by the loader before
+// the barrier that publishes them.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Index of the calling thread's wavefront as a wave-uniform (scalar) value,
 // so that branches on it are scalar and do not make the compiler wait for
 // outstanding loads at their joins.
@@ -263,7 +273,23 @@ hipError_t launch_sign_valu(const uint8_t* packed, const PackedGeom& g, const vo
 hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t stream);
 
 // ---- large batch: bf16 matrix-core GEMM (z bf16, or fp32 as a hi + lo pair).
-hipError_t launch_sign_mfma_large(const uint8_t* packed, const PackedGeom& g, const void* z,
+// z is first rewritten into the operand order of the product ("zp": per 16
+// batch rows and 128-column step a 4 KB block; nterm bf16 planes).
+struct ZpGeom {
+  int64_t B16, steps;
+  int nterm;
+  size_t bytes;
+};
+ZpGeom zp_geom(int64_t B, const PackedGeom& g, bool z_bf16);
+struct LargePlan {
+  int ppw, jb;      // panels per compute wavefront, 16-row batch tiles per workgroup
+};
+LargePlan plan_large(int64_t B, const PackedGeom& g, bool z_bf16);
+// kind 0: z fp32, 1: z bf16 (both B x L); 2: lift xt (B x K fp32) with M into
+// fp32-precision zp (two planes), 3: the same into bf16 zp (one plane).
+hipError_t launch_zp(const void* src, int kind, int64_t B, int64_t L, int64_t K, int d, int D,
+                     const float* M, const PackedGeom& g, void* zp, hipStream_t stream);
+hipError_t launch_sign_mfma_large(const uint8_t* packed, const PackedGeom& g, const void* zp,
                                   bool z_bf16, int64_t B, const float* row_scale, void* y,
                                   bool y_bf16, hipStream_t stream);
 

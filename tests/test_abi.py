@@ -117,7 +117,8 @@ def test_sign_gemm_validation_and_workspace():
     f = LIB.lq_sign_gemm_ex
     st, need = ws_size(1, 4096, 34416, LQ_F32, 1)
     assert st == LQ_OK and need > 0
-    assert ws_size(1, 4096, 34416, LQ_BF16, 3) == (LQ_OK, 0)
+    st3, need3 = ws_size(1, 4096, 34416, LQ_BF16, 3)
+    assert st3 == LQ_OK and need3 >= 34416 * 16 * 2     # z in operand order: 16 rows per tile
     assert ws_size(17, 4096, 34416, LQ_BF16, 2)[0] == LQ_ERR_UNSUPPORTED   # small MFMA: B <= 16
     assert ws_size(1, 4096, 34416, LQ_BF16, 9)[0] == LQ_ERR_INVALID_ARG
     assert ws_size(1, 4095, 34416, LQ_BF16, 0)[0] == LQ_ERR_UNSUPPORTED
