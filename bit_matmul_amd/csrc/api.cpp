@@ -133,7 +133,7 @@ struct Exec {
   lq::OperandShape os;
   lq::FusedPlan fu;
   int tickets;
-  size_t off_tickets, off_aop, off_partial, off_zf32, off_xt, off_zp, total;
+  size_t off_tickets, off_aop, off_partial, off_zf32, off_xt, off_zp, off_tslots, total;
 };
 
 // Plans a sign product of z (ztype) or, when `linear`, the whole operator
@@ -160,7 +160,7 @@ lq_status plan_exec(int64_t B, int64_t N, int64_t L, int64_t K, lq_dtype ztype, 
   }
   e->tickets = 0;
   e->off_tickets = e->off_aop = e->off_partial = 0;
-  e->off_zf32 = e->off_xt = e->off_zp = 0;
+  e->off_zf32 = e->off_xt = e->off_zp = e->off_tslots = 0;
   const size_t ctl = align_up(lq::kFusedControlBytes);
   size_t at = ctl;
   auto take = [&](size_t bytes) { const size_t o = at; at += align_up(bytes); return o; };
@@ -189,7 +189,11 @@ lq_status plan_exec(int64_t B, int64_t N, int64_t L, int64_t K, lq_dtype ztype, 
       break;
     case LQ_ALGO_MFMA_LARGE:
       if (linear) e->off_xt = take((size_t)B * K * sizeof(float));
-      e->off_zp = take(lq::zp_geom(B, e->g, ztype == LQ_BF16).bytes);
+      {
+        const lq::ZpGeom zg = lq::zp_geom(B, e->g, ztype == LQ_BF16);
+        e->off_zp = take(zg.bytes);
+        e->off_tslots = take(zg.tail_bytes);
+      }
       break;
     default:
       return LQ_ERR_INVALID_ARG;
@@ -266,7 +270,8 @@ lq_status run_exec(const Exec& e, const uint8_t* packed, const void* zin, lq_dty
       }
       if (s != LQ_OK) return s;
       return hip_status(profiled(st, [&] {
-        return lq::launch_sign_mfma_large(packed, e.g, zp, zb, B, row_scale, y, yb, st);
+        return lq::launch_sign_mfma_large(packed, e.g, zp, base + e.off_tslots, zb, B, row_scale, y,
+                                          yb, st);
       }));
     }
     default:

@@ -278,7 +278,8 @@ hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t stream);
 struct ZpGeom {
   int64_t B16, steps;
   int nterm;
-  size_t bytes;
+  size_t bytes;        // zp itself
+  size_t tail_bytes;   // the tail tile's slots in full-tile form (1 KB per panel), if L % 512
 };
 ZpGeom zp_geom(int64_t B, const PackedGeom& g, bool z_bf16);
 struct LargePlan {
@@ -290,7 +291,8 @@ LargePlan plan_large(int64_t B, const PackedGeom& g, bool z_bf16);
 hipError_t launch_zp(const void* src, int kind, int64_t B, int64_t L, int64_t K, int d, int D,
                      const float* M, const PackedGeom& g, void* zp, hipStream_t stream);
 hipError_t launch_sign_mfma_large(const uint8_t* packed, const PackedGeom& g, const void* zp,
-                                  bool z_bf16, int64_t B, const float* row_scale, void* y,
-                                  bool y_bf16, hipStream_t stream);
+                                  void* tail_slots, bool z_bf16, int64_t B,
+                                  const float* row_scale, void* y, bool y_bf16,
+                                  hipStream_t stream);
 
 }  // namespace lq

@@ -115,107 +115,153 @@ __global__ __launch_bounds__(256) void zp_kernel(const void* __restrict__ src, i
   if (NTERM == 2) zp[B16 * steps * (kZpBlock / 16) + unit] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
 }
 
+// ------------------------------------------------------------ tail slots
+// The slots of the partial tail tile of every panel, assembled once into
+// full-tile form (1 KB per panel), so that the product loads every tile's
+// slot with one 16-byte load from one of two addresses. Thread = (panel, lane).
+__global__ __launch_bounds__(256) void tail_slots_kernel(const uint8_t* __restrict__ packed,
+                                                         int64_t panels, int64_t panel_bytes,
+                                                         int full_tiles, int tail_bytes,
+                                                         uint4* __restrict__ out) {
+  const int64_t pnl = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (pnl >= panels) return;
+  out[pnl * 64 + lane] =
+      load_tail_slot(packed + pnl * panel_bytes, full_tiles, tail_bytes, lane >> 4, lane & 15);
+}
+
 // ------------------------------------------------------------ product
-// Workgroup tile: 4 * PPW panels (64 PPW rows) x 16 JB batch rows. Waves
-// 0..3 compute (wave w: panels w PPW .. w PPW + PPW - 1, all JB batch
-// tiles); wave 4 only copies zp blocks into LDS, one 128-column step ahead,
-// alternating between two stages. The packed slots go from memory straight
-// into registers, one tile (4 steps) ahead. Per step t, two workgroup
-// barriers: (A) every wave is done with step t - 1, whose stage the copy of
-// step t + 1 overwrites; (B) the copy of step t has landed (the loader waits
-// for its copies between A and B, then issues the next step's).
-template <int NTERM, int PPW, int JB, bool kYBF16>
-__global__ __launch_bounds__(320) void sign_mfma_large_kernel(
+// Workgroup: 4 wavefronts; tile 4 PW panels (64 PW rows) x 16 JB batch rows.
+// Wavefront w owns panels w PW .. w PW + PW - 1 and all JB batch tiles:
+// each B operand read from LDS feeds PW MFMAs, each sign operand built in
+// registers feeds JB (times the z terms). Four LDS stages, one per step of
+// a 512-column tile: at step t the four wavefronts copy the zp blocks of
+// step t + 3 into the stage of step t - 1 while they multiply step t. The
+// stages are separate LDS arrays, so the compiler knows a copy into one
+// does not alias the reads of another and does not make those reads wait
+// for it. One barrier per step: every wavefront has waited for its own
+// copies of step t (its copies of steps t + 1 and t + 2, issued later, may
+// still be in flight: memory operations complete in order) and is done
+// with step t - 1, whose stage the next copy overwrites. The packed slots
+// go from memory straight into registers, one tile (4 steps) ahead.
+template <int NTERM, int PW, int JB, bool kYBF16>
+__global__ __launch_bounds__(256) void sign_mfma_large_kernel(
     const uint8_t* __restrict__ packed, int64_t panels, int64_t panel_bytes, int full_tiles,
     int tail_bytes, int ext_tiles, const uint4* __restrict__ zp, int64_t B16, int64_t B,
-    const float* __restrict__ row_scale, void* __restrict__ y, int64_t N) {
-  extern __shared__ uint4 lds[];              // [stage 2][term][jb][s][g][r]
-  constexpr int kStageUnits = NTERM * JB * (kZpBlock / 16);
+    const uint4* __restrict__ tail_slots, const float* __restrict__ row_scale,
+    void* __restrict__ y, int64_t N) {
+  constexpr int kStageUnits = NTERM * JB * (kZpBlock / 16);   // [term][jb][s][g][r]
+  constexpr int kSlotUnits = 4 * PW * 64;                      // [wave][panel][lane]
+  __shared__ uint4 stage0[kStageUnits];
+  __shared__ uint4 stage1[kStageUnits];
+  __shared__ uint4 stage2[kStageUnits];
+  __shared__ uint4 stage3[kStageUnits];
+  __shared__ uint4 slotA[kSlotUnits];
+  __shared__ uint4 slotB[kSlotUnits];
   const int wave = wave_id(), lane = threadIdx.x & 63;
-  const int g = lane >> 4, r = lane & 15;
   const int64_t steps = 4 * (int64_t)ext_tiles;
+  const int64_t last = steps - 1;
   const int64_t jb0 = (int64_t)blockIdx.y * JB;
+  const int64_t pbase = (int64_t)blockIdx.x * 4 * PW + wave * PW;
 
-  if (wave == 4) {
-    auto copy_step = [&](int64_t t, int st) {
+  auto dma = [&](const void* src, uint4* dst) {
+    __builtin_amdgcn_global_load_lds(
+        (const void*)(reinterpret_cast<const uint8_t*>(src) + 16 * lane),
+        (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+  };
+  // zp blocks of one step: NTERM * JB blocks of 4 KB, i.e. 4 NTERM JB
+  // wavefront copies of 1 KB, spread over the 4 wavefronts.
+  auto copy_step = [&](int64_t t, uint4* dst) {
+#pragma unroll
+    for (int c = 0; c < NTERM * JB; ++c) {
+      const int term = c / JB, j = c % JB;
+      const int64_t jb = min(jb0 + j, B16 - 1);
+      dma(reinterpret_cast<const uint8_t*>(zp) + ((term * B16 + jb) * steps + t) * kZpBlock + 1024 * wave,
+          dst + (c * kZpBlock + 1024 * wave) / 16);
+    }
+  };
+  // The slots (1 KB per panel: the tile itself, or its assembled tail) of
+  // tile q for this wavefront's panels.
+  auto copy_slots = [&](int q, uint4* dst) {
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      const int64_t pnl = min(pbase + i, panels - 1);
+      const void* src = q < full_tiles
+                            ? (const void*)(packed + pnl * panel_bytes + (int64_t)q * kTileBytes)
+                            : (const void*)(tail_slots + pnl * 64);
+      dma(src, dst + (wave * PW + i) * 64);
+    }
+  };
+
+  f32x4 acc[PW][JB];
+#pragma unroll
+  for (int i = 0; i < PW; ++i)
+#pragma unroll
+    for (int j = 0; j < JB; ++j) acc[i][j] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto mult = [&](const uint4* st, const uint32_t (&w)[PW][4], int u) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 a[PW];
+#pragma unroll
+      for (int i = 0; i < PW; ++i) a[i] = sign_operand(w[i][u], s);
 #pragma unroll
       for (int term = 0; term < NTERM; ++term)
 #pragma unroll
         for (int j = 0; j < JB; ++j) {
-          const int64_t jb = min(jb0 + j, B16 - 1);
-          const uint8_t* srcb = reinterpret_cast<const uint8_t*>(zp) +
-                                ((term * B16 + jb) * steps + t) * kZpBlock;
-          uint8_t* dstb = reinterpret_cast<uint8_t*>(lds + st * kStageUnits) + (term * JB + j) * kZpBlock;
+          const uint4 bv = st[((term * JB + j) * 4 + s) * 64 + lane];
+          const u32x4 bop = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_global_load_lds((const void*)(srcb + 1024 * i + 16 * lane),
-                                             (__attribute__((address_space(3))) void*)(dstb + 1024 * i),
-                                             16, 0, 0);
+          for (int i = 0; i < PW; ++i) acc[i][j] = mfma_bf16(a[i], bop, acc[i][j]);
         }
-    };
-    copy_step(0, 0);
-    for (int64_t t = 0; t < steps; t += 2) {
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {              // step t + k, stage k
-        wg_barrier();                            // (A)
-        __builtin_amdgcn_s_waitcnt(0);           // the copy of step t + k
-        wg_barrier();                            // (B)
-        if (t + k + 1 < steps) copy_step(t + k + 1, k ^ 1);
-      }
     }
-    return;
+  };
+
+  // Every step issues its copies unconditionally (past the last step, the
+  // last step again, into a stage no later step reads), so that at least
+  // 2 kCopies copy instructions follow those of step t when step t begins:
+  // waiting until at most that many are outstanding means the copies of
+  // step t, and every copy issued before them (the slots of the current
+  // tile among them), have landed.
+  constexpr int kCopies = NTERM * JB;
+  constexpr int kWait2 = (7 << 4) | (15 << 8) | ((2 * kCopies) & 15) | (((2 * kCopies) >> 4) << 14);
+  static_assert(2 * kCopies <= 63, "vmcnt range");
+  copy_slots(0, slotA);
+  copy_step(0, stage0);
+  copy_step(min((int64_t)1, last), stage1);
+  copy_step(min((int64_t)2, last), stage2);
+
+  auto tile = [&](int q, const uint4* slot_cur, uint4* slot_next) {
+    uint32_t w[PW][4];
+    const int64_t t0 = 4 * (int64_t)q;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {                // step t = t0 + u, stage u
+      __builtin_amdgcn_s_waitcnt(kWait2);
+      wg_barrier();
+      if (u == 0) {
+#pragma unroll
+        for (int i = 0; i < PW; ++i) {
+          const uint4 v = slot_cur[(wave * PW + i) * 64 + lane];
+          w[i][0] = v.x; w[i][1] = v.y; w[i][2] = v.z; w[i][3] = v.w;
+        }
+      }
+      copy_step(min(t0 + u + 3, last), u == 0 ? stage3 : (u == 1 ? stage0 : (u == 2 ? stage1 : stage2)));
+      if (u == 0) copy_slots(min(q + 1, ext_tiles - 1), slot_next);
+      mult(u == 0 ? stage0 : (u == 1 ? stage1 : (u == 2 ? stage2 : stage3)), w, u);
+    }
+  };
+  for (int q = 0; q < ext_tiles; q += 2) {
+    tile(q, slotA, slotB);
+    if (q + 1 < ext_tiles) tile(q + 1, slotB, slotA);
   }
 
-  const int64_t pbase = (int64_t)blockIdx.x * 4 * PPW + wave * PPW;
-  const uint8_t* prow[PPW];
-#pragma unroll
-  for (int i = 0; i < PPW; ++i) prow[i] = packed + min(pbase + i, panels - 1) * panel_bytes;
-
-  f32x4 acc[PPW][JB];
-#pragma unroll
-  for (int i = 0; i < PPW; ++i)
-#pragma unroll
-    for (int j = 0; j < JB; ++j) acc[i][j] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-
-  uint4 wn[PPW];
-#pragma unroll
-  for (int i = 0; i < PPW; ++i) wn[i] = load_slot(prow[i], 0, full_tiles, tail_bytes, g, r);
-  for (int q = 0; q < ext_tiles; ++q) {
-    uint32_t w[PPW][4];
-#pragma unroll
-    for (int i = 0; i < PPW; ++i) {
-      w[i][0] = wn[i].x; w[i][1] = wn[i].y; w[i][2] = wn[i].z; w[i][3] = wn[i].w;
-    }
-    const int qn = min(q + 1, ext_tiles - 1);
-#pragma unroll
-    for (int i = 0; i < PPW; ++i) wn[i] = load_slot(prow[i], qn, full_tiles, tail_bytes, g, r);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {                // step 4q + u, stage u & 1
-      wg_barrier();                              // (A)
-      wg_barrier();                              // (B)
-      const uint4* st = lds + (u & 1) * kStageUnits;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        u32x4 a[PPW];
-#pragma unroll
-        for (int i = 0; i < PPW; ++i) a[i] = sign_operand(w[i][u], s);
-#pragma unroll
-        for (int term = 0; term < NTERM; ++term)
-#pragma unroll
-          for (int j = 0; j < JB; ++j) {
-            const uint4 bv = st[((term * JB + j) * 4 + s) * 64 + lane];
-            const u32x4 bop = {bv.x, bv.y, bv.z, bv.w};
-#pragma unroll
-            for (int i = 0; i < PPW; ++i) acc[i][j] = mfma_bf16(a[i], bop, acc[i][j]);
-          }
-      }
-    }
-  }
-
+  // No copy may still be writing LDS when the workgroup ends.
+  __builtin_amdgcn_s_waitcnt(0);
   // Epilogue: lane (g, r) of tile (i, j) holds rows 4g..4g+3 of panel
   // pbase + i for batch row 16 (jb0 + j) + r.
+  const int g = lane >> 4, r = lane & 15;
 #pragma unroll
-  for (int i = 0; i < PPW; ++i) {
+  for (int i = 0; i < PW; ++i) {
     const int64_t pnl = pbase + i;
     if (pnl >= panels) continue;
     const int64_t n0 = pnl * kPanelRows + 4 * g;
@@ -238,33 +284,28 @@ __global__ __launch_bounds__(320) void sign_mfma_large_kernel(
   }
 }
 
-template <int NTERM, int PPW, int JB, bool kYBF16>
+template <int NTERM, int PW, int JB, bool kYBF16>
 hipError_t launch_large_t(const uint8_t* packed, const PackedGeom& g, const uint4* zp, int64_t B,
-                          const float* row_scale, void* y, hipStream_t stream) {
-  const size_t lds = (size_t)2 * NTERM * JB * kZpBlock;
-  static size_t allowed = 0;
-  if (lds > 64 * 1024 && lds > allowed) {
-    const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&sign_mfma_large_kernel<NTERM, PPW, JB, kYBF16>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    allowed = lds;
-  }
+                          const uint4* tail_slots, const float* row_scale, void* y,
+                          hipStream_t stream) {
   const int64_t B16 = (B + 15) / 16;
-  const dim3 grid((unsigned)((g.panels + 4 * PPW - 1) / (4 * PPW)), (unsigned)((B16 + JB - 1) / JB));
-  return launch_timed(sign_mfma_large_kernel<NTERM, PPW, JB, kYBF16>, grid, dim3(320), lds, stream,
+  const dim3 grid((unsigned)((g.panels + 4 * PW - 1) / (4 * PW)), (unsigned)((B16 + JB - 1) / JB));
+  return launch_timed(sign_mfma_large_kernel<NTERM, PW, JB, kYBF16>, grid, dim3(256), 0, stream,
                       packed, g.panels, g.panel_bytes, g.full_tiles, g.tail_bytes, g.ext_tiles, zp,
-                      B16, B, row_scale, y, g.N);
+                      B16, B, tail_slots, row_scale, y, g.N);
 }
 
 template <int NTERM, bool kYBF16>
 hipError_t launch_large_y(const uint8_t* packed, const PackedGeom& g, const uint4* zp, int64_t B,
-                          const float* row_scale, void* y, const LargePlan& p, hipStream_t stream) {
-#define LQ_LARGE_CASE(PPW_, JB_)                                                                   \
-  if (p.ppw == PPW_ && p.jb == JB_)                                                                \
-    return launch_large_t<NTERM, PPW_, JB_, kYBF16>(packed, g, zp, B, row_scale, y, stream);
-  LQ_LARGE_CASE(2, 8) LQ_LARGE_CASE(2, 4) LQ_LARGE_CASE(2, 2) LQ_LARGE_CASE(2, 1)
-  LQ_LARGE_CASE(1, 8) LQ_LARGE_CASE(1, 4) LQ_LARGE_CASE(1, 2) LQ_LARGE_CASE(1, 1)
+                          const uint4* tail_slots, const float* row_scale, void* y,
+                          const LargePlan& p, hipStream_t stream) {
+#define LQ_LARGE_CASE(PW_, JB_)                                                                    \
+  if (p.ppw == PW_ && p.jb == JB_)                                                                 \
+    return launch_large_t<NTERM, PW_, JB_, kYBF16>(packed, g, zp, B, tail_slots, row_scale, y,    \
+                                                   stream);
+  LQ_LARGE_CASE(4, 4) LQ_LARGE_CASE(4, 2) LQ_LARGE_CASE(4, 1)
+  LQ_LARGE_CASE(2, 4) LQ_LARGE_CASE(2, 2) LQ_LARGE_CASE(2, 1)
+  LQ_LARGE_CASE(1, 4) LQ_LARGE_CASE(1, 2) LQ_LARGE_CASE(1, 1)
 #undef LQ_LARGE_CASE
   return hipErrorInvalidValue;
 }
@@ -277,17 +318,23 @@ ZpGeom zp_geom(int64_t B, const PackedGeom& g, bool z_bf16) {
   z.steps = 4 * (int64_t)g.ext_tiles;
   z.nterm = z_bf16 ? 1 : 2;
   z.bytes = (size_t)z.nterm * z.B16 * z.steps * kZpBlock;
+  z.tail_bytes = g.tail_bytes ? (size_t)g.panels * kTileBytes : 0;
   return z;
 }
 
 LargePlan plan_large(int64_t B, const PackedGeom& g, bool z_bf16) {
   LargePlan p;
   const int64_t B16 = (B + 15) / 16;
-  p.jb = B16 >= 8 ? 8 : (B16 >= 4 ? 4 : (B16 >= 2 ? 2 : 1));
+  // fp32 z (two bf16 planes) at most 2 batch tiles: four stages of 4 still
+  // fit LDS, but only just.
+  p.jb = B16 >= 4 && z_bf16 ? 4 : (B16 >= 2 ? 2 : 1);
   const int64_t bt = (B16 + p.jb - 1) / p.jb;
-  // Two panels per wavefront when that still gives >= 512 workgroups (more
-  // would not fit the registers of two wavefronts per SIMD).
-  p.ppw = ((g.panels + 7) / 8) * bt >= 512 ? 2 : 1;
+  // The most panels per wavefront (up to 4: more spill registers) that still
+  // give >= 512 workgroups.
+  p.ppw = 1;
+  for (int c : {4, 2}) {
+    if (((g.panels + 4 * c - 1) / (4 * c)) * bt >= 512) { p.ppw = c; break; }
+  }
   return p;
 }
 
@@ -313,16 +360,24 @@ hipError_t launch_zp(const void* src, int kind, int64_t B, int64_t L, int64_t K,
 }
 
 hipError_t launch_sign_mfma_large(const uint8_t* packed, const PackedGeom& g, const void* zp,
-                                  bool z_bf16, int64_t B, const float* row_scale, void* y,
-                                  bool y_bf16, hipStream_t stream) {
+                                  void* tail_slots, bool z_bf16, int64_t B,
+                                  const float* row_scale, void* y, bool y_bf16,
+                                  hipStream_t stream) {
   (void)hipGetLastError();   // clear a stale error of an earlier runtime call
   const LargePlan p = plan_large(B, g, z_bf16);
   const uint4* z = reinterpret_cast<const uint4*>(zp);
+  uint4* ts = reinterpret_cast<uint4*>(tail_slots);
+  if (g.tail_bytes) {
+    hipLaunchKernelGGL(tail_slots_kernel, dim3((unsigned)((g.panels + 3) / 4)), dim3(256), 0, stream,
+                       packed, g.panels, g.panel_bytes, g.full_tiles, g.tail_bytes, ts);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (z_bf16)
-    return y_bf16 ? launch_large_y<1, true>(packed, g, z, B, row_scale, y, p, stream)
-                  : launch_large_y<1, false>(packed, g, z, B, row_scale, y, p, stream);
-  return y_bf16 ? launch_large_y<2, true>(packed, g, z, B, row_scale, y, p, stream)
-                : launch_large_y<2, false>(packed, g, z, B, row_scale, y, p, stream);
+    return y_bf16 ? launch_large_y<1, true>(packed, g, z, B, ts, row_scale, y, p, stream)
+                  : launch_large_y<1, false>(packed, g, z, B, ts, row_scale, y, p, stream);
+  return y_bf16 ? launch_large_y<2, true>(packed, g, z, B, ts, row_scale, y, p, stream)
+                : launch_large_y<2, false>(packed, g, z, B, ts, row_scale, y, p, stream);
 }
 
 }  // namespace lq
