@@ -37,15 +37,26 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// A operand (8 bf16 +-1) of sub-step s (0..3) from one packed word.
-__device__ __forceinline__ u32x4 sign_operand(uint32_t w, int s) {
+// A operand (8 bf16 +-1) of sub-step s (0..3) from one packed word: per
+// dword one shift and one and-or of the two sign bits into 1.0. The mask and
+// the 1.0 pair are passed in registers (mask, one): with them as constants
+// the compiler emits a separate and and or, since these three-operand
+// instructions take no literal constants on this target.
+__device__ __forceinline__ u32x4 sign_operand(uint32_t w, int s, uint32_t mask, uint32_t one) {
   u32x4 a;
   const int p0 = 4 * s;
-  a.x = ((w << (15 - p0)) & 0x80008000u) | 0x3F803F80u;
-  a.y = ((w << (14 - p0)) & 0x80008000u) | 0x3F803F80u;
-  a.z = ((w << (13 - p0)) & 0x80008000u) | 0x3F803F80u;
-  a.w = ((w << (12 - p0)) & 0x80008000u) | 0x3F803F80u;
+  a.x = ((w << (15 - p0)) & mask) | one;
+  a.y = ((w << (14 - p0)) & mask) | one;
+  a.z = ((w << (13 - p0)) & mask) | one;
+  a.w = ((w << (12 - p0)) & mask) | one;
   return a;
+}
+
+// A 32-bit constant in a vector register, opaque to constant folding.
+__device__ __forceinline__ uint32_t vreg_const(uint32_t v) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
+  return r;
 }
 
 // ------------------------------------------------------------ zp
@@ -59,7 +70,8 @@ __global__ __launch_bounds__(256) void zp_kernel(const void* __restrict__ src, i
                                                  const float* __restrict__ M, int64_t steps,
                                                  int64_t B16, int64_t jb_base, uint4* __restrict__ zp) {
   __shared__ float Ms[kSrc == 2 ? 64 * 64 : 1];
-  __shared__ __align__(16) float xs[kSrc == 2 ? 16 * 256 : 1];
+  constexpr int kXs = 257;                      // row stride: rows in different banks
+  __shared__ __align__(16) float xs[kSrc == 2 ? 16 * kXs : 1];
   const int64_t step = blockIdx.x, jb = jb_base + blockIdx.y;
   const int t = threadIdx.x;
   const int s = t >> 6, g = (t >> 4) & 3, r = t & 15;
@@ -79,13 +91,13 @@ __global__ __launch_bounds__(256) void zp_kernel(const void* __restrict__ src, i
     for (int i = t; i < 16 * 256; i += 256) {
       const int rr = i >> 8, k = i & 255;
       const int64_t bb = 16 * jb + rr;
-      xs[i] = (bb < B && k < span) ? reinterpret_cast<const float*>(src)[bb * K + k_lo + k] : 0.0f;
+      xs[kXs * rr + k] = (bb < B && k < span) ? reinterpret_cast<const float*>(src)[bb * K + k_lo + k] : 0.0f;
     }
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int64_t c = c0 + (j < 4 ? j : 12 + j);
-      v[j] = (b < B && c < L) ? lift_column(Ms, xs + 256 * r, (int)c, d, D, (int)K, (int)k_lo) : 0.0f;
+      v[j] = (b < B && c < L) ? lift_column(Ms, xs + kXs * r, (int)c, d, D, (int)K, (int)k_lo) : 0.0f;
     }
   } else {
 #pragma unroll
@@ -199,21 +211,38 @@ __global__ __launch_bounds__(256) void sign_mfma_large_kernel(
 #pragma unroll
     for (int j = 0; j < JB; ++j) acc[i][j] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 
+  const uint32_t kMask = vreg_const(0x80008000u), kOne = vreg_const(0x3F803F80u);
+  // One step: 4 sub-steps; the B operands of sub-step s + 1 are read from
+  // LDS before the MFMAs of sub-step s are issued, so that the LDS latency
+  // hides behind them (reading each just before its use leaves it exposed).
   auto mult = [&](const uint4* st, const uint32_t (&w)[PW][4], int u) {
+    constexpr int NB = NTERM * JB;
+    uint4 bcur[NB], bnext[NB];
+#pragma unroll
+    for (int c = 0; c < NB; ++c) bcur[c] = st[(c * 4 + 0) * 64 + lane];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      if (s < 3) {
+#pragma unroll
+        for (int c = 0; c < NB; ++c) bnext[c] = st[(c * 4 + s + 1) * 64 + lane];
+      }
+      // Keep those reads here: the scheduler would otherwise sink each one
+      // next to its first use.
+      __builtin_amdgcn_sched_barrier(0);
       u32x4 a[PW];
 #pragma unroll
-      for (int i = 0; i < PW; ++i) a[i] = sign_operand(w[i][u], s);
+      for (int i = 0; i < PW; ++i) a[i] = sign_operand(w[i][u], s, kMask, kOne);
 #pragma unroll
-      for (int term = 0; term < NTERM; ++term)
+      for (int c = 0; c < NB; ++c) {
+        const int j = c % JB;
+        const u32x4 bop = {bcur[c].x, bcur[c].y, bcur[c].z, bcur[c].w};
 #pragma unroll
-        for (int j = 0; j < JB; ++j) {
-          const uint4 bv = st[((term * JB + j) * 4 + s) * 64 + lane];
-          const u32x4 bop = {bv.x, bv.y, bv.z, bv.w};
+        for (int i = 0; i < PW; ++i) acc[i][j] = mfma_bf16(a[i], bop, acc[i][j]);
+      }
+      if (s < 3) {
 #pragma unroll
-          for (int i = 0; i < PW; ++i) acc[i][j] = mfma_bf16(a[i], bop, acc[i][j]);
-        }
+        for (int c = 0; c < NB; ++c) bcur[c] = bnext[c];
+      }
     }
   };
 
@@ -299,11 +328,15 @@ template <int NTERM, bool kYBF16>
 hipError_t launch_large_y(const uint8_t* packed, const PackedGeom& g, const uint4* zp, int64_t B,
                           const uint4* tail_slots, const float* row_scale, void* y,
                           const LargePlan& p, hipStream_t stream) {
+  // (fp32 z: at most 2 batch tiles, or the LDS stages would not fit)
 #define LQ_LARGE_CASE(PW_, JB_)                                                                    \
-  if (p.ppw == PW_ && p.jb == JB_)                                                                 \
-    return launch_large_t<NTERM, PW_, JB_, kYBF16>(packed, g, zp, B, tail_slots, row_scale, y,    \
-                                                   stream);
-  LQ_LARGE_CASE(4, 4) LQ_LARGE_CASE(4, 2) LQ_LARGE_CASE(4, 1)
+  if constexpr (NTERM * JB_ <= 4 || (NTERM == 1 && JB_ == 8 && PW_ == 4)) {                        \
+    if (p.ppw == PW_ && p.jb == JB_)                                                               \
+      return launch_large_t<NTERM, PW_, JB_, kYBF16>(packed, g, zp, B, tail_slots, row_scale, y,  \
+                                                     stream);                                      \
+  }
+  LQ_LARGE_CASE(8, 4) LQ_LARGE_CASE(8, 2) LQ_LARGE_CASE(8, 1)
+  LQ_LARGE_CASE(4, 8) LQ_LARGE_CASE(4, 4) LQ_LARGE_CASE(4, 2) LQ_LARGE_CASE(4, 1)
   LQ_LARGE_CASE(2, 4) LQ_LARGE_CASE(2, 2) LQ_LARGE_CASE(2, 1)
   LQ_LARGE_CASE(1, 4) LQ_LARGE_CASE(1, 2) LQ_LARGE_CASE(1, 1)
 #undef LQ_LARGE_CASE
@@ -325,14 +358,21 @@ ZpGeom zp_geom(int64_t B, const PackedGeom& g, bool z_bf16) {
 LargePlan plan_large(int64_t B, const PackedGeom& g, bool z_bf16) {
   LargePlan p;
   const int64_t B16 = (B + 15) / 16;
-  // fp32 z (two bf16 planes) at most 2 batch tiles: four stages of 4 still
-  // fit LDS, but only just.
+  // bf16 z with >= 128 batch rows: 4 panels x 8 batch tiles per wavefront
+  // (each sign operand feeds 8 MFMAs), when that still gives >= 512
+  // workgroups; the four stages of 32 KB and the slots then fill LDS.
+  if (z_bf16 && B16 >= 8 && ((g.panels + 15) / 16) * ((B16 + 7) / 8) >= 512) {
+    p.jb = 8;
+    p.ppw = 4;
+    return p;
+  }
+  // fp32 z (two bf16 planes): at most 2 batch tiles, or the stages would
+  // not fit LDS.
   p.jb = B16 >= 4 && z_bf16 ? 4 : (B16 >= 2 ? 2 : 1);
   const int64_t bt = (B16 + p.jb - 1) / p.jb;
-  // The most panels per wavefront (up to 4: more spill registers) that still
-  // give >= 512 workgroups.
+  // The most panels per wavefront that still give >= 512 workgroups.
   p.ppw = 1;
-  for (int c : {4, 2}) {
+  for (int c : {8, 4, 2}) {
     if (((g.panels + 4 * c - 1) / (4 * c)) * bt >= 512) { p.ppw = c; break; }
   }
   return p;
