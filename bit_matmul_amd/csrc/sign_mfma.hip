@@ -60,71 +60,109 @@ __device__ __forceinline__ uint32_t vreg_const(uint32_t v) {
 }
 
 // ------------------------------------------------------------ zp
-// Workgroup (step, jb): the 4 KB block of batch rows 16 jb .. 16 jb + 15 and
-// columns 128 step .. 128 step + 127; thread t = unit (s, g, r) = t.
+// Workgroup (tile q, jb): batch rows 16 jb .. 16 jb + 15 and the tile's 512
+// columns, i.e. the 4 KB blocks of steps 4q .. 4q + 3. Thread (u, g, r)
+// (u = step in the tile) makes the 32 values of row 16 jb + r, columns
+// c = 128 (4q + u) + 32 g + [0, 32), and writes units (s, g, r) of step
+// 4q + u for s = 0..3: unit s holds columns c + 4s + {0..3} and
+// c + 16 + 4s + {0..3}. For a fixed s the 64 lanes of a wavefront write
+// 1 KB of consecutive units.
 // kSrc 0: z fp32, 1: z bf16 (B x L, row-major), 2: lift from xt (B x K fp32)
-// with M (the lq_linear path: z is never written in row-major form).
+// with M (the lq_linear path: z is never written in row-major form). For the
+// lift the workgroup stages M and the rows' original columns [k_lo, k_lo +
+// span) (span <= (511 / D + 2) d <= 639) in LDS (dynamic: d D + 16 xstride
+// floats).
 template <int kSrc, int NTERM>
 __global__ __launch_bounds__(256) void zp_kernel(const void* __restrict__ src, int64_t B, int64_t L,
                                                  int64_t K, int d, int D,
                                                  const float* __restrict__ M, int64_t steps,
-                                                 int64_t B16, int64_t jb_base, uint4* __restrict__ zp) {
-  __shared__ float Ms[kSrc == 2 ? 64 * 64 : 1];
-  constexpr int kXs = 257;                      // row stride: rows in different banks
-  __shared__ __align__(16) float xs[kSrc == 2 ? 16 * kXs : 1];
-  const int64_t step = blockIdx.x, jb = jb_base + blockIdx.y;
+                                                 int64_t B16, int64_t jb_base, int xstride,
+                                                 uint4* __restrict__ zp) {
+  extern __shared__ float lds_f[];
+  const int64_t q = blockIdx.x, jb = jb_base + blockIdx.y;
   const int t = threadIdx.x;
-  const int s = t >> 6, g = (t >> 4) & 3, r = t & 15;
+  const int u = t >> 6, g = (t >> 4) & 3, r = t & 15;
   const int64_t b = 16 * jb + r;
-  const int64_t c0 = 128 * step + 32 * g + 4 * s;
-  float v[8];                                   // z[b][c0 + j] (j < 4), z[b][c0 + 12 + j] (j >= 4)
+  const int64_t c_lo = 512 * q + 128 * u + 32 * g;
+  float v[32];
   if (kSrc == 2) {
-    // The d-blocks of columns [128 step, 128 step + 128): original columns
-    // [k_lo, k_lo + span), span <= (127 / D + 2) d <= 256.
-    const int64_t col_lo = 128 * step;
-    const int64_t blk_lo = col_lo / D;
-    const int64_t blk_hi = (min(col_lo + 127, L - 1)) / D;
+    float* Ms = lds_f;
+    float* xs = lds_f + d * D;
+    const int64_t tile_lo = 512 * q;
+    const int64_t blk_lo = tile_lo / D;
+    const int64_t blk_hi = (min(tile_lo + 511, L - 1)) / D;
     const int64_t k_lo = blk_lo * d;
-    const int64_t k_hi = min((blk_hi + 1) * d, K);
-    const int span = col_lo < L ? (int)(k_hi - k_lo) : 0;
+    const int span = (int)(min((blk_hi + 1) * d, K) - k_lo);
     for (int i = t; i < d * D; i += 256) Ms[i] = M[i];
-    for (int i = t; i < 16 * 256; i += 256) {
-      const int rr = i >> 8, k = i & 255;
+    for (int rr = 0; rr < 16; ++rr) {
       const int64_t bb = 16 * jb + rr;
-      xs[kXs * rr + k] = (bb < B && k < span) ? reinterpret_cast<const float*>(src)[bb * K + k_lo + k] : 0.0f;
+      for (int k = t; k < span; k += 256)
+        xs[xstride * rr + k] = bb < B ? reinterpret_cast<const float*>(src)[bb * K + k_lo + k] : 0.0f;
     }
     __syncthreads();
+    // Column c_lo + k is block blk, element e; walk them in order.
+    const float* xr = xs + xstride * r;
+    int64_t blk = c_lo / D;
+    int e = (int)(c_lo - blk * D);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t c = c0 + (j < 4 ? j : 12 + j);
-      v[j] = (b < B && c < L) ? lift_column(Ms, xs + kXs * r, (int)c, d, D, (int)K, (int)k_lo) : 0.0f;
+    for (int k = 0; k < 32; ++k) {
+      float acc = 0.0f;
+      if (b < B && c_lo + k < L) {
+        const int64_t kb = blk * d;
+        const int nk = (int)min((int64_t)d, K - kb);
+        const float* xb = xr + (kb - k_lo);
+        for (int i = 0; i < nk; ++i) acc = fmaf(Ms[i * D + e], xb[i], acc);
+      }
+      v[k] = acc;
+      if (++e == D) {
+        e = 0;
+        ++blk;
+      }
     }
   } else {
+    // 32 consecutive values (L % 8 == 0: every 8-value chunk is in or out).
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t c = c0 + (j < 4 ? j : 12 + j);
-      float x = 0.0f;
-      if (b < B && c < L) {
-        if (kSrc == 1) x = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(src)[b * L + c]);
-        else x = reinterpret_cast<const float*>(src)[b * L + c];
+    for (int k8 = 0; k8 < 4; ++k8) {
+      const int64_t c = c_lo + 8 * k8;
+      const bool in = b < B && c < L;
+      if (kSrc == 1) {
+        const uint4 w = in ? *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(src) + b * L + c)
+                           : make_uint4(0u, 0u, 0u, 0u);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          v[8 * k8 + 2 * h] = __uint_as_float(ww[h] << 16);
+          v[8 * k8 + 2 * h + 1] = __uint_as_float(ww[h] & 0xFFFF0000u);
+        }
+      } else {
+        const float* zr = reinterpret_cast<const float*>(src) + b * L + c;
+        const float4 lo = in ? *reinterpret_cast<const float4*>(zr) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 hi = in ? *reinterpret_cast<const float4*>(zr + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        v[8 * k8 + 0] = lo.x; v[8 * k8 + 1] = lo.y; v[8 * k8 + 2] = lo.z; v[8 * k8 + 3] = lo.w;
+        v[8 * k8 + 4] = hi.x; v[8 * k8 + 5] = hi.y; v[8 * k8 + 6] = hi.z; v[8 * k8 + 7] = hi.w;
       }
-      v[j] = x;
     }
   }
-  uint32_t hi[4], lo[4];
+  const int64_t step = 4 * q + u;
+  const int64_t base = (jb * steps + step) * (kZpBlock / 16) + g * 16 + r;
+  const int64_t plane = B16 * steps * (kZpBlock / 16);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t h0 = f32_to_bf16_bits(v[j]), h1 = f32_to_bf16_bits(v[4 + j]);
-    hi[j] = h0 | (h1 << 16);
-    if (NTERM == 2) {
-      const uint32_t l0 = f32_to_bf16_bits(v[j] - bf16_bits_to_f32(h0));
-      const uint32_t l1 = f32_to_bf16_bits(v[4 + j] - bf16_bits_to_f32(h1));
-      lo[j] = l0 | (l1 << 16);
+  for (int s = 0; s < 4; ++s) {
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a0 = v[4 * s + j], a1 = v[16 + 4 * s + j];
+      const uint32_t h0 = f32_to_bf16_bits(a0), h1 = f32_to_bf16_bits(a1);
+      hi[j] = h0 | (h1 << 16);
+      if (NTERM == 2) {
+        const uint32_t l0 = f32_to_bf16_bits(a0 - bf16_bits_to_f32(h0));
+        const uint32_t l1 = f32_to_bf16_bits(a1 - bf16_bits_to_f32(h1));
+        lo[j] = l0 | (l1 << 16);
+      }
     }
+    zp[base + s * 64] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    if (NTERM == 2) zp[plane + base + s * 64] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
   }
-  const int64_t unit = (jb * steps + step) * (kZpBlock / 16) + t;
-  zp[unit] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-  if (NTERM == 2) zp[B16 * steps * (kZpBlock / 16) + unit] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
 }
 
 // ------------------------------------------------------------ tail slots
@@ -383,14 +421,18 @@ hipError_t launch_zp(const void* src, int kind, int64_t B, int64_t L, int64_t K,
   (void)hipGetLastError();   // clear a stale error of an earlier runtime call
   const ZpGeom z = zp_geom(B, g, kind == 1 || kind == 3);
   uint4* out = reinterpret_cast<uint4*>(zp);
+  // Lift: LDS for M and 16 rows of the tile's original columns (odd stride).
+  const int span_max = kind >= 2 ? (int)((511 / D + 2) * d) : 0;
+  const int xstride = span_max | 1;
+  const size_t lds = kind >= 2 ? (size_t)(d * D + 16 * xstride) * sizeof(float) : 0;
   // Batch tiles map to grid.y, at most 65535 per launch.
   for (int64_t jb0 = 0; jb0 < z.B16; jb0 += 65535) {
-    const dim3 grid((unsigned)z.steps, (unsigned)min(z.B16 - jb0, (int64_t)65535));
+    const dim3 grid((unsigned)g.ext_tiles, (unsigned)min(z.B16 - jb0, (int64_t)65535));
     switch (kind) {
-      case 0: hipLaunchKernelGGL((zp_kernel<0, 2>), grid, dim3(256), 0, stream, src, B, L, K, d, D, M, z.steps, z.B16, jb0, out); break;
-      case 1: hipLaunchKernelGGL((zp_kernel<1, 1>), grid, dim3(256), 0, stream, src, B, L, K, d, D, M, z.steps, z.B16, jb0, out); break;
-      case 2: hipLaunchKernelGGL((zp_kernel<2, 2>), grid, dim3(256), 0, stream, src, B, L, K, d, D, M, z.steps, z.B16, jb0, out); break;
-      case 3: hipLaunchKernelGGL((zp_kernel<2, 1>), grid, dim3(256), 0, stream, src, B, L, K, d, D, M, z.steps, z.B16, jb0, out); break;
+      case 0: hipLaunchKernelGGL((zp_kernel<0, 2>), grid, dim3(256), lds, stream, src, B, L, K, d, D, M, z.steps, z.B16, jb0, xstride, out); break;
+      case 1: hipLaunchKernelGGL((zp_kernel<1, 1>), grid, dim3(256), lds, stream, src, B, L, K, d, D, M, z.steps, z.B16, jb0, xstride, out); break;
+      case 2: hipLaunchKernelGGL((zp_kernel<2, 2>), grid, dim3(256), lds, stream, src, B, L, K, d, D, M, z.steps, z.B16, jb0, xstride, out); break;
+      case 3: hipLaunchKernelGGL((zp_kernel<2, 1>), grid, dim3(256), lds, stream, src, B, L, K, d, D, M, z.steps, z.B16, jb0, xstride, out); break;
       default: return hipErrorInvalidValue;
     }
     const hipError_t e = hipGetLastError();
