@@ -17,7 +17,8 @@ Printed (one JSON line): whole-step packed-weight throughput in GB/s
 (`value`), the roofline of the dominant kernel (the sign product), timed
 with HIP events around each of its launches inside the timed graph, and the
 CPU oracle's rate on a bounded sample of the same workload. With
-`--prefill`, also the 2048-token prefill layer (d = 3, D = 8) in TFLOP/s.
+The 2048-token prefill layer (d = 3, D = 8) is timed too, in TFLOP/s (its
+own object in the line; `--no-prefill` skips it).
 
 Synthetic data: packed weights are uniformly random bytes (i.e. independent
 fair signs), M ~ N(0, 1/D), row scales ~ U[0.5, 1.5], channel scales ~
@@ -58,8 +59,8 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--prefill", action="store_true",
-                   help="also time the 2048-token prefill layer (TFLOP/s)")
+    p.add_argument("--no-prefill", action="store_true",
+                   help="skip the 2048-token prefill layer (TFLOP/s)")
     p.add_argument("--eager", action="store_true",
                    help="launch the timed steps eagerly, each sign product timed by its own "
                         "dispatch events (slows the launches down)")
@@ -508,7 +509,7 @@ def main():
             "algorithmic_bytes_per_launch": dec["bytes_per_launch"],
         },
     }
-    if args.prefill:
+    if not args.no_prefill:
         pf = run_prefill(args, torch, lq, ev)
         out["prefill"] = {
             "metric": "TFLOP/s (batch 2048), lifted flops 2*B*N*L",

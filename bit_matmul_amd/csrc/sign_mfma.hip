@@ -250,20 +250,20 @@ __global__ __launch_bounds__(256) void sign_mfma_large_kernel(
     for (int j = 0; j < JB; ++j) acc[i][j] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 
   const uint32_t kMask = vreg_const(0x80008000u), kOne = vreg_const(0x3F803F80u);
-  // One step: 4 sub-steps; the B operands of sub-step s + 1 are read from
-  // LDS before the MFMAs of sub-step s are issued, so that the LDS latency
-  // hides behind them (reading each just before its use leaves it exposed).
-  auto mult = [&](const uint4* st, const uint32_t (&w)[PW][4], int u) {
-    constexpr int NB = NTERM * JB;
-    uint4 bcur[NB], bnext[NB];
-#pragma unroll
-    for (int c = 0; c < NB; ++c) bcur[c] = st[(c * 4 + 0) * 64 + lane];
+  // One step: 4 sub-steps; the B operands of the next sub-step (for the
+  // last one, sub-step 0 of the next step, whose stage is complete by then)
+  // are read from LDS before the MFMAs of this one are issued, so that the
+  // LDS latency hides behind them (reading each just before its use leaves
+  // it exposed).
+  constexpr int NB = NTERM * JB;
+  auto mult = [&](const uint4* st, const uint4* st_next, const uint32_t (&w)[PW][4], int u,
+                  uint4 (&bcur)[NB]) {
+    uint4 bnext[NB];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      if (s < 3) {
 #pragma unroll
-        for (int c = 0; c < NB; ++c) bnext[c] = st[(c * 4 + s + 1) * 64 + lane];
-      }
+      for (int c = 0; c < NB; ++c)
+        bnext[c] = s < 3 ? st[(c * 4 + s + 1) * 64 + lane] : st_next[(c * 4) * 64 + lane];
       // Keep those reads here: the scheduler would otherwise sink each one
       // next to its first use.
       __builtin_amdgcn_sched_barrier(0);
@@ -277,33 +277,33 @@ __global__ __launch_bounds__(256) void sign_mfma_large_kernel(
 #pragma unroll
         for (int i = 0; i < PW; ++i) acc[i][j] = mfma_bf16(a[i], bop, acc[i][j]);
       }
-      if (s < 3) {
 #pragma unroll
-        for (int c = 0; c < NB; ++c) bcur[c] = bnext[c];
-      }
+      for (int c = 0; c < NB; ++c) bcur[c] = bnext[c];
     }
   };
 
   // Every step issues its copies unconditionally (past the last step, the
   // last step again, into a stage no later step reads), so that at least
-  // 2 kCopies copy instructions follow those of step t when step t begins:
-  // waiting until at most that many are outstanding means the copies of
-  // step t, and every copy issued before them (the slots of the current
-  // tile among them), have landed.
+  // kCopies copy instructions follow those of step t + 1 when step t
+  // begins: waiting until at most that many are outstanding means the copies
+  // of step t + 1, and every copy issued before them (the slots of the
+  // current tile among them), have landed. After the barrier, stages t and
+  // t + 1 are complete.
   constexpr int kCopies = NTERM * JB;
-  constexpr int kWait2 = (7 << 4) | (15 << 8) | ((2 * kCopies) & 15) | (((2 * kCopies) >> 4) << 14);
-  static_assert(2 * kCopies <= 63, "vmcnt range");
+  constexpr int kWait1 = (7 << 4) | (15 << 8) | (kCopies & 15) | ((kCopies >> 4) << 14);
+  static_assert(kCopies <= 63, "vmcnt range");
   copy_slots(0, slotA);
   copy_step(0, stage0);
   copy_step(min((int64_t)1, last), stage1);
   copy_step(min((int64_t)2, last), stage2);
+  uint4 bcur[NB];
 
   auto tile = [&](int q, const uint4* slot_cur, uint4* slot_next) {
     uint32_t w[PW][4];
     const int64_t t0 = 4 * (int64_t)q;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {                // step t = t0 + u, stage u
-      __builtin_amdgcn_s_waitcnt(kWait2);
+      __builtin_amdgcn_s_waitcnt(kWait1);
       wg_barrier();
       if (u == 0) {
 #pragma unroll
@@ -311,10 +311,15 @@ __global__ __launch_bounds__(256) void sign_mfma_large_kernel(
           const uint4 v = slot_cur[(wave * PW + i) * 64 + lane];
           w[i][0] = v.x; w[i][1] = v.y; w[i][2] = v.z; w[i][3] = v.w;
         }
+        if (q == 0) {
+#pragma unroll
+          for (int c = 0; c < NB; ++c) bcur[c] = stage0[(c * 4) * 64 + lane];
+        }
       }
       copy_step(min(t0 + u + 3, last), u == 0 ? stage3 : (u == 1 ? stage0 : (u == 2 ? stage1 : stage2)));
       if (u == 0) copy_slots(min(q + 1, ext_tiles - 1), slot_next);
-      mult(u == 0 ? stage0 : (u == 1 ? stage1 : (u == 2 ? stage2 : stage3)), w, u);
+      mult(u == 0 ? stage0 : (u == 1 ? stage1 : (u == 2 ? stage2 : stage3)),
+           u == 0 ? stage1 : (u == 1 ? stage2 : (u == 2 ? stage3 : stage0)), w, u, bcur);
     }
   };
   for (int q = 0; q < ext_tiles; q += 2) {
