@@ -250,15 +250,19 @@ __global__ __launch_bounds__(256) void sign_mfma_large_kernel(
     for (int j = 0; j < JB; ++j) acc[i][j] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 
   const uint32_t kMask = vreg_const(0x80008000u), kOne = vreg_const(0x3F803F80u);
-  // One step: 4 sub-steps; the B operands of the next sub-step (for the
-  // last one, sub-step 0 of the next step, whose stage is complete by then)
-  // are read from LDS before the MFMAs of this one are issued, so that the
-  // LDS latency hides behind them (reading each just before its use leaves
-  // it exposed).
+  // One step: 4 sub-steps. The B operands of the next sub-step (for the last
+  // one, sub-step 0 of the next step, whose stage is complete by then) are
+  // read from LDS before the MFMAs of this one are issued, so that the LDS
+  // latency hides behind them; the sign operands of the next sub-step are
+  // built into other registers while these MFMAs run (building them into the
+  // registers the MFMAs still read would stall on those reads). At the last
+  // sub-step of a tile the next tile's words are not loaded yet: its first
+  // sign operands are built at the start of the next step.
   constexpr int NB = NTERM * JB;
   auto mult = [&](const uint4* st, const uint4* st_next, const uint32_t (&w)[PW][4], int u,
-                  uint4 (&bcur)[NB]) {
+                  uint4 (&bcur)[NB], u32x4 (&acur)[PW]) {
     uint4 bnext[NB];
+    u32x4 anext[PW];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
@@ -267,18 +271,25 @@ __global__ __launch_bounds__(256) void sign_mfma_large_kernel(
       // Keep those reads here: the scheduler would otherwise sink each one
       // next to its first use.
       __builtin_amdgcn_sched_barrier(0);
-      u32x4 a[PW];
+      if (s < 3 || u < 3) {
 #pragma unroll
-      for (int i = 0; i < PW; ++i) a[i] = sign_operand(w[i][u], s, kMask, kOne);
+        for (int i = 0; i < PW; ++i)
+          anext[i] = sign_operand(w[i][s < 3 ? u : u + 1], (s + 1) & 3, kMask, kOne);
+      }
 #pragma unroll
-      for (int c = 0; c < NB; ++c) {
-        const int j = c % JB;
-        const u32x4 bop = {bcur[c].x, bcur[c].y, bcur[c].z, bcur[c].w};
+      for (int i = 0; i < PW; ++i) {
 #pragma unroll
-        for (int i = 0; i < PW; ++i) acc[i][j] = mfma_bf16(a[i], bop, acc[i][j]);
+        for (int c = 0; c < NB; ++c) {
+          const u32x4 bop = {bcur[c].x, bcur[c].y, bcur[c].z, bcur[c].w};
+          acc[i][c % JB] = mfma_bf16(acur[i], bop, acc[i][c % JB]);
+        }
       }
 #pragma unroll
       for (int c = 0; c < NB; ++c) bcur[c] = bnext[c];
+      if (s < 3 || u < 3) {
+#pragma unroll
+        for (int i = 0; i < PW; ++i) acur[i] = anext[i];
+      }
     }
   };
 
@@ -297,6 +308,7 @@ __global__ __launch_bounds__(256) void sign_mfma_large_kernel(
   copy_step(min((int64_t)1, last), stage1);
   copy_step(min((int64_t)2, last), stage2);
   uint4 bcur[NB];
+  u32x4 acur[PW];
 
   auto tile = [&](int q, const uint4* slot_cur, uint4* slot_next) {
     uint32_t w[PW][4];
@@ -315,11 +327,13 @@ __global__ __launch_bounds__(256) void sign_mfma_large_kernel(
 #pragma unroll
           for (int c = 0; c < NB; ++c) bcur[c] = stage0[(c * 4) * 64 + lane];
         }
+#pragma unroll
+        for (int i = 0; i < PW; ++i) acur[i] = sign_operand(w[i][0], 0, kMask, kOne);
       }
       copy_step(min(t0 + u + 3, last), u == 0 ? stage3 : (u == 1 ? stage0 : (u == 2 ? stage1 : stage2)));
       if (u == 0) copy_slots(min(q + 1, ext_tiles - 1), slot_next);
       mult(u == 0 ? stage0 : (u == 1 ? stage1 : (u == 2 ? stage2 : stage3)),
-           u == 0 ? stage1 : (u == 1 ? stage2 : (u == 2 ? stage3 : stage0)), w, u, bcur);
+           u == 0 ? stage1 : (u == 1 ? stage2 : (u == 2 ? stage3 : stage0)), w, u, bcur, acur);
     }
   };
   for (int q = 0; q < ext_tiles; q += 2) {
