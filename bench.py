@@ -46,7 +46,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 ROOT = os.path.dirname(os.path.abspath(__file__))
 SIGN_KERNEL = "sign_fp6_kernel"
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_sign_fp6_llama3_8b_mlp_b1.txt")
+LARGE_KERNEL = "sign_mfma_large_kernel"
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_llama3_8b_mlp_b1_and_prefill_8192_b2048.txt")
 COPY_BYTES = 256 << 20         # the calibration copy of --pmc-workload
 
 
@@ -107,8 +108,7 @@ def _read_rocprof_rows(d, kind):
             return rows
         for fn in glob.glob(os.path.join(d, "**", "*results.db"), recursive=True):
             db = sqlite3.connect(fn)
-            q = ("select k.name, p.counter_name, p.value, p.dispatch_id from pmc_events p "
-                 "join kernels k on k.dispatch_id = p.dispatch_id")
+            q = "select name, counter_name, counter_value, dispatch_id from pmc_events"
             try:
                 for name, cn, v, did in db.execute(q):
                     rows.append(dict(kernel=name, counter=cn, value=float(v), dispatch=did))
@@ -195,9 +195,9 @@ def summarize_pmc(fetch_dir, write_dir):
     return "\n".join(lines)
 
 
-def traffic_from_summary():
-    """HBM bytes per launch of the sign product from the committed counter
-    summary, or None when there is none or it was taken on other sources."""
+def traffic_from_summary(kernel=SIGN_KERNEL):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    or None when there is none or it was taken on other sources."""
     try:
         with open(TRAFFIC_SUMMARY) as f:
             text = f.read()
@@ -210,7 +210,7 @@ def traffic_from_summary():
         if len(parts) >= 2 and parts[0] in ("sources", "fetch_factor", "write_factor"):
             kv[parts[0]] = parts[1]
         m = re.match(r"^kernel (.*) fetch_kib ([0-9.]+) write_kib ([0-9.]+)$", line)
-        if m and SIGN_KERNEL in m.group(1):
+        if m and kernel in m.group(1):
             kern[m.group(1)] = (float(m.group(2)), float(m.group(3)))
     if kv.get("sources") != kernel_sources_hash() or not kern:
         return None
@@ -232,6 +232,9 @@ def pmc_workload(torch, lq):
         for l in layers[i % len(layers)]:
             x = x_in["down"] if l["name"] == "down" else x_in["gate"]
             lq.lq_linear(l["struct"], x, 1, ys[l["name"]], ws)
+    torch.cuda.synchronize()
+    pf = build_prefill_case(torch, lq)
+    lq.lq_linear(pf["struct"], pf["x"], pf["B"], pf["y"], pf["ws"])
     torch.cuda.synchronize()
     print("pmc workload done", flush=True)
 
@@ -366,10 +369,10 @@ def run_decode(args, torch, lq, ev):
                 n_sets=n_sets, timing=timing)
 
 
-def run_prefill(args, torch, lq, ev, steps=10):
+def build_prefill_case(torch, lq):
+    """The 2048-token prefill layer (8192 -> 8192, d = 3, D = 8) on the GPU."""
     from workloads import WORKLOADS
-    wl = WORKLOADS["prefill"]
-    s = wl.layers[0]
+    s = WORKLOADS["prefill"].layers[0]
     B = 2048
     dev = "cuda"
     gen = torch.Generator(device=dev)
@@ -383,6 +386,12 @@ def run_prefill(args, torch, lq, ev, steps=10):
     x = torch.randn(B, s.K, device=dev, generator=gen).to(torch.bfloat16)
     y = torch.empty(B, s.N, dtype=torch.bfloat16, device=dev)
     ws = torch.zeros(lq.lq_linear_workspace_size(st, B, torch.bfloat16), dtype=torch.uint8, device=dev)
+    return dict(spec=s, B=B, packed=packed, M=M, r=r, c=c, struct=st, x=x, y=y, ws=ws)
+
+
+def run_prefill(args, torch, lq, ev, steps=10):
+    pf = build_prefill_case(torch, lq)
+    s, B, st, x, y, ws = pf["spec"], pf["B"], pf["struct"], pf["x"], pf["y"], pf["ws"]
     for _ in range(2):
         lq.lq_linear(st, x, B, y, ws)
     torch.cuda.synchronize()
@@ -521,7 +530,7 @@ def main():
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(pf["kernel_tflops"] / BF16_PEAK_TFLOPS, 4),
                          "avg_launch_us": round(pf["kernel_ms"] * 1e3, 2),
-                         "traffic": None},
+                         "traffic": traffic_from_summary(LARGE_KERNEL)},
         }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
