@@ -60,6 +60,8 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--decode-algo", default="auto", choices=["auto", "small", "fused", "local", "valu"],
+                   help="algorithm of the decode lq_linear calls (lq_linear_ex; auto = lq_linear)")
     p.add_argument("--no-prefill", action="store_true",
                    help="skip the 2048-token prefill layer (TFLOP/s)")
     p.add_argument("--eager", action="store_true",
@@ -295,7 +297,8 @@ def build_decode_case(torch, lq, n_sets, seed=0):
         "down": torch.from_numpy(host[down_spec.name].x(1)).to(dev).to(torch.bfloat16),
     }
     ys = {p: torch.empty((1, s.N), dtype=torch.bfloat16, device=dev) for p, s in specs}
-    ws_bytes = max(lq.lq_linear_workspace_size(layers[0][i]["struct"], 1, torch.bfloat16) for i in range(3))
+    ws_bytes = max(lq.lq_linear_workspace_size_ex(layers[0][i]["struct"], 1, torch.bfloat16, a)
+                   for i in range(3) for a in (lq.LQ_ALGO_AUTO, lq.LQ_ALGO_MFMA_SMALL))
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)      # zeroed control area
     return specs, layers, x_in, ys, ws, M
 
@@ -305,10 +308,23 @@ def run_decode(args, torch, lq, ev):
     n_sets = len(layers)
     step_bytes = sum(l["bytes"] for l in layers[0])
 
+    algo = {"auto": None, "small": lq.LQ_ALGO_MFMA_SMALL, "fused": lq.LQ_ALGO_FUSED,
+            "local": lq.LQ_ALGO_FUSED_LOCAL, "valu": lq.LQ_ALGO_VALU}[args.decode_algo]
+
+    def call(l, x):
+        # An algorithm that does not apply to a layer falls back to lq_linear's choice.
+        if algo is not None and l.get("algo_ok", {}).get(algo, True):
+            try:
+                lq.lq_linear_ex(l["struct"], x, 1, ys[l["name"]], algo, ws)
+                return
+            except lq.LQError:
+                l.setdefault("algo_ok", {})[algo] = False
+        lq.lq_linear(l["struct"], x, 1, ys[l["name"]], ws)
+
     def step(i):
         for l in layers[i % n_sets]:
             x = x_in["down"] if l["name"] == "down" else x_in["gate"]
-            lq.lq_linear(l["struct"], x, 1, ys[l["name"]], ws)
+            call(l, x)
 
     for i in range(args.warmup):
         step(i)
@@ -503,6 +519,7 @@ def main():
             "weight_sets": dec["n_sets"],
             "packed_bytes_per_step": dec["step_bytes"],
             "graph": not args.eager,
+            "decode_algo": args.decode_algo,
         },
         "roofline": {
             "bound": "hbm",

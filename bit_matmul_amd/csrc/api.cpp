@@ -120,7 +120,7 @@ int device_cus() {
 }
 
 bool valid_algo(lq_algo algo, bool linear) {
-  return algo >= LQ_ALGO_AUTO && algo <= (linear ? LQ_ALGO_FUSED : LQ_ALGO_MFMA_LARGE);
+  return algo >= LQ_ALGO_AUTO && algo <= (linear ? LQ_ALGO_FUSED_LOCAL : LQ_ALGO_MFMA_LARGE);
 }
 
 // Everything one sign product (or one whole lq_linear) needs: algorithm,
@@ -132,6 +132,7 @@ struct Exec {
   lq::Fp6Plan fp;
   lq::OperandShape os;
   lq::FusedPlan fu;
+  lq::SelfPlan sp;
   int tickets;
   size_t off_tickets, off_aop, off_partial, off_zf32, off_xt, off_zp, off_tslots, total;
 };
@@ -141,8 +142,8 @@ struct Exec {
 // Every workspace that is used at all starts with the control area of the
 // one-launch decode (only that kernel writes it), so one workspace can serve
 // calls of every algorithm in turn.
-lq_status plan_exec(int64_t B, int64_t N, int64_t L, int64_t K, lq_dtype ztype, lq_algo algo,
-                    bool linear, Exec* e) {
+lq_status plan_exec(int64_t B, int64_t N, int64_t L, int64_t K, int d, int D, lq_dtype ztype,
+                    lq_algo algo, bool linear, Exec* e) {
   e->g = lq::make_geom(N, L);
   e->algo = algo;
   if (algo == LQ_ALGO_AUTO) {
@@ -186,6 +187,12 @@ lq_status plan_exec(int64_t B, int64_t N, int64_t L, int64_t K, lq_dtype ztype, 
       e->fu = lq::plan_fused(B, e->g, e->os, device_cus());
       if (!e->fu.ok) return LQ_ERR_UNSUPPORTED;
       e->off_aop = take(lq::operand_bytes(L, e->os));
+      break;
+    case LQ_ALGO_FUSED_LOCAL:
+      if (!linear) return LQ_ERR_INVALID_ARG;
+      e->os = lq::operand_shape(B, ztype == LQ_BF16);
+      e->sp = lq::plan_self(B, K, d, D, e->g, e->os);
+      if (!e->sp.ok) return LQ_ERR_UNSUPPORTED;
       break;
     case LQ_ALGO_MFMA_LARGE:
       if (linear) e->off_xt = take((size_t)B * K * sizeof(float));
@@ -257,6 +264,12 @@ lq_status run_exec(const Exec& e, const uint8_t* packed, const void* zin, lq_dty
                                        e.fu, st);
       }));
     }
+    case LQ_ALGO_FUSED_LOCAL:
+      return hip_status(profiled(st, [&] {
+        return lq::launch_decode_self(packed, e.g, zin, zb, layer->K, layer->d, layer->D,
+                                      layer->hb, layer->c, layer->M, e.os, row_scale, y, yb, e.sp,
+                                      st);
+      }));
     case LQ_ALGO_MFMA_LARGE: {
       void* zp = base + e.off_zp;
       if (layer) {
@@ -375,7 +388,7 @@ lq_status lq_sign_gemm_workspace_size(int64_t B, int64_t N, int64_t L, lq_dtype 
   if (s != LQ_OK) return s;
   if (B == 0 || N == 0) { *bytes = 0; return LQ_OK; }
   Exec e;
-  s = plan_exec(B, N, L, 0, ztype, algo, false, &e);
+  s = plan_exec(B, N, L, 0, 1, 1, ztype, algo, false, &e);
   if (s != LQ_OK) return s;
   *bytes = e.total;
   return LQ_OK;
@@ -390,7 +403,7 @@ lq_status lq_sign_gemm_ex(const uint8_t* packed, const void* z, lq_dtype ztype, 
   if (s != LQ_OK) return s;
   if (B == 0 || N == 0) return LQ_OK;
   Exec e;
-  s = plan_exec(B, N, L, 0, ztype, algo, false, &e);
+  s = plan_exec(B, N, L, 0, 1, 1, ztype, algo, false, &e);
   if (s != LQ_OK) return s;
   if (!aligned16(packed) || !aligned16(z) || !aligned16(row_scale) || !aligned16(y))
     return LQ_ERR_INVALID_ARG;
@@ -418,7 +431,7 @@ lq_status lq_linear_workspace_size_ex(const lq_layer* layer, int64_t B, lq_dtype
   if (!mul_ok(B, layer->K, kMaxElems)) return LQ_ERR_UNSUPPORTED;
   if (B == 0 || layer->N == 0) { *bytes = 0; return LQ_OK; }
   Exec e;
-  s = plan_exec(B, layer->N, L, layer->K, xtype, algo, true, &e);
+  s = plan_exec(B, layer->N, L, layer->K, layer->d, layer->D, xtype, algo, true, &e);
   if (s != LQ_OK) return s;
   *bytes = e.total;
   return LQ_OK;
@@ -444,7 +457,7 @@ lq_status lq_linear_ex(const lq_layer* layer, const void* x, lq_dtype xtype, int
       !aligned16(layer->c) || !aligned16(layer->row_scale))
     return LQ_ERR_INVALID_ARG;
   Exec e;
-  s = plan_exec(B, layer->N, L, layer->K, xtype, algo, true, &e);
+  s = plan_exec(B, layer->N, L, layer->K, layer->d, layer->D, xtype, algo, true, &e);
   if (s != LQ_OK) return s;
   s = check_ws(ws, ws_bytes, e.total);
   if (s != LQ_OK) return s;

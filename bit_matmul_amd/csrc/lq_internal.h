@@ -251,6 +251,19 @@ hipError_t launch_decode_fused(const uint8_t* packed, const PackedGeom& g, const
                                unsigned* ctl, const float* row_scale, void* y, bool y_bf16,
                                const FusedPlan& plan, hipStream_t stream);
 
+// One-launch decode without communication (batch 1, short rows): every
+// workgroup prepares the whole operand in LDS and multiplies 8 panels.
+struct SelfPlan {
+  bool ok;
+  int kx, groups, pw;   // K rounded up to 1024; workgroups; panels per workgroup
+  size_t lds_bytes;
+};
+SelfPlan plan_self(int64_t B, int64_t K, int d, int D, const PackedGeom& g, const OperandShape& s);
+hipError_t launch_decode_self(const uint8_t* packed, const PackedGeom& g, const void* x,
+                              bool x_bf16, int64_t K, int d, int D, int hb, const float* c,
+                              const float* M, const OperandShape& s, const float* row_scale,
+                              void* y, bool y_bf16, const SelfPlan& plan, hipStream_t stream);
+
 struct ValuPlan {
   int bt, tps, ksplit, groups;
   size_t partial_bytes;

@@ -197,19 +197,12 @@ __device__ __forceinline__ int fp6_slot(int jj, float& f) {
   return (jj & ~31) + ((n & 1) ? 16 : 0) + (n >> 1);
 }
 
-// FP6 terms of block blk of a tile whose 512 values sit in LDS in the
-// fp6_slot layout, by one lane. Returns the sum over the block's plane 0..2
+// FP6 terms of one block held in va, vb (as fp6_lane_block_terms wants
+// them, plane factors applied). Returns the sum over the block's plane 0..2
 // values (n < 24) of what the terms represent, divided by the plane factor:
 // the block's share of the plane-0..2 column sum the product adds back.
-__device__ __forceinline__ float fp6_lane_block(const float* zt, int blk, int nt, Fp6LaneTerms& r) {
-  lq_v16f va, vb;
-  const float4* p = reinterpret_cast<const float4*>(zt + 32 * blk);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float4 qa = p[i], qb = p[4 + i];
-    va[4 * i] = qa.x; va[4 * i + 1] = qa.y; va[4 * i + 2] = qa.z; va[4 * i + 3] = qa.w;
-    vb[4 * i] = qb.x; vb[4 * i + 1] = qb.y; vb[4 * i + 2] = qb.z; vb[4 * i + 3] = qb.w;
-  }
+__device__ __forceinline__ float fp6_lane_block_regs(lq_v16f& va, lq_v16f& vb, int nt,
+                                                     Fp6LaneTerms& r) {
   float oa[12], ob[12];
 #pragma unroll
   for (int i = 0; i < 12; ++i) {
@@ -225,6 +218,43 @@ __device__ __forceinline__ float fp6_lane_block(const float* zt, int blk, int nt
     tp = fmaf(ob[i] - vb[i], inv, tp);
   }
   return tp;
+}
+
+// FP6 terms of block blk of a tile whose 512 values sit in LDS in the
+// fp6_slot layout, by one lane.
+__device__ __forceinline__ float fp6_lane_block(const float* zt, int blk, int nt, Fp6LaneTerms& r) {
+  lq_v16f va, vb;
+  const float4* p = reinterpret_cast<const float4*>(zt + 32 * blk);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 qa = p[i], qb = p[4 + i];
+    va[4 * i] = qa.x; va[4 * i + 1] = qa.y; va[4 * i + 2] = qa.z; va[4 * i + 3] = qa.w;
+    vb[4 * i] = qb.x; vb[4 * i + 1] = qb.y; vb[4 * i + 2] = qb.z; vb[4 * i + 3] = qb.w;
+  }
+  return fp6_lane_block_regs(va, vb, nt, r);
+}
+
+// The same from the block's 32 lifted values in column order (16-byte
+// aligned, no factors applied): the fp6_slot placement and the plane factor
+// (a power of two, so the product is exact) are applied in registers. Slot s
+// of va holds column 8 (s % 4) + s / 4, of vb column 8 (s % 4) + 4 + s / 4,
+// both with the factor of plane s / 4.
+__device__ __forceinline__ float fp6_lane_block_cols(const float* z, int nt, Fp6LaneTerms& r) {
+  float v[32];
+  const float4* p = reinterpret_cast<const float4*>(z);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 q = p[i];
+    v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
+  }
+  lq_v16f va, vb;
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    const float f = s < 4 ? -4.0f : (s < 8 ? -2.0f : (s < 12 ? -1.0f : 1.0f));
+    va[s] = f * v[8 * (s % 4) + s / 4];
+    vb[s] = f * v[8 * (s % 4) + 4 + s / 4];
+  }
+  return fp6_lane_block_regs(va, vb, nt, r);
 }
 
 }  // namespace lq

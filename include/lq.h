@@ -96,7 +96,7 @@ typedef enum lq_algo {
                                fp32 accumulate */
   LQ_ALGO_MFMA_LARGE = 3,   /* any B: tiled GEMM on bf16 matrix cores, z as bf16
                                (bf16 z) or as a bf16 hi+lo pair (fp32 z) */
-  LQ_ALGO_FUSED = 4         /* lq_linear_ex only: the whole operator in ONE
+  LQ_ALGO_FUSED = 4,        /* lq_linear_ex only: the whole operator in ONE
                                launch, the MFMA_SMALL arithmetic (same FP6
                                terms, same results up to fp32 summation order):
                                the first workgroups whiten and lift x and
@@ -107,6 +107,14 @@ typedef enum lq_algo {
                                ceil(L/512)*B is at most both the number of
                                workgroups and of compute units; otherwise
                                UNSUPPORTED */
+  LQ_ALGO_FUSED_LOCAL = 5   /* lq_linear_ex only, batch 1: the whole operator
+                               in ONE launch with no communication between
+                               workgroups: each prepares the whole activation
+                               operand in LDS (same arithmetic as MFMA_SMALL)
+                               and multiplies its 4 panels. Applies when
+                               K <= 8192, d <= 16, L <= 10240 (+ tail) and the
+                               operand fits LDS; otherwise UNSUPPORTED. Needs
+                               no workspace */
 
 } lq_algo;
 

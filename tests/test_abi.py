@@ -165,7 +165,12 @@ def test_linear_ex_validation_and_control_area():
         assert st == LQ_OK
         # every workspace that is used at all starts with the control area
         assert need >= _lib.LQ_WS_CONTROL_BYTES + 34416 * 3 // 4
-    assert linear_ws_size(lay, 1, LQ_BF16, 5)[0] == LQ_ERR_INVALID_ARG
+    assert linear_ws_size(lay, 1, LQ_BF16, 6)[0] == LQ_ERR_INVALID_ARG
+    # one launch without communication: batch 1, rows up to 8192, no workspace
+    assert linear_ws_size(lay, 1, LQ_BF16, 5)[0] == LQ_ERR_UNSUPPORTED       # K = 14336
+    gate = LQLayer(14336, 4096, 10, 24, 1024, 0, P, P, P, P)
+    assert linear_ws_size(gate, 1, LQ_BF16, 5) == (LQ_OK, 0)
+    assert linear_ws_size(gate, 2, LQ_BF16, 5)[0] == LQ_ERR_UNSUPPORTED
     assert linear_ws_size(lay, 17, LQ_BF16, 4)[0] == LQ_ERR_UNSUPPORTED      # one launch: B <= 16
     assert linear_ws_size(lay, 8, LQ_BF16, 4)[0] == LQ_ERR_UNSUPPORTED       # 24 operand columns
     assert linear_ws_size(lay, 17, LQ_BF16, 1)[0] == LQ_ERR_UNSUPPORTED      # VALU linear: B <= 16

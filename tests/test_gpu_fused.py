@@ -203,3 +203,75 @@ def test_fused_deterministic(lq):
     y1 = layer.linear(lq, x, 1, torch.bfloat16, algo=lq.LQ_ALGO_FUSED)
     y2 = layer.linear(lq, x, 1, torch.bfloat16, algo=lq.LQ_ALGO_FUSED)
     assert torch.equal(y1, y2)
+
+
+# ---- one launch without communication (LQ_ALGO_FUSED_LOCAL): batch 1
+
+
+def _local_ok(lq, layer, xd):
+    try:
+        lq.lq_linear_workspace_size_ex(layer.struct, 1, xd, lq.LQ_ALGO_FUSED_LOCAL)
+        return True
+    except lq.LQError as e:
+        assert e.status == 2, e
+        return False
+
+
+def test_local_full_size_gate_up(lq):
+    """Llama-3-8B gate/up (K = 4096, L = 9840): sampled rows against the
+    oracle, and the whole output against the two-launch path."""
+    wl = WORKLOADS["llama3_8b_mlp"]
+    spec = wl.layers[0]
+    inp = make_layer(spec, wl, B_max=1)
+    layer = DeviceLayer(inp, lq)
+    assert _local_ok(lq, layer, torch.bfloat16)
+    rng = np.random.default_rng(spec.seed + 2)
+    rows = np.sort(rng.choice(spec.N, size=64, replace=False))
+    for xd in (torch.bfloat16, torch.float32):
+        x = dev(inp.x(1), xd)
+        yl = host(layer.linear(lq, x, 1, torch.float32, algo=lq.LQ_ALGO_FUSED_LOCAL))
+        ys = host(layer.linear(lq, x, 1, torch.float32, algo=lq.LQ_ALGO_MFMA_SMALL))
+        assert rel_l2(yl, ys) < 2e-6, xd
+        want = ref.linear(inp.x(1), inp.c, spec.hb, inp.M, inp.signs_rows(rows), inp.row_scale[rows])
+        assert rel_l2(yl[:, rows], want) < TOL[xd], xd
+
+
+LOCAL = [
+    # (N, K, d, D, hb, label)
+    (128, 1024, 10, 24, 1024, "3 tiles, ragged tail"),
+    (256, 2048, 4, 8, 512, "8 full tiles, no tail"),
+    (64, 1037, 10, 24, 1, "K not a multiple of d, hb=1"),
+    (8200 // 8 * 8 - 8, 512, 2, 5, 512, "1280 columns, many panels"),
+    (96, 600, 1, 8, 8, "d = 1"),
+    (48, 8192, 16, 16, 1024, "K = 8192, D = d, 16 full tiles"),
+    (40 * 16, 4096, 10, 24, 1024, "partial last workgroup (40 panels)"),
+    (16, 640, 10, 16, 128, "one panel"),
+]
+
+
+@pytest.mark.parametrize("N,K,d,D,hb,label", LOCAL, ids=[e[-1] for e in LOCAL])
+@pytest.mark.parametrize("xd", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_local_shapes(lq, N, K, d, D, hb, label, xd):
+    inp = make_layer_small(N, K, d, D, hb, seed=N + K + d + D + 11, B_max=1,
+                           xdtype="f32" if xd == torch.float32 else "bf16")
+    if label.startswith("K = 8192, D = d"):
+        inp.M = np.eye(d, dtype=np.float32)
+    layer = DeviceLayer(inp, lq)
+    assert _local_ok(lq, layer, xd), label
+    x = dev(inp.x(1), xd)
+    y = host(layer.linear(lq, x, 1, torch.float32, algo=lq.LQ_ALGO_FUSED_LOCAL))
+    want = ref.linear(inp.x(1), inp.c, hb, inp.M, inp.signs(), inp.row_scale)
+    assert rel_l2(y, want) < TOL[xd]
+    ys = host(layer.linear(lq, x, 1, torch.float32, algo=lq.LQ_ALGO_MFMA_SMALL))
+    assert rel_l2(y, ys) < 2e-6
+
+
+def test_local_bf16_output_and_determinism(lq):
+    inp = make_layer_small(512, 4096, 10, 24, 1024, seed=404, B_max=1, xdtype="bf16")
+    layer = DeviceLayer(inp, lq)
+    x = dev(inp.x(1), torch.bfloat16)
+    y1 = layer.linear(lq, x, 1, torch.bfloat16, algo=lq.LQ_ALGO_FUSED_LOCAL)
+    y2 = layer.linear(lq, x, 1, torch.bfloat16, algo=lq.LQ_ALGO_FUSED_LOCAL)
+    assert torch.equal(y1, y2)
+    want = ref.linear(inp.x(1), inp.c, 1024, inp.M, inp.signs(), inp.row_scale)
+    assert rel_l2(host(y1), want) < 5e-3          # bf16 output rounding
