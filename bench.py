@@ -47,6 +47,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 ROOT = os.path.dirname(os.path.abspath(__file__))
 SIGN_KERNEL = "sign_fp6_kernel"
 LARGE_KERNEL = "sign_mfma_large_kernel"
+WSPACE_KERNEL = "wspace_kernel"
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_llama3_8b_mlp_b1_and_prefill_8192_b2048.txt")
 COPY_BYTES = 256 << 20         # the calibration copy of --pmc-workload
 
@@ -62,6 +63,8 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--decode-algo", default="auto", choices=["auto", "small", "fused", "local", "valu"],
                    help="algorithm of the decode lq_linear calls (lq_linear_ex; auto = lq_linear)")
+    p.add_argument("--prefill-algo", default="auto", choices=["auto", "large", "wspace"],
+                   help="algorithm of the prefill lq_linear call (lq_linear_ex; auto = lq_linear)")
     p.add_argument("--no-prefill", action="store_true",
                    help="skip the 2048-token prefill layer (TFLOP/s)")
     p.add_argument("--eager", action="store_true",
@@ -385,7 +388,7 @@ def run_decode(args, torch, lq, ev):
                 n_sets=n_sets, timing=timing)
 
 
-def build_prefill_case(torch, lq):
+def build_prefill_case(torch, lq, algo=None):
     """The 2048-token prefill layer (8192 -> 8192, d = 3, D = 8) on the GPU."""
     from workloads import WORKLOADS
     s = WORKLOADS["prefill"].layers[0]
@@ -401,21 +404,34 @@ def build_prefill_case(torch, lq):
     st = lq.layer_struct(s.N, s.K, s.d, s.D, s.hb, packed, M, c, r)
     x = torch.randn(B, s.K, device=dev, generator=gen).to(torch.bfloat16)
     y = torch.empty(B, s.N, dtype=torch.bfloat16, device=dev)
-    ws = torch.zeros(lq.lq_linear_workspace_size(st, B, torch.bfloat16), dtype=torch.uint8, device=dev)
+    a = lq.LQ_ALGO_AUTO if algo is None else algo
+    ws = torch.zeros(lq.lq_linear_workspace_size_ex(st, B, torch.bfloat16, a), dtype=torch.uint8,
+                     device=dev)
     return dict(spec=s, B=B, packed=packed, M=M, r=r, c=c, struct=st, x=x, y=y, ws=ws)
 
 
+PREFILL_ALGOS = {"auto": None, "large": "LQ_ALGO_MFMA_LARGE", "wspace": "LQ_ALGO_WSPACE"}
+
+
 def run_prefill(args, torch, lq, ev, steps=10):
-    pf = build_prefill_case(torch, lq)
+    name = PREFILL_ALGOS[args.prefill_algo]
+    algo = None if name is None else getattr(lq, name)
+    pf = build_prefill_case(torch, lq, algo)
     s, B, st, x, y, ws = pf["spec"], pf["B"], pf["struct"], pf["x"], pf["y"], pf["ws"]
+
+    def call():
+        if algo is None:
+            lq.lq_linear(st, x, B, y, ws)
+        else:
+            lq.lq_linear_ex(st, x, B, y, algo, ws)
     for _ in range(2):
-        lq.lq_linear(st, x, B, y, ws)
+        call()
     torch.cuda.synchronize()
     starts, stops = ev.create(steps), ev.create(steps)
     lq.lq_profile_events(starts, stops)
     t0 = time.perf_counter()
     for _ in range(steps):
-        lq.lq_linear(st, x, B, y, ws)
+        call()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     lq.lq_profile_events([], [])
@@ -423,12 +439,18 @@ def run_prefill(args, torch, lq, ev, steps=10):
     ev.destroy(starts)
     ev.destroy(stops)
     flops = 2.0 * B * s.N * s.L
+    dense = 2.0 * B * s.N * s.Kpad
     kern_ms = sum(durs) / len(durs)
     ms = (t1 - t0) * 1e3 / steps
+    # The timed kernel and its algorithmic flops: the lifted product does
+    # 2 B N L, the W-space one 2 B N K' (the dense-equivalent product).
+    ws_path = algo is not None and name == "LQ_ALGO_WSPACE"
+    kflops = dense if ws_path else flops
     return dict(workload=f"prefill K={s.K} N={s.N} d={s.d} D={s.D} B={B}",
                 tflops_linear=flops / (ms * 1e-3) / 1e12, ms_linear=ms,
-                kernel_ms=kern_ms, kernel_tflops=flops / (kern_ms * 1e-3) / 1e12,
-                lifted_flops=flops, dense_equiv_flops=2.0 * B * s.N * s.Kpad)
+                kernel_ms=kern_ms, kernel_tflops=kflops / (kern_ms * 1e-3) / 1e12,
+                kernel=WSPACE_KERNEL if ws_path else LARGE_KERNEL,
+                kernel_flops=kflops, lifted_flops=flops, dense_equiv_flops=dense)
 
 
 def cpu_baseline(budget_s):
@@ -540,6 +562,9 @@ def main():
         out["prefill"] = {
             "metric": "TFLOP/s (batch 2048), lifted flops 2*B*N*L",
             "workload": pf["workload"],
+            "algo": args.prefill_algo,
+            "kernel": pf["kernel"],
+            "kernel_flops_per_launch": pf["kernel_flops"],
             "value": round(pf["tflops_linear"], 2),
             "unit": "TFLOP/s",
             "ms_per_linear": round(pf["ms_linear"], 4),
@@ -547,7 +572,7 @@ def main():
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(pf["kernel_tflops"] / BF16_PEAK_TFLOPS, 4),
                          "avg_launch_us": round(pf["kernel_ms"] * 1e3, 2),
-                         "traffic": traffic_from_summary(LARGE_KERNEL)},
+                         "traffic": traffic_from_summary(pf["kernel"])},
         }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

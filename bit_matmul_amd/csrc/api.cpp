@@ -120,7 +120,7 @@ int device_cus() {
 }
 
 bool valid_algo(lq_algo algo, bool linear) {
-  return algo >= LQ_ALGO_AUTO && algo <= (linear ? LQ_ALGO_FUSED_LOCAL : LQ_ALGO_MFMA_LARGE);
+  return algo >= LQ_ALGO_AUTO && algo <= (linear ? LQ_ALGO_WSPACE : LQ_ALGO_MFMA_LARGE);
 }
 
 // Everything one sign product (or one whole lq_linear) needs: algorithm,
@@ -135,6 +135,7 @@ struct Exec {
   lq::SelfPlan sp;
   int tickets;
   size_t off_tickets, off_aop, off_partial, off_zf32, off_xt, off_zp, off_tslots, total;
+  int d, D;
 };
 
 // Plans a sign product of z (ztype) or, when `linear`, the whole operator
@@ -146,6 +147,8 @@ lq_status plan_exec(int64_t B, int64_t N, int64_t L, int64_t K, int d, int D, lq
                     lq_algo algo, bool linear, Exec* e) {
   e->g = lq::make_geom(N, L);
   e->algo = algo;
+  e->d = d;
+  e->D = D;
   if (algo == LQ_ALGO_AUTO) {
     if (B > 16) {
       e->algo = LQ_ALGO_MFMA_LARGE;
@@ -200,6 +203,16 @@ lq_status plan_exec(int64_t B, int64_t N, int64_t L, int64_t K, int d, int D, lq
         const lq::ZpGeom zg = lq::zp_geom(B, e->g, ztype == LQ_BF16);
         e->off_zp = take(zg.bytes);
         e->off_tslots = take(zg.tail_bytes);
+      }
+      break;
+    case LQ_ALGO_WSPACE:
+      if (!linear) return LQ_ERR_INVALID_ARG;
+      if (ztype != LQ_BF16 || !lq::wspace_supported(d, D)) return LQ_ERR_UNSUPPORTED;
+      e->off_xt = take((size_t)B * K * sizeof(float));
+      {
+        const lq::XpGeom xg = lq::xp_geom(B, e->g, D);
+        e->off_zp = take(xg.bytes);
+        e->off_tslots = take(xg.tail_bytes);
       }
       break;
     default:
@@ -285,6 +298,18 @@ lq_status run_exec(const Exec& e, const uint8_t* packed, const void* zin, lq_dty
       return hip_status(profiled(st, [&] {
         return lq::launch_sign_mfma_large(packed, e.g, zp, base + e.off_tslots, zb, B, row_scale, y,
                                           yb, st);
+      }));
+    }
+    case LQ_ALGO_WSPACE: {
+      float* xt = reinterpret_cast<float*>(base + e.off_xt);
+      void* xp = base + e.off_zp;
+      s = hip_status(lq::launch_hadamard_scale(zin, zb, B, layer->K, layer->hb, layer->c, xt, st));
+      if (s != LQ_OK) return s;
+      s = hip_status(lq::launch_xp(xt, B, layer->K, e.d, e.D, e.g, xp, st));
+      if (s != LQ_OK) return s;
+      return hip_status(profiled(st, [&] {
+        return lq::launch_wspace(packed, e.g, xp, base + e.off_tslots, B, layer->M, e.d, e.D,
+                                 row_scale, y, yb, st);
       }));
     }
     default:

@@ -307,5 +307,26 @@ hipError_t launch_sign_mfma_large(const uint8_t* packed, const PackedGeom& g, co
                                   void* tail_slots, bool z_bf16, int64_t B,
                                   const float* row_scale, void* y, bool y_bf16,
                                   hipStream_t stream);
+// The tail tile's slots of every panel in full-tile form (1 KB per panel;
+// columns past L read as +1 signs).
+hipError_t launch_tail_slots(const uint8_t* packed, const PackedGeom& g, void* out,
+                             hipStream_t stream);
+
+// ---- large batch in W space: the dense weights rebuilt per block from the
+// signs (a table of the 2^D sign patterns' weight vectors), bf16 MFMAs over
+// K' = d Kb. D in {4, 8} (whole blocks per packed word), d <= 4.
+bool wspace_supported(int d, int D);
+struct XpGeom {
+  int64_t B16, steps;
+  size_t bytes;        // xp: per 16 batch rows and 128-column step, 16 / D KB
+  size_t tail_bytes;   // as ZpGeom
+};
+XpGeom xp_geom(int64_t B, const PackedGeom& g, int D);
+LargePlan plan_wspace(int64_t B, const PackedGeom& g, int D);
+hipError_t launch_xp(const float* xt, int64_t B, int64_t K, int d, int D, const PackedGeom& g,
+                     void* xp, hipStream_t stream);
+hipError_t launch_wspace(const uint8_t* packed, const PackedGeom& g, const void* xp,
+                         void* tail_slots, int64_t B, const float* M, int d, int D,
+                         const float* row_scale, void* y, bool y_bf16, hipStream_t stream);
 
 }  // namespace lq

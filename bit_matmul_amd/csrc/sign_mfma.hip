@@ -460,6 +460,14 @@ hipError_t launch_zp(const void* src, int kind, int64_t B, int64_t L, int64_t K,
   return hipSuccess;
 }
 
+hipError_t launch_tail_slots(const uint8_t* packed, const PackedGeom& g, void* out,
+                             hipStream_t stream) {
+  hipLaunchKernelGGL(tail_slots_kernel, dim3((unsigned)((g.panels + 3) / 4)), dim3(256), 0, stream,
+                     packed, g.panels, g.panel_bytes, g.full_tiles, g.tail_bytes,
+                     reinterpret_cast<uint4*>(out));
+  return hipGetLastError();
+}
+
 hipError_t launch_sign_mfma_large(const uint8_t* packed, const PackedGeom& g, const void* zp,
                                   void* tail_slots, bool z_bf16, int64_t B,
                                   const float* row_scale, void* y, bool y_bf16,
@@ -469,9 +477,7 @@ hipError_t launch_sign_mfma_large(const uint8_t* packed, const PackedGeom& g, co
   const uint4* z = reinterpret_cast<const uint4*>(zp);
   uint4* ts = reinterpret_cast<uint4*>(tail_slots);
   if (g.tail_bytes) {
-    hipLaunchKernelGGL(tail_slots_kernel, dim3((unsigned)((g.panels + 3) / 4)), dim3(256), 0, stream,
-                       packed, g.panels, g.panel_bytes, g.full_tiles, g.tail_bytes, ts);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launch_tail_slots(packed, g, ts, stream);
     if (e != hipSuccess) return e;
   }
   if (z_bf16)

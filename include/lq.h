@@ -107,7 +107,7 @@ typedef enum lq_algo {
                                ceil(L/512)*B is at most both the number of
                                workgroups and of compute units; otherwise
                                UNSUPPORTED */
-  LQ_ALGO_FUSED_LOCAL = 5   /* lq_linear_ex only, batch 1: the whole operator
+  LQ_ALGO_FUSED_LOCAL = 5,  /* lq_linear_ex only, batch 1: the whole operator
                                in ONE launch with no communication between
                                workgroups: each prepares the whole activation
                                operand in LDS (same arithmetic as MFMA_SMALL)
@@ -115,6 +115,17 @@ typedef enum lq_algo {
                                K <= 8192, d <= 16, L <= 10240 (+ tail) and the
                                operand fits LDS; otherwise UNSUPPORTED. Needs
                                no workspace */
+  LQ_ALGO_WSPACE = 6        /* lq_linear_ex only, bf16 x, any B: the product in
+                               W space ([paper] §3: the weights a block's signs
+                               represent are M times the sign vector). The
+                               dense weights W[n][b*d+i] = sum_e M[i][e] s_e
+                               are rebuilt per block on the fly (fp32 sums in
+                               order of e, rounded to bf16), and bf16 matrix
+                               cores reduce over the d*ceil(K/d) inputs
+                               (transformed x rounded to bf16) instead of the
+                               L lifted columns: D/d times fewer MACs. Applies
+                               when D is 4 or 8 and d <= 4; otherwise (and for
+                               fp32 x) UNSUPPORTED */
 
 } lq_algo;
 

@@ -165,7 +165,22 @@ def test_linear_ex_validation_and_control_area():
         assert st == LQ_OK
         # every workspace that is used at all starts with the control area
         assert need >= _lib.LQ_WS_CONTROL_BYTES + 34416 * 3 // 4
-    assert linear_ws_size(lay, 1, LQ_BF16, 6)[0] == LQ_ERR_INVALID_ARG
+    assert linear_ws_size(lay, 1, LQ_BF16, 7)[0] == LQ_ERR_INVALID_ARG
+    # W space: D in {4, 8}, d <= 4, bf16 x, any batch
+    assert linear_ws_size(lay, 1, LQ_BF16, 6)[0] == LQ_ERR_UNSUPPORTED       # D = 24
+    pre = LQLayer(8192, 8192, 3, 8, 1024, 0, P, P, P, P)
+    st, need = linear_ws_size(pre, 2048, LQ_BF16, 6)
+    L = 2731 * 8
+    tiles = -(-L // 512)
+    assert st == LQ_OK
+    assert need >= (_lib.LQ_WS_CONTROL_BYTES + 2048 * 8192 * 4          # xt
+                    + 128 * 4 * tiles * 2048                              # xp: 2 KB per step
+                    + 512 * 1024)                                         # tail slots
+    assert linear_ws_size(pre, 2048, LQ_F32, 6)[0] == LQ_ERR_UNSUPPORTED    # fp32 x
+    assert linear_ws_size(LQLayer(8192, 8192, 5, 8, 1024, 0, P, P, P, P), 64, LQ_BF16, 6)[0] \
+        == LQ_ERR_UNSUPPORTED                                                # d > 4
+    assert linear_ws_size(LQLayer(4096, 512, 2, 4, 512, 0, P, P, P, P), 3, LQ_BF16, 6)[0] == LQ_OK
+    assert ws_size(64, 8192, L, LQ_BF16, 6)[0] == LQ_ERR_INVALID_ARG       # sign_gemm: no W space
     # one launch without communication: batch 1, rows up to 8192, no workspace
     assert linear_ws_size(lay, 1, LQ_BF16, 5)[0] == LQ_ERR_UNSUPPORTED       # K = 14336
     gate = LQLayer(14336, 4096, 10, 24, 1024, 0, P, P, P, P)
@@ -180,6 +195,7 @@ def test_linear_ex_validation_and_control_area():
     need = linear_ws_size(lay, 1, LQ_BF16, 2)[1]
     assert f(ctypes.byref(lay), P, LQ_BF16, 1, P, LQ_BF16, 2, P, need - 1, None) == LQ_ERR_WORKSPACE
     assert f(ctypes.byref(lay), P, LQ_BF16, 1, P, LQ_BF16, 7, P, need, None) == LQ_ERR_INVALID_ARG
+    assert f(ctypes.byref(lay), P, LQ_BF16, 1, P, LQ_BF16, 6, P, need, None) == LQ_ERR_UNSUPPORTED
     assert f(ctypes.byref(lay), P, LQ_BF16, 17, P, LQ_BF16, 4, P, need, None) == LQ_ERR_UNSUPPORTED
     assert f(ctypes.byref(lay), P, LQ_BF16, 0, P, LQ_BF16, 4, None, 0, None) == LQ_OK
 
