@@ -208,7 +208,6 @@ lq_status plan_exec(int64_t B, int64_t N, int64_t L, int64_t K, int d, int D, lq
     case LQ_ALGO_WSPACE:
       if (!linear) return LQ_ERR_INVALID_ARG;
       if (ztype != LQ_BF16 || !lq::wspace_supported(d, D)) return LQ_ERR_UNSUPPORTED;
-      e->off_xt = take((size_t)B * K * sizeof(float));
       {
         const lq::XpGeom xg = lq::xp_geom(B, e->g, D);
         e->off_zp = take(xg.bytes);
@@ -301,11 +300,8 @@ lq_status run_exec(const Exec& e, const uint8_t* packed, const void* zin, lq_dty
       }));
     }
     case LQ_ALGO_WSPACE: {
-      float* xt = reinterpret_cast<float*>(base + e.off_xt);
       void* xp = base + e.off_zp;
-      s = hip_status(lq::launch_hadamard_scale(zin, zb, B, layer->K, layer->hb, layer->c, xt, st));
-      if (s != LQ_OK) return s;
-      s = hip_status(lq::launch_xp(xt, B, layer->K, e.d, e.D, e.g, xp, st));
+      s = hip_status(lq::launch_xpw(zin, zb, B, layer->K, layer->hb, layer->c, e.d, e.D, e.g, xp, st));
       if (s != LQ_OK) return s;
       return hip_status(profiled(st, [&] {
         return lq::launch_wspace(packed, e.g, xp, base + e.off_tslots, B, layer->M, e.d, e.D,

@@ -323,8 +323,9 @@ struct XpGeom {
 };
 XpGeom xp_geom(int64_t B, const PackedGeom& g, int D);
 LargePlan plan_wspace(int64_t B, const PackedGeom& g, int D);
-hipError_t launch_xp(const float* xt, int64_t B, int64_t K, int d, int D, const PackedGeom& g,
-                     void* xp, hipStream_t stream);
+// Whitening of x straight into xp (no xt in memory).
+hipError_t launch_xpw(const void* x, bool x_bf16, int64_t B, int64_t K, int hb, const float* c,
+                      int d, int D, const PackedGeom& g, void* xp, hipStream_t stream);
 hipError_t launch_wspace(const uint8_t* packed, const PackedGeom& g, const void* xp,
                          void* tail_slots, int64_t B, const float* M, int d, int D,
                          const float* row_scale, void* y, bool y_bf16, hipStream_t stream);

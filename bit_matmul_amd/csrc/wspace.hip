@@ -18,11 +18,13 @@
 // for the same two blocks b, i < 4 (zero for i >= d and past K).
 //
 // xt is first written in that order ("xp", bf16): per 16 batch rows and
-// 128-column step an F KB block of 16-byte units [s][g][r]. The pipeline is
+// 128-column step an F KB block of 16-byte units [s][g][r]; the whitening
+// itself writes it (xt never goes to memory). The pipeline is
 // that of the lifted large-batch product (four LDS stages filled by DMA three
 // steps ahead, slots DMA-copied per tile, B operands and table reads of the
 // next sub-step issued before this sub-step's MFMAs).
 #include "lq_internal.h"
+#include "lq_prep.h"
 
 namespace lq {
 namespace {
@@ -36,33 +38,105 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// ------------------------------------------------------------ xp
-// Workgroup (tile q, jb); thread (u, g, r): step 4 q + u, lane group g, batch
-// row 16 jb + r; it writes the F units (s, g, r) of that step.
-template <int D>
-__global__ __launch_bounds__(256) void xp_kernel(const float* __restrict__ xt, int64_t B,
-                                                 int64_t K, int d, int64_t steps, int64_t jb_base,
-                                                 uint4* __restrict__ xp) {
+// ------------------------------------------------------------ whitening + xp
+// Workgroup (chunk h of 1024 inputs, 16 batch rows jb): x * c of the rows'
+// chunk into LDS, the Walsh-Hadamard transform of every hb block (a
+// wavefront per row), then the xp units of every block with inputs in the
+// chunk. Slot (block b, position i) belongs to the chunk holding input
+// min(b d + min(i, d - 1), K - 1): a unit whose eight slots all belong to
+// this chunk is stored whole, one that straddles two chunks slot by slot (2
+// bytes each; the other chunk's workgroup stores the rest). The last chunk
+// also covers the virtual pad and the blocks past L up to the end of the
+// last tile (zeros).
+constexpr int kXpwStride = 1028;   // LDS row stride (floats): 16-byte aligned, rows 4 banks apart
+
+template <int D, bool kXBF16>
+__global__ __launch_bounds__(256) void xpw_kernel(const void* __restrict__ x,
+                                                  const float* __restrict__ c, int64_t B,
+                                                  int64_t K, int d, int lhb, float norm,
+                                                  int64_t steps, int64_t blk_end, int64_t jb_base,
+                                                  uint4* __restrict__ xp) {
   constexpr int F = 16 / D;
-  const int64_t q = blockIdx.x, jb = jb_base + blockIdx.y;
-  const int t = threadIdx.x;
-  const int u = t >> 6, g = (t >> 4) & 3, r = t & 15;
-  const int64_t b = 16 * jb + r;
-  const int64_t blk0 = (512 * q + 128 * u + 32 * g) / D;
-  const float* xr = xt + min(b, B - 1) * K;
+  __shared__ __align__(16) float xs[16 * kXpwStride];
+  const int h = blockIdx.x;
+  const int64_t jb = jb_base + blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t k_lo = (int64_t)h * 1024;
+  const int n = (int)min((int64_t)1024, K - k_lo);
+
+  // x * c: thread t takes inputs 4t .. 4t + 3 of every row
+  const int k4 = 4 * tid;
+  float cv[4];
 #pragma unroll
-  for (int s = 0; s < F; ++s) {
-    uint32_t w[4];
+  for (int i = 0; i < 4; ++i) cv[i] = k4 + i < n ? c[k_lo + k4 + i] : 0.0f;
+#pragma unroll 4
+  for (int rr = 0; rr < 16; ++rr) {
+    const int64_t b = 16 * jb + rr;
+    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (b < B) {
+      const int64_t at = b * K + k_lo + k4;
+      if (k4 + 3 < n && (at & 3) == 0) {
+        if (kXBF16) {
+          const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(x) + at);
+          v[0] = bf16_bits_to_f32(w.x & 0xFFFFu); v[1] = bf16_bits_to_f32(w.x >> 16);
+          v[2] = bf16_bits_to_f32(w.y & 0xFFFFu); v[3] = bf16_bits_to_f32(w.y >> 16);
+        } else {
+          const float4 w = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + at);
+          v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+        }
+      } else {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t k0 = (blk0 + 2 * s + h) * d;
-      float v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = (b < B && i < d && k0 + i < K) ? xr[k0 + i] : 0.0f;
-      w[2 * h] = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-      w[2 * h + 1] = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+        for (int i = 0; i < 4; ++i)
+          if (k4 + i < n)
+            v[i] = kXBF16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(x)[at + i])
+                          : reinterpret_cast<const float*>(x)[at + i];
+      }
     }
-    xp[((jb * steps + 4 * q + u) * F + s) * 64 + 16 * g + r] = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<float4*>(xs + rr * kXpwStride + k4) =
+        make_float4(v[0] * cv[0], v[1] * cv[1], v[2] * cv[2], v[3] * cv[3]);
+  }
+  __syncthreads();
+  // (every hb block lies inside the chunk: hb divides 1024 and K; past n
+  // the values are zero and stay zero)
+  for (int rr = wave; rr < 16; rr += 4) wave_fwht_1024(xs + rr * kXpwStride, lhb, lane);
+  __syncthreads();
+
+  const bool last = k_lo + 1024 >= K;
+  const int64_t b_first = k_lo / d;
+  const int64_t b_last = last ? blk_end - 1 : (k_lo + 1023) / d;
+  const int64_t u_lo = b_first / 2, nu = b_last / 2 - u_lo + 1;
+  auto owner = [&](int64_t bb, int i) -> int64_t {
+    return min(bb * d + min(i, d - 1), K - 1) >> 10;
+  };
+  for (int64_t idx = tid; idx < nu * 16; idx += 256) {
+    const int64_t U = u_lo + (idx >> 4);
+    const int r = (int)(idx & 15);
+    const int64_t b0 = 2 * U;
+    const int64_t col = b0 * D;
+    const int64_t q = col >> 9;
+    const int cu = (int)((col >> 7) & 3), g = (int)((col >> 5) & 3), s = (int)((col & 31) / D) >> 1;
+    uint4* dst = xp + ((jb * steps + 4 * q + cu) * F + s) * 64 + 16 * g + r;
+    const float* xr = xs + r * kXpwStride;
+    uint32_t hv[8];
+    bool own[8];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t k = (b0 + hh) * d + i;
+        const bool o = owner(b0 + hh, i) == h;
+        own[4 * hh + i] = o;
+        hv[4 * hh + i] = f32_to_bf16_bits(o && i < d && k < K ? xr[k - k_lo] * norm : 0.0f);
+      }
+    if (own[0] && own[7]) {
+      *dst = make_uint4(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16),
+                        hv[6] | (hv[7] << 16));
+    } else {
+      uint16_t* p = reinterpret_cast<uint16_t*>(dst);
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        if (own[m]) p[m] = (uint16_t)hv[m];
+    }
   }
 }
 
@@ -321,18 +395,28 @@ LargePlan plan_wspace(int64_t B, const PackedGeom& g, int D) {
   return p;
 }
 
-hipError_t launch_xp(const float* xt, int64_t B, int64_t K, int d, int D, const PackedGeom& g,
-                     void* xp, hipStream_t stream) {
+hipError_t launch_xpw(const void* x, bool x_bf16, int64_t B, int64_t K, int hb, const float* c,
+                      int d, int D, const PackedGeom& g, void* xp, hipStream_t stream) {
   (void)hipGetLastError();   // clear a stale error of an earlier runtime call
-  if (!wspace_supported(d, D)) return hipErrorInvalidValue;
-  const XpGeom x = xp_geom(B, g, D);
+  if (!wspace_supported(d, D) || hb < 1 || hb > 1024 || (hb & (hb - 1)) || K % hb) return hipErrorInvalidValue;
+  const XpGeom xg = xp_geom(B, g, D);
+  int lhb = 0;
+  while ((1 << lhb) < hb) ++lhb;
+  const float norm = (lhb % 2 == 0) ? ldexpf(1.0f, -lhb / 2) : (float)(1.0 / sqrt((double)hb));
+  const int64_t blk_end = (int64_t)g.ext_tiles * (kTileCols / D);
+  const unsigned chunks = (unsigned)((K + 1023) / 1024);
   uint4* out = reinterpret_cast<uint4*>(xp);
-  for (int64_t jb0 = 0; jb0 < x.B16; jb0 += 65535) {
-    const dim3 grid((unsigned)g.ext_tiles, (unsigned)min(x.B16 - jb0, (int64_t)65535));
-    if (D == 8)
-      hipLaunchKernelGGL(xp_kernel<8>, grid, dim3(256), 0, stream, xt, B, K, d, x.steps, jb0, out);
-    else
-      hipLaunchKernelGGL(xp_kernel<4>, grid, dim3(256), 0, stream, xt, B, K, d, x.steps, jb0, out);
+  for (int64_t jb0 = 0; jb0 < xg.B16; jb0 += 65535) {
+    const dim3 grid(chunks, (unsigned)min(xg.B16 - jb0, (int64_t)65535));
+#define LQ_XPW(D_, BF_)                                                                            \
+    hipLaunchKernelGGL((xpw_kernel<D_, BF_>), grid, dim3(256), 0, stream, x, c, B, K, d, lhb, norm, \
+                       xg.steps, blk_end, jb0, out)
+    if (D == 8) {
+      if (x_bf16) LQ_XPW(8, true); else LQ_XPW(8, false);
+    } else {
+      if (x_bf16) LQ_XPW(4, true); else LQ_XPW(4, false);
+    }
+#undef LQ_XPW
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

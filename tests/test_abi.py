@@ -173,9 +173,10 @@ def test_linear_ex_validation_and_control_area():
     L = 2731 * 8
     tiles = -(-L // 512)
     assert st == LQ_OK
-    assert need >= (_lib.LQ_WS_CONTROL_BYTES + 2048 * 8192 * 4          # xt
+    assert need >= (_lib.LQ_WS_CONTROL_BYTES
                     + 128 * 4 * tiles * 2048                              # xp: 2 KB per step
                     + 512 * 1024)                                         # tail slots
+    assert need < _lib.LQ_WS_CONTROL_BYTES + 2048 * 8192 * 4               # no fp32 xt
     assert linear_ws_size(pre, 2048, LQ_F32, 6)[0] == LQ_ERR_UNSUPPORTED    # fp32 x
     assert linear_ws_size(LQLayer(8192, 8192, 5, 8, 1024, 0, P, P, P, P), 64, LQ_BF16, 6)[0] \
         == LQ_ERR_UNSUPPORTED                                                # d > 4
