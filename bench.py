@@ -82,13 +82,14 @@ def parse_args():
 # ------------------------------------------------------------ profiling aids
 
 def kernel_sources_hash():
-    """Hash of the HIP sources of the decode path (a counter summary taken
-    on other sources is stale)."""
+    """Hash of the kernel sources (.hip and the headers they include; a
+    counter summary taken on other kernels is stale). Host-only files such
+    as the C-ABI dispatch do not change what a kernel reads or writes."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_matmul_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")):
+        if name.endswith((".hip", ".h")):
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -444,7 +445,8 @@ def run_prefill(args, torch, lq, ev, steps=10):
     ms = (t1 - t0) * 1e3 / steps
     # The timed kernel and its algorithmic flops: the lifted product does
     # 2 B N L, the W-space one 2 B N K' (the dense-equivalent product).
-    ws_path = algo is not None and name == "LQ_ALGO_WSPACE"
+    ws_path = lq.lq_linear_algo(st, B, torch.bfloat16,
+                                lq.LQ_ALGO_AUTO if algo is None else algo) == lq.LQ_ALGO_WSPACE
     kflops = dense if ws_path else flops
     return dict(workload=f"prefill K={s.K} N={s.N} d={s.d} D={s.D} B={B}",
                 tflops_linear=flops / (ms * 1e-3) / 1e12, ms_linear=ms,

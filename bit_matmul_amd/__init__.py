@@ -23,6 +23,7 @@ __all__ = [
     "lq_version", "lq_packed_size", "lq_pack_signs", "lq_unpack_signs", "lq_hadamard_scale",
     "lq_lift_activations", "lq_sign_gemm_workspace_size", "lq_sign_gemm", "lq_sign_gemm_ex",
     "lq_linear_workspace_size", "lq_linear", "lq_linear_workspace_size_ex", "lq_linear_ex",
+    "lq_linear_algo",
     "lq_workspace_init", "lq_profile_events", "layer_struct", "LQError", "LQLayer",
     "LQ_F32", "LQ_BF16", "LQ_ALGO_AUTO", "LQ_ALGO_VALU", "LQ_ALGO_MFMA_SMALL",
     "LQ_ALGO_MFMA_LARGE", "LQ_ALGO_FUSED", "LQ_ALGO_FUSED_LOCAL", "LQ_ALGO_WSPACE", "LQ_MAX_D", "LQ_MAX_HB", "LQ_WS_CONTROL_BYTES",
@@ -144,6 +145,15 @@ def lq_linear_workspace_size_ex(layer: LQLayer, B, xtype, algo) -> int:
     xt = _DTYPES[xtype] if isinstance(xtype, torch.dtype) else int(xtype)
     _check(_lib.LIB.lq_linear_workspace_size_ex(ctypes.byref(layer), B, xt, algo, ctypes.byref(out)),
            "lq_linear_workspace_size_ex")
+    return out.value
+
+
+def lq_linear_algo(layer: LQLayer, B, xtype, algo=0) -> int:
+    """The algorithm lq_linear_ex runs for these arguments (AUTO resolved)."""
+    out = ctypes.c_int()
+    xt = _DTYPES[xtype] if isinstance(xtype, torch.dtype) else int(xtype)
+    _check(_lib.LIB.lq_linear_algo(ctypes.byref(layer), B, xt, algo, ctypes.byref(out)),
+           "lq_linear_algo")
     return out.value
 
 

@@ -22,7 +22,7 @@ EXPORTS = [
     "lq_pack_signs", "lq_unpack_signs", "lq_hadamard_scale", "lq_lift_activations",
     "lq_sign_gemm_workspace_size", "lq_sign_gemm", "lq_sign_gemm_ex",
     "lq_linear_workspace_size", "lq_linear", "lq_linear_workspace_size_ex", "lq_linear_ex",
-    "lq_workspace_init", "lq_profile_events",
+    "lq_linear_algo", "lq_workspace_init", "lq_profile_events",
 ]
 
 
@@ -66,6 +66,7 @@ def _load():
         "lq_linear_workspace_size": (c_int, [POINTER(LQLayer), i64, c_int, POINTER(sz)]),
         "lq_linear": (c_int, [POINTER(LQLayer), vp, c_int, i64, vp, c_int, vp, sz, vp]),
         "lq_linear_workspace_size_ex": (c_int, [POINTER(LQLayer), i64, c_int, c_int, POINTER(sz)]),
+        "lq_linear_algo": (c_int, [POINTER(LQLayer), i64, c_int, c_int, POINTER(c_int)]),
         "lq_linear_ex": (c_int, [POINTER(LQLayer), vp, c_int, i64, vp, c_int, c_int, vp, sz, vp]),
         "lq_workspace_init": (c_int, [vp, sz, vp]),
         "lq_profile_events": (c_int, [POINTER(vp), POINTER(vp), i32]),

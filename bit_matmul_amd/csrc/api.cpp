@@ -151,7 +151,10 @@ lq_status plan_exec(int64_t B, int64_t N, int64_t L, int64_t K, int d, int D, lq
   e->D = D;
   if (algo == LQ_ALGO_AUTO) {
     if (B > 16) {
-      e->algo = LQ_ALGO_MFMA_LARGE;
+      // W space where it applies: D / d times fewer MACs on the same bf16
+      // operands (bf16 x: the lifted product would round z to bf16 too).
+      e->algo = linear && ztype == LQ_BF16 && lq::wspace_supported(d, D) ? LQ_ALGO_WSPACE
+                                                                          : LQ_ALGO_MFMA_LARGE;
     } else if (ztype == LQ_F32) {
       e->algo = LQ_ALGO_VALU;
     } else {
@@ -455,6 +458,23 @@ lq_status lq_linear_workspace_size_ex(const lq_layer* layer, int64_t B, lq_dtype
   s = plan_exec(B, layer->N, L, layer->K, layer->d, layer->D, xtype, algo, true, &e);
   if (s != LQ_OK) return s;
   *bytes = e.total;
+  return LQ_OK;
+}
+
+lq_status lq_linear_algo(const lq_layer* layer, int64_t B, lq_dtype xtype, lq_algo algo,
+                         lq_algo* resolved) {
+  if (resolved == nullptr || !valid_dtype(xtype) || B < 1) return LQ_ERR_INVALID_ARG;
+  if (!valid_algo(algo, true)) return LQ_ERR_INVALID_ARG;
+  int64_t L = 0;
+  lq_status s = check_layer(layer, &L);
+  if (s != LQ_OK) return s;
+  s = check_sign_dims(B, layer->N, L);
+  if (s != LQ_OK) return s;
+  if (!mul_ok(B, layer->K, kMaxElems)) return LQ_ERR_UNSUPPORTED;
+  Exec e;
+  s = plan_exec(B, layer->N, L, layer->K, layer->d, layer->D, xtype, algo, true, &e);
+  if (s != LQ_OK) return s;
+  *resolved = e.algo;
   return LQ_OK;
 }
 

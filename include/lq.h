@@ -239,14 +239,23 @@ lq_status lq_linear(const lq_layer* layer, const void* x, lq_dtype xtype, int64_
 
 /*
  * As lq_linear, with the algorithm chosen by the caller: LQ_ALGO_AUTO (what
- * lq_linear does: B > 16 MFMA_LARGE; fp32 x VALU; bf16 x MFMA_SMALL),
- * VALU (B <= 16), MFMA_SMALL (B <= 16; whitening,
- * lift and operand in one preparation launch, then the product launch),
- * MFMA_LARGE, or FUSED (one launch; UNSUPPORTED where it does not apply).
+ * lq_linear does: B > 16: WSPACE for bf16 x where it applies, else
+ * MFMA_LARGE; B <= 16: fp32 x VALU, bf16 x MFMA_SMALL), VALU (B <= 16),
+ * MFMA_SMALL (B <= 16; whitening, lift and operand in one preparation
+ * launch, then the product launch), MFMA_LARGE, FUSED, FUSED_LOCAL or WSPACE
+ * (UNSUPPORTED where they do not apply).
  * The workspace size depends on the algorithm.
  */
 lq_status lq_linear_workspace_size_ex(const lq_layer* layer, int64_t B, lq_dtype xtype,
                                       lq_algo algo, size_t* bytes);
+
+/*
+ * The algorithm lq_linear_ex(layer, ., xtype, B, ., ., algo, ...) runs
+ * (AUTO resolved), written to *resolved; host-only, launches nothing.
+ * Errors: as lq_linear_workspace_size_ex, and INVALID_ARG for B < 1.
+ */
+lq_status lq_linear_algo(const lq_layer* layer, int64_t B, lq_dtype xtype, lq_algo algo,
+                         lq_algo* resolved);
 lq_status lq_linear_ex(const lq_layer* layer, const void* x, lq_dtype xtype, int64_t B, void* y,
                        lq_dtype ytype, lq_algo algo, void* ws, size_t ws_bytes, void* stream);
 

@@ -217,3 +217,25 @@ def test_profile_events_validation():
     nulls = (ctypes.c_void_p * 2)(P, None)
     assert f(arr, nulls, 2) == LQ_ERR_INVALID_ARG
     assert f(None, None, 0) == LQ_OK
+
+
+def test_linear_algo_resolution():
+    f = LIB.lq_linear_algo
+    out = ctypes.c_int(-1)
+
+    def res(lay, B, xt, algo=0):
+        st = f(ctypes.byref(lay), B, xt, algo, ctypes.byref(out))
+        return st, out.value
+    gate = LQLayer(14336, 4096, 10, 24, 1024, 0, P, P, P, P)
+    pre = LQLayer(8192, 8192, 3, 8, 1024, 0, P, P, P, P)
+    qwen = LQLayer(27648, 5120, 2, 5, 1024, 0, P, P, P, P)
+    assert res(gate, 1, LQ_BF16) == (LQ_OK, 2)        # MFMA_SMALL
+    assert res(gate, 1, 0) == (LQ_OK, 1)              # fp32 x: VALU
+    assert res(pre, 2048, LQ_BF16) == (LQ_OK, 6)      # W space
+    assert res(pre, 2048, 0) == (LQ_OK, 3)            # fp32 x: lifted MFMA
+    assert res(qwen, 64, LQ_BF16) == (LQ_OK, 3)       # D = 5: lifted MFMA
+    assert res(pre, 2048, LQ_BF16, 3) == (LQ_OK, 3)   # explicit choice kept
+    assert res(gate, 2, LQ_BF16, 5)[0] == LQ_ERR_UNSUPPORTED
+    assert res(gate, 0, LQ_BF16)[0] == LQ_ERR_INVALID_ARG
+    assert f(ctypes.byref(gate), 1, LQ_BF16, 0, None) == LQ_ERR_INVALID_ARG
+    assert res(gate, 1, LQ_BF16, 7)[0] == LQ_ERR_INVALID_ARG
