@@ -47,7 +47,7 @@ import numpy as np
 __all__ = [
     "hadamard", "whitening_block", "whiten", "pad_blocks", "decode_weight",
     "linear", "lift", "sign_matmul", "packed_bits", "bits_per_weight",
-    "codebook", "sign_pattern",
+    "codebook", "sign_pattern", "encode_nn", "train_m_step", "orthonormal_rows",
 ]
 
 
@@ -206,3 +206,65 @@ def codebook(M: np.ndarray) -> np.ndarray:
     M = np.asarray(M, dtype=np.float64)
     D = M.shape[1]
     return np.stack([M @ sign_pattern(i, D) for i in range(1 << D)])
+
+
+def encode_nn(w: np.ndarray, M: np.ndarray):
+    """Nearest-neighbour encoding of d-blocks: for every row w_b of w (n x d),
+    the sign vector s in {+1,-1}^D whose codeword M s is closest to w_b in
+    Euclidean distance. This is the inner minimisation of [paper] §3.1
+    Eq. (1), which the paper names the nearest-neighbour search, i.e. the
+    quantization step. Exhaustive over the 2^D codewords of ``codebook``;
+    among equally close codewords the lowest ``sign_pattern`` index wins.
+
+    Returns (signs (n, D) of +-1, squared distances (n,))."""
+    M = np.asarray(M, dtype=np.float64)
+    d, D = M.shape
+    w = np.asarray(w, dtype=np.float64).reshape(-1, d)
+    cb = codebook(M)                                   # (2^D, d)
+    n = w.shape[0]
+    idx = np.empty(n, dtype=np.int64)
+    best = np.empty(n)
+    step = max(1, (1 << 22) >> D)                      # blocks per chunk (bounded memory)
+    for a in range(0, n, step):
+        diff = w[a:a + step, None, :] - cb[None, :, :]
+        dist = (diff * diff).sum(axis=2)               # (chunk, 2^D)
+        i = np.argmin(dist, axis=1)                    # first minimum: lowest index
+        idx[a:a + step] = i
+        best[a:a + step] = dist[np.arange(i.size), i]
+    signs = np.stack([sign_pattern(int(i), D) for i in idx]) if n else np.zeros((0, D))
+    return signs, best
+
+
+def orthonormal_rows(G: np.ndarray, d: int) -> np.ndarray:
+    """A d x D matrix with orthonormal rows, from a D x D Gaussian draw G: the
+    first d columns of the Q factor of G, transposed ([paper] §3.1 "Optimising
+    M": the rows of M are initialised as orthonormal vectors)."""
+    q, r = np.linalg.qr(np.asarray(G, dtype=np.float64))
+    q = q * np.sign(np.diag(r))[None, :]               # the unique Q with diag(R) > 0
+    return q[:, :d].T.copy()
+
+
+def train_m_step(M: np.ndarray, w: np.ndarray, lr: float):
+    """One gradient step on the objective of [paper] §3.1 Eq. (1) estimated on
+    the samples w (n x d, drawn from N(0, I_d)):
+
+        loss(M) = mean_b min_s || w_b - M s ||      (the norm as printed)
+
+    The minimiser s_b* is piecewise constant in M, so wherever it is unique
+    the gradient of the minimum is the gradient of || w_b - M s_b* || with
+    s_b* held fixed (Danskin's theorem): -(r_b / ||r_b||) s_b*^T with
+    r_b = w_b - M s_b* (zero where r_b = 0). Plain gradient descent:
+    M <- M - lr * mean_b of that gradient.
+
+    Returns (the updated M, the loss at the old M)."""
+    M = np.asarray(M, dtype=np.float64)
+    d, D = M.shape
+    w = np.asarray(w, dtype=np.float64).reshape(-1, d)
+    signs, _ = encode_nn(w, M)
+    r = w - signs @ M.T                                # (n, d) residuals
+    norm = np.sqrt((r * r).sum(axis=1))
+    loss = float(norm.mean()) if norm.size else 0.0
+    unit = np.where(norm[:, None] > 0, r / np.where(norm > 0, norm, 1.0)[:, None], 0.0)
+    grad = -(unit.T @ signs) / max(1, w.shape[0])      # d x D
+    return M - lr * grad, loss
+

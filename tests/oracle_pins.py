@@ -19,9 +19,16 @@ What pins what:
   special case, which reduces to a plain integer matrix product.
 * The lifted route S (M^T T x) against the dense route W (T x).
 * Row scale, zero padding and storage size (the pages' worked bit-widths).
+* Nearest-neighbour encoding: a pure-Python loop over every sign vector
+  (itertools, no codebook helper); the M = I case in closed form
+  (s = sign(w), sign(0) = +1); odd symmetry and scale invariance.
+* Training step of Eq. (1): central finite differences of the loss (the
+  gradient of a minimum is the gradient at its minimiser), descent on the
+  same samples, and orthonormal rows of the initial M.
 """
 from __future__ import annotations
 
+import itertools
 from fractions import Fraction
 from pathlib import Path
 
@@ -299,10 +306,110 @@ def pin_pack_layout_bijective(o, rp):
         assert np.array_equal(np.sort(idx), np.arange(N * L)), "layout must be a bijection"
 
 
+def pin_encode_bruteforce(o, rp):
+    rng = np.random.default_rng(23)
+    for (d, D) in [(1, 1), (1, 3), (2, 5), (3, 6), (4, 4), (2, 7)]:
+        M = rng.standard_normal((d, D)) / np.sqrt(D)
+        w = rng.standard_normal((9, d))
+        signs, dist = o.encode_nn(w, M)
+        assert signs.shape == (9, D) and dist.shape == (9,)
+        for b in range(9):
+            best, arg = None, None
+            for s in itertools.product((1.0, -1.0), repeat=D):
+                acc = 0.0
+                for i in range(d):
+                    v = w[b, i]
+                    for e in range(D):
+                        v -= M[i, e] * s[e]
+                    acc += v * v
+                if best is None or acc < best - 1e-12:
+                    best, arg = acc, s
+            assert np.array_equal(signs[b], np.array(arg)), (d, D, b)
+            assert abs(dist[b] - best) <= 1e-12 * max(1.0, best)
+
+
+def pin_encode_identity(o, rp):
+    rng = np.random.default_rng(29)
+    for d in (1, 3, 6):
+        w = rng.standard_normal((20, d))
+        w[0, 0] = 0.0                                  # a tie: both signs equally close
+        signs, dist = o.encode_nn(w, np.eye(d))
+        want = np.where(w >= 0, 1.0, -1.0)
+        assert np.array_equal(signs, want)
+        assert np.allclose(dist, ((np.abs(w) - 1.0) ** 2).sum(axis=1), rtol=0, atol=1e-12)
+
+
+def pin_encode_symmetry(o, rp):
+    rng = np.random.default_rng(31)
+    M = rng.standard_normal((3, 8)) / np.sqrt(8)
+    w = rng.standard_normal((40, 3))
+    s, dist = o.encode_nn(w, M)
+    s_neg, dist_neg = o.encode_nn(-w, M)
+    assert np.array_equal(s_neg, -s)
+    assert np.allclose(dist_neg, dist, rtol=1e-12, atol=0)
+    s2, dist2 = o.encode_nn(2.0 * w, 2.0 * M)
+    assert np.array_equal(s2, s)
+    assert np.allclose(dist2, 4.0 * dist, rtol=1e-12, atol=0)
+
+
+def _eq1_loss(o, M, w):
+    """mean_b min_s ||w_b - M s|| evaluated from scratch (codebook distances)."""
+    cb = o.codebook(M)
+    dist = ((w[:, None, :] - cb[None, :, :]) ** 2).sum(axis=2)
+    return float(np.sqrt(dist.min(axis=1)).mean()), dist.argmin(axis=1)
+
+
+def pin_train_gradient_fd(o, rp):
+    rng = np.random.default_rng(37)
+    d, D = 2, 5
+    M = rng.standard_normal((d, D)) / np.sqrt(D)
+    w = rng.standard_normal((64, d))
+    lr = 1e-3
+    M_new, loss = o.train_m_step(M, w, lr)
+    l0, arg0 = _eq1_loss(o, M, w)
+    assert abs(loss - l0) <= 1e-12
+    grad = (M - M_new) / lr
+    h = 1e-6
+    for i in range(d):
+        for e in range(D):
+            E = np.zeros_like(M)
+            E[i, e] = h
+            lp, argp = _eq1_loss(o, M + E, w)
+            lm, argm = _eq1_loss(o, M - E, w)
+            assert np.array_equal(argp, arg0) and np.array_equal(argm, arg0)
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - grad[i, e]) <= 1e-6 * max(1.0, abs(fd)), (i, e, fd, grad[i, e])
+
+
+def pin_train_descends(o, rp):
+    rng = np.random.default_rng(41)
+    G = rng.standard_normal((8, 8))
+    M = o.orthonormal_rows(G, 3)
+    w = rng.standard_normal((2000, 3))
+    M1, l0 = o.train_m_step(M, w, 0.02)
+    l1, _ = _eq1_loss(o, M1, w)
+    assert l1 < l0, (l0, l1)
+    assert abs(l0 - _eq1_loss(o, M, w)[0]) <= 1e-12
+
+
+def pin_orthonormal_rows(o, rp):
+    rng = np.random.default_rng(43)
+    for (d, D) in [(3, 8), (10, 24), (4, 4)]:
+        G = rng.standard_normal((D, D))
+        M = o.orthonormal_rows(G, d)
+        assert M.shape == (d, D)
+        assert np.allclose(M @ M.T, np.eye(d), rtol=0, atol=1e-12)
+        # the rows span the same space as the first d columns of G (Gram-Schmidt)
+        proj = M.T @ M
+        assert np.allclose(proj @ G[:, :d], G[:, :d], rtol=0, atol=1e-10)
+
+
 ALL_PINS = [
     pin_hadamard_library, pin_hadamard_structure, pin_whiten_unit_vectors,
     pin_whiten_norm_and_diag, pin_codebook_bruteforce, pin_multiblock_bruteforce,
     pin_identity_mapping, pin_lifted_route, pin_lift_bruteforce,
     pin_sign_matmul_integer, pin_row_scale, pin_zero_pad, pin_rates,
     pin_memory_fit, pin_storage_exact, pin_pack_layout_bijective,
+    pin_encode_bruteforce, pin_encode_identity, pin_encode_symmetry,
+    pin_train_gradient_fd, pin_train_descends, pin_orthonormal_rows,
 ]

@@ -175,6 +175,67 @@ def _mutants():
             return orig(n, np.where(j % 128 >= 32, j - 32, j), N, L)
         rp.bit_index = bi
 
+    @m("encoder picks the farthest codeword")
+    def _(o, rp):
+        def enc(w, M):
+            M = np.asarray(M, float)
+            d, D = M.shape
+            w = np.asarray(w, float).reshape(-1, d)
+            cb = o.codebook(M)
+            dist = ((w[:, None, :] - cb[None, :, :]) ** 2).sum(axis=2)
+            i = dist.argmax(axis=1)
+            return np.stack([o.sign_pattern(int(k), D) for k in i]), dist[np.arange(len(i)), i]
+        o.encode_nn = enc
+
+    @m("encoder returns the complement of the chosen signs")
+    def _(o, rp):
+        orig = o.encode_nn
+
+        def enc(w, M):
+            s, dist = orig(w, M)
+            return -s, dist
+        o.encode_nn = enc
+
+    @m("encoder breaks ties toward the highest index")
+    def _(o, rp):
+        def enc(w, M):
+            M = np.asarray(M, float)
+            d, D = M.shape
+            w = np.asarray(w, float).reshape(-1, d)
+            cb = o.codebook(M)
+            dist = ((w[:, None, :] - cb[None, :, :]) ** 2).sum(axis=2)
+            i = (dist.shape[1] - 1) - dist[:, ::-1].argmin(axis=1)
+            return np.stack([o.sign_pattern(int(k), D) for k in i]), dist[np.arange(len(i)), i]
+        o.encode_nn = enc
+
+    @m("training step ascends")
+    def _(o, rp):
+        orig = o.train_m_step
+
+        def step(M, w, lr):
+            return orig(M, w, -lr)
+        o.train_m_step = step
+
+    @m("training step uses the squared norm")
+    def _(o, rp):
+        def step(M, w, lr):
+            M = np.asarray(M, float)
+            d, D = M.shape
+            w = np.asarray(w, float).reshape(-1, d)
+            s, _ = o.encode_nn(w, M)
+            r = w - s @ M.T
+            loss = float(np.sqrt((r * r).sum(axis=1)).mean())
+            grad = -2.0 * (r.T @ s) / w.shape[0]
+            return M - lr * grad, loss
+        o.train_m_step = step
+
+    @m("initial M with orthonormal columns of a tall draw")
+    def _(o, rp):
+        def orth(G, d):
+            q, _ = np.linalg.qr(np.asarray(G, float)[:, :d])
+            return q.T[:, :G.shape[0]] * 1.5
+        o.orthonormal_rows = orth
+
     return out
 
 
