@@ -14,7 +14,7 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import (LQ_ALGO_AUTO, LQ_ALGO_FUSED, LQ_ALGO_FUSED_LOCAL, LQ_ALGO_MFMA_LARGE, LQ_ALGO_WSPACE,
+from ._lib import (LQ_ENCODE_MAX_D, LQ_ENCODE_MAX_SMALL_D, LQ_ALGO_AUTO, LQ_ALGO_FUSED, LQ_ALGO_FUSED_LOCAL, LQ_ALGO_MFMA_LARGE, LQ_ALGO_WSPACE,
                    LQ_ALGO_MFMA_SMALL,
                    LQ_ALGO_VALU, LQ_BF16, LQ_F32, LQ_MAX_D, LQ_MAX_HB, LQ_WS_CONTROL_BYTES,
                    LQ_WS_ERROR_WORD, LQError, LQLayer)
@@ -23,7 +23,8 @@ __all__ = [
     "lq_version", "lq_packed_size", "lq_pack_signs", "lq_unpack_signs", "lq_hadamard_scale",
     "lq_lift_activations", "lq_sign_gemm_workspace_size", "lq_sign_gemm", "lq_sign_gemm_ex",
     "lq_linear_workspace_size", "lq_linear", "lq_linear_workspace_size_ex", "lq_linear_ex",
-    "lq_linear_algo",
+    "lq_linear_algo", "lq_encode", "lq_train_m_step_workspace_size", "lq_train_m_step",
+    "LQ_ENCODE_MAX_D", "LQ_ENCODE_MAX_SMALL_D",
     "lq_workspace_init", "lq_profile_events", "layer_struct", "LQError", "LQLayer",
     "LQ_F32", "LQ_BF16", "LQ_ALGO_AUTO", "LQ_ALGO_VALU", "LQ_ALGO_MFMA_SMALL",
     "LQ_ALGO_MFMA_LARGE", "LQ_ALGO_FUSED", "LQ_ALGO_FUSED_LOCAL", "LQ_ALGO_WSPACE", "LQ_MAX_D", "LQ_MAX_HB", "LQ_WS_CONTROL_BYTES",
@@ -163,6 +164,37 @@ def lq_linear_ex(layer: LQLayer, x, B, y, algo, ws=None, stream=None) -> None:
     _check(_lib.LIB.lq_linear_ex(ctypes.byref(layer), _dev(x, "x"), _dtype(x, "x"), B, _dev(y, "y"),
                                  _dtype(y, "y"), algo, ws_ptr, ws_bytes, _stream(stream)),
            "lq_linear_ex")
+
+
+def lq_encode(w, nblocks, d, D, M, signs, dist2=None, stream=None) -> None:
+    """Nearest-neighbour encoding: signs[b] = argmin_s ||w_b - M s|| (float32
+    w, M; int8 signs; optional float32 squared distances)."""
+    for t, name, dt in ((w, "w", torch.float32), (M, "M", torch.float32), (signs, "signs", torch.int8)):
+        if t.dtype != dt:
+            raise ValueError(f"{name} must be {dt}")
+    if dist2 is not None and dist2.dtype != torch.float32:
+        raise ValueError("dist2 must be float32")
+    _check(_lib.LIB.lq_encode(_dev(w, "w"), nblocks, d, D, _dev(M, "M"), _dev(signs, "signs"),
+                              _opt(dist2, "dist2"), _stream(stream)), "lq_encode")
+
+
+def lq_train_m_step_workspace_size(n, d, D) -> int:
+    out = ctypes.c_size_t()
+    _check(_lib.LIB.lq_train_m_step_workspace_size(n, d, D, ctypes.byref(out)),
+           "lq_train_m_step_workspace_size")
+    return out.value
+
+
+def lq_train_m_step(M, w, n, d, D, lr, loss=None, ws=None, stream=None) -> None:
+    """One gradient step of Eq. (1) on M (float32, updated in place) over the
+    samples w (n x d float32); loss (one float32) receives the loss at the
+    old M."""
+    if M.dtype != torch.float32 or w.dtype != torch.float32:
+        raise ValueError("M and w must be float32")
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.LIB.lq_train_m_step(_dev(M, "M"), _dev(w, "w"), n, d, D, float(lr),
+                                    _opt(loss, "loss"), _opt(ws, "ws"), ws_bytes, _stream(stream)),
+           "lq_train_m_step")
 
 
 def lq_workspace_init(ws, stream=None) -> None:

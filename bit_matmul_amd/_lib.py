@@ -2,7 +2,7 @@
 from __future__ import annotations
 
 import ctypes
-from ctypes import POINTER, c_char_p, c_int, c_int32, c_int64, c_size_t, c_void_p
+from ctypes import POINTER, c_char_p, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
 from pathlib import Path
 
 LIB_PATH = Path(__file__).resolve().parent / "liblq.so"
@@ -15,6 +15,8 @@ LQ_MAX_D = 64
 LQ_MAX_HB = 1024
 LQ_WS_CONTROL_BYTES = 16896
 LQ_WS_ERROR_WORD = 96
+LQ_ENCODE_MAX_D = 24
+LQ_ENCODE_MAX_SMALL_D = 16
 
 # Every symbol include/lq.h declares.
 EXPORTS = [
@@ -22,7 +24,8 @@ EXPORTS = [
     "lq_pack_signs", "lq_unpack_signs", "lq_hadamard_scale", "lq_lift_activations",
     "lq_sign_gemm_workspace_size", "lq_sign_gemm", "lq_sign_gemm_ex",
     "lq_linear_workspace_size", "lq_linear", "lq_linear_workspace_size_ex", "lq_linear_ex",
-    "lq_linear_algo", "lq_workspace_init", "lq_profile_events",
+    "lq_linear_algo", "lq_workspace_init", "lq_profile_events", "lq_encode",
+    "lq_train_m_step_workspace_size", "lq_train_m_step",
 ]
 
 
@@ -67,6 +70,9 @@ def _load():
         "lq_linear": (c_int, [POINTER(LQLayer), vp, c_int, i64, vp, c_int, vp, sz, vp]),
         "lq_linear_workspace_size_ex": (c_int, [POINTER(LQLayer), i64, c_int, c_int, POINTER(sz)]),
         "lq_linear_algo": (c_int, [POINTER(LQLayer), i64, c_int, c_int, POINTER(c_int)]),
+        "lq_encode": (c_int, [vp, i64, c_int32, c_int32, vp, vp, vp, vp]),
+        "lq_train_m_step_workspace_size": (c_int, [i64, c_int32, c_int32, POINTER(sz)]),
+        "lq_train_m_step": (c_int, [vp, vp, i64, c_int32, c_int32, c_float, vp, vp, sz, vp]),
         "lq_linear_ex": (c_int, [POINTER(LQLayer), vp, c_int, i64, vp, c_int, c_int, vp, sz, vp]),
         "lq_workspace_init": (c_int, [vp, sz, vp]),
         "lq_profile_events": (c_int, [POINTER(vp), POINTER(vp), i32]),

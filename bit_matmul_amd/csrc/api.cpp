@@ -519,6 +519,49 @@ lq_status lq_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   return hip_status(lq::launch_zero_u32(static_cast<unsigned*>(ws), (int)n, (hipStream_t)stream));
 }
 
+static_assert(LQ_ENCODE_MAX_D == lq::kEncodeMaxD && LQ_ENCODE_MAX_SMALL_D == lq::kEncodeMaxSmallD,
+              "encoder limits");
+
+static lq_status check_encode_dims(int64_t n, int32_t d, int32_t D) {
+  if (n < 0 || d < 1 || D < 1) return LQ_ERR_INVALID_ARG;
+  if (d > D) return LQ_ERR_INVALID_ARG;
+  if (d > LQ_ENCODE_MAX_SMALL_D || D > LQ_ENCODE_MAX_D) return LQ_ERR_UNSUPPORTED;
+  if (!mul_ok(n, D, kMaxElems) || !mul_ok(n, d, kMaxElems)) return LQ_ERR_UNSUPPORTED;
+  return LQ_OK;
+}
+
+static bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+lq_status lq_encode(const float* w, int64_t nblocks, int32_t d, int32_t D, const float* M,
+                    int8_t* signs, float* dist2, void* stream) {
+  lq_status s = check_encode_dims(nblocks, d, D);
+  if (s != LQ_OK) return s;
+  if (nblocks == 0) return LQ_OK;
+  if (w == nullptr || M == nullptr || signs == nullptr) return LQ_ERR_INVALID_ARG;
+  if (!aligned4(w) || !aligned4(M) || !aligned4(dist2)) return LQ_ERR_INVALID_ARG;
+  return hip_status(lq::launch_encode(w, nblocks, d, D, M, signs, dist2, (hipStream_t)stream));
+}
+
+lq_status lq_train_m_step_workspace_size(int64_t n, int32_t d, int32_t D, size_t* bytes) {
+  if (bytes == nullptr) return LQ_ERR_INVALID_ARG;
+  lq_status s = check_encode_dims(n, d, D);
+  if (s != LQ_OK) return s;
+  *bytes = n == 0 ? 0 : lq::train_workspace_bytes(n, d, D);
+  return LQ_OK;
+}
+
+lq_status lq_train_m_step(float* M, const float* w, int64_t n, int32_t d, int32_t D, float lr,
+                          float* loss, void* ws, size_t ws_bytes, void* stream) {
+  lq_status s = check_encode_dims(n, d, D);
+  if (s != LQ_OK) return s;
+  if (n == 0) return LQ_OK;
+  if (w == nullptr || M == nullptr) return LQ_ERR_INVALID_ARG;
+  if (!aligned4(w) || !aligned4(M) || !aligned4(loss)) return LQ_ERR_INVALID_ARG;
+  s = check_ws(ws, ws_bytes, lq::train_workspace_bytes(n, d, D));
+  if (s != LQ_OK) return s;
+  return hip_status(lq::launch_train_step(M, w, n, d, D, lr, loss, ws, (hipStream_t)stream));
+}
+
 lq_status lq_profile_events(void* const* starts, void* const* stops, int32_t count) {
   if (count < 0 || (count > 0 && (starts == nullptr || stops == nullptr))) return LQ_ERR_INVALID_ARG;
   ProfileRing& ring = profile_ring();

@@ -1,0 +1,248 @@
+// Nearest-neighbour encoding of weight blocks, and one gradient step of the
+// mapping matrix M on it ([paper] §3.1, Eq. (1): the inner minimisation over
+// the sign vectors is the quantization step; the outer one trains M on
+// Gaussian blocks).
+//
+// Search: every sign vector s in {+1,-1}^D is visited once, in Gray-code
+// order, carrying the residual r = w - M s in fp64 (a flip of sign e moves it
+// by +-2 M[:, e]: d adds and d fused multiply-adds for the squared distance
+// per visit). The minimum is taken on (distance, pattern index), index bit e
+// set meaning s_e = -1, so that equal distances go to the lowest index. For
+// D <= 10 one lane walks all 2^D vectors of its block; beyond, a wavefront
+// shares a block: lane l walks the 2^(D-6) vectors whose top six bits are l,
+// and the wavefront reduces.
+#include "lq_internal.h"
+
+namespace lq {
+namespace {
+
+constexpr int kEncThreads = 256;
+
+// 2 M[i][e] as doubles at [e][DM] (rows past d zero: they add exact zeros).
+template <int DM>
+__device__ __forceinline__ void stage_m2(double* m2, const float* __restrict__ M, int d, int D) {
+  for (int j = threadIdx.x; j < D * DM; j += kEncThreads) {
+    const int e = j / DM, i = j - e * DM;
+    m2[j] = i < d ? 2.0 * (double)M[i * D + e] : 0.0;
+  }
+}
+
+// The search over patterns p = prefix | q, q < 2^nfree, for one block.
+// Returns the best (distance, index) of this lane.
+template <int DM>
+__device__ __forceinline__ void walk(const double* m2, const double (&wv)[DM], int D,
+                                     uint32_t prefix, int nfree, double& best, uint32_t& bidx) {
+  // residual of the first pattern: r = w - M s, s_e = -1 where bit e is set
+  double r[DM];
+#pragma unroll
+  for (int i = 0; i < DM; ++i) r[i] = wv[i];
+  for (int e = 0; e < D; ++e) {
+    const double sgn = ((prefix >> e) & 1) ? 0.5 : -0.5;   // - s_e / 2 (m2 holds 2 M)
+#pragma unroll
+    for (int i = 0; i < DM; ++i) r[i] = fma(sgn, m2[e * DM + i], r[i]);
+  }
+  double dist = 0.0;
+#pragma unroll
+  for (int i = 0; i < DM; ++i) dist = fma(r[i], r[i], dist);
+  best = dist;
+  bidx = prefix;
+  uint32_t pat = prefix;
+  const uint32_t count = 1u << nfree;
+  for (uint32_t k = 1; k < count; ++k) {
+    const int e = __builtin_ctz(k);
+    pat ^= 1u << e;
+    // s_e became -1: M s lost 2 M[:, e], r gains it; became +1: r loses it
+    const double sg = ((pat >> e) & 1) ? 1.0 : -1.0;
+    const double* col = m2 + e * DM;
+    double dd = 0.0;
+#pragma unroll
+    for (int i = 0; i < DM; ++i) {
+      r[i] = fma(sg, col[i], r[i]);
+      dd = fma(r[i], r[i], dd);
+    }
+    if (dd < best || (dd == best && pat < bidx)) {
+      best = dd;
+      bidx = pat;
+    }
+  }
+}
+
+__device__ __forceinline__ void better(double& best, uint32_t& bidx, double ob, uint32_t oi) {
+  if (ob < best || (ob == best && oi < bidx)) {
+    best = ob;
+    bidx = oi;
+  }
+}
+
+// kWave: one wavefront per block (D > 10), else one lane per block.
+// Writes signs[b][e] = +-1 and, if dist2 is not null, the squared distance.
+template <int DM, bool kWave>
+__global__ __launch_bounds__(kEncThreads) void encode_kernel(const float* __restrict__ w,
+                                                             int64_t nblocks, int d, int D,
+                                                             const float* __restrict__ M,
+                                                             int8_t* __restrict__ signs,
+                                                             float* __restrict__ dist2) {
+  __shared__ double m2[32 * DM];
+  stage_m2<DM>(m2, M, d, D);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int64_t b = kWave ? (int64_t)blockIdx.x * (kEncThreads / 64) + (threadIdx.x >> 6)
+                          : (int64_t)blockIdx.x * kEncThreads + threadIdx.x;
+  if (b >= nblocks) return;                    // (after the only barrier)
+  double wv[DM];
+#pragma unroll
+  for (int i = 0; i < DM; ++i) wv[i] = i < d ? (double)w[b * d + i] : 0.0;
+  double best;
+  uint32_t bidx;
+  if (kWave) {
+    const int nfree = D - 6;
+    walk<DM>(m2, wv, D, (uint32_t)lane << nfree, nfree, best, bidx);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const double ob = __shfl_xor(best, o, 64);
+      const uint32_t oi = (uint32_t)__shfl_xor((int)bidx, o, 64);
+      better(best, bidx, ob, oi);
+    }
+    // lane e writes sign e
+    if (lane < D) signs[b * D + lane] = ((bidx >> lane) & 1) ? (int8_t)-1 : (int8_t)1;
+    if (lane == 0 && dist2 != nullptr) dist2[b] = (float)best;
+  } else {
+    walk<DM>(m2, wv, D, 0u, D, best, bidx);
+    for (int e = 0; e < D; ++e) signs[b * D + e] = ((bidx >> e) & 1) ? (int8_t)-1 : (int8_t)1;
+    if (dist2 != nullptr) dist2[b] = (float)best;
+  }
+}
+
+// ------------------------------------------------------------ training step
+// Workgroup g takes samples 256 g .. 256 g + 255. Phase 1, thread = sample:
+// r = w - M s* and u = r / ||r|| (zero where r = 0) in fp64, into LDS with
+// the signs. Phase 2, thread = entry (i, e) of the gradient: -sum over the
+// workgroup's samples, in order, of u[i] s*[e]; thread d D sums ||r||. One
+// (d D + 1)-double partial per workgroup; deterministic.
+template <int DM>
+__global__ __launch_bounds__(kEncThreads) void train_grad_kernel(
+    const float* __restrict__ w, const int8_t* __restrict__ signs, int64_t n, int d, int D,
+    const float* __restrict__ M, double* __restrict__ partial) {
+  __shared__ double us[kEncThreads * DM];
+  __shared__ double norms[kEncThreads];
+  __shared__ int8_t ss[kEncThreads * 32];
+  const int t = threadIdx.x;
+  const int64_t b = (int64_t)blockIdx.x * kEncThreads + t;
+  if (b < n) {
+    double r[DM];
+    double nrm = 0.0;
+#pragma unroll
+    for (int i = 0; i < DM; ++i) {
+      double v = 0.0;
+      if (i < d) {
+        v = (double)w[b * d + i];
+        for (int e = 0; e < D; ++e) v -= (double)M[i * D + e] * (double)signs[b * D + e];
+      }
+      r[i] = v;
+      nrm = fma(v, v, nrm);
+    }
+    nrm = sqrt(nrm);
+    norms[t] = nrm;
+#pragma unroll
+    for (int i = 0; i < DM; ++i) us[t * DM + i] = nrm > 0.0 ? r[i] / nrm : 0.0;
+    for (int e = 0; e < D; ++e) ss[t * 32 + e] = signs[b * D + e];
+  } else {
+    norms[t] = 0.0;
+#pragma unroll
+    for (int i = 0; i < DM; ++i) us[t * DM + i] = 0.0;
+    for (int e = 0; e < D; ++e) ss[t * 32 + e] = 0;
+  }
+  __syncthreads();
+  const int width = d * D + 1;
+  for (int j = t; j < width; j += kEncThreads) {
+    double acc = 0.0;
+    if (j < d * D) {
+      const int i = j / D, e = j - i * D;
+      for (int k = 0; k < kEncThreads; ++k) acc -= us[k * DM + i] * (double)ss[k * 32 + e];
+    } else {
+      for (int k = 0; k < kEncThreads; ++k) acc += norms[k];
+    }
+    partial[(int64_t)blockIdx.x * width + j] = acc;
+  }
+}
+
+// One workgroup: the partials in workgroup order, the mean, the update
+// M <- M - lr * grad (fp64, stored as fp32), the loss (the mean of ||r|| at
+// the old M).
+__global__ __launch_bounds__(kEncThreads) void train_update_kernel(const double* __restrict__ partial,
+                                                                   int groups, int64_t n, int d,
+                                                                   int D, float lr,
+                                                                   float* __restrict__ M,
+                                                                   float* __restrict__ loss) {
+  const int width = d * D + 1;
+  for (int j = threadIdx.x; j < width; j += kEncThreads) {
+    double acc = 0.0;
+    for (int g = 0; g < groups; ++g) acc += partial[(int64_t)g * width + j];
+    acc /= (double)n;
+    if (j < d * D) M[j] = (float)((double)M[j] - (double)lr * acc);
+    else if (loss != nullptr) *loss = (float)acc;
+  }
+}
+
+template <int DM>
+hipError_t launch_encode_t(const float* w, int64_t nblocks, int d, int D, const float* M,
+                           int8_t* signs, float* dist2, hipStream_t stream) {
+  if (D > 10) {
+    const int64_t groups = (nblocks + 3) / 4;
+    hipLaunchKernelGGL((encode_kernel<DM, true>), dim3((unsigned)groups), dim3(kEncThreads), 0,
+                       stream, w, nblocks, d, D, M, signs, dist2);
+  } else {
+    const int64_t groups = (nblocks + kEncThreads - 1) / kEncThreads;
+    hipLaunchKernelGGL((encode_kernel<DM, false>), dim3((unsigned)groups), dim3(kEncThreads), 0,
+                       stream, w, nblocks, d, D, M, signs, dist2);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_encode(const float* w, int64_t nblocks, int d, int D, const float* M,
+                         int8_t* signs, float* dist2, hipStream_t stream) {
+  (void)hipGetLastError();   // clear a stale error of an earlier runtime call
+  if (d < 1 || d > D || D > kEncodeMaxD || d > kEncodeMaxSmallD) return hipErrorInvalidValue;
+  if (nblocks == 0) return hipSuccess;
+  if (d <= 4) return launch_encode_t<4>(w, nblocks, d, D, M, signs, dist2, stream);
+  if (d <= 8) return launch_encode_t<8>(w, nblocks, d, D, M, signs, dist2, stream);
+  if (d <= 12) return launch_encode_t<12>(w, nblocks, d, D, M, signs, dist2, stream);
+  return launch_encode_t<16>(w, nblocks, d, D, M, signs, dist2, stream);
+}
+
+int train_groups(int64_t n) { return (int)((n + kEncThreads - 1) / kEncThreads); }
+
+size_t train_workspace_bytes(int64_t n, int d, int D) {
+  // signs (n D bytes, 16-byte aligned), then the partials
+  const size_t sb = ((size_t)n * D + 15) / 16 * 16;
+  return sb + (size_t)train_groups(n) * (d * D + 1) * sizeof(double);
+}
+
+hipError_t launch_train_step(float* M, const float* w, int64_t n, int d, int D, float lr,
+                             float* loss, void* ws, hipStream_t stream) {
+  (void)hipGetLastError();
+  if (d < 1 || d > D || D > kTrainMaxD || d > kEncodeMaxSmallD) return hipErrorInvalidValue;
+  int8_t* signs = reinterpret_cast<int8_t*>(ws);
+  double* partial = reinterpret_cast<double*>(reinterpret_cast<char*>(ws) +
+                                              ((size_t)n * D + 15) / 16 * 16);
+  hipError_t e = launch_encode(w, n, d, D, M, signs, nullptr, stream);
+  if (e != hipSuccess) return e;
+  const int groups = train_groups(n);
+#define LQ_TRAIN(DM_)                                                                             \
+  hipLaunchKernelGGL(train_grad_kernel<DM_>, dim3((unsigned)groups), dim3(kEncThreads), 0, stream, \
+                     w, signs, n, d, D, M, partial)
+  if (d <= 4) LQ_TRAIN(4);
+  else if (d <= 8) LQ_TRAIN(8);
+  else if (d <= 12) LQ_TRAIN(12);
+  else LQ_TRAIN(16);
+#undef LQ_TRAIN
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(train_update_kernel, dim3(1), dim3(kEncThreads), 0, stream, partial, groups,
+                     n, d, D, lr, M, loss);
+  return hipGetLastError();
+}
+
+}  // namespace lq

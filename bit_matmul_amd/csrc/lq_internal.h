@@ -323,6 +323,17 @@ struct XpGeom {
 };
 XpGeom xp_geom(int64_t B, const PackedGeom& g, int D);
 LargePlan plan_wspace(int64_t B, const PackedGeom& g, int D);
+// ---- nearest-neighbour encoding and the training step of M (encode.hip)
+constexpr int kEncodeMaxD = 24;        // exhaustive search: 2^D sign vectors per block
+constexpr int kEncodeMaxSmallD = 16;   // d (the residual lives in registers)
+constexpr int kTrainMaxD = 24;
+hipError_t launch_encode(const float* w, int64_t nblocks, int d, int D, const float* M,
+                         int8_t* signs, float* dist2, hipStream_t stream);
+int train_groups(int64_t n);
+size_t train_workspace_bytes(int64_t n, int d, int D);
+hipError_t launch_train_step(float* M, const float* w, int64_t n, int d, int D, float lr,
+                             float* loss, void* ws, hipStream_t stream);
+
 // Whitening of x straight into xp (no xt in memory).
 hipError_t launch_xpw(const void* x, bool x_bf16, int64_t B, int64_t K, int hb, const float* c,
                       int d, int D, const PackedGeom& g, void* xp, hipStream_t stream);

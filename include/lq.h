@@ -267,6 +267,45 @@ lq_status lq_linear_ex(const lq_layer* layer, const void* x, lq_dtype xtype, int
 lq_status lq_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Nearest-neighbour encoding ([paper] §3.1, Eq. (1): the inner minimisation,
+ * which the paper names the nearest-neighbour search, i.e. the quantization
+ * step): for every d-block w_b,
+ *     s_b = argmin over s in {+1,-1}^D of || w_b - M s ||_2,
+ * searched exhaustively over the 2^D sign vectors (fp64 residuals); among
+ * equally close vectors the one with the lowest index, index bit e set
+ * meaning s_e = -1.
+ * w: nblocks x d floats (device; for a weight matrix already in the lifted
+ * model's frame, its rows' d-blocks in order), M: d x D floats (device),
+ * signs: nblocks x D int8 (device, +1 / -1: the input of lq_pack_signs),
+ * dist2: nblocks floats (device, may be NULL): the squared distance.
+ * Limits: 1 <= d <= LQ_ENCODE_MAX_SMALL_D, d <= D <= LQ_ENCODE_MAX_D
+ * (UNSUPPORTED beyond). Errors: INVALID_ARG for NULL pointers with
+ * nblocks > 0, float pointers not 4-byte aligned, nblocks < 0 or d > D.
+ */
+#define LQ_ENCODE_MAX_D 24
+#define LQ_ENCODE_MAX_SMALL_D 16
+lq_status lq_encode(const float* w, int64_t nblocks, int32_t d, int32_t D, const float* M,
+                    int8_t* signs, float* dist2, void* stream);
+
+/*
+ * One gradient step on M of the objective of [paper] §3.1 Eq. (1), on the
+ * caller's samples w (n x d floats on the device, drawn from N(0, I_d)):
+ *     loss(M) = mean_b min_s || w_b - M s ||_2     (the norm as printed).
+ * The minimiser s_b* (lq_encode's) is piecewise constant in M, so the
+ * gradient of the minimum is that of ||w_b - M s_b*|| with s_b* held fixed,
+ * -(r_b / ||r_b||) s_b*^T, r_b = w_b - M s_b* (zero where r_b = 0); the step
+ * is M <- M - lr * (its mean over the samples), in fp64, stored back into M
+ * (d x D floats, device, in place). loss: one float (device, may be NULL):
+ * the loss at the old M. Deterministic: fixed summation order.
+ * ws: device workspace of lq_train_m_step_workspace_size bytes (16-byte
+ * aligned). Limits as lq_encode. Errors: as lq_encode, WORKSPACE for a
+ * missing or short workspace.
+ */
+lq_status lq_train_m_step_workspace_size(int64_t n, int32_t d, int32_t D, size_t* bytes);
+lq_status lq_train_m_step(float* M, const float* w, int64_t n, int32_t d, int32_t D, float lr,
+                          float* loss, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Profiling aid: time the sign-product kernel itself. `starts` and `stops`
  * are host arrays of `count` hipEvent_t handles (passed as void*) created by
  * the caller. While set, every sign-product kernel launched by lq_sign_gemm,

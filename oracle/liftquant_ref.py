@@ -213,25 +213,31 @@ def encode_nn(w: np.ndarray, M: np.ndarray):
     the sign vector s in {+1,-1}^D whose codeword M s is closest to w_b in
     Euclidean distance. This is the inner minimisation of [paper] §3.1
     Eq. (1), which the paper names the nearest-neighbour search, i.e. the
-    quantization step. Exhaustive over the 2^D codewords of ``codebook``;
-    among equally close codewords the lowest ``sign_pattern`` index wins.
+    quantization step. Exhaustive over the 2^D sign vectors, numbered as in
+    ``sign_pattern`` and visited in that order (in chunks, to bound memory);
+    among equally close codewords the lowest number wins.
 
     Returns (signs (n, D) of +-1, squared distances (n,))."""
     M = np.asarray(M, dtype=np.float64)
     d, D = M.shape
     w = np.asarray(w, dtype=np.float64).reshape(-1, d)
-    cb = codebook(M)                                   # (2^D, d)
     n = w.shape[0]
-    idx = np.empty(n, dtype=np.int64)
-    best = np.empty(n)
-    step = max(1, (1 << 22) >> D)                      # blocks per chunk (bounded memory)
-    for a in range(0, n, step):
-        diff = w[a:a + step, None, :] - cb[None, :, :]
-        dist = (diff * diff).sum(axis=2)               # (chunk, 2^D)
-        i = np.argmin(dist, axis=1)                    # first minimum: lowest index
-        idx[a:a + step] = i
-        best[a:a + step] = dist[np.arange(i.size), i]
-    signs = np.stack([sign_pattern(int(i), D) for i in idx]) if n else np.zeros((0, D))
+    best = np.full(n, np.inf)
+    idx = np.zeros(n, dtype=np.int64)
+    chunk = 1 << min(D, 16)
+    for p0 in range(0, 1 << D, chunk):
+        numbers = np.arange(p0, p0 + chunk, dtype=np.int64)
+        S = np.where((numbers[:, None] >> np.arange(D)[None, :]) & 1, -1.0, 1.0)   # sign_pattern rows
+        cw = S @ M.T                                                               # codewords M s
+        for a in range(0, n, 64):
+            diff = w[a:a + 64, None, :] - cw[None, :, :]
+            dist = (diff * diff).sum(axis=2)                                       # (<=64, chunk)
+            i = np.argmin(dist, axis=1)                                            # first minimum
+            v = dist[np.arange(i.size), i]
+            take = v < best[a:a + 64]                                              # strictly closer only
+            best[a:a + 64] = np.where(take, v, best[a:a + 64])
+            idx[a:a + 64] = np.where(take, p0 + i, idx[a:a + 64])
+    signs = np.where((idx[:, None] >> np.arange(D)[None, :]) & 1, -1.0, 1.0)
     return signs, best
 
 

@@ -239,3 +239,32 @@ def test_linear_algo_resolution():
     assert res(gate, 0, LQ_BF16)[0] == LQ_ERR_INVALID_ARG
     assert f(ctypes.byref(gate), 1, LQ_BF16, 0, None) == LQ_ERR_INVALID_ARG
     assert res(gate, 1, LQ_BF16, 7)[0] == LQ_ERR_INVALID_ARG
+
+
+def test_encode_and_train_validation():
+    f = LIB.lq_encode
+    assert f(P, 0, 3, 8, P, P, None, None) == LQ_OK                     # nothing to do
+    assert f(None, 4, 3, 8, P, P, None, None) == LQ_ERR_INVALID_ARG
+    assert f(P, 4, 3, 8, None, P, None, None) == LQ_ERR_INVALID_ARG
+    assert f(P, 4, 3, 8, P, None, None, None) == LQ_ERR_INVALID_ARG
+    assert f(P, -1, 3, 8, P, P, None, None) == LQ_ERR_INVALID_ARG
+    assert f(P, 4, 9, 8, P, P, None, None) == LQ_ERR_INVALID_ARG       # d > D
+    assert f(P, 4, 0, 8, P, P, None, None) == LQ_ERR_INVALID_ARG
+    assert f(P, 4, 3, 25, P, P, None, None) == LQ_ERR_UNSUPPORTED      # 2^25 per block
+    assert f(P, 4, 17, 24, P, P, None, None) == LQ_ERR_UNSUPPORTED     # d > 16
+    odd = P + 2
+    assert f(odd, 4, 3, 8, P, P, None, None) == LQ_ERR_INVALID_ARG
+    assert f(P, 4, 3, 8, P, P, odd, None) == LQ_ERR_INVALID_ARG
+    out = ctypes.c_size_t()
+    g = LIB.lq_train_m_step_workspace_size
+    assert g(1000, 3, 8, ctypes.byref(out)) == LQ_OK
+    assert out.value >= 1000 * 8 + 4 * (3 * 8 + 1) * 8                 # signs + partials
+    assert g(0, 3, 8, ctypes.byref(out)) == LQ_OK and out.value == 0
+    assert g(10, 3, 8, None) == LQ_ERR_INVALID_ARG
+    assert g(10, 3, 30, ctypes.byref(out)) == LQ_ERR_UNSUPPORTED
+    t = LIB.lq_train_m_step
+    need = 1000 * 8 + 4 * (3 * 8 + 1) * 8
+    assert t(P, P, 1000, 3, 8, ctypes.c_float(0.1), None, P, 16, None) == LQ_ERR_WORKSPACE
+    assert t(P, P, 1000, 3, 8, ctypes.c_float(0.1), None, None, 0, None) == LQ_ERR_WORKSPACE
+    assert t(None, P, 1000, 3, 8, ctypes.c_float(0.1), None, P, need, None) == LQ_ERR_INVALID_ARG
+    assert t(P, P, 0, 3, 8, ctypes.c_float(0.1), None, None, 0, None) == LQ_OK
