@@ -18,7 +18,9 @@ Printed (one JSON line): whole-step packed-weight throughput in GB/s
 with HIP events around each of its launches inside the timed graph, and the
 CPU oracle's rate on a bounded sample of the same workload. With
 The 2048-token prefill layer (d = 3, D = 8) is timed too, in TFLOP/s (its
-own object in the line; `--no-prefill` skips it).
+own object in the line; `--no-prefill` skips it), and so are the
+nearest-neighbour encoder and the training step of M (`encode` object;
+`--no-encode` skips it).
 
 Synthetic data: packed weights are uniformly random bytes (i.e. independent
 fair signs), M ~ N(0, 1/D), row scales ~ U[0.5, 1.5], channel scales ~
@@ -43,9 +45,12 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP64_PEAK_TFLOPS = 78.6        # MI355X fp64 vector (FMA = 2 flops), TFLOP/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 ROOT = os.path.dirname(os.path.abspath(__file__))
 SIGN_KERNEL = "sign_fp6_kernel"
+# The files of the kernels whose HBM traffic the committed summary holds.
+TRAFFIC_SOURCES = ("sign_fp6.hip", "prep.hip", "sign_mfma.hip", "wspace.hip")
 LARGE_KERNEL = "sign_mfma_large_kernel"
 WSPACE_KERNEL = "wspace_kernel"
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_llama3_8b_mlp_b1_and_prefill_8192_b2048.txt")
@@ -67,6 +72,8 @@ def parse_args():
                    help="algorithm of the prefill lq_linear call (lq_linear_ex; auto = lq_linear)")
     p.add_argument("--no-prefill", action="store_true",
                    help="skip the 2048-token prefill layer (TFLOP/s)")
+    p.add_argument("--no-encode", action="store_true",
+                   help="skip the encoder and training-step timings")
     p.add_argument("--eager", action="store_true",
                    help="launch the timed steps eagerly, each sign product timed by its own "
                         "dispatch events (slows the launches down)")
@@ -82,14 +89,15 @@ def parse_args():
 # ------------------------------------------------------------ profiling aids
 
 def kernel_sources_hash():
-    """Hash of the kernel sources (.hip and the headers they include; a
-    counter summary taken on other kernels is stale). Host-only files such
-    as the C-ABI dispatch do not change what a kernel reads or writes."""
+    """Hash of the sources of the kernels the counter summary covers (their
+    .hip files and every header; a summary taken on other code is stale).
+    Host-only files such as the C-ABI dispatch, and kernels the summary does
+    not cover, do not change what these kernels read or write."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_matmul_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
+        if name.endswith(".h") or name in TRAFFIC_SOURCES:
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -455,16 +463,81 @@ def run_prefill(args, torch, lq, ev, steps=10):
                 kernel_flops=kflops, lifted_flops=flops, dense_equiv_flops=dense)
 
 
+def run_encode(torch, lq, reps=3):
+    """lq_encode at the 2.4-bit rate (d = 10, D = 24: 2^24 sign vectors per
+    block) on 4096 blocks and at the prefill rate (d = 3, D = 8) on a whole
+    8192 x 8192 layer's blocks; lq_train_m_step (d = 3, D = 8) on 65536
+    Gaussian samples. Kernel time from torch events on the stream the
+    library launches on (its current stream)."""
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(3)
+
+    def orth(d, D):
+        q, r = torch.linalg.qr(torch.randn(D, D, device=dev, generator=gen, dtype=torch.float64))
+        return (q * torch.sign(torch.diagonal(r))[None, :])[:, :d].T.contiguous().float()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b) / reps
+    out = []
+    for d, D, n, label in ((10, 24, 4096, "2.4-bit rate (d=10, D=24), 4096 blocks"),
+                           (3, 8, 8192 * 2731, "2.67-bit rate (d=3, D=8), the 8192x8192 layer's 22.4M blocks")):
+        M = orth(d, D)
+        w = torch.randn(n, d, device=dev, generator=gen)
+        signs = torch.empty(n, D, dtype=torch.int8, device=dev)
+        ms = timed(lambda: lq.lq_encode(w, n, d, D, M, signs))
+        flops = float(n) * (1 << D) * 4 * d        # per visited vector: d updates + d distance FMAs
+        out.append(dict(workload=label, d=d, D=D, blocks=n, ms=ms, blocks_per_s=n / (ms * 1e-3),
+                        tflops=flops / (ms * 1e-3) / 1e12))
+    d, D, n = 3, 8, 65536
+    M = orth(d, D)
+    w = torch.randn(n, d, device=dev, generator=gen)
+    loss = torch.zeros(1, device=dev)
+    ws = torch.zeros(lq.lq_train_m_step_workspace_size(n, d, D), dtype=torch.uint8, device=dev)
+    ms_train = timed(lambda: lq.lq_train_m_step(M, w, n, d, D, 0.01, loss, ws))
+    return out, dict(workload=f"one Eq. (1) step, d={d}, D={D}, {n} Gaussian samples", ms=ms_train)
+
+
+def encode_cpu_baseline():
+    """The oracle's exhaustive search on a small sample of the same blocks."""
+    import numpy as np
+    from oracle import liftquant_ref as ref
+    rng = np.random.default_rng(3)
+    res = []
+    for d, D, n in ((10, 24, 1), (3, 8, 20000)):
+        M = ref.orthonormal_rows(rng.standard_normal((D, D)), d)
+        w = rng.standard_normal((n, d))
+        t0 = time.perf_counter()
+        ref.encode_nn(w, M)
+        dt = time.perf_counter() - t0
+        res.append(dict(d=d, D=D, blocks=n, seconds=round(dt, 3), blocks_per_s=round(n / dt, 3)))
+    return res
+
+
+def cpu_threads():
+    """Threads the oracle's numpy uses (its BLAS pool)."""
+    try:
+        import numpy  # noqa: F401  (loads the BLAS pool threadpoolctl inspects)
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        return 1
+
+
 def cpu_baseline(budget_s):
     """The oracle as it stands, on rows sampled from the same three layers."""
     import numpy as np
     from oracle import liftquant_ref as ref
     from workloads import WORKLOADS, make_layer
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        threads = 1
+    threads = cpu_threads()
     wl = WORKLOADS["llama3_8b_mlp"]
     gate, down = wl.layers
     inputs = {s.name: make_layer(s, wl, B_max=1) for s in (gate, down)}
@@ -576,6 +649,25 @@ def main():
                          "avg_launch_us": round(pf["kernel_ms"] * 1e3, 2),
                          "traffic": traffic_from_summary(pf["kernel"])},
         }
+    if not args.no_encode:
+        enc, train = run_encode(torch, lq)
+        big = enc[0]
+        out["encode"] = {
+            "metric": "blocks/s encoded (exhaustive nearest-neighbour search, Eq. (1) inner minimisation)",
+            "workloads": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in e.items()}
+                          for e in enc],
+            "kernel": "encode_kernel",
+            "roofline": {"bound": "alu", "achieved": round(big["tflops"], 2),
+                         "peak": FP64_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(big["tflops"] / FP64_PEAK_TFLOPS, 4),
+                         "workload": big["workload"],
+                         "flops": "4 d fp64 flops per visited sign vector (2^D per block)",
+                         "traffic": None},
+            "train_step": {"workload": train["workload"], "ms": round(train["ms"], 4)},
+        }
+        if not args.no_cpu_baseline:
+            out["encode"]["cpu_baseline"] = {"kind": "oracle", "cores": cpu_threads(),
+                                             "samples": encode_cpu_baseline()}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)

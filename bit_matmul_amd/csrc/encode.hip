@@ -41,10 +41,13 @@ __device__ __forceinline__ void walk(const double* m2, const double (&wv)[DM], i
 #pragma unroll
     for (int i = 0; i < DM; ++i) r[i] = fma(sgn, m2[e * DM + i], r[i]);
   }
-  double dist = 0.0;
+  double d0 = 0.0, d1 = 0.0;
 #pragma unroll
-  for (int i = 0; i < DM; ++i) dist = fma(r[i], r[i], dist);
-  best = dist;
+  for (int i = 0; i < DM; ++i) {
+    if (i & 1) d1 = fma(r[i], r[i], d1);
+    else d0 = fma(r[i], r[i], d0);
+  }
+  best = d0 + d1;
   bidx = prefix;
   uint32_t pat = prefix;
   const uint32_t count = 1u << nfree;
@@ -54,12 +57,15 @@ __device__ __forceinline__ void walk(const double* m2, const double (&wv)[DM], i
     // s_e became -1: M s lost 2 M[:, e], r gains it; became +1: r loses it
     const double sg = ((pat >> e) & 1) ? 1.0 : -1.0;
     const double* col = m2 + e * DM;
-    double dd = 0.0;
+    // two partial sums: half the dependent chain
+    double d0 = 0.0, d1 = 0.0;
 #pragma unroll
     for (int i = 0; i < DM; ++i) {
       r[i] = fma(sg, col[i], r[i]);
-      dd = fma(r[i], r[i], dd);
+      if (i & 1) d1 = fma(r[i], r[i], d1);
+      else d0 = fma(r[i], r[i], d0);
     }
+    const double dd = d0 + d1;
     if (dd < best || (dd == best && pat < bidx)) {
       best = dd;
       bidx = pat;

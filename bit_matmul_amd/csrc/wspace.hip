@@ -357,7 +357,7 @@ hipError_t launch_ws_y(const uint8_t* packed, const PackedGeom& g, const uint4* 
       return launch_ws_t<D, PW_, JB_, kYBF16>(packed, g, xp, B, tail_slots, M, d, row_scale, y,   \
                                               stream);                                             \
   }
-  LQ_WS_CASE(8, 8) LQ_WS_CASE(8, 4) LQ_WS_CASE(8, 2) LQ_WS_CASE(8, 1)
+  LQ_WS_CASE(8, 4) LQ_WS_CASE(8, 2) LQ_WS_CASE(8, 1)
   LQ_WS_CASE(4, 8) LQ_WS_CASE(4, 4) LQ_WS_CASE(4, 2) LQ_WS_CASE(4, 1)
   LQ_WS_CASE(2, 4) LQ_WS_CASE(2, 2) LQ_WS_CASE(2, 1)
   LQ_WS_CASE(1, 4) LQ_WS_CASE(1, 2) LQ_WS_CASE(1, 1)
