@@ -66,7 +66,8 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--decode-algo", default="auto", choices=["auto", "small", "fused", "local", "valu"],
+    p.add_argument("--decode-algo", default="auto",
+                   choices=["auto", "small", "fused", "local", "split", "valu"],
                    help="algorithm of the decode lq_linear calls (lq_linear_ex; auto = lq_linear)")
     p.add_argument("--prefill-algo", default="auto", choices=["auto", "large", "wspace"],
                    help="algorithm of the prefill lq_linear call (lq_linear_ex; auto = lq_linear)")
@@ -309,8 +310,13 @@ def build_decode_case(torch, lq, n_sets, seed=0):
         "down": torch.from_numpy(host[down_spec.name].x(1)).to(dev).to(torch.bfloat16),
     }
     ys = {p: torch.empty((1, s.N), dtype=torch.bfloat16, device=dev) for p, s in specs}
-    ws_bytes = max(lq.lq_linear_workspace_size_ex(layers[0][i]["struct"], 1, torch.bfloat16, a)
-                   for i in range(3) for a in (lq.LQ_ALGO_AUTO, lq.LQ_ALGO_MFMA_SMALL))
+    def need(st, a):
+        try:
+            return lq.lq_linear_workspace_size_ex(st, 1, torch.bfloat16, a)
+        except lq.LQError:                                     # does not apply to this layer
+            return 0
+    ws_bytes = max(need(layers[0][i]["struct"], a) for i in range(3)
+                   for a in (lq.LQ_ALGO_AUTO, lq.LQ_ALGO_MFMA_SMALL, lq.LQ_ALGO_FUSED_SPLIT))
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)      # zeroed control area
     return specs, layers, x_in, ys, ws, M
 
@@ -321,7 +327,8 @@ def run_decode(args, torch, lq, ev):
     step_bytes = sum(l["bytes"] for l in layers[0])
 
     algo = {"auto": None, "small": lq.LQ_ALGO_MFMA_SMALL, "fused": lq.LQ_ALGO_FUSED,
-            "local": lq.LQ_ALGO_FUSED_LOCAL, "valu": lq.LQ_ALGO_VALU}[args.decode_algo]
+            "local": lq.LQ_ALGO_FUSED_LOCAL, "split": lq.LQ_ALGO_FUSED_SPLIT,
+            "valu": lq.LQ_ALGO_VALU}[args.decode_algo]
 
     def call(l, x):
         # An algorithm that does not apply to a layer falls back to lq_linear's choice.

@@ -14,7 +14,7 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import (LQ_ENCODE_MAX_D, LQ_ENCODE_MAX_SMALL_D, LQ_ALGO_AUTO, LQ_ALGO_FUSED, LQ_ALGO_FUSED_LOCAL, LQ_ALGO_MFMA_LARGE, LQ_ALGO_WSPACE,
+from ._lib import (LQ_ENCODE_MAX_D, LQ_ENCODE_MAX_SMALL_D, LQ_ALGO_AUTO, LQ_ALGO_FUSED, LQ_ALGO_FUSED_LOCAL, LQ_ALGO_MFMA_LARGE, LQ_ALGO_WSPACE, LQ_ALGO_FUSED_SPLIT,
                    LQ_ALGO_MFMA_SMALL,
                    LQ_ALGO_VALU, LQ_BF16, LQ_F32, LQ_MAX_D, LQ_MAX_HB, LQ_WS_CONTROL_BYTES,
                    LQ_WS_ERROR_WORD, LQError, LQLayer)
@@ -27,7 +27,7 @@ __all__ = [
     "LQ_ENCODE_MAX_D", "LQ_ENCODE_MAX_SMALL_D",
     "lq_workspace_init", "lq_profile_events", "layer_struct", "LQError", "LQLayer",
     "LQ_F32", "LQ_BF16", "LQ_ALGO_AUTO", "LQ_ALGO_VALU", "LQ_ALGO_MFMA_SMALL",
-    "LQ_ALGO_MFMA_LARGE", "LQ_ALGO_FUSED", "LQ_ALGO_FUSED_LOCAL", "LQ_ALGO_WSPACE", "LQ_MAX_D", "LQ_MAX_HB", "LQ_WS_CONTROL_BYTES",
+    "LQ_ALGO_MFMA_LARGE", "LQ_ALGO_FUSED", "LQ_ALGO_FUSED_LOCAL", "LQ_ALGO_WSPACE", "LQ_ALGO_FUSED_SPLIT", "LQ_MAX_D", "LQ_MAX_HB", "LQ_WS_CONTROL_BYTES",
     "LQ_WS_ERROR_WORD", "library_path",
 ]
 

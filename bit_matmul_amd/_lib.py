@@ -10,10 +10,10 @@ LIB_PATH = Path(__file__).resolve().parent / "liblq.so"
 LQ_OK, LQ_ERR_INVALID_ARG, LQ_ERR_UNSUPPORTED, LQ_ERR_WORKSPACE, LQ_ERR_HIP = range(5)
 LQ_F32, LQ_BF16 = 0, 1
 (LQ_ALGO_AUTO, LQ_ALGO_VALU, LQ_ALGO_MFMA_SMALL, LQ_ALGO_MFMA_LARGE, LQ_ALGO_FUSED,
- LQ_ALGO_FUSED_LOCAL, LQ_ALGO_WSPACE) = range(7)
+ LQ_ALGO_FUSED_LOCAL, LQ_ALGO_WSPACE, LQ_ALGO_FUSED_SPLIT) = range(8)
 LQ_MAX_D = 64
 LQ_MAX_HB = 1024
-LQ_WS_CONTROL_BYTES = 16896
+LQ_WS_CONTROL_BYTES = 20992
 LQ_WS_ERROR_WORD = 96
 LQ_ENCODE_MAX_D = 24
 LQ_ENCODE_MAX_SMALL_D = 16

@@ -94,7 +94,7 @@ hipError_t profiled(hipStream_t stream, Fn fn) {
 }
 
 
-static_assert(lq::kFusedControlBytes == LQ_WS_CONTROL_BYTES, "control area size");
+static_assert(lq::kControlBytes == LQ_WS_CONTROL_BYTES, "control area size");
 static_assert(lq::kFusedErrorWord == LQ_WS_ERROR_WORD, "error word");
 
 // Compute units of the current device (0 when there is none), cached.
@@ -120,7 +120,7 @@ int device_cus() {
 }
 
 bool valid_algo(lq_algo algo, bool linear) {
-  return algo >= LQ_ALGO_AUTO && algo <= (linear ? LQ_ALGO_WSPACE : LQ_ALGO_MFMA_LARGE);
+  return algo >= LQ_ALGO_AUTO && algo <= (linear ? LQ_ALGO_FUSED_SPLIT : LQ_ALGO_MFMA_LARGE);
 }
 
 // Everything one sign product (or one whole lq_linear) needs: algorithm,
@@ -133,6 +133,7 @@ struct Exec {
   lq::OperandShape os;
   lq::FusedPlan fu;
   lq::SelfPlan sp;
+  lq::SplitPlan spl;
   int tickets;
   size_t off_tickets, off_aop, off_partial, off_zf32, off_xt, off_zp, off_tslots, total;
   int d, D;
@@ -168,7 +169,7 @@ lq_status plan_exec(int64_t B, int64_t N, int64_t L, int64_t K, int d, int D, lq
   e->tickets = 0;
   e->off_tickets = e->off_aop = e->off_partial = 0;
   e->off_zf32 = e->off_xt = e->off_zp = e->off_tslots = 0;
-  const size_t ctl = align_up(lq::kFusedControlBytes);
+  const size_t ctl = align_up(lq::kControlBytes);
   size_t at = ctl;
   auto take = [&](size_t bytes) { const size_t o = at; at += align_up(bytes); return o; };
   switch (e->algo) {
@@ -199,6 +200,13 @@ lq_status plan_exec(int64_t B, int64_t N, int64_t L, int64_t K, int d, int D, lq
       e->os = lq::operand_shape(B, ztype == LQ_BF16);
       e->sp = lq::plan_self(B, K, d, D, e->g, e->os);
       if (!e->sp.ok) return LQ_ERR_UNSUPPORTED;
+      break;
+    case LQ_ALGO_FUSED_SPLIT:
+      if (!linear) return LQ_ERR_INVALID_ARG;
+      e->os = lq::operand_shape(B, ztype == LQ_BF16);
+      e->spl = lq::plan_split(B, K, d, D, e->g, e->os, device_cus());
+      if (!e->spl.ok) return LQ_ERR_UNSUPPORTED;
+      e->off_partial = take(e->spl.partial_bytes);
       break;
     case LQ_ALGO_MFMA_LARGE:
       if (linear) e->off_xt = take((size_t)B * K * sizeof(float));
@@ -285,6 +293,14 @@ lq_status run_exec(const Exec& e, const uint8_t* packed, const void* zin, lq_dty
                                       layer->hb, layer->c, layer->M, e.os, row_scale, y, yb, e.sp,
                                       st);
       }));
+    case LQ_ALGO_FUSED_SPLIT: {
+      unsigned* tickets = reinterpret_cast<unsigned*>(base + lq::kFusedControlBytes);
+      return hip_status(profiled(st, [&] {
+        return lq::launch_decode_split(packed, e.g, zin, zb, layer->K, layer->d, layer->D,
+                                       layer->hb, layer->c, layer->M, e.os, row_scale, y, yb,
+                                       e.spl, partial, tickets, st);
+      }));
+    }
     case LQ_ALGO_MFMA_LARGE: {
       void* zp = base + e.off_zp;
       if (layer) {

@@ -31,7 +31,8 @@ constexpr int kSelfThreads = 64 * kSelfWaves;
 constexpr int kSelfMaxTiles = 20;        // full tiles of a panel (registers of its 2 wavefronts)
 
 // DM: an upper bound of d (the lift keeps a block's inputs in registers).
-template <int kXKind, int DM>
+// XL: x values per thread (K <= 512 XL).
+template <int kXKind, int DM, int XL>
 __global__ __launch_bounds__(kSelfThreads) void decode_self_kernel(
     const uint8_t* __restrict__ packed, int panels, int64_t panel_bytes, int full_tiles,
     int tail_bytes, const void* __restrict__ x, int K, int Kx, int d, int D, int lhb, float norm,
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(kSelfThreads) void decode_self_kernel(
   // at the branch's end); an index past the end reads an element the
   // thread's first load covers (spread over the array: every workgroup reads
   // these, and one hot line would queue them).
-  float xv[16], cv[16];
+  float xv[XL], cv[XL];
   const int kalt = tid % K;
   auto load_x = [&](int j) {
     const int k = j * kSelfThreads + tid < K ? j * kSelfThreads + tid : kalt;
@@ -71,7 +72,7 @@ __global__ __launch_bounds__(kSelfThreads) void decode_self_kernel(
     cv[j] = c[k];
   };
 #pragma unroll
-  for (int j = 0; j < 16; ++j) load_x(j);
+  for (int j = 0; j < XL; ++j) load_x(j);
   constexpr int kMPer = 8;                   // M values per thread (d * D <= 4096)
   float mv[kMPer];
   const int malt = tid % (d * D);
@@ -97,12 +98,12 @@ __global__ __launch_bounds__(kSelfThreads) void decode_self_kernel(
   // the loaded inputs are all used here (a loaded register left unused would
   // be reused later, and waited for there, behind every weight load)
 #pragma unroll
-  for (int j = 0; j < 16; ++j) asm volatile("" ::"v"(xv[j]), "v"(cv[j]));
+  for (int j = 0; j < XL; ++j) asm volatile("" ::"v"(xv[j]), "v"(cv[j]));
 #pragma unroll
   for (int j = 0; j < kMPer; ++j) asm volatile("" ::"v"(mv[j]));
 
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < XL; ++j) {
     const int k = j * kSelfThreads + tid;
     if (k < Kx) xs[k] = k < K ? xv[j] * cv[j] : 0.0f;
   }
@@ -119,49 +120,10 @@ __global__ __launch_bounds__(kSelfThreads) void decode_self_kernel(
   for (int ch = wave; ch * 1024 < Kx; ch += kSelfWaves) wave_fwht_1024(xs + 1024 * ch, lhb, lane);
   __syncthreads();
 
-  // ---- lift: one d-block per thread: its inputs into registers, then its D
-  // columns four at a time (four independent sums in flight), each summed
-  // over i in order as the two-launch path does; M is read by all lanes at
-  // the same addresses (LDS broadcast). Reads are unconditional (past D they
-  // land in z, and nothing of them is stored); a block with fewer than DM
-  // inputs (d < DM, or the ragged last block) selects its sums.
-  const int Kb = (K + d - 1) / d;
-  for (int blk = tid; blk < Kb; blk += kSelfThreads) {
-    const int kb = blk * d;
-    const int nk = min(d, K - kb);
-    float xb[DM];
-#pragma unroll
-    for (int i = 0; i < DM; ++i) xb[i] = xs[kb + min(i, nk - 1)];
-    float* zo = zt + blk * D;
-    const bool whole = nk == DM;
-    for (int e0 = 0; e0 < D; e0 += 4) {
-      float mr[4][DMr];
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-#pragma unroll
-        for (int i = 0; i < DMr; i += 4)
-          *reinterpret_cast<float4*>(&mr[k][i]) =
-              *reinterpret_cast<const float4*>(Ms + (e0 + k) * DMr + i);
-      float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (whole) {
-#pragma unroll
-        for (int i = 0; i < DM; ++i)
-#pragma unroll
-          for (int k = 0; k < 4; ++k) a[k] = fmaf(mr[k][i], xb[i], a[k]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < DM; ++i)
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float t = fmaf(mr[k][i], xb[i], a[k]);
-            a[k] = i < nk ? t : a[k];
-          }
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (e0 + k < D) zo[e0 + k] = a[k];
-    }
-  }
+  // ---- lift on the fp32 matrix cores, row tiles of 16 blocks over the
+  // wavefronts
+  mfma_lift<DM, DMr>(xs, 0, Ms, 0, (K + d - 1) / d, d, D, K, wave, kSelfWaves, lane,
+                     [&](int b, int e, float v) { zt[b * D + e] = v; });
   __syncthreads();
 
   // ---- FP6 terms: one 32-value block per thread (16 per tile)
@@ -243,7 +205,7 @@ __global__ __launch_bounds__(kSelfThreads) void decode_self_kernel(
   }
 }
 
-template <int kXKind, int DM>
+template <int kXKind, int DM, int XL>
 hipError_t launch_self_t(const uint8_t* packed, const PackedGeom& g, const void* x, int64_t K,
                          int d, int D, int hb, const float* c, const float* M, int nt, int rec,
                          const float* row_scale, void* y, bool y_bf16, const SelfPlan& plan,
@@ -254,30 +216,49 @@ hipError_t launch_self_t(const uint8_t* packed, const PackedGeom& g, const void*
   static size_t allowed = 0;
   if (plan.lds_bytes > allowed) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&decode_self_kernel<kXKind, DM>),
+        reinterpret_cast<const void*>(&decode_self_kernel<kXKind, DM, XL>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)plan.lds_bytes);
     if (e != hipSuccess) return e;
     allowed = plan.lds_bytes;
   }
-  return launch_timed(decode_self_kernel<kXKind, DM>, dim3((unsigned)plan.groups),
+  return launch_timed(decode_self_kernel<kXKind, DM, XL>, dim3((unsigned)plan.groups),
                       dim3(kSelfThreads), plan.lds_bytes, stream, packed, (int)g.panels,
                       g.panel_bytes, g.full_tiles, g.tail_bytes, x, (int)K, plan.kx, d, D, lhb,
                       norm, c, M, (int)g.L, nt, rec, row_scale, y, y_bf16 ? 1 : 0);
 }
 
-template <int kXKind>
+template <int kXKind, int XL>
 hipError_t launch_self_d(const uint8_t* packed, const PackedGeom& g, const void* x, int64_t K,
                          int d, int D, int hb, const float* c, const float* M, int nt, int rec,
                          const float* row_scale, void* y, bool y_bf16, const SelfPlan& plan,
                          hipStream_t stream) {
   if (d <= 4)
-    return launch_self_t<kXKind, 4>(packed, g, x, K, d, D, hb, c, M, nt, rec, row_scale, y,
+    return launch_self_t<kXKind, 4, XL>(packed, g, x, K, d, D, hb, c, M, nt, rec, row_scale, y,
                                         y_bf16, plan, stream);
   if (d <= 10)
-    return launch_self_t<kXKind, 10>(packed, g, x, K, d, D, hb, c, M, nt, rec, row_scale, y,
+    return launch_self_t<kXKind, 10, XL>(packed, g, x, K, d, D, hb, c, M, nt, rec, row_scale, y,
                                          y_bf16, plan, stream);
-  return launch_self_t<kXKind, 16>(packed, g, x, K, d, D, hb, c, M, nt, rec, row_scale, y,
+  return launch_self_t<kXKind, 16, XL>(packed, g, x, K, d, D, hb, c, M, nt, rec, row_scale, y,
                                        y_bf16, plan, stream);
+}
+
+template <int kXKind>
+hipError_t launch_self_x(const uint8_t* packed, const PackedGeom& g, const void* x, int64_t K,
+                         int d, int D, int hb, const float* c, const float* M, int nt, int rec,
+                         const float* row_scale, void* y, bool y_bf16, const SelfPlan& plan,
+                         hipStream_t stream) {
+  // 2 x values per thread per 1024 inputs (K rounded up to 1024)
+  switch (plan.kx >> 9) {
+    case 2: return launch_self_d<kXKind, 2>(packed, g, x, K, d, D, hb, c, M, nt, rec, row_scale, y,
+                                            y_bf16, plan, stream);
+    case 4: return launch_self_d<kXKind, 4>(packed, g, x, K, d, D, hb, c, M, nt, rec, row_scale, y,
+                                            y_bf16, plan, stream);
+    case 6:
+    case 8: return launch_self_d<kXKind, 8>(packed, g, x, K, d, D, hb, c, M, nt, rec, row_scale, y,
+                                            y_bf16, plan, stream);
+    default: return launch_self_d<kXKind, 16>(packed, g, x, K, d, D, hb, c, M, nt, rec, row_scale,
+                                              y, y_bf16, plan, stream);
+  }
 }
 
 }  // namespace
@@ -307,9 +288,9 @@ hipError_t launch_decode_self(const uint8_t* packed, const PackedGeom& g, const 
                               void* y, bool y_bf16, const SelfPlan& plan, hipStream_t stream) {
   (void)hipGetLastError();   // clear a stale error of an earlier runtime call
   if (!plan.ok || d > 16 || plan.pw != kSelfWaves / 2) return hipErrorInvalidValue;
-  return x_bf16 ? launch_self_d<1>(packed, g, x, K, d, D, hb, c, M, s.nt, s.rec, row_scale, y,
+  return x_bf16 ? launch_self_x<1>(packed, g, x, K, d, D, hb, c, M, s.nt, s.rec, row_scale, y,
                                    y_bf16, plan, stream)
-                : launch_self_d<0>(packed, g, x, K, d, D, hb, c, M, s.nt, s.rec, row_scale, y,
+                : launch_self_x<0>(packed, g, x, K, d, D, hb, c, M, s.nt, s.rec, row_scale, y,
                                    y_bf16, plan, stream);
 }
 

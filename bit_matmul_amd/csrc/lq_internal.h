@@ -238,6 +238,9 @@ constexpr int kFusedCtlWords = 128;    // epoch, ticket, done, error words (128 
 constexpr int kFusedErrorWord = 96;
 constexpr int kMaxFusedTiles = 256;    // flags [tile][16] for at most this many column tiles
 constexpr size_t kFusedControlBytes = (size_t)(kFusedCtlWords + kMaxFusedTiles * 16) * 4;
+// The split one-launch decode's per-panel-group tickets follow.
+constexpr int kSplitTickets = 1024;
+constexpr size_t kControlBytes = kFusedControlBytes + (size_t)kSplitTickets * 4;
 struct FusedPlan {
   bool ok;          // applicable (one column set, producers <= workgroups, LDS fits)
   int p, tpc, nch, chunk_bytes, groups, producers;
@@ -250,6 +253,23 @@ hipError_t launch_decode_fused(const uint8_t* packed, const PackedGeom& g, const
                                const float* c, const float* M, const OperandPlan& op,
                                unsigned* ctl, const float* row_scale, void* y, bool y_bf16,
                                const FusedPlan& plan, hipStream_t stream);
+
+// One-launch decode split over the reduction (batch 1): workgroup (tile
+// group, 16-panel group) prepares the operand of its tiles only; the tile
+// groups' partial row sums meet through a ticket per panel group.
+struct SplitPlan {
+  bool ok;
+  int tpg, kgroups, pgroups;   // tiles per group, tile groups, panel groups
+  int xl;                      // x values per thread (2 per 1024-input chunk of the span)
+  size_t lds_bytes, partial_bytes;
+};
+SplitPlan plan_split(int64_t B, int64_t K, int d, int D, const PackedGeom& g,
+                     const OperandShape& s, int cus);
+hipError_t launch_decode_split(const uint8_t* packed, const PackedGeom& g, const void* x,
+                               bool x_bf16, int64_t K, int d, int D, int hb, const float* c,
+                               const float* M, const OperandShape& s, const float* row_scale,
+                               void* y, bool y_bf16, const SplitPlan& plan, float* partial,
+                               unsigned* tickets, hipStream_t stream);
 
 // One-launch decode without communication (batch 1, short rows): every
 // workgroup prepares the whole operand in LDS and multiplies 8 panels.

@@ -110,6 +110,56 @@ __device__ __forceinline__ void wave_fwht_1024(float* xs, int lhb, int lane) {
   }
 }
 
+// The same transform of the 1024 values xs[0..1023] by 256 threads (four
+// wavefronts; t = 0..255 within the group), every thread of the workgroup
+// calling it the same number of times (it holds two workgroup barriers);
+// `active` false: the thread only takes part in the barriers. Thread t holds
+// xs[4t + i]: bits 0 and 1 pair registers, bits 2..7 pair lanes t ^ 1 ..
+// t ^ 32 (shuffles); then, through LDS, thread t holds xs[t + 256j] and bits
+// 8 and 9 pair registers. The stages run in the order of their bit, as in
+// wave_fwht_1024, so both give identical results.
+__device__ __forceinline__ void block_fwht_1024(float* xs, int lhb, int t, bool active) {
+  float v[4];
+  if (active) {
+    const float4 q = *reinterpret_cast<const float4*>(xs + 4 * t);
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    if (lhb > 0) {
+      float a = v[0], b = v[1]; v[0] = a + b; v[1] = a - b;
+      a = v[2]; b = v[3]; v[2] = a + b; v[3] = a - b;
+    }
+    if (lhb > 1) {
+      float a = v[0], b = v[2]; v[0] = a + b; v[2] = a - b;
+      a = v[1]; b = v[3]; v[1] = a + b; v[3] = a - b;
+    }
+    for (int s = 1; s < 64 && (s << 2) < (1 << lhb); s <<= 1) {
+      const bool upper = (t & s) != 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float o = __shfl_xor(v[i], s, 64);
+        v[i] = upper ? (o - v[i]) : (v[i] + o);
+      }
+    }
+    *reinterpret_cast<float4*>(xs + 4 * t) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+  __syncthreads();
+  if (active && lhb > 8) {
+    float w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = xs[t + 256 * j];
+    {
+      float a = w[0], b = w[1]; w[0] = a + b; w[1] = a - b;
+      a = w[2]; b = w[3]; w[2] = a + b; w[3] = a - b;
+    }
+    if (lhb > 9) {
+      float a = w[0], b = w[2]; w[0] = a + b; w[2] = a - b;
+      a = w[1]; b = w[3]; w[1] = a + b; w[3] = a - b;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xs[t + 256 * j] = w[j];
+  }
+  __syncthreads();
+}
+
 // One lifted value z[col] = sum_{i < min(d, K - kb)} Ms[i * D + e] *
 // xs[kb + i - h_lo] with col = blk * D + e and kb = blk * d (the lift of
 // d-block blk; rows of the virtual zero pad are skipped). Products are added

@@ -41,8 +41,8 @@
  *   - Functions never throw; they are thread-safe. Calls that share a
  *     workspace buffer must be ordered by the caller.
  *   - Workspaces: the first LQ_WS_CONTROL_BYTES bytes of a workspace hold
- *     control words through which the workgroups of the one-launch decode
- *     (LQ_ALGO_FUSED) order themselves. Before its first use a workspace
+ *     control words through which the workgroups of the one-launch decodes
+ *     (LQ_ALGO_FUSED, LQ_ALGO_FUSED_SPLIT) order themselves. Before its first use a workspace
  *     must be zero-filled (allocate it zeroed, or call lq_workspace_init);
  *     afterwards the library keeps those words consistent from call to call,
  *     and the caller must not write them. After LQ_ERR_HIP or a device fault,
@@ -115,7 +115,7 @@ typedef enum lq_algo {
                                K <= 8192, d <= 16, L <= 10240 (+ tail) and the
                                operand fits LDS; otherwise UNSUPPORTED. Needs
                                no workspace */
-  LQ_ALGO_WSPACE = 6        /* lq_linear_ex only, bf16 x, any B: the product in
+  LQ_ALGO_WSPACE = 6,       /* lq_linear_ex only, bf16 x, any B: the product in
                                W space ([paper] §3: the weights a block's signs
                                represent are M times the sign vector). The
                                dense weights W[n][b*d+i] = sum_e M[i][e] s_e
@@ -126,6 +126,20 @@ typedef enum lq_algo {
                                L lifted columns: D/d times fewer MACs. Applies
                                when D is 4 or 8 and d <= 4; otherwise (and for
                                fp32 x) UNSUPPORTED */
+  LQ_ALGO_FUSED_SPLIT = 7   /* lq_linear_ex only, batch 1: the whole operator
+                               in ONE launch split over the reduction: each
+                               workgroup whitens, lifts and converts (the
+                               MFMA_SMALL arithmetic) only the <= 6 column
+                               tiles of its tile group, for its 16 panels;
+                               the tile groups' partial row sums are added by
+                               the group's last workgroup in a fixed order
+                               (deterministic), through the workspace and a
+                               ticket per 16-panel group in its control area
+                               (reset by that workgroup: calls sharing a
+                               workspace must not overlap). Applies when
+                               d <= 16, D <= 32, d*D <= 512, at least one full
+                               tile, the whitened span of a group <= 5120
+                               inputs and N <= 262144; otherwise UNSUPPORTED */
 
 } lq_algo;
 
@@ -134,7 +148,7 @@ typedef enum lq_algo {
 #define LQ_MAX_HB 1024       /* hb a power of two, 1 <= hb <= 1024, hb | K */
 
 /* Workspace control area (see the conventions above). */
-#define LQ_WS_CONTROL_BYTES 16896
+#define LQ_WS_CONTROL_BYTES 20992
 /* 32-bit word of the control area that the one-launch decode sets non-zero
  * when a workgroup gave up waiting for the activation operand (about one
  * second; possible only when other work holds the GPU's compute units): the

@@ -165,7 +165,14 @@ def test_linear_ex_validation_and_control_area():
         assert st == LQ_OK
         # every workspace that is used at all starts with the control area
         assert need >= _lib.LQ_WS_CONTROL_BYTES + 34416 * 3 // 4
-    assert linear_ws_size(lay, 1, LQ_BF16, 7)[0] == LQ_ERR_INVALID_ARG
+    assert linear_ws_size(lay, 1, LQ_BF16, 8)[0] == LQ_ERR_INVALID_ARG
+    # one launch split over the reduction: batch 1, a partial per tile group
+    gate7 = LQLayer(14336, 4096, 10, 24, 1024, 0, P, P, P, P)
+    st, need7 = linear_ws_size(gate7, 1, LQ_BF16, 7)
+    assert st == LQ_OK and need7 >= _lib.LQ_WS_CONTROL_BYTES + 14336 * 4
+    assert linear_ws_size(lay, 1, LQ_BF16, 7)[0] == LQ_OK                   # down, K = 14336
+    assert linear_ws_size(lay, 2, LQ_BF16, 7)[0] == LQ_ERR_UNSUPPORTED     # batch 1 only
+    assert ws_size(1, 4096, 34416, LQ_BF16, 7)[0] == LQ_ERR_INVALID_ARG    # sign_gemm: no
     # W space: D in {4, 8}, d <= 4, bf16 x, any batch
     assert linear_ws_size(lay, 1, LQ_BF16, 6)[0] == LQ_ERR_UNSUPPORTED       # D = 24
     pre = LQLayer(8192, 8192, 3, 8, 1024, 0, P, P, P, P)
@@ -195,7 +202,7 @@ def test_linear_ex_validation_and_control_area():
     f = LIB.lq_linear_ex
     need = linear_ws_size(lay, 1, LQ_BF16, 2)[1]
     assert f(ctypes.byref(lay), P, LQ_BF16, 1, P, LQ_BF16, 2, P, need - 1, None) == LQ_ERR_WORKSPACE
-    assert f(ctypes.byref(lay), P, LQ_BF16, 1, P, LQ_BF16, 7, P, need, None) == LQ_ERR_INVALID_ARG
+    assert f(ctypes.byref(lay), P, LQ_BF16, 1, P, LQ_BF16, 8, P, need, None) == LQ_ERR_INVALID_ARG
     assert f(ctypes.byref(lay), P, LQ_BF16, 1, P, LQ_BF16, 6, P, need, None) == LQ_ERR_UNSUPPORTED
     assert f(ctypes.byref(lay), P, LQ_BF16, 17, P, LQ_BF16, 4, P, need, None) == LQ_ERR_UNSUPPORTED
     assert f(ctypes.byref(lay), P, LQ_BF16, 0, P, LQ_BF16, 4, None, 0, None) == LQ_OK
@@ -238,7 +245,8 @@ def test_linear_algo_resolution():
     assert res(gate, 2, LQ_BF16, 5)[0] == LQ_ERR_UNSUPPORTED
     assert res(gate, 0, LQ_BF16)[0] == LQ_ERR_INVALID_ARG
     assert f(ctypes.byref(gate), 1, LQ_BF16, 0, None) == LQ_ERR_INVALID_ARG
-    assert res(gate, 1, LQ_BF16, 7)[0] == LQ_ERR_INVALID_ARG
+    assert res(gate, 1, LQ_BF16, 8)[0] == LQ_ERR_INVALID_ARG
+    assert res(gate, 1, LQ_BF16, 7) == (LQ_OK, 7)
 
 
 def test_encode_and_train_validation():

@@ -275,3 +275,124 @@ def test_local_bf16_output_and_determinism(lq):
     assert torch.equal(y1, y2)
     want = ref.linear(inp.x(1), inp.c, 1024, inp.M, inp.signs(), inp.row_scale)
     assert rel_l2(host(y1), want) < 5e-3          # bf16 output rounding
+
+
+# ---- one launch split over the reduction (LQ_ALGO_FUSED_SPLIT): batch 1
+
+
+@pytest.mark.parametrize("li", [0, 1], ids=["gate_up", "down"])
+def test_split_full_size(lq, li):
+    """Llama-3-8B gate/up and down at full size: sampled rows against the
+    oracle, the whole output against the two-launch path, and a second call
+    on the same workspace (the tickets reset themselves)."""
+    wl = WORKLOADS["llama3_8b_mlp"]
+    spec = wl.layers[li]
+    inp = make_layer(spec, wl)
+    layer = DeviceLayer(inp, lq)
+    rng = np.random.default_rng(spec.seed + 9)
+    rows = np.sort(rng.choice(spec.N, size=48, replace=False))
+    rows[0], rows[-1] = 0, spec.N - 1
+    x = dev(inp.x(1), torch.bfloat16)
+    nbytes = lq.lq_linear_workspace_size_ex(layer.struct, 1, torch.bfloat16, lq.LQ_ALGO_FUSED_SPLIT)
+    ws = workspace(lq, nbytes)
+    outs = []
+    for _ in range(2):
+        y = torch.empty((1, spec.N), dtype=torch.float32, device="cuda")
+        note(f"lq_linear_ex FUSED_SPLIT N={spec.N} K={spec.K}")
+        lq.lq_linear_ex(layer.struct, x, 1, y, lq.LQ_ALGO_FUSED_SPLIT, ws)
+        torch.cuda.synchronize()
+        outs.append(host(y))
+    assert np.array_equal(outs[0], outs[1])
+    ys = host(layer.linear(lq, x, 1, torch.float32, algo=lq.LQ_ALGO_MFMA_SMALL))
+    assert rel_l2(outs[0], ys) < 2e-6
+    want = ref.linear(inp.x(1), inp.c, spec.hb, inp.M, inp.signs_rows(rows), inp.row_scale[rows])
+    assert rel_l2(outs[0][:, rows], want) < 1e-2
+
+
+SPLIT = [
+    # (N, K, d, D, hb, label)
+    (128, 1024, 10, 24, 1024, "3 tiles, ragged tail"),
+    (256, 2048, 4, 8, 512, "8 full tiles, no tail"),
+    (64, 1037, 10, 24, 1, "K not a multiple of d, hb=1"),
+    (8200 // 8 * 8 - 8, 512, 2, 5, 512, "1280 columns, many panels"),
+    (96, 600, 1, 8, 8, "d = 1"),
+    (48, 8192, 16, 16, 1024, "K = 8192, D = d, 16 full tiles"),
+    (40 * 16, 4096, 10, 24, 1024, "partial last panel group (40 panels)"),
+    (16, 640, 10, 16, 128, "one panel"),
+    (32, 14336, 10, 24, 1024, "long rows (68 tiles)"),
+    (64, 2600, 3, 8, 8, "tail-only last group"),
+]
+
+
+@pytest.mark.parametrize("N,K,d,D,hb,label", SPLIT, ids=[e[-1] for e in SPLIT])
+@pytest.mark.parametrize("xd", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_split_shapes(lq, N, K, d, D, hb, label, xd):
+    inp = make_layer_small(N, K, d, D, hb, seed=N + K + d + D + 13, B_max=1,
+                           xdtype="f32" if xd == torch.float32 else "bf16")
+    if label.startswith("K = 8192, D = d"):
+        inp.M = np.eye(d, dtype=np.float32)
+    layer = DeviceLayer(inp, lq)
+    x = dev(inp.x(1), xd)
+    y = host(layer.linear(lq, x, 1, torch.float32, algo=lq.LQ_ALGO_FUSED_SPLIT))
+    want = ref.linear(inp.x(1), inp.c, hb, inp.M, inp.signs(), inp.row_scale)
+    assert rel_l2(y, want) < TOL[xd]
+    ys = host(layer.linear(lq, x, 1, torch.float32, algo=lq.LQ_ALGO_MFMA_SMALL))
+    assert rel_l2(y, ys) < 2e-6
+
+
+def test_split_bf16_output_and_shared_workspace(lq):
+    """bf16 output, and one workspace shared by interleaved calls of two
+    layers and of the other algorithms."""
+    a = make_layer_small(512, 4096, 10, 24, 1024, seed=405, B_max=4, xdtype="bf16")
+    b = make_layer_small(256, 2048, 3, 8, 512, seed=406, B_max=4, xdtype="bf16")
+    la, lb = DeviceLayer(a, lq), DeviceLayer(b, lq)
+    xa, xb = dev(a.x(1), torch.bfloat16), dev(b.x(1), torch.bfloat16)
+    algos = [lq.LQ_ALGO_FUSED_SPLIT, lq.LQ_ALGO_MFMA_SMALL, lq.LQ_ALGO_FUSED_SPLIT]
+    need = max(lq.lq_linear_workspace_size_ex(l.struct, 1, torch.bfloat16, al)
+               for l in (la, lb) for al in algos)
+    ws = workspace(lq, need)
+    ref_a = ref.linear(a.x(1), a.c, 1024, a.M, a.signs(), a.row_scale)
+    ref_b = ref.linear(b.x(1), b.c, 512, b.M, b.signs(), b.row_scale)
+    first = {}
+    for it in range(3):
+        for name, l, x, want in (("a", la, xa, ref_a), ("b", lb, xb, ref_b)):
+            for al in algos:
+                y = torch.empty((1, l.N), dtype=torch.bfloat16, device="cuda")
+                note(f"shared workspace it={it} layer={name} algo={al}")
+                lq.lq_linear_ex(l.struct, x, 1, y, al, ws)
+                torch.cuda.synchronize()
+                got = host(y)
+                assert rel_l2(got, want) < 5e-3
+                if al == lq.LQ_ALGO_FUSED_SPLIT:
+                    if name in first:
+                        assert np.array_equal(got, first[name])
+                    first[name] = got
+    assert control_error(lq, ws) == 0
+
+
+def test_split_graph_replay(lq):
+    inp = make_layer_small(1024, 4096, 10, 24, 1024, seed=407, B_max=1, xdtype="bf16")
+    layer = DeviceLayer(inp, lq)
+    x = dev(inp.x(1), torch.bfloat16)
+    need = lq.lq_linear_workspace_size_ex(layer.struct, 1, torch.bfloat16, lq.LQ_ALGO_FUSED_SPLIT)
+    ws = workspace(lq, need)
+    y = torch.empty((1, inp.spec.N), dtype=torch.float32, device="cuda")
+    lq.lq_linear_ex(layer.struct, x, 1, y, lq.LQ_ALGO_FUSED_SPLIT, ws)
+    torch.cuda.synchronize()
+    eager = host(y).copy()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            lq.lq_linear_ex(layer.struct, x, 1, y, lq.LQ_ALGO_FUSED_SPLIT, ws, stream=s)
+    torch.cuda.synchronize()
+    for i in range(4):
+        y.zero_()
+        note(f"split graph replay {i}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(y), eager)
+        lq.lq_linear_ex(layer.struct, x, 1, y, lq.LQ_ALGO_MFMA_SMALL,
+                        workspace(lq, lq.lq_linear_workspace_size_ex(layer.struct, 1, torch.bfloat16,
+                                                                     lq.LQ_ALGO_MFMA_SMALL)))
+        torch.cuda.synchronize()
