@@ -220,7 +220,7 @@ lq_status plan_exec(int64_t B, int64_t N, int64_t L, int64_t K, int d, int D, lq
       if (!linear) return LQ_ERR_INVALID_ARG;
       if (ztype != LQ_BF16 || !lq::wspace_supported(d, D)) return LQ_ERR_UNSUPPORTED;
       {
-        const lq::XpGeom xg = lq::xp_geom(B, e->g, D);
+        const lq::XpGeom xg = lq::xp_geom(B, e->g, d, D);
         e->off_zp = take(xg.bytes);
         e->off_tslots = take(xg.tail_bytes);
       }

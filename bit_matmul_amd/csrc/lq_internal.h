@@ -338,11 +338,11 @@ hipError_t launch_tail_slots(const uint8_t* packed, const PackedGeom& g, void* o
 bool wspace_supported(int d, int D);
 struct XpGeom {
   int64_t B16, steps;
-  size_t bytes;        // xp: per 16 batch rows and 128-column step, 16 / D KB
+  size_t bytes;        // xp: per 16 batch rows and step (8 blocks per lane), d KB
   size_t tail_bytes;   // as ZpGeom
 };
-XpGeom xp_geom(int64_t B, const PackedGeom& g, int D);
-LargePlan plan_wspace(int64_t B, const PackedGeom& g, int D);
+XpGeom xp_geom(int64_t B, const PackedGeom& g, int d, int D);
+int plan_wspace_jb(int64_t B, const PackedGeom& g, int d);   // 16-row batch tiles per workgroup
 // ---- nearest-neighbour encoding and the training step of M (encode.hip)
 constexpr int kEncodeMaxD = 24;        // exhaustive search: 2^D sign vectors per block
 constexpr int kEncodeMaxSmallD = 16;   // d (the residual lives in registers)

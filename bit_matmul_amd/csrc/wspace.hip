@@ -10,19 +10,23 @@
 // group g). For D dividing 32 the packed word u of slot (g, r) holds row r's
 // sign bits of 32 / D whole blocks (tile columns 128 u + 32 g + [0, 32)), so
 // lane (g, r) builds its W values from its own bits: the D-bit pattern of a
-// block indexes a table of the 2^D possible weight vectors (4 bf16 each,
-// positions i >= d zero), computed per workgroup in LDS from M (fp32 sums in
-// order of e, then rounded to bf16 once). One A operand = two blocks, 8 bf16;
-// a 128-column step gives F = 16 / D of them (sub-steps). The B operand of
-// lane (g, r) in sub-step s carries the matching inputs: xt[16 jb + r][d b + i]
-// for the same two blocks b, i < 4 (zero for i >= d and past K).
+// block indexes a table of the 2^D possible weight vectors (fp32 sums in
+// order of e, rounded to bf16 once; 4 bf16 per entry, zero past d), computed
+// per workgroup in LDS from M. A step is 8 blocks of every lane (D / 4 words:
+// 256 tile columns for D = 8, 128 for D = 4); their 8 d weights, block after
+// block, are exactly d A operands of 8 bf16 (sub-steps), no padding. The B
+// operand of lane (g, r) in sub-step f carries the matching inputs:
+// xt[16 jb + r][b d + i] for the same stream positions 8 f .. 8 f + 7 (zero
+// past K).
 //
-// xt is first written in that order ("xp", bf16): per 16 batch rows and
-// 128-column step an F KB block of 16-byte units [s][g][r]; the whitening
-// itself writes it (xt never goes to memory). The pipeline is
-// that of the lifted large-batch product (four LDS stages filled by DMA three
-// steps ahead, slots DMA-copied per tile, B operands and table reads of the
-// next sub-step issued before this sub-step's MFMAs).
+// xt is first written in that order ("xp", bf16): per 16 batch rows and step
+// a d KB block of 16-byte units [f][g][r]; the whitening itself writes it
+// (xt never goes to memory). The pipeline is that of the lifted large-batch
+// product (four LDS stages filled by DMA three steps ahead, slots
+// DMA-copied per tile, B operands of the next sub-step read before this
+// sub-step's MFMAs).
+#include <type_traits>
+
 #include "lq_internal.h"
 #include "lq_prep.h"
 
@@ -41,10 +45,10 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
 // ------------------------------------------------------------ whitening + xp
 // Workgroup (chunk h of 1024 inputs, 16 batch rows jb): x * c of the rows'
 // chunk into LDS, the Walsh-Hadamard transform of every hb block (a
-// wavefront per row), then the xp units of every block with inputs in the
-// chunk. Slot (block b, position i) belongs to the chunk holding input
-// min(b d + min(i, d - 1), K - 1): a unit whose eight slots all belong to
-// this chunk is stored whole, one that straddles two chunks slot by slot (2
+// wavefront per row), then the xp units of every step of the tiles whose
+// blocks draw on the chunk. Slot (block b, input i < d) belongs to the chunk
+// holding input min(b d + i, K - 1): a unit whose eight slots all belong to
+// this chunk is stored whole, one that straddles chunks slot by slot (2
 // bytes each; the other chunk's workgroup stores the rest). The last chunk
 // also covers the virtual pad and the blocks past L up to the end of the
 // last tile (zeros).
@@ -56,7 +60,6 @@ __global__ __launch_bounds__(256) void xpw_kernel(const void* __restrict__ x,
                                                   int64_t K, int d, int lhb, float norm,
                                                   int64_t steps, int64_t blk_end, int64_t jb_base,
                                                   uint4* __restrict__ xp) {
-  constexpr int F = 16 / D;
   __shared__ __align__(16) float xs[16 * kXpwStride];
   const int h = blockIdx.x;
   const int64_t jb = jb_base + blockIdx.y;
@@ -102,40 +105,50 @@ __global__ __launch_bounds__(256) void xpw_kernel(const void* __restrict__ x,
   __syncthreads();
 
   const bool last = k_lo + 1024 >= K;
+  constexpr int BPT = 512 / D;                    // blocks per tile
+  constexpr int WPS = D / 4;                      // packed words per step
+  constexpr int SPT = 4 / WPS;                    // steps per tile
+  constexpr int BPW = 32 / D;                     // blocks per word of a lane
   const int64_t b_first = k_lo / d;
   const int64_t b_last = last ? blk_end - 1 : (k_lo + 1023) / d;
-  const int64_t u_lo = b_first / 2, nu = b_last / 2 - u_lo + 1;
-  auto owner = [&](int64_t bb, int i) -> int64_t {
-    return min(bb * d + min(i, d - 1), K - 1) >> 10;
-  };
-  for (int64_t idx = tid; idx < nu * 16; idx += 256) {
-    const int64_t U = u_lo + (idx >> 4);
+  const int64_t q_lo = b_first / BPT, nq = b_last / BPT - q_lo + 1;
+  // items: (tile, step, lane group, sub-step, row), row fastest
+  const int64_t items = nq * SPT * 4 * d * 16;
+  for (int64_t idx = tid; idx < items; idx += 256) {
     const int r = (int)(idx & 15);
-    const int64_t b0 = 2 * U;
-    const int64_t col = b0 * D;
-    const int64_t q = col >> 9;
-    const int cu = (int)((col >> 7) & 3), g = (int)((col >> 5) & 3), s = (int)((col & 31) / D) >> 1;
-    uint4* dst = xp + ((jb * steps + 4 * q + cu) * F + s) * 64 + 16 * g + r;
+    int64_t rest = idx >> 4;
+    const int f = (int)(rest % d);
+    rest /= d;
+    const int g = (int)(rest & 3);
+    rest >>= 2;
+    const int sg = (int)(rest % SPT);
+    const int64_t q = q_lo + rest / SPT;
+    const int64_t t = q * SPT + sg;
+    uint4* dst = xp + ((jb * steps + t) * d + f) * 64 + 16 * g + r;
     const float* xr = xs + r * kXpwStride;
     uint32_t hv[8];
     bool own[8];
+    bool all = true, any = false;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t k = (b0 + hh) * d + i;
-        const bool o = owner(b0 + hh, i) == h;
-        own[4 * hh + i] = o;
-        hv[4 * hh + i] = f32_to_bf16_bits(o && i < d && k < K ? xr[k - k_lo] * norm : 0.0f);
-      }
-    if (own[0] && own[7]) {
+    for (int e = 0; e < 8; ++e) {
+      const int pos = 8 * f + e, lam = pos / d, i = pos - lam * d;
+      const int u = sg * WPS + lam / BPW, tt = lam % BPW;
+      const int64_t blk = q * BPT + u * (BPT / 4) + g * BPW + tt;
+      const int64_t k = blk * d + i;
+      const bool o = (min(k, K - 1) >> 10) == h;
+      own[e] = o;
+      all = all && o;
+      any = any || o;
+      hv[e] = f32_to_bf16_bits(o && k < K ? xr[k - k_lo] * norm : 0.0f);
+    }
+    if (all) {
       *dst = make_uint4(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16),
                         hv[6] | (hv[7] << 16));
-    } else {
+    } else if (any) {
       uint16_t* p = reinterpret_cast<uint16_t*>(dst);
 #pragma unroll
-      for (int m = 0; m < 8; ++m)
-        if (own[m]) p[m] = (uint16_t)hv[m];
+      for (int e = 0; e < 8; ++e)
+        if (own[e]) p[e] = (uint16_t)hv[e];
     }
   }
 }
@@ -143,15 +156,51 @@ __global__ __launch_bounds__(256) void xpw_kernel(const void* __restrict__ x,
 // ------------------------------------------------------------ product
 // Workgroup: 4 wavefronts; tile 4 PW panels x 16 JB batch rows; wavefront w
 // owns panels w PW .. w PW + PW - 1 and all JB batch tiles.
-template <int D, int PW, int JB, bool kYBF16>
+constexpr int kWsPW = 4;
+
+// The DD A operands of one step from the table entries e[0..7] of its 8
+// blocks (entry j: dwords .x = v0 | v1 << 16, .y = v2 | v3 << 16, zero past
+// DD): the stream of 8 DD weights, block after block, cut into operands of 8.
+template <int DD>
+__device__ __forceinline__ void pack_step(const uint2 (&e)[8], u32x4 (&a)[DD]) {
+  if constexpr (DD == 4) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+      a[f] = (u32x4){e[2 * f].x, e[2 * f].y, e[2 * f + 1].x, e[2 * f + 1].y};
+  } else if constexpr (DD == 2) {
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+      a[f] = (u32x4){e[4 * f].x, e[4 * f + 1].x, e[4 * f + 2].x, e[4 * f + 3].x};
+  } else if constexpr (DD == 1) {
+    a[0] = (u32x4){e[0].x | (e[1].x << 16), e[2].x | (e[3].x << 16), e[4].x | (e[5].x << 16),
+                   e[6].x | (e[7].x << 16)};
+  } else {
+    // three bf16 per block: a pair of blocks (x, y) fills three dwords
+    uint32_t dw[12];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint2 x = e[2 * j], y = e[2 * j + 1];
+      dw[3 * j] = x.x;
+      dw[3 * j + 1] = x.y | (y.x << 16);
+      dw[3 * j + 2] = __builtin_amdgcn_alignbit(y.y, y.x, 16);
+    }
+#pragma unroll
+    for (int f = 0; f < 3; ++f) a[f] = (u32x4){dw[4 * f], dw[4 * f + 1], dw[4 * f + 2], dw[4 * f + 3]};
+  }
+}
+
+template <int D, int DD, int JB>
 __global__ __launch_bounds__(256) void wspace_kernel(
     const uint8_t* __restrict__ packed, int64_t panels, int64_t panel_bytes, int full_tiles,
     int ext_tiles, const uint4* __restrict__ xp, int64_t B16, int64_t B,
-    const uint4* __restrict__ tail_slots, const float* __restrict__ M, int d,
+    const uint4* __restrict__ tail_slots, const float* __restrict__ M, int y_bf16,
     const float* __restrict__ row_scale, void* __restrict__ y, int64_t N) {
-  constexpr int F = 16 / D;                       // sub-steps per step
-  constexpr int kChunks = JB * F;                 // 1 KB chunks of a step's B operands
-  constexpr int kStageUnits = kChunks * 64;       // [jb][s][g][r]
+  constexpr int PW = kWsPW;
+  constexpr int WPS = D / 4;                      // packed words per step
+  constexpr int SPT = 4 / WPS;                    // steps per tile
+  constexpr int BPW = 32 / D;                     // blocks per word of a lane
+  constexpr int kChunks = JB * DD;                // 1 KB chunks of a step's B operands
+  constexpr int kStageUnits = kChunks * 64;       // [jb][f][g][r]
   constexpr int kSlotUnits = 4 * PW * 64;         // [wave][panel][lane]
   constexpr int kLut = 1 << D;
   __shared__ uint4 stage0[kStageUnits];
@@ -162,7 +211,7 @@ __global__ __launch_bounds__(256) void wspace_kernel(
   __shared__ uint4 slotB[kSlotUnits];
   __shared__ uint2 lut[kLut];
   const int wave = wave_id(), lane = threadIdx.x & 63;
-  const int64_t steps = 4 * (int64_t)ext_tiles;
+  const int64_t steps = SPT * (int64_t)ext_tiles;
   const int64_t last = steps - 1;
   const int64_t jb0 = (int64_t)blockIdx.y * JB;
   const int64_t pbase = (int64_t)blockIdx.x * 4 * PW + wave * PW;
@@ -174,7 +223,7 @@ __global__ __launch_bounds__(256) void wspace_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float a = 0.0f;
-      if (i < d) {
+      if (i < DD) {
 #pragma unroll
         for (int e = 0; e < D; ++e) a = fmaf(M[i * D + e], ((p >> e) & 1) ? -1.0f : 1.0f, a);
       }
@@ -183,7 +232,7 @@ __global__ __launch_bounds__(256) void wspace_kernel(
     lut[p] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
   }
 
-  auto dma = [&](const void* src, uint4* dst) {
+  auto dma = [&](const void* src, uint4* dst) __attribute__((always_inline)) {
     __builtin_amdgcn_global_load_lds(
         (const void*)(reinterpret_cast<const uint8_t*>(src) + 16 * lane),
         (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
@@ -191,16 +240,16 @@ __global__ __launch_bounds__(256) void wspace_kernel(
   // The B operands of one step: kChunks copies of 1 KB spread over the four
   // wavefronts (clamped: a repeated copy writes the same bytes again).
   constexpr int kCopies = (kChunks + 3) / 4;
-  auto copy_step = [&](int64_t t, uint4* dst) {
+  auto copy_step = [&](int64_t t, uint4* dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < kCopies; ++k) {
       const int ch = min(wave + 4 * k, kChunks - 1);
-      const int c = ch / F, s = ch % F;
+      const int c = ch / DD, f = ch % DD;
       const int64_t jb = min(jb0 + c, B16 - 1);
-      dma(xp + ((jb * steps + t) * F + s) * 64, dst + ch * 64);
+      dma(xp + ((jb * steps + t) * DD + f) * 64, dst + ch * 64);
     }
   };
-  auto copy_slots = [&](int q, uint4* dst) {
+  auto copy_slots = [&](int q, uint4* dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
       const int64_t pnl = min(pbase + i, panels - 1);
@@ -210,12 +259,15 @@ __global__ __launch_bounds__(256) void wspace_kernel(
       dma(src, dst + (wave * PW + i) * 64);
     }
   };
-  // A operand of sub-step s from word w: the table entries of blocks 2 s and
-  // 2 s + 1 of the word.
-  auto a_operand = [&](uint32_t w, int s) -> u32x4 {
-    const uint2 e0 = lut[(w >> (2 * s * D)) & (kLut - 1)];
-    const uint2 e1 = lut[(w >> ((2 * s + 1) * D)) & (kLut - 1)];
-    return (u32x4){e0.x, e0.y, e1.x, e1.y};
+  // The A operands of step sg of the tile whose words are w.
+  auto a_step = [&](const uint32_t (&w)[4], int sg, u32x4 (&a)[DD]) __attribute__((always_inline)) {
+    uint2 e[8];
+#pragma unroll
+    for (int lam = 0; lam < 8; ++lam) {
+      const uint32_t word = w[sg * WPS + lam / BPW];
+      e[lam] = lut[(word >> (D * (lam % BPW))) & (kLut - 1)];
+    }
+    pack_step<DD>(e, a);
   };
 
   f32x4 acc[PW][JB];
@@ -224,24 +276,17 @@ __global__ __launch_bounds__(256) void wspace_kernel(
 #pragma unroll
     for (int j = 0; j < JB; ++j) acc[i][j] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 
-  // One step: F sub-steps. The B operands and table reads of the next
-  // sub-step (for the last one, sub-step 0 of the next step, whose stage is
-  // complete by then) are issued before the MFMAs of this one. At the last
-  // sub-step of a tile the next tile's words are not loaded yet: its first A
-  // operands are read at the start of the next step.
-  auto mult = [&](const uint4* st, const uint4* st_next, const uint32_t (&w)[PW][4], int u,
-                  uint4 (&bcur)[JB], u32x4 (&acur)[PW]) {
+  // One step: DD sub-steps. The B operands of the next sub-step (for the
+  // last one, sub-step 0 of the next step, whose stage is complete by then)
+  // are read before the MFMAs of this one.
+  auto mult = [&](const uint4* st, const uint4* st_next, const u32x4 (&a)[PW][DD],
+                  uint4 (&bcur)[JB]) __attribute__((always_inline)) {
     uint4 bnext[JB];
-    u32x4 anext[PW];
 #pragma unroll
-    for (int s = 0; s < F; ++s) {
+    for (int f = 0; f < DD; ++f) {
 #pragma unroll
       for (int c = 0; c < JB; ++c)
-        bnext[c] = s < F - 1 ? st[(c * F + s + 1) * 64 + lane] : st_next[(c * F) * 64 + lane];
-      if (s < F - 1 || u < 3) {
-#pragma unroll
-        for (int i = 0; i < PW; ++i) anext[i] = a_operand(w[i][s < F - 1 ? u : u + 1], (s + 1) % F);
-      }
+        bnext[c] = f < DD - 1 ? st[(c * DD + f + 1) * 64 + lane] : st_next[(c * DD) * 64 + lane];
       // Keep those reads here: the scheduler would otherwise sink each one
       // next to its first use.
       __builtin_amdgcn_sched_barrier(0);
@@ -250,15 +295,11 @@ __global__ __launch_bounds__(256) void wspace_kernel(
 #pragma unroll
         for (int c = 0; c < JB; ++c) {
           const u32x4 bop = {bcur[c].x, bcur[c].y, bcur[c].z, bcur[c].w};
-          acc[i][c] = mfma_bf16(acur[i], bop, acc[i][c]);
+          acc[i][c] = mfma_bf16(a[i][f], bop, acc[i][c]);
         }
       }
 #pragma unroll
       for (int c = 0; c < JB; ++c) bcur[c] = bnext[c];
-      if (s < F - 1 || u < 3) {
-#pragma unroll
-        for (int i = 0; i < PW; ++i) acur[i] = anext[i];
-      }
     }
   };
 
@@ -267,44 +308,69 @@ __global__ __launch_bounds__(256) void wspace_kernel(
   // t begins: waiting until at most that many are outstanding means step
   // t + 1's copies, and everything issued before them, have landed.
   constexpr int kWait1 = (7 << 4) | (15 << 8) | (kCopies & 15) | ((kCopies >> 4) << 14);
-  static_assert(kCopies <= 63, "vmcnt range");
+  constexpr int kWait2 = (7 << 4) | (15 << 8) | ((2 * kCopies) & 15) | (((2 * kCopies) >> 4) << 14);
+  static_assert(2 * kCopies <= 63, "vmcnt range");
   copy_slots(0, slotA);
   copy_step(0, stage0);
   copy_step(min((int64_t)1, last), stage1);
   copy_step(min((int64_t)2, last), stage2);
   uint4 bcur[JB];
-  u32x4 acur[PW];
 
-  auto tile = [&](int q, const uint4* slot_cur, uint4* slot_next) {
-    uint32_t w[PW][4];
-    const int64_t t0 = 4 * (int64_t)q;
+  // Stage of step t: t mod 4, selected at compile time (the stages are
+  // separate arrays, so the compiler knows a copy into one does not alias
+  // the reads of another and makes those reads wait for nothing).
+  auto stage_c = [&](auto ic) __attribute__((always_inline)) -> uint4* {
+    constexpr int i = decltype(ic)::value & 3;
+    if constexpr (i == 0) return stage0;
+    else if constexpr (i == 1) return stage1;
+    else if constexpr (i == 2) return stage2;
+    else return stage3;
+  };
+  // Step sg of tile q, whose first step uses stage `off` (tiles alternate
+  // between the slot buffers and, for D = 8, between stages 0-1 and 2-3).
+  auto do_step = [&](auto sgc, auto offc, int q, const uint4* slot_cur, uint4* slot_next,
+                     uint32_t (&w)[PW][4]) __attribute__((always_inline)) {
+    constexpr int sg = decltype(sgc)::value;
+    constexpr int su = (decltype(offc)::value + sg) & 3;
+    const int64_t t = (int64_t)q * SPT + sg;
+    __builtin_amdgcn_s_waitcnt(kWait1);
+    wg_barrier();
+    if constexpr (sg == 0) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {                // step t = t0 + u, stage u
-      __builtin_amdgcn_s_waitcnt(kWait1);
-      wg_barrier();                              // (the first one also publishes the table)
-      if (u == 0) {
-#pragma unroll
-        for (int i = 0; i < PW; ++i) {
-          const uint4 v = slot_cur[(wave * PW + i) * 64 + lane];
-          w[i][0] = v.x; w[i][1] = v.y; w[i][2] = v.z; w[i][3] = v.w;
-        }
-        if (q == 0) {
-#pragma unroll
-          for (int c = 0; c < JB; ++c) bcur[c] = stage0[(c * F) * 64 + lane];
-        }
-#pragma unroll
-        for (int i = 0; i < PW; ++i) acur[i] = a_operand(w[i][0], 0);
+      for (int i = 0; i < PW; ++i) {
+        const uint4 v = slot_cur[(wave * PW + i) * 64 + lane];
+        w[i][0] = v.x; w[i][1] = v.y; w[i][2] = v.z; w[i][3] = v.w;
       }
-      copy_step(min(t0 + u + 3, last), u == 0 ? stage3 : (u == 1 ? stage0 : (u == 2 ? stage1 : stage2)));
-      if (u == 0) copy_slots(min(q + 1, ext_tiles - 1), slot_next);
-      mult(u == 0 ? stage0 : (u == 1 ? stage1 : (u == 2 ? stage2 : stage3)),
-           u == 0 ? stage1 : (u == 1 ? stage2 : (u == 2 ? stage3 : stage0)), w, u, bcur, acur);
+    }
+    u32x4 a[PW][DD];
+#pragma unroll
+    for (int i = 0; i < PW; ++i) a_step(w[i], sg, a[i]);
+    copy_step(min(t + 3, last), stage_c(std::integral_constant<int, su + 3>{}));
+    if constexpr (sg == 0) copy_slots(min(q + 1, ext_tiles - 1), slot_next);
+    mult(stage_c(std::integral_constant<int, su>{}), stage_c(std::integral_constant<int, su + 1>{}),
+         a, bcur);
+  };
+  auto tile = [&](auto offc, int q, const uint4* slot_cur, uint4* slot_next) __attribute__((always_inline)) {
+    uint32_t w[PW][4];
+    do_step(std::integral_constant<int, 0>{}, offc, q, slot_cur, slot_next, w);
+    do_step(std::integral_constant<int, 1>{}, offc, q, slot_cur, slot_next, w);
+    if constexpr (SPT > 2) {
+      do_step(std::integral_constant<int, 2>{}, offc, q, slot_cur, slot_next, w);
+      do_step(std::integral_constant<int, 3>{}, offc, q, slot_cur, slot_next, w);
     }
   };
-  for (int q = 0; q < ext_tiles; q += 2) {
-    tile(q, slotA, slotB);
-    if (q + 1 < ext_tiles) tile(q + 1, slotB, slotA);
+  // Sub-step 0 of step 0 is read before the loop (step 1's and 2's copies
+  // may still be in flight); the barrier also publishes the table.
+  __builtin_amdgcn_s_waitcnt(kWait2);
+  wg_barrier();
+#pragma unroll
+  for (int c = 0; c < JB; ++c) bcur[c] = stage0[(c * DD) * 64 + lane];
+  int q = 0;
+  for (; q + 1 < ext_tiles; q += 2) {
+    tile(std::integral_constant<int, 0>{}, q, slotA, slotB);
+    tile(std::integral_constant<int, SPT & 3>{}, q + 1, slotB, slotA);
   }
+  if (q < ext_tiles) tile(std::integral_constant<int, 0>{}, q, slotA, slotB);
 
   // No copy may still be writing LDS when the workgroup ends.
   __builtin_amdgcn_s_waitcnt(0);
@@ -323,7 +389,7 @@ __global__ __launch_bounds__(256) void wspace_kernel(
       if (b >= B) continue;
       const float v0 = rs.x * acc[i][j][0], v1 = rs.y * acc[i][j][1];
       const float v2 = rs.z * acc[i][j][2], v3 = rs.w * acc[i][j][3];
-      if (kYBF16) {
+      if (y_bf16) {
         uint16_t* yp = reinterpret_cast<uint16_t*>(y) + b * N + n0;
         const uint32_t lo = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
         const uint32_t hi = f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16);
@@ -335,71 +401,74 @@ __global__ __launch_bounds__(256) void wspace_kernel(
   }
 }
 
-template <int D, int PW, int JB, bool kYBF16>
+template <int D, int DD, int JB>
 hipError_t launch_ws_t(const uint8_t* packed, const PackedGeom& g, const uint4* xp, int64_t B,
-                       const uint4* tail_slots, const float* M, int d, const float* row_scale,
-                       void* y, hipStream_t stream) {
+                       const uint4* tail_slots, const float* M, const float* row_scale, void* y,
+                       bool y_bf16, hipStream_t stream) {
   const int64_t B16 = (B + 15) / 16;
-  const dim3 grid((unsigned)((g.panels + 4 * PW - 1) / (4 * PW)), (unsigned)((B16 + JB - 1) / JB));
-  return launch_timed(wspace_kernel<D, PW, JB, kYBF16>, grid, dim3(256), 0, stream, packed,
-                      g.panels, g.panel_bytes, g.full_tiles, g.ext_tiles, xp, B16, B, tail_slots,
-                      M, d, row_scale, y, g.N);
+  const dim3 grid((unsigned)((g.panels + 4 * kWsPW - 1) / (4 * kWsPW)), (unsigned)((B16 + JB - 1) / JB));
+  return launch_timed(wspace_kernel<D, DD, JB>, grid, dim3(256), 0, stream, packed, g.panels,
+                      g.panel_bytes, g.full_tiles, g.ext_tiles, xp, B16, B, tail_slots, M,
+                      y_bf16 ? 1 : 0, row_scale, y, g.N);
 }
 
-template <int D, bool kYBF16>
-hipError_t launch_ws_y(const uint8_t* packed, const PackedGeom& g, const uint4* xp, int64_t B,
-                       const uint4* tail_slots, const float* M, int d, const float* row_scale,
-                       void* y, const LargePlan& p, hipStream_t stream) {
-  // (D = 4: at most 4 batch tiles, or the four stages would not fit LDS)
-#define LQ_WS_CASE(PW_, JB_)                                                                       \
-  if constexpr ((16 / D) * JB_ <= 16) {                                                            \
-    if (p.ppw == PW_ && p.jb == JB_)                                                               \
-      return launch_ws_t<D, PW_, JB_, kYBF16>(packed, g, xp, B, tail_slots, M, d, row_scale, y,   \
-                                              stream);                                             \
+template <int D, int DD>
+hipError_t launch_ws_jb(const uint8_t* packed, const PackedGeom& g, const uint4* xp, int64_t B,
+                        const uint4* tail_slots, const float* M, const float* row_scale, void* y,
+                        bool y_bf16, int jb, hipStream_t stream) {
+  switch (jb) {
+    case 8:
+      if constexpr (DD <= 3)
+        return launch_ws_t<D, DD, 8>(packed, g, xp, B, tail_slots, M, row_scale, y, y_bf16, stream);
+      else
+        return hipErrorInvalidValue;
+    case 4: return launch_ws_t<D, DD, 4>(packed, g, xp, B, tail_slots, M, row_scale, y, y_bf16, stream);
+    case 2: return launch_ws_t<D, DD, 2>(packed, g, xp, B, tail_slots, M, row_scale, y, y_bf16, stream);
+    case 1: return launch_ws_t<D, DD, 1>(packed, g, xp, B, tail_slots, M, row_scale, y, y_bf16, stream);
+    default: return hipErrorInvalidValue;
   }
-  LQ_WS_CASE(8, 4) LQ_WS_CASE(8, 2) LQ_WS_CASE(8, 1)
-  LQ_WS_CASE(4, 8) LQ_WS_CASE(4, 4) LQ_WS_CASE(4, 2) LQ_WS_CASE(4, 1)
-  LQ_WS_CASE(2, 4) LQ_WS_CASE(2, 2) LQ_WS_CASE(2, 1)
-  LQ_WS_CASE(1, 4) LQ_WS_CASE(1, 2) LQ_WS_CASE(1, 1)
-#undef LQ_WS_CASE
-  return hipErrorInvalidValue;
+}
+
+template <int D>
+hipError_t launch_ws_d(const uint8_t* packed, const PackedGeom& g, const uint4* xp, int64_t B,
+                       const uint4* tail_slots, const float* M, int d, const float* row_scale,
+                       void* y, bool y_bf16, int jb, hipStream_t stream) {
+  switch (d) {
+    case 1: return launch_ws_jb<D, 1>(packed, g, xp, B, tail_slots, M, row_scale, y, y_bf16, jb, stream);
+    case 2: return launch_ws_jb<D, 2>(packed, g, xp, B, tail_slots, M, row_scale, y, y_bf16, jb, stream);
+    case 3: return launch_ws_jb<D, 3>(packed, g, xp, B, tail_slots, M, row_scale, y, y_bf16, jb, stream);
+    case 4: return launch_ws_jb<D, 4>(packed, g, xp, B, tail_slots, M, row_scale, y, y_bf16, jb, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
 bool wspace_supported(int d, int D) { return (D == 4 || D == 8) && d >= 1 && d <= 4 && d <= D; }
 
-XpGeom xp_geom(int64_t B, const PackedGeom& g, int D) {
+XpGeom xp_geom(int64_t B, const PackedGeom& g, int d, int D) {
   XpGeom x;
   x.B16 = (B + 15) / 16;
-  x.steps = 4 * (int64_t)g.ext_tiles;
-  x.bytes = (size_t)x.B16 * x.steps * (16 / D) * 1024;
+  x.steps = (16 / D) * (int64_t)g.ext_tiles;
+  x.bytes = (size_t)x.B16 * x.steps * d * 1024;
   x.tail_bytes = g.tail_bytes ? (size_t)g.panels * kTileBytes : 0;
   return x;
 }
 
-LargePlan plan_wspace(int64_t B, const PackedGeom& g, int D) {
-  LargePlan p;
+int plan_wspace_jb(int64_t B, const PackedGeom& g, int d) {
   const int64_t B16 = (B + 15) / 16;
-  if (D == 8 && B16 >= 8 && ((g.panels + 15) / 16) * ((B16 + 7) / 8) >= 512) {
-    p.jb = 8;
-    p.ppw = 4;
-    return p;
-  }
-  p.jb = B16 >= 4 ? 4 : (B16 >= 2 ? 2 : 1);
-  const int64_t bt = (B16 + p.jb - 1) / p.jb;
-  p.ppw = 1;
-  for (int c : {8, 4, 2}) {
-    if (((g.panels + 4 * c - 1) / (4 * c)) * bt >= 512) { p.ppw = c; break; }
-  }
-  return p;
+  const int64_t pgroups = (g.panels + 4 * kWsPW - 1) / (4 * kWsPW);
+  // 8 batch tiles per workgroup (each A operand feeds 8 MFMAs) where that
+  // still gives >= 512 workgroups and the stages fit LDS (d <= 3)
+  if (d <= 3 && B16 >= 8 && pgroups * ((B16 + 7) / 8) >= 512) return 8;
+  return B16 >= 4 ? 4 : (B16 >= 2 ? 2 : 1);
 }
 
 hipError_t launch_xpw(const void* x, bool x_bf16, int64_t B, int64_t K, int hb, const float* c,
                       int d, int D, const PackedGeom& g, void* xp, hipStream_t stream) {
   (void)hipGetLastError();   // clear a stale error of an earlier runtime call
   if (!wspace_supported(d, D) || hb < 1 || hb > 1024 || (hb & (hb - 1)) || K % hb) return hipErrorInvalidValue;
-  const XpGeom xg = xp_geom(B, g, D);
+  const XpGeom xg = xp_geom(B, g, d, D);
   int lhb = 0;
   while ((1 << lhb) < hb) ++lhb;
   const float norm = (lhb % 2 == 0) ? ldexpf(1.0f, -lhb / 2) : (float)(1.0 / sqrt((double)hb));
@@ -428,18 +497,15 @@ hipError_t launch_wspace(const uint8_t* packed, const PackedGeom& g, const void*
                          const float* row_scale, void* y, bool y_bf16, hipStream_t stream) {
   (void)hipGetLastError();   // clear a stale error of an earlier runtime call
   if (!wspace_supported(d, D)) return hipErrorInvalidValue;
-  const LargePlan p = plan_wspace(B, g, D);
+  const int jb = plan_wspace_jb(B, g, d);
   const uint4* x = reinterpret_cast<const uint4*>(xp);
   uint4* ts = reinterpret_cast<uint4*>(tail_slots);
   if (g.tail_bytes) {
     const hipError_t e = launch_tail_slots(packed, g, ts, stream);
     if (e != hipSuccess) return e;
   }
-  if (D == 8)
-    return y_bf16 ? launch_ws_y<8, true>(packed, g, x, B, ts, M, d, row_scale, y, p, stream)
-                  : launch_ws_y<8, false>(packed, g, x, B, ts, M, d, row_scale, y, p, stream);
-  return y_bf16 ? launch_ws_y<4, true>(packed, g, x, B, ts, M, d, row_scale, y, p, stream)
-                : launch_ws_y<4, false>(packed, g, x, B, ts, M, d, row_scale, y, p, stream);
+  if (D == 8) return launch_ws_d<8>(packed, g, x, B, ts, M, d, row_scale, y, y_bf16, jb, stream);
+  return launch_ws_d<4>(packed, g, x, B, ts, M, d, row_scale, y, y_bf16, jb, stream);
 }
 
 }  // namespace lq

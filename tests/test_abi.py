@@ -181,7 +181,7 @@ def test_linear_ex_validation_and_control_area():
     tiles = -(-L // 512)
     assert st == LQ_OK
     assert need >= (_lib.LQ_WS_CONTROL_BYTES
-                    + 128 * 4 * tiles * 2048                              # xp: 2 KB per step
+                    + 128 * 2 * tiles * 3 * 1024                          # xp: d KB per step
                     + 512 * 1024)                                         # tail slots
     assert need < _lib.LQ_WS_CONTROL_BYTES + 2048 * 8192 * 4               # no fp32 xt
     assert linear_ws_size(pre, 2048, LQ_F32, 6)[0] == LQ_ERR_UNSUPPORTED    # fp32 x
