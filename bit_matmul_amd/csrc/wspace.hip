@@ -43,112 +43,197 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
 }
 
 // ------------------------------------------------------------ whitening + xp
-// Workgroup (chunk h of 1024 inputs, 16 batch rows jb): x * c of the rows'
-// chunk into LDS, the Walsh-Hadamard transform of every hb block (a
-// wavefront per row), then the xp units of every step of the tiles whose
-// blocks draw on the chunk. Slot (block b, input i < d) belongs to the chunk
-// holding input min(b d + i, K - 1): a unit whose eight slots all belong to
-// this chunk is stored whole, one that straddles chunks slot by slot (2
-// bytes each; the other chunk's workgroup stores the rest). The last chunk
-// also covers the virtual pad and the blocks past L up to the end of the
-// last tile (zeros).
-constexpr int kXpwStride = 1028;   // LDS row stride (floats): 16-byte aligned, rows 4 banks apart
+// Workgroup (chunk h of 1024 inputs, 8 batch rows): wavefront w whitens rows
+// w and w + 4 of the chunk (x * c, then the Walsh-Hadamard transform of every
+// hb block, in registers with one pass through a per-wavefront LDS buffer),
+// scales by 1/sqrt(hb) and keeps the bf16 results in LDS. Then every thread
+// builds whole lane-steps (step t, lane group g, row r): the 8 d values of a
+// step, which are BPW-block runs of consecutive inputs, and stores their d
+// units. Input k belongs to the chunk holding min(k, K - 1): a lane-step
+// whose values all lie in this chunk is stored whole, one that straddles
+// chunks value by value (2 bytes each; the other chunk's workgroup stores
+// the rest). The last chunk also covers the virtual pad and the blocks past
+// L up to the end of the last tile (zeros).
+constexpr int kXpwRows = 8;
+constexpr int kXpwOut = 1040;      // bf16 per LDS row: rows 8 banks apart
 
-template <int D, bool kXBF16>
+// Stages 0..9 of the transform (those below lhb) of the 1024 values whose
+// lane l holds 16 l + j in a[j], in the order of the shared wavefront
+// transform; the scaled bf16 results go to out[0..1023].
+__device__ __forceinline__ void fwht_row_to_bf16(float (&a)[16], float* buf, int lhb, int lane,
+                                                 float norm, uint16_t* out) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    if (s < lhb) {
+      const int hs = 1 << s;
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if ((k & hs) == 0) {
+          const float x0 = a[k], x1 = a[k | hs];
+          a[k] = x0 + x1;
+          a[k | hs] = x0 - x1;
+        }
+    }
+  }
+  if (lhb > 4) lane_stage<1>(a, lane);
+  if (lhb > 5) lane_stage<2>(a, lane);
+  float4* dst = reinterpret_cast<float4*>(buf + 16 * lane);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[i] = make_float4(a[4 * i], a[4 * i + 1], a[4 * i + 2], a[4 * i + 3]);
+  // The wavefront's own LDS writes are seen by its later reads.
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int k = 0; k < 16; ++k) a[k] = buf[lane + 64 * k];
+#pragma unroll
+  for (int s = 6; s < 10; ++s) {
+    if (s < lhb) {
+      const int hs = 1 << (s - 6);
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if ((k & hs) == 0) {
+          const float x0 = a[k], x1 = a[k | hs];
+          a[k] = x0 + x1;
+          a[k | hs] = x0 - x1;
+        }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) out[lane + 64 * k] = (uint16_t)f32_to_bf16_bits(a[k] * norm);
+}
+
+template <int D, int DD, bool kXBF16>
 __global__ __launch_bounds__(256) void xpw_kernel(const void* __restrict__ x,
                                                   const float* __restrict__ c, int64_t B,
-                                                  int64_t K, int d, int lhb, float norm,
-                                                  int64_t steps, int64_t blk_end, int64_t jb_base,
+                                                  int64_t K, int lhb, float norm, int64_t steps,
+                                                  int64_t blk_end, int64_t jr_base,
                                                   uint4* __restrict__ xp) {
-  __shared__ __align__(16) float xs[16 * kXpwStride];
+  __shared__ __align__(16) float buf[4][1024];
+  __shared__ __align__(16) uint16_t xo[kXpwRows * kXpwOut];
   const int h = blockIdx.x;
-  const int64_t jb = jb_base + blockIdx.y;
+  const int64_t jr = jr_base + blockIdx.y;        // rows 8 jr .. 8 jr + 7
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t k_lo = (int64_t)h * 1024;
   const int n = (int)min((int64_t)1024, K - k_lo);
+  const int k16 = 16 * lane;
 
-  // x * c: thread t takes inputs 4t .. 4t + 3 of every row
-  const int k4 = 4 * tid;
-  float cv[4];
+  // x * c: lane l takes inputs 16 l .. 16 l + 15 of its wavefront's rows
+  float cv[16], a[2][16];
+  const bool full = k16 + 16 <= n;
+  if (full && (reinterpret_cast<uintptr_t>(c) & 15) == 0) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) cv[i] = k4 + i < n ? c[k_lo + k4 + i] : 0.0f;
-#pragma unroll 4
-  for (int rr = 0; rr < 16; ++rr) {
-    const int64_t b = 16 * jb + rr;
-    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 0; i < 4; ++i) {
+      const float4 v = *reinterpret_cast<const float4*>(c + k_lo + k16 + 4 * i);
+      cv[4 * i] = v.x; cv[4 * i + 1] = v.y; cv[4 * i + 2] = v.z; cv[4 * i + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) cv[j] = k16 + j < n ? c[k_lo + k16 + j] : 0.0f;
+  }
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int64_t b = 8 * jr + wave + 4 * m;
+    const int64_t at = b * K + k_lo + k16;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) a[m][j] = 0.0f;
     if (b < B) {
-      const int64_t at = b * K + k_lo + k4;
-      if (k4 + 3 < n && (at & 3) == 0) {
-        if (kXBF16) {
-          const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(x) + at);
-          v[0] = bf16_bits_to_f32(w.x & 0xFFFFu); v[1] = bf16_bits_to_f32(w.x >> 16);
-          v[2] = bf16_bits_to_f32(w.y & 0xFFFFu); v[3] = bf16_bits_to_f32(w.y >> 16);
+      if (full && (at & 7) == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0) {
+        if constexpr (kXBF16) {
+          const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + at);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const uint4 w = p[i];
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              a[m][8 * i + 2 * e] = bf16_bits_to_f32(ww[e] & 0xFFFFu);
+              a[m][8 * i + 2 * e + 1] = bf16_bits_to_f32(ww[e] >> 16);
+            }
+          }
         } else {
-          const float4 w = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + at);
-          v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+          const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + at);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float4 w = p[i];
+            a[m][4 * i] = w.x; a[m][4 * i + 1] = w.y; a[m][4 * i + 2] = w.z; a[m][4 * i + 3] = w.w;
+          }
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (k4 + i < n)
-            v[i] = kXBF16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(x)[at + i])
-                          : reinterpret_cast<const float*>(x)[at + i];
+        for (int j = 0; j < 16; ++j)
+          if (k16 + j < n)
+            a[m][j] = kXBF16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(x)[at + j])
+                             : reinterpret_cast<const float*>(x)[at + j];
       }
     }
-    *reinterpret_cast<float4*>(xs + rr * kXpwStride + k4) =
-        make_float4(v[0] * cv[0], v[1] * cv[1], v[2] * cv[2], v[3] * cv[3]);
   }
-  __syncthreads();
   // (every hb block lies inside the chunk: hb divides 1024 and K; past n
   // the values are zero and stay zero)
-  for (int rr = wave; rr < 16; rr += 4) wave_fwht_1024(xs + rr * kXpwStride, lhb, lane);
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) a[m][j] *= cv[j];
+    fwht_row_to_bf16(a[m], buf[wave], lhb, lane, norm, xo + (wave + 4 * m) * kXpwOut);
+  }
   __syncthreads();
 
-  const bool last = k_lo + 1024 >= K;
   constexpr int BPT = 512 / D;                    // blocks per tile
-  constexpr int WPS = D / 4;                      // packed words per step
+  constexpr int WPS = D / 4;                      // packed words per step = runs per lane-step
   constexpr int SPT = 4 / WPS;                    // steps per tile
-  constexpr int BPW = 32 / D;                     // blocks per word of a lane
-  const int64_t b_first = k_lo / d;
-  const int64_t b_last = last ? blk_end - 1 : (k_lo + 1023) / d;
+  constexpr int BPW = 32 / D;                     // blocks per word = per run
+  constexpr int RUN = BPW * DD;                   // inputs per run (even)
+  const int64_t k_hi = k_lo + n;                  // this chunk's inputs: [k_lo, k_hi)
+  const bool last = k_lo + 1024 >= K;
+  const int64_t b_first = k_lo / DD;
+  const int64_t b_last = last ? blk_end - 1 : (k_lo + 1023) / DD;
   const int64_t q_lo = b_first / BPT, nq = b_last / BPT - q_lo + 1;
-  // items: (tile, step, lane group, sub-step, row), row fastest
-  const int64_t items = nq * SPT * 4 * d * 16;
+  const int64_t jb = jr >> 1;
+  const int r16 = 8 * (int)(jr & 1);
+  // items: (tile, step, lane group, row), row fastest
+  const int64_t items = nq * SPT * 4 * kXpwRows;
   for (int64_t idx = tid; idx < items; idx += 256) {
-    const int r = (int)(idx & 15);
-    int64_t rest = idx >> 4;
-    const int f = (int)(rest % d);
-    rest /= d;
-    const int g = (int)(rest & 3);
-    rest >>= 2;
+    const int r = (int)(idx & 7);
+    const int g = (int)((idx >> 3) & 3);
+    const int64_t rest = idx >> 5;
     const int sg = (int)(rest % SPT);
     const int64_t q = q_lo + rest / SPT;
     const int64_t t = q * SPT + sg;
-    uint4* dst = xp + ((jb * steps + t) * d + f) * 64 + 16 * g + r;
-    const float* xr = xs + r * kXpwStride;
-    uint32_t hv[8];
-    bool own[8];
-    bool all = true, any = false;
+    uint4* dst = xp + (jb * steps + t) * DD * 64 + 16 * g + r16 + r;
+    const uint16_t* row = xo + r * kXpwOut;
+    int64_t k0[WPS];
+    bool fast = true;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int pos = 8 * f + e, lam = pos / d, i = pos - lam * d;
-      const int u = sg * WPS + lam / BPW, tt = lam % BPW;
-      const int64_t blk = q * BPT + u * (BPT / 4) + g * BPW + tt;
-      const int64_t k = blk * d + i;
-      const bool o = (min(k, K - 1) >> 10) == h;
-      own[e] = o;
-      all = all && o;
-      any = any || o;
-      hv[e] = f32_to_bf16_bits(o && k < K ? xr[k - k_lo] * norm : 0.0f);
+    for (int R = 0; R < WPS; ++R) {
+      k0[R] = (q * BPT + (sg * WPS + R) * (BPT / 4) + g * BPW) * DD;
+      fast = fast && k0[R] >= k_lo && k0[R] + RUN <= k_hi;
     }
-    if (all) {
-      *dst = make_uint4(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16),
-                        hv[6] | (hv[7] << 16));
-    } else if (any) {
-      uint16_t* p = reinterpret_cast<uint16_t*>(dst);
+    if (fast) {
+      // the runs' RUN / 2 words each, in stream order, are the d units
+      uint32_t wv[4 * DD];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (own[e]) p[e] = (uint16_t)hv[e];
+      for (int R = 0; R < WPS; ++R) {
+        const uint2* p = reinterpret_cast<const uint2*>(row + (k0[R] - k_lo));
+#pragma unroll
+        for (int i = 0; i < RUN / 4; ++i) {
+          const uint2 v = p[i];
+          wv[R * (RUN / 2) + 2 * i] = v.x;
+          wv[R * (RUN / 2) + 2 * i + 1] = v.y;
+        }
+      }
+#pragma unroll
+      for (int f = 0; f < DD; ++f)
+        dst[f * 64] = make_uint4(wv[4 * f], wv[4 * f + 1], wv[4 * f + 2], wv[4 * f + 3]);
+    } else {
+#pragma unroll
+      for (int R = 0; R < WPS; ++R) {
+#pragma unroll
+        for (int e = 0; e < RUN; ++e) {
+          const int64_t k = k0[R] + e;
+          if ((min(k, K - 1) >> 10) != h) continue;
+          const uint16_t v = k < K ? row[k - k_lo] : (uint16_t)0;
+          const int p = R * RUN + e;                   // stream position
+          reinterpret_cast<uint16_t*>(dst + (p >> 3) * 64)[p & 7] = v;
+        }
+      }
     }
   }
 }
@@ -474,16 +559,26 @@ hipError_t launch_xpw(const void* x, bool x_bf16, int64_t B, int64_t K, int hb, 
   const float norm = (lhb % 2 == 0) ? ldexpf(1.0f, -lhb / 2) : (float)(1.0 / sqrt((double)hb));
   const int64_t blk_end = (int64_t)g.ext_tiles * (kTileCols / D);
   const unsigned chunks = (unsigned)((K + 1023) / 1024);
+  const int64_t groups = 2 * xg.B16;             // 8-row groups
   uint4* out = reinterpret_cast<uint4*>(xp);
-  for (int64_t jb0 = 0; jb0 < xg.B16; jb0 += 65535) {
-    const dim3 grid(chunks, (unsigned)min(xg.B16 - jb0, (int64_t)65535));
-#define LQ_XPW(D_, BF_)                                                                            \
-    hipLaunchKernelGGL((xpw_kernel<D_, BF_>), grid, dim3(256), 0, stream, x, c, B, K, d, lhb, norm, \
-                       xg.steps, blk_end, jb0, out)
-    if (D == 8) {
-      if (x_bf16) LQ_XPW(8, true); else LQ_XPW(8, false);
-    } else {
-      if (x_bf16) LQ_XPW(4, true); else LQ_XPW(4, false);
+  for (int64_t jr0 = 0; jr0 < groups; jr0 += 65535) {
+    const dim3 grid(chunks, (unsigned)min(groups - jr0, (int64_t)65535));
+#define LQ_XPW(D_, DD_)                                                                          \
+    if (x_bf16)                                                                                  \
+      hipLaunchKernelGGL((xpw_kernel<D_, DD_, true>), grid, dim3(256), 0, stream, x, c, B, K,   \
+                         lhb, norm, xg.steps, blk_end, jr0, out);                                \
+    else                                                                                         \
+      hipLaunchKernelGGL((xpw_kernel<D_, DD_, false>), grid, dim3(256), 0, stream, x, c, B, K,  \
+                         lhb, norm, xg.steps, blk_end, jr0, out)
+    switch (D * 8 + d) {
+      case 8 * 8 + 1: LQ_XPW(8, 1); break;
+      case 8 * 8 + 2: LQ_XPW(8, 2); break;
+      case 8 * 8 + 3: LQ_XPW(8, 3); break;
+      case 8 * 8 + 4: LQ_XPW(8, 4); break;
+      case 4 * 8 + 1: LQ_XPW(4, 1); break;
+      case 4 * 8 + 2: LQ_XPW(4, 2); break;
+      case 4 * 8 + 3: LQ_XPW(4, 3); break;
+      default: LQ_XPW(4, 4); break;
     }
 #undef LQ_XPW
     const hipError_t e = hipGetLastError();
