@@ -344,15 +344,23 @@ __global__ __launch_bounds__(256) void wspace_kernel(
       dma(src, dst + (wave * PW + i) * 64);
     }
   };
-  // The A operands of step sg of the tile whose words are w.
-  auto a_step = [&](const uint32_t (&w)[4], int sg, u32x4 (&a)[DD]) __attribute__((always_inline)) {
-    uint2 e[8];
+  // The table entries of step sg of the tiles whose words are w: 8 per panel.
+  auto lut_step = [&](const uint32_t (&w)[PW][4], int sg, uint2 (&e)[PW][8])
+                      __attribute__((always_inline)) {
 #pragma unroll
-    for (int lam = 0; lam < 8; ++lam) {
-      const uint32_t word = w[sg * WPS + lam / BPW];
-      e[lam] = lut[(word >> (D * (lam % BPW))) & (kLut - 1)];
+    for (int i = 0; i < PW; ++i)
+#pragma unroll
+      for (int lam = 0; lam < 8; ++lam) {
+        const uint32_t word = w[i][sg * WPS + lam / BPW];
+        e[i][lam] = lut[(word >> (D * (lam % BPW))) & (kLut - 1)];
+      }
+  };
+  auto read_words = [&](const uint4* slot, uint32_t (&w)[PW][4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      const uint4 v = slot[(wave * PW + i) * 64 + lane];
+      w[i][0] = v.x; w[i][1] = v.y; w[i][2] = v.z; w[i][3] = v.w;
     }
-    pack_step<DD>(e, a);
   };
 
   f32x4 acc[PW][JB];
@@ -363,9 +371,10 @@ __global__ __launch_bounds__(256) void wspace_kernel(
 
   // One step: DD sub-steps. The B operands of the next sub-step (for the
   // last one, sub-step 0 of the next step, whose stage is complete by then)
-  // are read before the MFMAs of this one.
-  auto mult = [&](const uint4* st, const uint4* st_next, const u32x4 (&a)[PW][DD],
-                  uint4 (&bcur)[JB]) __attribute__((always_inline)) {
+  // are read before the MFMAs of this one; the A operands of the next step
+  // are packed from its table entries e between the last sub-step's MFMAs.
+  auto mult = [&](const uint4* st, const uint4* st_next, u32x4 (&a)[PW][DD], uint4 (&bcur)[JB],
+                  const uint2 (&e)[PW][8]) __attribute__((always_inline)) {
     uint4 bnext[JB];
 #pragma unroll
     for (int f = 0; f < DD; ++f) {
@@ -383,23 +392,43 @@ __global__ __launch_bounds__(256) void wspace_kernel(
           acc[i][c] = mfma_bf16(a[i][f], bop, acc[i][c]);
         }
       }
+      if (f == DD - 1) {
+        u32x4 an[PW][DD];
+#pragma unroll
+        for (int i = 0; i < PW; ++i) pack_step<DD>(e[i], an[i]);
+        // one MFMA, then up to 4 VALU instructions, and so on
+#pragma unroll
+        for (int k = 0; k < PW * JB; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < PW; ++i)
+#pragma unroll
+          for (int g = 0; g < DD; ++g) a[i][g] = an[i][g];
+      }
 #pragma unroll
       for (int c = 0; c < JB; ++c) bcur[c] = bnext[c];
     }
   };
 
   // Copies are issued unconditionally (past the last step, the last step
-  // again), so kCopies copy instructions follow those of step t + 1 when step
-  // t begins: waiting until at most that many are outstanding means step
-  // t + 1's copies, and everything issued before them, have landed.
+  // again), slots before stage, so kCopies copy instructions follow those of
+  // step t + 1 when step t begins: waiting until at most that many are
+  // outstanding means step t + 1's copies, and everything issued before them
+  // (the next tile's slots too, from the second step of a tile on), have
+  // landed.
   constexpr int kWait1 = (7 << 4) | (15 << 8) | (kCopies & 15) | ((kCopies >> 4) << 14);
   constexpr int kWait2 = (7 << 4) | (15 << 8) | ((2 * kCopies) & 15) | (((2 * kCopies) >> 4) << 14);
   static_assert(2 * kCopies <= 63, "vmcnt range");
+  static_assert(SPT >= 2, "the next tile's words are read in a tile's second step or later");
   copy_slots(0, slotA);
   copy_step(0, stage0);
   copy_step(min((int64_t)1, last), stage1);
   copy_step(min((int64_t)2, last), stage2);
   uint4 bcur[JB];
+  u32x4 a[PW][DD];
+  uint32_t w[PW][4];
 
   // Stage of step t: t mod 4, selected at compile time (the stages are
   // separate arrays, so the compiler knows a copy into one does not alias
@@ -413,49 +442,54 @@ __global__ __launch_bounds__(256) void wspace_kernel(
   };
   // Step sg of tile q, whose first step uses stage `off` (tiles alternate
   // between the slot buffers and, for D = 8, between stages 0-1 and 2-3).
-  auto do_step = [&](auto sgc, auto offc, int q, const uint4* slot_cur, uint4* slot_next,
-                     uint32_t (&w)[PW][4]) __attribute__((always_inline)) {
+  // On entry a holds the step's A operands; the step looks up the next
+  // step's table entries (in its last step, from the next tile's words).
+  auto do_step = [&](auto sgc, auto offc, int q, uint4* slot_next) __attribute__((always_inline)) {
     constexpr int sg = decltype(sgc)::value;
     constexpr int su = (decltype(offc)::value + sg) & 3;
     const int64_t t = (int64_t)q * SPT + sg;
     __builtin_amdgcn_s_waitcnt(kWait1);
     wg_barrier();
-    if constexpr (sg == 0) {
-#pragma unroll
-      for (int i = 0; i < PW; ++i) {
-        const uint4 v = slot_cur[(wave * PW + i) * 64 + lane];
-        w[i][0] = v.x; w[i][1] = v.y; w[i][2] = v.z; w[i][3] = v.w;
-      }
+    uint2 e[PW][8];
+    if constexpr (sg + 1 < SPT) {
+      lut_step(w, sg + 1, e);
+    } else {
+      read_words(slot_next, w);
+      lut_step(w, 0, e);
     }
-    u32x4 a[PW][DD];
-#pragma unroll
-    for (int i = 0; i < PW; ++i) a_step(w[i], sg, a[i]);
-    copy_step(min(t + 3, last), stage_c(std::integral_constant<int, su + 3>{}));
     if constexpr (sg == 0) copy_slots(min(q + 1, ext_tiles - 1), slot_next);
+    copy_step(min(t + 3, last), stage_c(std::integral_constant<int, su + 3>{}));
     mult(stage_c(std::integral_constant<int, su>{}), stage_c(std::integral_constant<int, su + 1>{}),
-         a, bcur);
+         a, bcur, e);
   };
-  auto tile = [&](auto offc, int q, const uint4* slot_cur, uint4* slot_next) __attribute__((always_inline)) {
-    uint32_t w[PW][4];
-    do_step(std::integral_constant<int, 0>{}, offc, q, slot_cur, slot_next, w);
-    do_step(std::integral_constant<int, 1>{}, offc, q, slot_cur, slot_next, w);
+  auto tile = [&](auto offc, int q, uint4* slot_next) __attribute__((always_inline)) {
+    do_step(std::integral_constant<int, 0>{}, offc, q, slot_next);
+    do_step(std::integral_constant<int, 1>{}, offc, q, slot_next);
     if constexpr (SPT > 2) {
-      do_step(std::integral_constant<int, 2>{}, offc, q, slot_cur, slot_next, w);
-      do_step(std::integral_constant<int, 3>{}, offc, q, slot_cur, slot_next, w);
+      do_step(std::integral_constant<int, 2>{}, offc, q, slot_next);
+      do_step(std::integral_constant<int, 3>{}, offc, q, slot_next);
     }
   };
-  // Sub-step 0 of step 0 is read before the loop (step 1's and 2's copies
-  // may still be in flight); the barrier also publishes the table.
+  // Before the loop: the first tile's words, step 0's A operands and
+  // sub-step 0 of its B operands (steps 1 and 2 may still be in flight);
+  // the barrier also publishes the table.
   __builtin_amdgcn_s_waitcnt(kWait2);
   wg_barrier();
+  {
+    uint2 e[PW][8];
+    read_words(slotA, w);
+    lut_step(w, 0, e);
+#pragma unroll
+    for (int i = 0; i < PW; ++i) pack_step<DD>(e[i], a[i]);
+  }
 #pragma unroll
   for (int c = 0; c < JB; ++c) bcur[c] = stage0[(c * DD) * 64 + lane];
   int q = 0;
   for (; q + 1 < ext_tiles; q += 2) {
-    tile(std::integral_constant<int, 0>{}, q, slotA, slotB);
-    tile(std::integral_constant<int, SPT & 3>{}, q + 1, slotB, slotA);
+    tile(std::integral_constant<int, 0>{}, q, slotB);
+    tile(std::integral_constant<int, SPT & 3>{}, q + 1, slotA);
   }
-  if (q < ext_tiles) tile(std::integral_constant<int, 0>{}, q, slotA, slotB);
+  if (q < ext_tiles) tile(std::integral_constant<int, 0>{}, q, slotB);
 
   // No copy may still be writing LDS when the workgroup ends.
   __builtin_amdgcn_s_waitcnt(0);
