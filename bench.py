@@ -75,6 +75,9 @@ def parse_args():
                    help="skip the 2048-token prefill layer (TFLOP/s)")
     p.add_argument("--no-encode", action="store_true",
                    help="skip the encoder and training-step timings")
+    p.add_argument("--gate-up", default="multi", choices=["multi", "separate"],
+                   help="decode: gate and up (same x) in one lq_linear_multi call, or as two "
+                        "lq_linear calls")
     p.add_argument("--eager", action="store_true",
                    help="launch the timed steps eagerly, each sign product timed by its own "
                         "dispatch events (slows the launches down)")
@@ -317,6 +320,8 @@ def build_decode_case(torch, lq, n_sets, seed=0):
             return 0
     ws_bytes = max(need(layers[0][i]["struct"], a) for i in range(3)
                    for a in (lq.LQ_ALGO_AUTO, lq.LQ_ALGO_MFMA_SMALL, lq.LQ_ALGO_FUSED_SPLIT))
+    ws_bytes = max(ws_bytes, lq.lq_linear_multi_workspace_size(
+        [layers[0][0]["struct"], layers[0][1]["struct"]], 1, torch.bfloat16))
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)      # zeroed control area
     return specs, layers, x_in, ys, ws, M
 
@@ -340,17 +345,27 @@ def run_decode(args, torch, lq, ev):
                 l.setdefault("algo_ok", {})[algo] = False
         lq.lq_linear(l["struct"], x, 1, ys[l["name"]], ws)
 
+    # gate and up read the same x: one lq_linear_multi call (one preparation
+    # and one product launch for both) unless another algorithm is forced
+    grouped = args.gate_up == "multi" and algo is None
+    ys_gu = [ys["gate"], ys["up"]]
+
     def step(i):
-        for l in layers[i % n_sets]:
-            x = x_in["down"] if l["name"] == "down" else x_in["gate"]
-            call(l, x)
+        gate, up, down = layers[i % n_sets]
+        if grouped:
+            lq.lq_linear_multi([gate["struct"], up["struct"]], x_in["gate"], 1, ys_gu, ws)
+        else:
+            call(gate, x_in["gate"])
+            call(up, x_in["gate"])
+        call(down, x_in["down"])
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
     K = args.steps
-    n_launch = 3 * K
+    per_step = 2 if grouped else 3              # product launches per step
+    n_launch = per_step * K
     starts, stops = ev.create(n_launch), ev.create(n_launch)
     if args.eager:
         lq.lq_profile_events(starts, stops)
@@ -393,15 +408,17 @@ def run_decode(args, torch, lq, ev):
     ms_step = (t1 - t0) * 1e3 / K
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
     kern_ms = sum(durs) / len(durs)
-    bytes_per_launch = step_bytes / 3.0          # N*L/8 of the three layers, averaged
+    # N*L/8 of the layers a product launch reads, averaged over the launches
+    bytes_per_launch = step_bytes / per_step
     achieved = bytes_per_launch / (kern_ms * 1e-3) / 1e9
     per_proj = {}
-    for j, (pname, s) in enumerate(specs):
-        d = durs[j::3]
+    names = ["gate+up", "down"] if grouped else [p for p, _ in specs]
+    for j, pname in enumerate(names):
+        d = durs[j::per_step]
         per_proj[pname] = round(sum(d) / len(d) * 1e3, 3)
     return dict(ms_step=ms_step, gbs=gbs, kern_ms=kern_ms, achieved=achieved,
                 step_bytes=step_bytes, bytes_per_launch=bytes_per_launch, per_proj_us=per_proj,
-                n_sets=n_sets, timing=timing)
+                n_sets=n_sets, timing=timing, grouped=grouped)
 
 
 def build_prefill_case(torch, lq, algo=None):
@@ -618,7 +635,10 @@ def main():
         "config": {
             "workload": "Llama-3-8B MLP decode at 2.4 bit (d=10, D=24): gate and up "
                         "K=4096->N=14336, down K=14336->N=4096, batch 1, bf16 activations, "
-                        "Hadamard block 1024; one step = the three lq_linear calls",
+                        "Hadamard block 1024; one step = the three projections"
+                        + (" (gate and up, which read the same x, in one lq_linear_multi "
+                           "call; down in one lq_linear call)" if dec["grouped"]
+                           else " as three lq_linear calls"),
             "global_batch": 1,
             "weight_sets": dec["n_sets"],
             "packed_bytes_per_step": dec["step_bytes"],

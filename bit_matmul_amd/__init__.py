@@ -14,7 +14,7 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import (LQ_ENCODE_MAX_D, LQ_ENCODE_MAX_SMALL_D, LQ_ALGO_AUTO, LQ_ALGO_FUSED, LQ_ALGO_FUSED_LOCAL, LQ_ALGO_MFMA_LARGE, LQ_ALGO_WSPACE, LQ_ALGO_FUSED_SPLIT,
+from ._lib import (LQ_MULTI_MAX, LQ_ENCODE_MAX_D, LQ_ENCODE_MAX_SMALL_D, LQ_ALGO_AUTO, LQ_ALGO_FUSED, LQ_ALGO_FUSED_LOCAL, LQ_ALGO_MFMA_LARGE, LQ_ALGO_WSPACE, LQ_ALGO_FUSED_SPLIT,
                    LQ_ALGO_MFMA_SMALL,
                    LQ_ALGO_VALU, LQ_BF16, LQ_F32, LQ_MAX_D, LQ_MAX_HB, LQ_WS_CONTROL_BYTES,
                    LQ_WS_ERROR_WORD, LQError, LQLayer)
@@ -23,7 +23,8 @@ __all__ = [
     "lq_version", "lq_packed_size", "lq_pack_signs", "lq_unpack_signs", "lq_hadamard_scale",
     "lq_lift_activations", "lq_sign_gemm_workspace_size", "lq_sign_gemm", "lq_sign_gemm_ex",
     "lq_linear_workspace_size", "lq_linear", "lq_linear_workspace_size_ex", "lq_linear_ex",
-    "lq_linear_algo", "lq_encode", "lq_train_m_step_workspace_size", "lq_train_m_step",
+    "lq_linear_algo", "lq_linear_multi_workspace_size", "lq_linear_multi", "LQ_MULTI_MAX",
+    "lq_encode", "lq_train_m_step_workspace_size", "lq_train_m_step",
     "LQ_ENCODE_MAX_D", "LQ_ENCODE_MAX_SMALL_D",
     "lq_workspace_init", "lq_profile_events", "layer_struct", "LQError", "LQLayer",
     "LQ_F32", "LQ_BF16", "LQ_ALGO_AUTO", "LQ_ALGO_VALU", "LQ_ALGO_MFMA_SMALL",
@@ -164,6 +165,40 @@ def lq_linear_ex(layer: LQLayer, x, B, y, algo, ws=None, stream=None) -> None:
     _check(_lib.LIB.lq_linear_ex(ctypes.byref(layer), _dev(x, "x"), _dtype(x, "x"), B, _dev(y, "y"),
                                  _dtype(y, "y"), algo, ws_ptr, ws_bytes, _stream(stream)),
            "lq_linear_ex")
+
+
+def _layer_array(layers):
+    arr = (LQLayer * len(layers))()
+    for i, l in enumerate(layers):
+        arr[i] = l
+    return arr
+
+
+def lq_linear_multi_workspace_size(layers, B, xtype) -> int:
+    """Workspace bytes of lq_linear_multi for these layers (same K)."""
+    out = ctypes.c_size_t()
+    xt = _DTYPES[xtype] if isinstance(xtype, torch.dtype) else int(xtype)
+    arr = _layer_array(layers)
+    _check(_lib.LIB.lq_linear_multi_workspace_size(arr, len(layers), B, xt, ctypes.byref(out)),
+           "lq_linear_multi_workspace_size")
+    return out.value
+
+
+def lq_linear_multi(layers, x, B, ys, ws=None, stream=None) -> None:
+    """ys[i] = lq_linear(layers[i], x) for every layer (same K, same x, one
+    y dtype): one preparation and one product launch where that applies."""
+    if len(ys) != len(layers):
+        raise ValueError("one output per layer")
+    ws_ptr = _opt(ws, "ws")
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    ydt = _dtype(ys[0], "y")
+    for y in ys:
+        if _dtype(y, "y") != ydt:
+            raise ValueError("every output must have the same dtype")
+    ptrs = (ctypes.c_void_p * len(ys))(*[_dev(y, "y") for y in ys])
+    arr = _layer_array(layers)
+    _check(_lib.LIB.lq_linear_multi(arr, len(layers), _dev(x, "x"), _dtype(x, "x"), B, ptrs, ydt,
+                                    ws_ptr, ws_bytes, _stream(stream)), "lq_linear_multi")
 
 
 def lq_encode(w, nblocks, d, D, M, signs, dist2=None, stream=None) -> None:

@@ -17,6 +17,7 @@ LQ_WS_CONTROL_BYTES = 20992
 LQ_WS_ERROR_WORD = 96
 LQ_ENCODE_MAX_D = 24
 LQ_ENCODE_MAX_SMALL_D = 16
+LQ_MULTI_MAX = 4
 
 # Every symbol include/lq.h declares.
 EXPORTS = [
@@ -25,7 +26,8 @@ EXPORTS = [
     "lq_sign_gemm_workspace_size", "lq_sign_gemm", "lq_sign_gemm_ex",
     "lq_linear_workspace_size", "lq_linear", "lq_linear_workspace_size_ex", "lq_linear_ex",
     "lq_linear_algo", "lq_workspace_init", "lq_profile_events", "lq_encode",
-    "lq_train_m_step_workspace_size", "lq_train_m_step",
+    "lq_train_m_step_workspace_size", "lq_train_m_step", "lq_linear_multi_workspace_size",
+    "lq_linear_multi",
 ]
 
 
@@ -74,6 +76,10 @@ def _load():
         "lq_train_m_step_workspace_size": (c_int, [i64, c_int32, c_int32, POINTER(sz)]),
         "lq_train_m_step": (c_int, [vp, vp, i64, c_int32, c_int32, c_float, vp, vp, sz, vp]),
         "lq_linear_ex": (c_int, [POINTER(LQLayer), vp, c_int, i64, vp, c_int, c_int, vp, sz, vp]),
+        "lq_linear_multi_workspace_size": (c_int, [POINTER(LQLayer), c_int32, i64, c_int,
+                                                   POINTER(sz)]),
+        "lq_linear_multi": (c_int, [POINTER(LQLayer), c_int32, vp, c_int, i64, POINTER(vp), c_int,
+                                    vp, sz, vp]),
         "lq_workspace_init": (c_int, [vp, sz, vp]),
         "lq_profile_events": (c_int, [POINTER(vp), POINTER(vp), i32]),
     }

@@ -96,6 +96,7 @@ hipError_t profiled(hipStream_t stream, Fn fn) {
 
 static_assert(lq::kControlBytes == LQ_WS_CONTROL_BYTES, "control area size");
 static_assert(lq::kFusedErrorWord == LQ_WS_ERROR_WORD, "error word");
+static_assert(lq::kMultiMax == LQ_MULTI_MAX, "layers per grouped call");
 
 // Compute units of the current device (0 when there is none), cached.
 int device_cus() {
@@ -349,6 +350,56 @@ lq_status check_layer(const lq_layer* layer, int64_t* L) {
   return LQ_OK;
 }
 
+// lq_linear_multi's plan: every layer checked and planned as lq_linear would;
+// grouped (one preparation and one product launch) when every layer runs the
+// small-batch matrix-core path with plans that can share one launch.
+struct MultiPlan {
+  int n;                    // layers with work (N > 0)
+  int idx[LQ_MULTI_MAX];    // their indices
+  Exec e[LQ_MULTI_MAX];
+  int64_t L[LQ_MULTI_MAX];
+  bool grouped;
+  size_t off_aop[LQ_MULTI_MAX];
+  size_t total;
+};
+
+lq_status plan_multi(const lq_layer* layers, int32_t n, int64_t B, lq_dtype xtype, MultiPlan* mp) {
+  if (layers == nullptr || n < 1 || n > LQ_MULTI_MAX || !valid_dtype(xtype) || B < 0)
+    return LQ_ERR_INVALID_ARG;
+  mp->n = 0;
+  mp->grouped = true;
+  mp->total = 0;
+  for (int i = 0; i < n; ++i) {
+    int64_t L = 0;
+    lq_status s = check_layer(&layers[i], &L);
+    if (s != LQ_OK) return s;
+    if (layers[i].K != layers[0].K) return LQ_ERR_INVALID_ARG;
+    s = check_sign_dims(B, layers[i].N, L);
+    if (s != LQ_OK) return s;
+    if (!mul_ok(B, layers[i].K, kMaxElems)) return LQ_ERR_UNSUPPORTED;
+    if (B == 0 || layers[i].N == 0) continue;
+    const int j = mp->n++;
+    mp->idx[j] = i;
+    mp->L[j] = L;
+    s = plan_exec(B, layers[i].N, L, layers[i].K, layers[i].d, layers[i].D, xtype, LQ_ALGO_AUTO,
+                  true, &mp->e[j]);
+    if (s != LQ_OK) return s;
+    mp->total = std::max(mp->total, mp->e[j].total);
+    if (mp->e[j].algo != LQ_ALGO_MFMA_SMALL || !lq::fp6_plans_match(mp->e[j].fp, mp->e[0].fp))
+      mp->grouped = false;
+  }
+  if (mp->n < 2) mp->grouped = false;
+  if (mp->grouped) {
+    size_t at = align_up(lq::kControlBytes);
+    for (int j = 0; j < mp->n; ++j) {
+      mp->off_aop[j] = at;
+      at += align_up(lq::operand_bytes(mp->L[j], mp->e[j].os));
+    }
+    mp->total = at;
+  }
+  return LQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -525,6 +576,59 @@ lq_status lq_linear_ex(const lq_layer* layer, const void* x, lq_dtype xtype, int
 lq_status lq_linear(const lq_layer* layer, const void* x, lq_dtype xtype, int64_t B, void* y,
                     lq_dtype ytype, void* ws, size_t ws_bytes, void* stream) {
   return lq_linear_ex(layer, x, xtype, B, y, ytype, LQ_ALGO_AUTO, ws, ws_bytes, stream);
+}
+
+lq_status lq_linear_multi_workspace_size(const lq_layer* layers, int32_t n, int64_t B,
+                                         lq_dtype xtype, size_t* bytes) {
+  if (bytes == nullptr) return LQ_ERR_INVALID_ARG;
+  MultiPlan mp;
+  const lq_status s = plan_multi(layers, n, B, xtype, &mp);
+  if (s != LQ_OK) return s;
+  *bytes = mp.total;
+  return LQ_OK;
+}
+
+lq_status lq_linear_multi(const lq_layer* layers, int32_t n, const void* x, lq_dtype xtype,
+                          int64_t B, void* const* ys, lq_dtype ytype, void* ws, size_t ws_bytes,
+                          void* stream) {
+  if (!valid_dtype(ytype) || ys == nullptr) return LQ_ERR_INVALID_ARG;
+  MultiPlan mp;
+  lq_status s = plan_multi(layers, n, B, xtype, &mp);
+  if (s != LQ_OK) return s;
+  if (mp.n == 0) return LQ_OK;
+  if (!aligned16(x)) return LQ_ERR_INVALID_ARG;
+  for (int j = 0; j < mp.n; ++j) {
+    const lq_layer& l = layers[mp.idx[j]];
+    if (!aligned16(ys[mp.idx[j]]) || !aligned16(l.packed) || !aligned16(l.M) ||
+        !aligned16(l.c) || !aligned16(l.row_scale))
+      return LQ_ERR_INVALID_ARG;
+  }
+  s = check_ws(ws, ws_bytes, mp.total);
+  if (s != LQ_OK) return s;
+  const hipStream_t st = (hipStream_t)stream;
+  if (!mp.grouped) {
+    for (int j = 0; j < mp.n; ++j) {
+      const lq_layer& l = layers[mp.idx[j]];
+      s = run_exec(mp.e[j], l.packed, x, xtype, B, l.N, mp.L[j], l.row_scale, ys[mp.idx[j]],
+                   ytype, ws, st, &l);
+      if (s != LQ_OK) return s;
+    }
+    return LQ_OK;
+  }
+  uint8_t* base = reinterpret_cast<uint8_t*>(ws);
+  lq::PrepLayerDesc pd[LQ_MULTI_MAX];
+  lq::SignLayerDesc sd[LQ_MULTI_MAX];
+  for (int j = 0; j < mp.n; ++j) {
+    const lq_layer& l = layers[mp.idx[j]];
+    uint8_t* aop = base + mp.off_aop[j];
+    pd[j] = lq::PrepLayerDesc{l.d, l.D, l.hb, mp.L[j], l.c, l.M, aop};
+    sd[j] = lq::SignLayerDesc{l.packed, mp.e[j].g, aop, l.row_scale, ys[mp.idx[j]], mp.e[j].fp};
+  }
+  s = hip_status(lq::launch_prep_multi(x, xtype == LQ_BF16, B, layers[0].K, mp.n, pd, mp.e[0].os, st));
+  if (s != LQ_OK) return s;
+  return hip_status(profiled(st, [&] {
+    return lq::launch_sign_fp6_multi(mp.n, sd, mp.e[0].os, B, ytype == LQ_BF16, st);
+  }));
 }
 
 lq_status lq_workspace_init(void* ws, size_t ws_bytes, void* stream) {

@@ -290,6 +290,35 @@ struct ValuPlan {
 };
 ValuPlan plan_valu(int64_t B, const PackedGeom& g);
 
+// Several layers that read the same x (same K) in one preparation launch and
+// one product launch: at most this many.
+constexpr int kMultiMax = 4;
+// One layer of a preparation launch (kernel argument, by value).
+struct PrepLayer {
+  const float* c;
+  const float* M;
+  uint8_t* aop;
+  int d, D, lhb, L;
+  float norm;
+  int tile_begin;   // its first workgroup along the grid's x dimension
+};
+struct PrepTable {
+  int n;
+  PrepLayer l[kMultiMax];
+};
+// A layer of launch_prep_multi, as the caller describes it.
+struct PrepLayerDesc {
+  int d, D, hb;
+  int64_t L;
+  const float* c;
+  const float* M;
+  uint8_t* aop;     // its operand records (operand_bytes(L, s))
+};
+// The FP6 operands of n <= kMultiMax layers for the same x (bf16 or fp32).
+hipError_t launch_prep_multi(const void* x, bool x_bf16, int64_t B, int64_t K, int n,
+                             const PrepLayerDesc* layers, const OperandShape& s,
+                             hipStream_t stream);
+
 // xkind: 0 x fp32, 1 x bf16 (whiten + lift), 2 z fp32, 3 z bf16 (as given).
 // op == nullptr: write fp32 z to zf32 (B x L); else the FP6 operand.
 hipError_t launch_prep(const void* x, int xkind, int64_t B, int64_t K, int d, int D, int hb,
@@ -299,6 +328,36 @@ hipError_t launch_prep(const void* x, int xkind, int64_t B, int64_t K, int d, in
 hipError_t launch_sign_fp6(const uint8_t* packed, const PackedGeom& g, const OperandPlan& op,
                            int64_t B, const float* row_scale, void* y, bool y_bf16,
                            const Fp6Plan& plan, hipStream_t stream);
+// One layer of a small-batch product launch (kernel argument, by value).
+struct SignLayer {
+  const uint8_t* packed;
+  const uint8_t* aop;
+  const float* row_scale;
+  void* y;
+  int64_t panel_bytes;
+  int panels, full_tiles, tail_bytes, nch, N;
+  int group_begin;   // its first workgroup
+};
+struct SignTable {
+  int n;
+  SignLayer l[kMultiMax];
+};
+// A layer of launch_sign_fp6_multi: its geometry, operand, outputs and the
+// plan a call of its own would use.
+struct SignLayerDesc {
+  const uint8_t* packed;
+  PackedGeom g;
+  const uint8_t* aop;
+  const float* row_scale;
+  void* y;
+  Fp6Plan plan;
+};
+// Whether two layers' plans can share one launch (same kernel instance and
+// chunk size): then every workgroup computes exactly what it would in a call
+// of its own.
+bool fp6_plans_match(const Fp6Plan& a, const Fp6Plan& b);
+hipError_t launch_sign_fp6_multi(int n, const SignLayerDesc* layers, const OperandShape& s,
+                                 int64_t B, bool y_bf16, hipStream_t stream);
 hipError_t launch_sign_valu(const uint8_t* packed, const PackedGeom& g, const void* z,
                             bool z_bf16, int64_t B, const float* row_scale, void* y, bool y_bf16,
                             const ValuPlan& plan, float* partial, unsigned* tickets,

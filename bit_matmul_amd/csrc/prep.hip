@@ -19,7 +19,8 @@
 //     with the packed conversion instructions. The record also gets the sum
 //     over the tile's plane-0..2 columns of the values the terms represent.
 // Workgroup (0, 0) also clears the split-K tickets of the VALU product that
-// follows on the same stream.
+// follows on the same stream. One launch can prepare several layers that read
+// the same x (their tiles one after another along the grid's x dimension).
 #include "lq_prep.h"
 
 namespace lq {
@@ -33,19 +34,28 @@ constexpr int kThreads = 512;
 // Index arithmetic is 32-bit (K, L < 2^31 is checked on the host).
 template <int kMode, int kXKind>
 __global__ __launch_bounds__(kThreads) void prep_kernel(
-    const void* __restrict__ x, int B, int K, int d, int D, int lhb, float norm,
-    const float* __restrict__ c, const float* __restrict__ M, int L,
+    const void* __restrict__ x, int B, int K, PrepTable tab,
     float* __restrict__ zf32,                      // kMode 0: B x L
-    uint8_t* __restrict__ aop, int nt, int ncv, int rec,
-    unsigned* __restrict__ tickets, int n_tickets) {
+    int nt, int ncv, int rec, unsigned* __restrict__ tickets, int n_tickets) {
   __shared__ __align__(16) float xs[kSpanMax];
   __shared__ __align__(16) float zt[kTileCols];   // kMode 1: fp6_slot layout, plane factors applied
   __shared__ float Ms[64 * 64];
-  const int q = blockIdx.x;
+  // this workgroup's layer (a wave-uniform choice among at most kMultiMax)
+  int li = 0;
+#pragma unroll
+  for (int i = 1; i < kMultiMax; ++i)
+    if (i < tab.n && (int)blockIdx.x >= tab.l[i].tile_begin) li = i;
+  const PrepLayer& ly = tab.l[li];
+  const int d = ly.d, D = ly.D, lhb = ly.lhb, L = ly.L;
+  const float norm = ly.norm;
+  const float* __restrict__ c = ly.c;
+  const float* __restrict__ M = ly.M;
+  uint8_t* __restrict__ aop = ly.aop;
+  const int q = (int)blockIdx.x - ly.tile_begin;
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
 
-  if (q == 0 && b == 0)
+  if (blockIdx.x == 0 && b == 0)
     for (int i = tid; i < n_tickets; i += blockDim.x) tickets[i] = 0u;
 
   const int c_lo = q * kTileCols;
@@ -162,19 +172,49 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
 }
 
 template <int kMode, int kXKind>
-hipError_t launch_prep_t(const void* x, int64_t B, int64_t K, int d, int D, int hb, const float* c,
-                         const float* M, int64_t L, float* zf32, const OperandPlan* op,
-                         unsigned* tickets, int n_tickets, hipStream_t stream) {
+hipError_t launch_prep_t(const void* x, int64_t B, int64_t K, const PrepTable& tab, int tiles,
+                         float* zf32, const OperandShape* s, unsigned* tickets, int n_tickets,
+                         hipStream_t stream) {
+  const int nt = s ? s->nt : 0, ncv = s ? s->ncv : 0, rec = s ? s->rec : 0;
+  hipLaunchKernelGGL((prep_kernel<kMode, kXKind>), dim3((unsigned)tiles, (unsigned)B), dim3(kThreads),
+                     0, stream, x, (int)B, (int)K, tab, zf32, nt, ncv, rec, tickets, n_tickets);
+  return hipGetLastError();
+}
+
+PrepLayer prep_layer(int d, int D, int hb, const float* c, const float* M, int64_t L, uint8_t* aop,
+                     int tile_begin) {
+  PrepLayer l;
   int k = 0;
   while ((1 << k) < hb) ++k;
-  const float norm = (k % 2 == 0) ? ldexpf(1.0f, -k / 2) : (float)(1.0 / sqrt((double)hb));
-  const int ext = (int)((L + kTileCols - 1) / kTileCols);
-  uint8_t* aop = op ? op->aop : nullptr;
-  const int nt = op ? op->s.nt : 0, ncv = op ? op->s.ncv : 0, rec = op ? op->s.rec : 0;
-  hipLaunchKernelGGL((prep_kernel<kMode, kXKind>), dim3((unsigned)ext, (unsigned)B), dim3(kThreads), 0,
-                     stream, x, (int)B, (int)K, d, D, k, norm, c, M, (int)L, zf32, aop, nt, ncv,
-                     rec, tickets, n_tickets);
-  return hipGetLastError();
+  l.norm = (k % 2 == 0) ? ldexpf(1.0f, -k / 2) : (float)(1.0 / sqrt((double)hb));
+  l.d = d;
+  l.D = D;
+  l.lhb = k;
+  l.L = (int)L;
+  l.c = c;
+  l.M = M;
+  l.aop = aop;
+  l.tile_begin = tile_begin;
+  return l;
+}
+
+hipError_t launch_prep_table(const void* x, int xkind, int64_t B, int64_t K, const PrepTable& tab,
+                             int tiles, float* zf32, const OperandShape* s, unsigned* tickets,
+                             int n_tickets, hipStream_t stream) {
+  if (s == nullptr) {
+    switch (xkind) {
+      case 0: return launch_prep_t<0, 0>(x, B, K, tab, tiles, zf32, s, tickets, n_tickets, stream);
+      case 1: return launch_prep_t<0, 1>(x, B, K, tab, tiles, zf32, s, tickets, n_tickets, stream);
+      case 2: return launch_prep_t<0, 2>(x, B, K, tab, tiles, zf32, s, tickets, n_tickets, stream);
+      default: return launch_prep_t<0, 3>(x, B, K, tab, tiles, zf32, s, tickets, n_tickets, stream);
+    }
+  }
+  switch (xkind) {
+    case 0: return launch_prep_t<1, 0>(x, B, K, tab, tiles, zf32, s, tickets, n_tickets, stream);
+    case 1: return launch_prep_t<1, 1>(x, B, K, tab, tiles, zf32, s, tickets, n_tickets, stream);
+    case 2: return launch_prep_t<1, 2>(x, B, K, tab, tiles, zf32, s, tickets, n_tickets, stream);
+    default: return launch_prep_t<1, 3>(x, B, K, tab, tiles, zf32, s, tickets, n_tickets, stream);
+  }
 }
 
 }  // namespace
@@ -201,20 +241,30 @@ hipError_t launch_prep(const void* x, int xkind, int64_t B, int64_t K, int d, in
                        const OperandPlan* op, unsigned* tickets, int n_tickets,
                        hipStream_t stream) {
   (void)hipGetLastError();   // clear a stale error of an earlier runtime call
-  if (op == nullptr) {
-    switch (xkind) {
-      case 0: return launch_prep_t<0, 0>(x, B, K, d, D, hb, c, M, L, zf32, op, tickets, n_tickets, stream);
-      case 1: return launch_prep_t<0, 1>(x, B, K, d, D, hb, c, M, L, zf32, op, tickets, n_tickets, stream);
-      case 2: return launch_prep_t<0, 2>(x, B, K, d, D, hb, c, M, L, zf32, op, tickets, n_tickets, stream);
-      default: return launch_prep_t<0, 3>(x, B, K, d, D, hb, c, M, L, zf32, op, tickets, n_tickets, stream);
-    }
+  PrepTable tab;
+  tab.n = 1;
+  tab.l[0] = prep_layer(d, D, hb, c, M, L, op ? op->aop : nullptr, 0);
+  for (int i = 1; i < kMultiMax; ++i) tab.l[i] = tab.l[0];
+  const int ext = (int)((L + kTileCols - 1) / kTileCols);
+  return launch_prep_table(x, xkind, B, K, tab, ext, zf32, op ? &op->s : nullptr, tickets,
+                           n_tickets, stream);
+}
+
+hipError_t launch_prep_multi(const void* x, bool x_bf16, int64_t B, int64_t K, int n,
+                             const PrepLayerDesc* layers, const OperandShape& s,
+                             hipStream_t stream) {
+  (void)hipGetLastError();
+  if (n < 1 || n > kMultiMax) return hipErrorInvalidValue;
+  PrepTable tab;
+  tab.n = n;
+  int tiles = 0;
+  for (int i = 0; i < n; ++i) {
+    const PrepLayerDesc& l = layers[i];
+    tab.l[i] = prep_layer(l.d, l.D, l.hb, l.c, l.M, l.L, l.aop, tiles);
+    tiles += (int)((l.L + kTileCols - 1) / kTileCols);
   }
-  switch (xkind) {
-    case 0: return launch_prep_t<1, 0>(x, B, K, d, D, hb, c, M, L, zf32, op, tickets, n_tickets, stream);
-    case 1: return launch_prep_t<1, 1>(x, B, K, d, D, hb, c, M, L, zf32, op, tickets, n_tickets, stream);
-    case 2: return launch_prep_t<1, 2>(x, B, K, d, D, hb, c, M, L, zf32, op, tickets, n_tickets, stream);
-    default: return launch_prep_t<1, 3>(x, B, K, d, D, hb, c, M, L, zf32, op, tickets, n_tickets, stream);
-  }
+  for (int i = n; i < kMultiMax; ++i) tab.l[i] = tab.l[n - 1];
+  return launch_prep_table(x, x_bf16 ? 1 : 0, B, K, tab, tiles, nullptr, &s, nullptr, 0, stream);
 }
 
 }  // namespace lq

@@ -44,16 +44,27 @@ namespace lq {
 namespace {
 
 template <int P, int CS, int W, int TPC>
-__global__ __launch_bounds__(64 * (W + 1)) void sign_fp6_kernel(
-    const uint8_t* __restrict__ packed, int panels, int64_t panel_bytes, int full_tiles,
-    int tail_bytes, const uint8_t* __restrict__ aop, int rec, int ncv, int B, int nch,
-    int chunk_bytes, const float* __restrict__ row_scale, void* __restrict__ y, int y_bf16, int N) {
+__global__ __launch_bounds__(64 * (W + 1)) void sign_fp6_kernel(SignTable tab, int rec, int ncv,
+                                                                int B, int chunk_bytes, int y_bf16) {
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr int CT = W * TPC;                       // full tiles per chunk
+  // this workgroup's layer (a wave-uniform choice among at most kMultiMax)
+  int li = 0;
+#pragma unroll
+  for (int i = 1; i < kMultiMax; ++i)
+    if (i < tab.n && (int)blockIdx.x >= tab.l[i].group_begin) li = i;
+  const SignLayer& ly = tab.l[li];
+  const uint8_t* __restrict__ packed = ly.packed;
+  const uint8_t* __restrict__ aop = ly.aop;
+  const float* __restrict__ row_scale = ly.row_scale;
+  void* __restrict__ y = ly.y;
+  const int64_t panel_bytes = ly.panel_bytes;
+  const int panels = ly.panels, full_tiles = ly.full_tiles, tail_bytes = ly.tail_bytes;
+  const int nch = ly.nch, N = ly.N;
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int g = lane >> 4, r = lane & 15;
   const bool loader = wave == W;
-  const int pbase = blockIdx.x * P;
+  const int pbase = ((int)blockIdx.x - ly.group_begin) * P;
 
   // This lane's MFMA column in each column set; unused columns read the
   // set's last column (their products are never read).
@@ -285,10 +296,9 @@ __global__ __launch_bounds__(64 * (W + 1)) void sign_fp6_kernel(
 }
 
 template <int P, int CS, int W, int TPC>
-hipError_t launch_fp6_t(const uint8_t* packed, const PackedGeom& g, const OperandPlan& op,
-                        int64_t B, const float* row_scale, void* y, bool y_bf16,
-                        const Fp6Plan& plan, hipStream_t stream) {
-  const dim3 grid((unsigned)plan.groups);
+hipError_t launch_fp6_t(const SignTable& tab, int groups, const OperandShape& s, int64_t B,
+                        bool y_bf16, const Fp6Plan& plan, hipStream_t stream) {
+  const dim3 grid((unsigned)groups);
   const dim3 block(64 * (W + 1));
   if (plan.lds_bytes > 160 * 1024) return hipErrorInvalidValue;   // a compute unit's LDS
   // Dynamic LDS beyond the default 64 KB limit has to be allowed per kernel.
@@ -300,10 +310,8 @@ hipError_t launch_fp6_t(const uint8_t* packed, const PackedGeom& g, const Operan
     if (e != hipSuccess) return e;
     allowed = plan.lds_bytes;
   }
-  return launch_timed(sign_fp6_kernel<P, CS, W, TPC>, grid, block, plan.lds_bytes, stream,
-                      packed, (int)g.panels, g.panel_bytes, g.full_tiles, g.tail_bytes, op.aop,
-                      op.s.rec, op.s.ncv, (int)B, plan.nch, plan.chunk_bytes, row_scale, y,
-                      y_bf16 ? 1 : 0, (int)g.N);
+  return launch_timed(sign_fp6_kernel<P, CS, W, TPC>, grid, block, plan.lds_bytes, stream, tab,
+                      s.rec, s.ncv, (int)B, plan.chunk_bytes, y_bf16 ? 1 : 0);
 }
 
 // Compute wavefronts and tiles per wavefront per chunk for each column-set
@@ -340,20 +348,71 @@ Fp6Plan plan_fp6(int64_t B, const PackedGeom& g, const OperandShape& s) {
   return p;
 }
 
-hipError_t launch_sign_fp6(const uint8_t* packed, const PackedGeom& g, const OperandPlan& op,
-                           int64_t B, const float* row_scale, void* y, bool y_bf16,
-                           const Fp6Plan& plan, hipStream_t stream) {
+namespace {
+
+SignLayer sign_layer(const uint8_t* packed, const PackedGeom& g, const uint8_t* aop,
+                     const float* row_scale, void* y, int nch, int group_begin) {
+  SignLayer l;
+  l.packed = packed;
+  l.aop = aop;
+  l.row_scale = row_scale;
+  l.y = y;
+  l.panel_bytes = g.panel_bytes;
+  l.panels = (int)g.panels;
+  l.full_tiles = (int)g.full_tiles;
+  l.tail_bytes = (int)g.tail_bytes;
+  l.nch = nch;
+  l.N = (int)g.N;
+  l.group_begin = group_begin;
+  return l;
+}
+
+hipError_t launch_fp6_table(const SignTable& tab, int groups, const OperandShape& s, int64_t B,
+                            bool y_bf16, const Fp6Plan& plan, hipStream_t stream) {
   (void)hipGetLastError();   // clear a stale error of an earlier runtime call
 #define LQ_FP6_CASE(P_, CS_, TPC_)                                                          \
-  if (plan.p == P_ && op.s.cs == CS_ && plan.tpc == TPC_ && plan.w == waves_for(P_, CS_))   \
-    return launch_fp6_t<P_, CS_, waves_for(P_, CS_), TPC_>(packed, g, op, B, row_scale, y,  \
-                                                           y_bf16, plan, stream);
+  if (plan.p == P_ && s.cs == CS_ && plan.tpc == TPC_ && plan.w == waves_for(P_, CS_))      \
+    return launch_fp6_t<P_, CS_, waves_for(P_, CS_), TPC_>(tab, groups, s, B, y_bf16, plan, stream);
   LQ_FP6_CASE(1, 1, 3) LQ_FP6_CASE(2, 1, 3) LQ_FP6_CASE(4, 1, 3)
   LQ_FP6_CASE(1, 1, 1) LQ_FP6_CASE(2, 1, 1) LQ_FP6_CASE(4, 1, 1) LQ_FP6_CASE(8, 1, 1)
   LQ_FP6_CASE(1, 2, 1) LQ_FP6_CASE(2, 2, 1) LQ_FP6_CASE(4, 2, 1) LQ_FP6_CASE(8, 2, 1)
   LQ_FP6_CASE(1, 3, 1) LQ_FP6_CASE(2, 3, 1) LQ_FP6_CASE(4, 3, 1)
 #undef LQ_FP6_CASE
   return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_sign_fp6(const uint8_t* packed, const PackedGeom& g, const OperandPlan& op,
+                           int64_t B, const float* row_scale, void* y, bool y_bf16,
+                           const Fp6Plan& plan, hipStream_t stream) {
+  SignTable tab;
+  tab.n = 1;
+  tab.l[0] = sign_layer(packed, g, op.aop, row_scale, y, plan.nch, 0);
+  for (int i = 1; i < kMultiMax; ++i) tab.l[i] = tab.l[0];
+  return launch_fp6_table(tab, plan.groups, op.s, B, y_bf16, plan, stream);
+}
+
+bool fp6_plans_match(const Fp6Plan& a, const Fp6Plan& b) {
+  return a.p == b.p && a.w == b.w && a.tpc == b.tpc && a.chunk_bytes == b.chunk_bytes;
+}
+
+hipError_t launch_sign_fp6_multi(int n, const SignLayerDesc* layers, const OperandShape& s,
+                                 int64_t B, bool y_bf16, hipStream_t stream) {
+  if (n < 1 || n > kMultiMax) return hipErrorInvalidValue;
+  SignTable tab;
+  tab.n = n;
+  Fp6Plan plan = layers[0].plan;
+  int groups = 0;
+  for (int i = 0; i < n; ++i) {
+    const SignLayerDesc& l = layers[i];
+    if (!fp6_plans_match(l.plan, plan)) return hipErrorInvalidValue;
+    plan.lds_bytes = std::max(plan.lds_bytes, l.plan.lds_bytes);
+    tab.l[i] = sign_layer(l.packed, l.g, l.aop, l.row_scale, l.y, l.plan.nch, groups);
+    groups += l.plan.groups;
+  }
+  for (int i = n; i < kMultiMax; ++i) tab.l[i] = tab.l[n - 1];
+  return launch_fp6_table(tab, groups, s, B, y_bf16, plan, stream);
 }
 
 }  // namespace lq

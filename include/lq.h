@@ -274,6 +274,28 @@ lq_status lq_linear_ex(const lq_layer* layer, const void* x, lq_dtype xtype, int
                        lq_dtype ytype, lq_algo algo, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Several layers on the same input (as the gate and up projections of a
+ * transformer MLP): ys[i] = lq_linear(&layers[i], x) for i < n, with
+ * 1 <= n <= LQ_MULTI_MAX and every layer of the same K (d, D, hb, M, c and N
+ * may differ). Each output is bit-for-bit what lq_linear writes. Where
+ * lq_linear would run the small-batch matrix-core path (MFMA_SMALL) for every
+ * layer with the same product plan (B <= 16, bf16 x; layers of the same
+ * shape), the n operands come from one preparation launch and the n products
+ * from one product launch, whose workgroups are those of the n single calls;
+ * otherwise the layers run one after another as n lq_linear calls.
+ * ys: host array of n device pointers (B x N_i in ytype each).
+ * ws: device workspace of at least lq_linear_multi_workspace_size bytes.
+ * Errors: as lq_linear, and INVALID_ARG for NULL layers or ys, n outside
+ * [1, LQ_MULTI_MAX] or layers of different K.
+ */
+#define LQ_MULTI_MAX 4
+lq_status lq_linear_multi_workspace_size(const lq_layer* layers, int32_t n, int64_t B,
+                                         lq_dtype xtype, size_t* bytes);
+lq_status lq_linear_multi(const lq_layer* layers, int32_t n, const void* x, lq_dtype xtype,
+                          int64_t B, void* const* ys, lq_dtype ytype, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/*
  * Prepare a workspace for first use: zero-fill its control area (the first
  * min(ws_bytes, LQ_WS_CONTROL_BYTES) bytes, with a kernel on `stream`).
  * Errors: INVALID_ARG for a NULL or unaligned ws with ws_bytes > 0.

@@ -276,3 +276,40 @@ def test_encode_and_train_validation():
     assert t(P, P, 1000, 3, 8, ctypes.c_float(0.1), None, None, 0, None) == LQ_ERR_WORKSPACE
     assert t(None, P, 1000, 3, 8, ctypes.c_float(0.1), None, P, need, None) == LQ_ERR_INVALID_ARG
     assert t(P, P, 0, 3, 8, ctypes.c_float(0.1), None, None, 0, None) == LQ_OK
+
+
+def multi_ws_size(layers, B, xt, n=None):
+    arr = (LQLayer * max(1, len(layers)))(*layers)
+    out = ctypes.c_size_t()
+    st = LIB.lq_linear_multi_workspace_size(arr, len(layers) if n is None else n, B, xt,
+                                            ctypes.byref(out))
+    return st, out.value
+
+
+def test_linear_multi_plan_and_validation():
+    gate = LQLayer(14336, 4096, 10, 24, 1024, 0, P, P, P, P)
+    down = LQLayer(4096, 14336, 10, 24, 1024, 0, P, P, P, P)
+    st, one = linear_ws_size(gate, 1, LQ_BF16, 0)
+    assert st == LQ_OK
+    # grouped (bf16 x, batch 1): the control area and one operand per layer
+    st, two = multi_ws_size([gate, gate], 1, LQ_BF16)
+    assert st == LQ_OK
+    assert two == _lib.LQ_WS_CONTROL_BYTES + 2 * (one - _lib.LQ_WS_CONTROL_BYTES)
+    st, four = multi_ws_size([gate] * 4, 1, LQ_BF16)
+    assert st == LQ_OK and four == _lib.LQ_WS_CONTROL_BYTES + 4 * (one - _lib.LQ_WS_CONTROL_BYTES)
+    # fp32 x and large batches run the layers one after another: one call's workspace
+    assert multi_ws_size([gate, gate], 1, LQ_F32) == linear_ws_size(gate, 1, LQ_F32, 0)
+    assert multi_ws_size([gate, gate], 64, LQ_BF16) == linear_ws_size(gate, 64, LQ_BF16, 0)
+    # one layer: as lq_linear
+    assert multi_ws_size([gate], 1, LQ_BF16) == (LQ_OK, one)
+    # errors: layers of different K, no layers, too many, bad layer, NULL outputs
+    assert multi_ws_size([gate, down], 1, LQ_BF16)[0] == LQ_ERR_INVALID_ARG
+    assert multi_ws_size([gate], 1, LQ_BF16, n=0)[0] == LQ_ERR_INVALID_ARG
+    assert multi_ws_size([gate] * 5, 1, LQ_BF16)[0] == LQ_ERR_INVALID_ARG
+    bad = LQLayer(14336, 4096, 10, 24, 1000, 0, P, P, P, P)              # hb not a power of 2
+    assert multi_ws_size([gate, bad], 1, LQ_BF16)[0] == LQ_ERR_INVALID_ARG
+    arr = (LQLayer * 2)(gate, gate)
+    assert LIB.lq_linear_multi(arr, 2, P, LQ_BF16, 1, None, LQ_BF16, P, two, None) == LQ_ERR_INVALID_ARG
+    ys = (ctypes.c_void_p * 2)(P, P)
+    assert LIB.lq_linear_multi(arr, 2, P, LQ_BF16, 1, ys, LQ_BF16, P, two - 16, None) == LQ_ERR_WORKSPACE
+    assert LIB.lq_linear_multi(arr, 2, P, LQ_BF16, 0, ys, LQ_BF16, None, 0, None) == LQ_OK   # B = 0
