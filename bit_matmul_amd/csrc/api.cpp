@@ -390,6 +390,15 @@ lq_status plan_multi(const lq_layer* layers, int32_t n, int64_t B, lq_dtype xtyp
   }
   if (mp->n < 2) mp->grouped = false;
   if (mp->grouped) {
+    // panels per workgroup chosen for all the layers' panels together
+    int64_t panels = 0;
+    for (int j = 0; j < mp->n; ++j) panels += mp->e[j].g.panels;
+    const int pp = lq::fp6_panels_per_group(panels, mp->e[0].os);
+    for (int j = 0; j < mp->n; ++j) mp->e[j].fp = lq::plan_fp6(B, mp->e[j].g, mp->e[j].os, pp);
+    for (int j = 1; j < mp->n; ++j)
+      if (!lq::fp6_plans_match(mp->e[j].fp, mp->e[0].fp)) mp->grouped = false;
+  }
+  if (mp->grouped) {
     size_t at = align_up(lq::kControlBytes);
     for (int j = 0; j < mp->n; ++j) {
       mp->off_aop[j] = at;

@@ -229,7 +229,9 @@ struct Fp6Plan {
   size_t lds_bytes; // dynamic LDS per workgroup
   int groups;       // workgroups
 };
-Fp6Plan plan_fp6(int64_t B, const PackedGeom& g, const OperandShape& s);
+// panels_per_group 0: chosen for this layer alone (fp6_panels_per_group).
+Fp6Plan plan_fp6(int64_t B, const PackedGeom& g, const OperandShape& s, int panels_per_group = 0);
+int fp6_panels_per_group(int64_t panels, const OperandShape& s);
 
 // Fused decode (whitening, lift, operand and product in one launch; the
 // operand record of each (tile, batch row) is produced by one workgroup and

@@ -324,16 +324,20 @@ constexpr int tiles_for(int p, int cs) { return cs == 1 && p <= 4 ? 3 : 1; }
 
 }  // namespace
 
-Fp6Plan plan_fp6(int64_t B, const PackedGeom& g, const OperandShape& s) {
-  (void)B;
-  Fp6Plan p;
+int fp6_panels_per_group(int64_t panels, const OperandShape& s) {
   // Panels per workgroup: enough workgroups to cover the 256 compute units,
   // as many panels as possible sharing each activation-operand read.
-  p.p = 1;
   for (int cand : {8, 4, 2}) {
     if (cand == 8 && s.cs >= 3) continue;      // register budget
-    if ((g.panels + cand - 1) / cand >= 200) { p.p = cand; break; }
+    if ((panels + cand - 1) / cand >= 200) return cand;
   }
+  return 1;
+}
+
+Fp6Plan plan_fp6(int64_t B, const PackedGeom& g, const OperandShape& s, int panels_per_group) {
+  (void)B;
+  Fp6Plan p;
+  p.p = panels_per_group > 0 ? panels_per_group : fp6_panels_per_group(g.panels, s);
   p.w = waves_for(p.p, s.cs);
   const int budget = 112 * 1024;   // two chunks of activation records
   p.tpc = 1;

@@ -277,12 +277,15 @@ lq_status lq_linear_ex(const lq_layer* layer, const void* x, lq_dtype xtype, int
  * Several layers on the same input (as the gate and up projections of a
  * transformer MLP): ys[i] = lq_linear(&layers[i], x) for i < n, with
  * 1 <= n <= LQ_MULTI_MAX and every layer of the same K (d, D, hb, M, c and N
- * may differ). Each output is bit-for-bit what lq_linear writes. Where
- * lq_linear would run the small-batch matrix-core path (MFMA_SMALL) for every
- * layer with the same product plan (B <= 16, bf16 x; layers of the same
- * shape), the n operands come from one preparation launch and the n products
- * from one product launch, whose workgroups are those of the n single calls;
- * otherwise the layers run one after another as n lq_linear calls.
+ * may differ). Where lq_linear would run the small-batch matrix-core path
+ * (MFMA_SMALL) for every layer (B <= 16, bf16 x) and the layers' product
+ * plans agree once the panels per workgroup are chosen for all their panels
+ * together (layers of the same shape do), the n operands come from one
+ * preparation launch and the n products from one product launch: the same
+ * arithmetic as lq_linear, its fp32 partial sums split among wavefronts as
+ * that choice of panels per workgroup gives (bit-for-bit lq_linear's result
+ * where the choice is the single call's, else within fp32 rounding of it).
+ * Otherwise the layers run one after another as n lq_linear calls.
  * ys: host array of n device pointers (B x N_i in ytype each).
  * ws: device workspace of at least lq_linear_multi_workspace_size bytes.
  * Errors: as lq_linear, and INVALID_ARG for NULL layers or ys, n outside
