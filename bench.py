@@ -246,10 +246,10 @@ def pmc_workload(torch, lq):
     dst.copy_(src)
     torch.cuda.synchronize()
     specs, layers, x_in, ys, ws, M = build_decode_case(torch, lq, 4)
-    for i in range(3):
-        for l in layers[i % len(layers)]:
-            x = x_in["down"] if l["name"] == "down" else x_in["gate"]
-            lq.lq_linear(l["struct"], x, 1, ys[l["name"]], ws)
+    for i in range(3):                           # the decode step as the benchmark runs it
+        gate, up, down = layers[i % len(layers)]
+        lq.lq_linear_multi([gate["struct"], up["struct"]], x_in["gate"], 1, [ys["gate"], ys["up"]], ws)
+        lq.lq_linear(down["struct"], x_in["down"], 1, ys["down"], ws)
     torch.cuda.synchronize()
     pf = build_prefill_case(torch, lq)
     lq.lq_linear(pf["struct"], pf["x"], pf["B"], pf["y"], pf["ws"])
