@@ -158,7 +158,8 @@ __global__ __launch_bounds__(64 * (W + 1)) void sign_fp6_kernel(SignTable tab, i
   // the compute wavefronts' waits on their slot loads never include the
   // loader's copies (which the compiler would otherwise have to assume may
   // still be in flight). The tail tile (its record and the P panels'
-  // row-major tail bytes) is multiplied by the loader at the end.
+  // row-major tail bytes) is multiplied by the loader while the compute
+  // wavefronts work on the first chunk.
   const bool tail = tail_bytes > 0;
   uint8_t* trec_lds = buf1 + chunk_bytes;
   uint8_t* tslot_lds = trec_lds + ((rec + 1023) / 1024) * 1024;
@@ -185,16 +186,9 @@ __global__ __launch_bounds__(64 * (W + 1)) void sign_fp6_kernel(SignTable tab, i
     wg_barrier();
     __builtin_amdgcn_s_waitcnt(0);                    // chunks 0, 1, the tail, the row scales
     wg_barrier();
-    for (int c = 0; c < nch; c += 2) {
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {                   // step c + k
-        __builtin_amdgcn_s_waitcnt(0);                // chunk c + k + 1 is in LDS
-        wg_barrier();
-        if (c + k + 2 < nch) dma_chunk(c + k + 2, k == 0 ? buf0 : buf1);
-        wg_barrier();
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
+    // The tail tile while the compute wavefronts multiply the first chunk
+    // (its record and slots landed with chunk 0): at the end it would delay
+    // the final reduction.
     if (tail) {
       // Slot (g, r) of the tail: bytes 16u + 4g .. + 3 of row r (zero past
       // the row's tail_bytes), as in load_tail_slot.
@@ -218,6 +212,16 @@ __global__ __launch_bounds__(64 * (W + 1)) void sign_fp6_kernel(SignTable tab, i
       }
       tile_mfma(trec_lds, TS);
     }
+    for (int c = 0; c < nch; c += 2) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {                   // step c + k
+        __builtin_amdgcn_s_waitcnt(0);                // chunk c + k + 1 is in LDS
+        wg_barrier();
+        if (c + k + 2 < nch) dma_chunk(c + k + 2, k == 0 ? buf0 : buf1);
+        wg_barrier();
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
   } else {
     wg_barrier();
     issue_A(0, A0);
@@ -325,13 +329,12 @@ constexpr int tiles_for(int p, int cs) { return cs == 1 && p <= 4 ? 3 : 1; }
 }  // namespace
 
 int fp6_panels_per_group(int64_t panels, const OperandShape& s) {
-  // Panels per workgroup: enough workgroups to cover the 256 compute units,
-  // as many panels as possible sharing each activation-operand read.
-  for (int cand : {8, 4, 2}) {
-    if (cand == 8 && s.cs >= 3) continue;      // register budget
-    if ((panels + cand - 1) / cand >= 200) return cand;
-  }
-  return 1;
+  // Panels per workgroup: the fewest that still give at most one workgroup
+  // per compute unit (so that none streams more than its share), which also
+  // lets as many panels as possible share each activation-operand read.
+  const int64_t cus = 256;
+  const int most = s.cs >= 3 ? 4 : 8;          // register budget
+  return (int)std::min<int64_t>(most, std::max<int64_t>(1, (panels + cus - 1) / cus));
 }
 
 Fp6Plan plan_fp6(int64_t B, const PackedGeom& g, const OperandShape& s, int panels_per_group) {
@@ -341,7 +344,8 @@ Fp6Plan plan_fp6(int64_t B, const PackedGeom& g, const OperandShape& s, int pane
   p.w = waves_for(p.p, s.cs);
   const int budget = 112 * 1024;   // two chunks of activation records
   p.tpc = 1;
-  if (tiles_for(p.p, s.cs) == 3 && 2 * p.w * 3 * s.rec + 2048 <= budget) p.tpc = 3;
+  const int tpc = tiles_for(p.p, s.cs);
+  if (tpc > 1 && 2 * p.w * tpc * s.rec + 2048 <= budget) p.tpc = tpc;
   const int ct = p.w * p.tpc;
   p.nch = (g.full_tiles + ct - 1) / ct;
   p.chunk_bytes = ((ct * s.rec + 1023) / 1024) * 1024;
@@ -377,10 +381,12 @@ hipError_t launch_fp6_table(const SignTable& tab, int groups, const OperandShape
 #define LQ_FP6_CASE(P_, CS_, TPC_)                                                          \
   if (plan.p == P_ && s.cs == CS_ && plan.tpc == TPC_ && plan.w == waves_for(P_, CS_))      \
     return launch_fp6_t<P_, CS_, waves_for(P_, CS_), TPC_>(tab, groups, s, B, y_bf16, plan, stream);
-  LQ_FP6_CASE(1, 1, 3) LQ_FP6_CASE(2, 1, 3) LQ_FP6_CASE(4, 1, 3)
-  LQ_FP6_CASE(1, 1, 1) LQ_FP6_CASE(2, 1, 1) LQ_FP6_CASE(4, 1, 1) LQ_FP6_CASE(8, 1, 1)
-  LQ_FP6_CASE(1, 2, 1) LQ_FP6_CASE(2, 2, 1) LQ_FP6_CASE(4, 2, 1) LQ_FP6_CASE(8, 2, 1)
-  LQ_FP6_CASE(1, 3, 1) LQ_FP6_CASE(2, 3, 1) LQ_FP6_CASE(4, 3, 1)
+  LQ_FP6_CASE(1, 1, 3) LQ_FP6_CASE(2, 1, 3) LQ_FP6_CASE(3, 1, 3) LQ_FP6_CASE(4, 1, 3)
+  LQ_FP6_CASE(1, 1, 1) LQ_FP6_CASE(2, 1, 1) LQ_FP6_CASE(3, 1, 1) LQ_FP6_CASE(4, 1, 1)
+  LQ_FP6_CASE(5, 1, 1) LQ_FP6_CASE(6, 1, 1) LQ_FP6_CASE(7, 1, 1) LQ_FP6_CASE(8, 1, 1)
+  LQ_FP6_CASE(1, 2, 1) LQ_FP6_CASE(2, 2, 1) LQ_FP6_CASE(3, 2, 1) LQ_FP6_CASE(4, 2, 1)
+  LQ_FP6_CASE(5, 2, 1) LQ_FP6_CASE(6, 2, 1) LQ_FP6_CASE(7, 2, 1) LQ_FP6_CASE(8, 2, 1)
+  LQ_FP6_CASE(1, 3, 1) LQ_FP6_CASE(2, 3, 1) LQ_FP6_CASE(3, 3, 1) LQ_FP6_CASE(4, 3, 1)
 #undef LQ_FP6_CASE
   return hipErrorInvalidValue;
 }

@@ -179,6 +179,23 @@ def test_sign_gemm(lq, algo, zdtype, N, L, B):
     assert err < sign_tol(algo, zdtype, B), err
 
 
+@pytest.mark.parametrize("P", [2, 3, 5, 6, 7, 8])
+@pytest.mark.parametrize("B", [1, 6, 13])
+def test_sign_gemm_panels_per_workgroup(lq, P, B):
+    """The small-batch product with P 16-row panels per workgroup (the plan
+    takes the fewest that give at most one workgroup per compute unit: N =
+    16 * 256 * P rows; at most 4 beyond 32 operand columns): two full tiles
+    and a tail."""
+    N, L = 16 * 256 * P, 1096
+    S, z, r = _sign_inputs(N, L, B, 7 * P + B, torch.bfloat16)
+    packed = dev(rp.refpack(S))
+    y = sign_gemm(lq, packed, dev(z, torch.bfloat16), B, N, L, dev(r), torch.float32,
+                  ALGOS["mfma_small"])
+    want = ref.sign_matmul(S, z, r)
+    err = rel_l2(host(y), want)
+    assert err < sign_tol("mfma_small", torch.bfloat16, B), err
+
+
 @pytest.mark.parametrize("algo", ["valu", "mfma_large"])
 @pytest.mark.parametrize("B", [17, 33, 64, 100])
 def test_sign_gemm_larger_batches(lq, algo, B):
