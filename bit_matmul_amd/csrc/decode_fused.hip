@@ -105,7 +105,7 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(
   const int col = min(r, ncs - 1);
   const int boff = aop_data_offset(0, 0, g, col, ncs);
   const int soff = aop_scale_offset(ncv, 0, g, col, ncs);
-  const int u_str = 4 * 32 * ncs;
+  const int u_str = aop_u_stride(ncs);
   const int tpoff = aop_tpart_offset(ncv) + 4 * min(lane, B - 1);
 
   const uint8_t* prow[P];
@@ -192,9 +192,7 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(
     for (int t = 0; t < 4; ++t) {
       if (t < nt) {
         const int cc = pb * nt + t;
-        uint4* dst = reinterpret_cast<uint4*>(prec + aop_data_offset(0, u, gg, cc, ncs));
-        dst[0] = make_uint4(rt.dw[t][0], rt.dw[t][1], rt.dw[t][2], rt.dw[t][3]);
-        dst[1] = make_uint4(rt.dw[t][4], rt.dw[t][5], 0u, 0u);
+        aop_store_block(prec + aop_data_offset(0, u, gg, cc, ncs), rt.dw[t]);
         prec[aop_scale_offset(ncv, 0, gg, cc, ncs) + u] = (uint8_t)(127 + rt.e[t]);
       }
     }
@@ -252,14 +250,14 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(
       // blocks, their scale dwords, its plane sum; then, after a release
       // fence, the flag.
       uint8_t* grec = aop + (int64_t)pq * rec;
-      const int items = nt * 16 * 8 + nt * 4 + 1;
+      const int items = nt * 16 * 6 + nt * 4 + 1;
       for (int i = lane; i < items; i += 64) {
         int off;
-        if (i < nt * 128) {
-          const int t = i >> 7, blk = (i >> 3) & 15, k = i & 7;
+        if (i < nt * 96) {
+          const int t = i / 96, blk = (i % 96) / 6, k = i % 6;
           off = aop_data_offset(0, blk >> 2, blk & 3, pb * nt + t, ncs) + 4 * k;
-        } else if (i < nt * 128 + nt * 4) {
-          const int j = i - nt * 128, t = j >> 2, gg = j & 3;
+        } else if (i < nt * 96 + nt * 4) {
+          const int j = i - nt * 96, t = j >> 2, gg = j & 3;
           off = aop_scale_offset(ncv, 0, gg, pb * nt + t, ncs);
         } else {
           off = aop_tpart_offset(ncv) + 4 * pb;

@@ -133,9 +133,7 @@ __global__ __launch_bounds__(kSpThreads) void decode_split_kernel(
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       if (t < nt) {
-        uint4* dst = reinterpret_cast<uint4*>(recp + aop_data_offset(0, u, gg, t, ncs));
-        dst[0] = make_uint4(rt.dw[t][0], rt.dw[t][1], rt.dw[t][2], rt.dw[t][3]);
-        dst[1] = make_uint4(rt.dw[t][4], rt.dw[t][5], 0u, 0u);
+        aop_store_block(recp + aop_data_offset(0, u, gg, t, ncs), rt.dw[t]);
         recp[aop_scale_offset(nt, 0, gg, t, ncs) + u] = (uint8_t)(127 + rt.e[t]);
       }
     }
@@ -149,7 +147,7 @@ __global__ __launch_bounds__(kSpThreads) void decode_split_kernel(
   const int col = min(r, ncs - 1);
   const int boff = aop_data_offset(0, 0, g, col, ncs);
   const int soff = aop_scale_offset(nt, 0, g, col, ncs);
-  const int u_str = 4 * 32 * ncs;
+  const int u_str = aop_u_stride(ncs);
   const int tpoff = aop_tpart_offset(nt);
   f32x4 acc0 = (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
   float tacc = 0.0f;

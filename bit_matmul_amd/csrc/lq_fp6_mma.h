@@ -24,11 +24,11 @@ __device__ __forceinline__ f32x4 mfma_fp4_fp6(uint32_t w, const i32x8& b, uint32
 }
 
 __device__ __forceinline__ i32x8 lds_b_operand(const uint8_t* p) {
-  const uint4 lo = *reinterpret_cast<const uint4*>(p);
-  const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
+  const uint2* q = reinterpret_cast<const uint2*>(p);
+  const uint2 a = q[0], c = q[1], e = q[2];
   i32x8 b;
-  b[0] = (int)lo.x; b[1] = (int)lo.y; b[2] = (int)lo.z; b[3] = (int)lo.w;
-  b[4] = (int)hi.x; b[5] = (int)hi.y; b[6] = 0; b[7] = 0;
+  b[0] = (int)a.x; b[1] = (int)a.y; b[2] = (int)c.x; b[3] = (int)c.y;
+  b[4] = (int)e.x; b[5] = (int)e.y; b[6] = 0; b[7] = 0;
   return b;
 }
 

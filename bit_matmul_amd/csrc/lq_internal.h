@@ -192,12 +192,12 @@ hipError_t launch_lift(const float* xt, int64_t B, int64_t K, int d, int D, cons
 // columns cc = b * nt + t (term t), grouped in sets of 16 (cs = cc / 16,
 // c = cc % 16, ncs = columns in the set). Per full or tail tile one record
 // of `rec` bytes:
-//   data   [cs][u][g][c] 32 bytes: 6 dwords of FP6 E2M3 codes (code m at bit
-//          6m, the value meeting reduction index k = 32g + m of MFMA u) and
-//          2 zero dwords; set cs starts at 512 * 16 * cs
-//   scales [cs][g][c] dword at 512 * ncv + 256 * cs: byte u is the E8M0
+//   data   [cs][u][g][c] 24 bytes: 6 dwords of FP6 E2M3 codes (code m at bit
+//          6m, the value meeting reduction index k = 32g + m of MFMA u); set
+//          cs starts at 384 * 16 * cs (blocks are 8-byte aligned)
+//   scales [cs][g][c] dword at 384 * ncv + 256 * cs: byte u is the E8M0
 //          scale of that 32-value block
-//   tpart  [b] float at 528 * ncv: sum over the tile's plane-0..2 columns of
+//   tpart  [b] float at 400 * ncv: sum over the tile's plane-0..2 columns of
 //          the values the terms represent
 struct OperandShape {
   int nt;     // terms per batch row
@@ -205,13 +205,23 @@ struct OperandShape {
   int cs;     // 16-column sets
   int rec;    // bytes per tile record (multiple of 16)
 };
+constexpr int kAopBlockBytes = 24;
 __host__ __device__ __forceinline__ int aop_data_offset(int cs, int u, int g, int c, int ncs) {
-  return 512 * 16 * cs + ((u * 4 + g) * ncs + c) * 32;
+  return 384 * 16 * cs + ((u * 4 + g) * ncs + c) * kAopBlockBytes;
 }
+// bytes between the blocks of MFMA u and u + 1 of one column
+__host__ __device__ __forceinline__ int aop_u_stride(int ncs) { return 4 * kAopBlockBytes * ncs; }
 __host__ __device__ __forceinline__ int aop_scale_offset(int ncv, int cs, int g, int c, int ncs) {
-  return 512 * ncv + 256 * cs + (g * ncs + c) * 4;
+  return 384 * ncv + 256 * cs + (g * ncs + c) * 4;
 }
-__host__ __device__ __forceinline__ int aop_tpart_offset(int ncv) { return 528 * ncv; }
+__host__ __device__ __forceinline__ int aop_tpart_offset(int ncv) { return 400 * ncv; }
+// Store one block's six code dwords (8-byte aligned).
+__device__ __forceinline__ void aop_store_block(uint8_t* p, const uint32_t* dw) {
+  uint2* q = reinterpret_cast<uint2*>(p);
+  q[0] = make_uint2(dw[0], dw[1]);
+  q[1] = make_uint2(dw[2], dw[3]);
+  q[2] = make_uint2(dw[4], dw[5]);
+}
 
 struct OperandPlan {
   OperandShape s;

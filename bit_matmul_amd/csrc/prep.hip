@@ -159,9 +159,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     if (t < nt) {
       const int cc = b * nt + t, cs = cc >> 4, cl = cc & 15;
       const int ncs = min(16, ncv - 16 * cs);
-      uint4* dst = reinterpret_cast<uint4*>(recp + aop_data_offset(cs, u, g, cl, ncs));
-      dst[0] = make_uint4(r.dw[t][0], r.dw[t][1], r.dw[t][2], r.dw[t][3]);
-      dst[1] = make_uint4(r.dw[t][4], r.dw[t][5], 0u, 0u);
+      aop_store_block(recp + aop_data_offset(cs, u, g, cl, ncs), r.dw[t]);
       recp[aop_scale_offset(ncv, cs, g, cl, ncs) + u] = (uint8_t)(127 + r.e[t]);
     }
   }
@@ -227,7 +225,7 @@ OperandShape operand_shape(int64_t B, bool z_bf16) {
   s.ncv = (int)B * s.nt;
   s.cs = (s.ncv + 15) / 16;
   // Records are 128-byte aligned: a cache line never holds parts of two.
-  s.rec = ((528 * s.ncv + 4 * (int)B) + 127) / 128 * 128;
+  s.rec = ((400 * s.ncv + 4 * (int)B) + 127) / 128 * 128;
   return s;
 }
 

@@ -78,7 +78,7 @@ __global__ __launch_bounds__(64 * (W + 1)) void sign_fp6_kernel(SignTable tab, i
   }
   int u_str[CS];                                    // bytes between the u blocks of a set
 #pragma unroll
-  for (int cs = 0; cs < CS; ++cs) u_str[cs] = 4 * 32 * max(1, min(16, ncv - 16 * cs));
+  for (int cs = 0; cs < CS; ++cs) u_str[cs] = aop_u_stride(max(1, min(16, ncv - 16 * cs)));
   const int tpoff = aop_tpart_offset(ncv) + 4 * min(lane, B - 1);
 
   const uint8_t* prow[P];
