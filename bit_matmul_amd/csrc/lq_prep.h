@@ -115,12 +115,24 @@ __device__ __forceinline__ void wave_fwht_1024(float* xs, int lhb, int lane) {
 // calling it the same number of times (it holds two workgroup barriers);
 // `active` false: the thread only takes part in the barriers. Thread t holds
 // xs[4t + i]: bits 0 and 1 pair registers, bits 2..7 pair lanes t ^ 1 ..
-// t ^ 32 (shuffles); then, through LDS, thread t holds xs[t + 256j] and bits
-// 8 and 9 pair registers. The stages run in the order of their bit, as in
+// t ^ 32 (DPP, swizzles, a permute for 32); then, through LDS, thread t holds
+// xs[t + 256j] and bits 8 and 9 pair registers. The stages run in the order
+// of their bit and every butterfly is the same single add or subtract as in
 // wave_fwht_1024, so both give identical results.
+template <int X>
+__device__ __forceinline__ void lane_stage4(float (&v)[4], int t, int lhb, int bit) {
+  if (bit < lhb) {
+    float o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = lane_xor<X>(v[i]);
+    const bool upper = (t & X) != 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = upper ? o[i] - v[i] : v[i] + o[i];
+  }
+}
 __device__ __forceinline__ void block_fwht_1024(float* xs, int lhb, int t, bool active) {
-  float v[4];
   if (active) {
+    float v[4];
     const float4 q = *reinterpret_cast<const float4*>(xs + 4 * t);
     v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
     if (lhb > 0) {
@@ -131,14 +143,12 @@ __device__ __forceinline__ void block_fwht_1024(float* xs, int lhb, int t, bool 
       float a = v[0], b = v[2]; v[0] = a + b; v[2] = a - b;
       a = v[1]; b = v[3]; v[1] = a + b; v[3] = a - b;
     }
-    for (int s = 1; s < 64 && (s << 2) < (1 << lhb); s <<= 1) {
-      const bool upper = (t & s) != 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float o = __shfl_xor(v[i], s, 64);
-        v[i] = upper ? (o - v[i]) : (v[i] + o);
-      }
-    }
+    lane_stage4<1>(v, t, lhb, 2);
+    lane_stage4<2>(v, t, lhb, 3);
+    lane_stage4<4>(v, t, lhb, 4);
+    lane_stage4<8>(v, t, lhb, 5);
+    lane_stage4<16>(v, t, lhb, 6);
+    lane_stage4<32>(v, t, lhb, 7);
     *reinterpret_cast<float4*>(xs + 4 * t) = make_float4(v[0], v[1], v[2], v[3]);
   }
   __syncthreads();
@@ -163,7 +173,7 @@ __device__ __forceinline__ void block_fwht_1024(float* xs, int lhb, int t, bool 
 // One lifted value z[col] = sum_{i < min(d, K - kb)} Ms[i * D + e] *
 // xs[kb + i - h_lo] with col = blk * D + e and kb = blk * d (the lift of
 // d-block blk; rows of the virtual zero pad are skipped). Products are added
-// in order of i; the LDS reads of 8 terms are issued before they are used.
+// in order of i; the LDS reads of 16 terms are issued before they are used.
 __device__ __forceinline__ float lift_column(const float* Ms, const float* xs, int col, int d,
                                              int D, int K, int h_lo) {
   const int blk = col / D;
@@ -171,16 +181,16 @@ __device__ __forceinline__ float lift_column(const float* Ms, const float* xs, i
   const int kb = blk * d;
   const int nk = min(d, K - kb);
   float acc = 0.0f;
-  for (int i0 = 0; i0 < nk; i0 += 8) {
-    float mv[8], xv[8];
+  for (int i0 = 0; i0 < nk; i0 += 16) {
+    float mv[16], xv[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < 16; ++u) {
       const int i = min(i0 + u, nk - 1);
       mv[u] = Ms[i * D + e];
       xv[u] = xs[kb + i - h_lo];
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < 16; ++u)
       if (i0 + u < nk) acc = fmaf(mv[u], xv[u], acc);
   }
   return acc;

@@ -93,11 +93,9 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     for (int j = 0; j < 4096 / kThreads; ++j) Ms[tid + kThreads * j] = mv[j] * norm;   // fold 1/sqrt(hb) into M
     __syncthreads();
     // Fast Walsh-Hadamard transform of each hb-block of the span, 1024
-    // values per wavefront (hb divides 1024; values past the span are
-    // transformed too and never read).
-    const int wave = tid >> 6;
-    if (1024 * wave < span) wave_fwht_1024(xs + 1024 * wave, lhb, tid & 63);
-    __syncthreads();
+    // values per 256 threads (hb divides 1024; values past the span are
+    // transformed too and never read). Ends with a workgroup barrier.
+    block_fwht_1024(xs + 1024 * (tid >> 8), lhb, tid & 255, 1024 * (tid >> 8) < span);
     // Lift the tile: one column per thread, d multiply-adds.
 #pragma unroll
     for (int jr = 0; jr < kTileCols / kThreads; ++jr) {
