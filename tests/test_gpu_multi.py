@@ -126,3 +126,34 @@ def test_errors(lq, gate_up):
         lq.lq_linear_multi(small, x, 1, ys[:1], None)
     with pytest.raises(lq.LQError):                   # more than LQ_MULTI_MAX layers
         lq.lq_linear_multi_workspace_size(small * 3, 1, torch.bfloat16)
+
+
+def test_empty_layer_and_graph_replay(lq):
+    """A layer with N = 0 is skipped; the grouped launches captured in a HIP
+    graph replay to the eager result every time (eager work and
+    synchronisation between the replays)."""
+    K = 1024
+    inps = [make_layer_small(64, K, 3, 8, 1024, seed=s, B_max=2, xdtype="bf16") for s in (31, 32)]
+    layers = [DeviceLayer(i, lq) for i in inps]
+    empty = lq.layer_struct(0, K, 3, 8, 1024, layers[0].packed, layers[0].M, layers[0].c, layers[0].r)
+    x = dev(inps[0].x(2).astype(np.float32), torch.bfloat16)
+    structs = [layers[0].struct, empty, layers[1].struct]
+    ys = [torch.full((2, 64), -7.0, device="cuda"), torch.empty((2, 0), device="cuda"),
+          torch.full((2, 64), -7.0, device="cuda")]
+    ws = workspace(lq, lq.lq_linear_multi_workspace_size(structs, 2, torch.bfloat16))
+    note("lq_linear_multi with an empty layer, then a graph of it")
+    lq.lq_linear_multi(structs, x, 2, ys, ws)
+    torch.cuda.synchronize()
+    eager = [y.clone() for y in ys]
+    for l, y in zip([layers[0], layers[1]], [eager[0], eager[2]]):
+        assert torch.equal(y, l.linear(lq, x, 2, torch.float32))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lq.lq_linear_multi(structs, x, 2, ys, ws)
+    for _ in range(3):
+        ys[0].fill_(-1.0)
+        ys[2].fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ys[0], eager[0]) and torch.equal(ys[2], eager[2])
