@@ -34,6 +34,10 @@ Profiling helpers (the summaries under profiles/ are made with these):
                           runs (their output directories), scaled by the copy
   --summarize-stats DIR   per-kernel calls and durations of a
                           rocprofv3 --kernel-trace --stats run
+  --summarize-util DIR    per-kernel matrix-core and LDS utilisation from a
+                          rocprofv3 --pmc run of --pmc-workload with
+                          SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA
+                          SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE
 """
 from __future__ import annotations
 
@@ -84,6 +88,7 @@ def parse_args():
     p.add_argument("--pmc-workload", action="store_true",
                    help="calibration copy plus a few eager decode steps, for rocprofv3 --pmc")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    p.add_argument("--summarize-util", metavar="PMC_DIR")
     p.add_argument("--summarize-stats", metavar="DIR")
     p.add_argument("--profiled-steps", type=int, default=None,
                    help="with --summarize-stats: the --steps of the profiled run")
@@ -210,6 +215,40 @@ def summarize_pmc(fetch_dir, write_dir):
     for k in sorted(out["FETCH_SIZE"]):
         lines.append(f"kernel {k} fetch_kib {out['FETCH_SIZE'][k]:.1f} "
                      f"write_kib {out['WRITE_SIZE'].get(k, float('nan')):.1f}")
+    return "\n".join(lines)
+
+
+XCDS, CUS, SIMDS_PER_CU = 8, 256, 4
+
+
+def summarize_util(d):
+    """Per-kernel averages over dispatches of the counters of one rocprofv3
+    --pmc run, and what they give: the matrix pipe busy fraction
+    (SQ_VALU_MFMA_BUSY_CYCLES, summed over the 1024 SIMDs, over the kernel's
+    cycles: GRBM_GUI_ACTIVE summed over the 8 XCDs, divided by 8), LDS busy
+    and bank-conflict fractions (SQ_LDS_IDX_ACTIVE and SQ_LDS_BANK_CONFLICT,
+    summed over compute units, over the same cycles times 256), and cycles
+    per MFMA instruction per SIMD."""
+    per = {}
+    for r in _read_rocprof_rows(d, "pmc"):
+        k = _short(r["kernel"])
+        if not k.startswith("lq::"):
+            continue
+        per.setdefault(k, {}).setdefault(r["counter"], []).append(r["value"])
+    lines = ["kernel | dispatches | gpu cycles | mfma busy | mfma insts | cycles per mfma "
+             "per SIMD | lds busy | lds bank-conflict cycles"]
+    for k in sorted(per):
+        c = {n: sum(v) / len(v) for n, v in per[k].items()}
+        if "GRBM_GUI_ACTIVE" not in c or c.get("SQ_INSTS_MFMA", 0) == 0:
+            continue
+        cyc = c["GRBM_GUI_ACTIVE"] / XCDS
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / (cyc * CUS * SIMDS_PER_CU)
+        per_simd = c["SQ_VALU_MFMA_BUSY_CYCLES"] / c["SQ_INSTS_MFMA"]
+        lds = c.get("SQ_LDS_IDX_ACTIVE", float("nan")) / (cyc * CUS)
+        bank = c.get("SQ_LDS_BANK_CONFLICT", float("nan")) / (cyc * CUS)
+        n = len(next(iter(per[k].values())))
+        lines.append(f"{k} | {n} | {cyc:.0f} | {busy:.3f} | {c['SQ_INSTS_MFMA']:.0f} | "
+                     f"{per_simd:.1f} | {lds:.3f} | {bank:.3f}")
     return "\n".join(lines)
 
 
@@ -602,6 +641,9 @@ def main():
         return
     if args.summarize_pmc:
         print(summarize_pmc(*args.summarize_pmc))
+        return
+    if args.summarize_util:
+        print(summarize_util(args.summarize_util))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
