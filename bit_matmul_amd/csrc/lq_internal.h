@@ -34,12 +34,11 @@ inline PackedGeom make_geom(int64_t N, int64_t L) {
   return g;
 }
 
+// bf16 bits of f, rounded to nearest, ties to even (gfx950's
+// v_cvt_pk_bf16_f32; fp32 denormals are kept, so every finite value rounds
+// as the IEEE rule says; NaNs come out quiet).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u)               // inf / nan: keep, quiet nans
-    return (u >> 16) | ((u & 0xffffu) ? 0x40u : 0u);
-  u += 0x7fffu + ((u >> 16) & 1u);                     // round to nearest, ties to even
-  return u >> 16;
+  return __builtin_bit_cast(unsigned short, (__bf16)f);
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {

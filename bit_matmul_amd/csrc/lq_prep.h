@@ -50,9 +50,11 @@ __device__ __forceinline__ void lane_stage(float (&a)[16], int lane) {
   float p[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) p[k] = lane_xor<X>(a[k]);
-  const bool upper = (lane & X) != 0;
+  // a + p in the lower lane, p - a in the upper one, as one fma with a
+  // multiplier of +-1 (exact, so the same single rounding as the add)
+  const float sgn = (lane & X) != 0 ? -1.0f : 1.0f;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) a[k] = upper ? p[k] - a[k] : a[k] + p[k];
+  for (int k = 0; k < 16; ++k) a[k] = fmaf(a[k], sgn, p[k]);
 }
 
 // In-place fast Walsh-Hadamard transform (unnormalised) of every 2^lhb-value
@@ -125,9 +127,9 @@ __device__ __forceinline__ void lane_stage4(float (&v)[4], int t, int lhb, int b
     float o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = lane_xor<X>(v[i]);
-    const bool upper = (t & X) != 0;
+    const float sgn = (t & X) != 0 ? -1.0f : 1.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = upper ? o[i] - v[i] : v[i] + o[i];
+    for (int i = 0; i < 4; ++i) v[i] = fmaf(v[i], sgn, o[i]);
   }
 }
 __device__ __forceinline__ void block_fwht_1024(float* xs, int lhb, int t, bool active) {
