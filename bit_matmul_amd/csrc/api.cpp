@@ -37,7 +37,6 @@ lq_status hip_status(hipError_t e) {
 bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 bool valid_dtype(lq_dtype t) { return t == LQ_F32 || t == LQ_BF16; }
-size_t dtype_size(lq_dtype t) { return t == LQ_F32 ? 4 : 2; }
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
 bool mul_ok(int64_t a, int64_t b, int64_t lim) { return a == 0 || b <= lim / a; }
@@ -238,6 +237,7 @@ lq_status plan_exec(int64_t B, int64_t N, int64_t L, int64_t K, int d, int D, lq
 lq_status run_exec(const Exec& e, const uint8_t* packed, const void* zin, lq_dtype ztype,
                    int64_t B, int64_t N, int64_t L, const float* row_scale, void* y,
                    lq_dtype ytype, void* ws, hipStream_t st, const lq_layer* layer) {
+  (void)N;   // carried by e.g
   char* base = static_cast<char*>(ws);
   const bool zb = ztype == LQ_BF16, yb = ytype == LQ_BF16;
   unsigned* tickets = reinterpret_cast<unsigned*>(base + e.off_tickets);
