@@ -61,6 +61,27 @@ def test_prefill_full_size(lq, li):
     assert rel_l2(got, yl) < 2 * TOL
 
 
+def test_ragged_batch_eight_tiles_per_workgroup(lq):
+    """B = 2103 on the 8192 x 8192 layer: 132 batch tiles in workgroups of 8
+    (the last group holds 4 real tiles, the last tile 7 real rows); sampled
+    rows and batch rows, the last ones included."""
+    wl = WORKLOADS["prefill"]
+    spec = wl.layers[0]
+    B = 2103
+    inp = make_layer(spec, wl, B_max=B)
+    layer = DeviceLayer(inp, lq)
+    x = inp.x(B)
+    rng = np.random.default_rng(2103)
+    rows = np.sort(rng.choice(spec.N, size=24, replace=False))
+    rows[0], rows[-1] = 0, spec.N - 1
+    bsel = np.unique(np.concatenate([rng.choice(B, 24, replace=False), np.arange(B - 9, B)]))
+    want = ref.linear(x[bsel], inp.c, spec.hb, inp.M, inp.signs_rows(rows), inp.row_scale[rows])
+    y = host(layer.linear(lq, dev(x, torch.bfloat16), B, torch.float32, algo=lq.LQ_ALGO_WSPACE))
+    assert np.all(np.isfinite(y))
+    err = rel_l2(y[np.ix_(bsel, rows)], want)
+    assert err < TOL, err
+
+
 SMALL = [
     # (N, K, d, D, hb, label)
     (256, 2048, 3, 8, 1024, "prefill rate, 12 tiles + tail"),
