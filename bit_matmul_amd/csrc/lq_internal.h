@@ -46,10 +46,14 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
 }
 
 // The 16-byte slot (g, r) of full tile q of one panel, as four 32-bit words:
-// word u, bit b = sign bit of row r at tile column 128u + 32g + b.
+// word u, bit b = sign bit of row r at tile column 128u + 32g + b. A
+// non-temporal load: the products that use it read each weight byte once.
 __device__ __forceinline__ uint4 load_full_slot(const uint8_t* __restrict__ panel, int q, int g,
                                                 int r) {
-  return *reinterpret_cast<const uint4*>(panel + (int64_t)q * kTileBytes + 16 * (16 * g + r));
+  typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
+  const v4u_t v = __builtin_nontemporal_load(
+      reinterpret_cast<const v4u_t*>(panel + (int64_t)q * kTileBytes + 16 * (16 * g + r)));
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 // The same slot of the partial tail tile, assembled from the row-major tail

@@ -43,6 +43,8 @@
 namespace lq {
 namespace {
 
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
 template <int P, int CS, int W, int TPC>
 __global__ __launch_bounds__(64 * (W + 1)) void sign_fp6_kernel(SignTable tab, int rec, int ncv,
                                                                 int B, int chunk_bytes, int y_bf16) {
@@ -105,7 +107,12 @@ __global__ __launch_bounds__(64 * (W + 1)) void sign_fp6_kernel(SignTable tab, i
       const int t = min(c * CT + wave * TPC + q, last_full);
       const int off = live ? t * kTileBytes + 16 * lane : 0;
 #pragma unroll
-      for (int p = 0; p < P; ++p) A[q][p] = *reinterpret_cast<const uint4*>(prow[p] + off);
+      for (int p = 0; p < P; ++p) {
+        // Each weight byte is read once per call: a non-temporal load keeps
+        // the stream from displacing the activation records in the caches.
+        const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(prow[p] + off));
+        A[q][p] = make_uint4(v.x, v.y, v.z, v.w);
+      }
     }
   };
   // The MFMAs of one tile whose activation record starts at `recp` (LDS).
