@@ -17,7 +17,7 @@ from . import _lib
 from ._lib import (LQ_MULTI_MAX, LQ_ENCODE_MAX_D, LQ_ENCODE_MAX_SMALL_D, LQ_ALGO_AUTO, LQ_ALGO_FUSED, LQ_ALGO_FUSED_LOCAL, LQ_ALGO_MFMA_LARGE, LQ_ALGO_WSPACE, LQ_ALGO_FUSED_SPLIT,
                    LQ_ALGO_MFMA_SMALL,
                    LQ_ALGO_VALU, LQ_BF16, LQ_F32, LQ_MAX_D, LQ_MAX_HB, LQ_WS_CONTROL_BYTES,
-                   LQ_WS_ERROR_WORD, LQError, LQLayer)
+                   LQ_WS_ERROR_WORD, LQ_NOALLOC_SCRATCH_BYTES, LQError, LQLayer)
 
 __all__ = [
     "lq_version", "lq_packed_size", "lq_pack_signs", "lq_unpack_signs", "lq_hadamard_scale",
@@ -29,7 +29,7 @@ __all__ = [
     "lq_workspace_init", "lq_profile_events", "layer_struct", "LQError", "LQLayer",
     "LQ_F32", "LQ_BF16", "LQ_ALGO_AUTO", "LQ_ALGO_VALU", "LQ_ALGO_MFMA_SMALL",
     "LQ_ALGO_MFMA_LARGE", "LQ_ALGO_FUSED", "LQ_ALGO_FUSED_LOCAL", "LQ_ALGO_WSPACE", "LQ_ALGO_FUSED_SPLIT", "LQ_MAX_D", "LQ_MAX_HB", "LQ_WS_CONTROL_BYTES",
-    "LQ_WS_ERROR_WORD", "library_path",
+    "LQ_WS_ERROR_WORD", "library_path", "lq_linear_noalloc", "LQ_NOALLOC_SCRATCH_BYTES",
 ]
 
 _DTYPES = {torch.float32: LQ_F32, torch.bfloat16: LQ_BF16}
@@ -140,6 +140,13 @@ def lq_linear(layer: LQLayer, x, B, y, ws=None, stream=None) -> None:
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(_lib.LIB.lq_linear(ctypes.byref(layer), _dev(x, "x"), _dtype(x, "x"), B, _dev(y, "y"),
                               _dtype(y, "y"), ws_ptr, ws_bytes, _stream(stream)), "lq_linear")
+
+
+def lq_linear_noalloc(layer: LQLayer, x, B, y, stream=None) -> None:
+    """lq_linear with the library's own device scratch (no workspace)."""
+    _check(_lib.LIB.lq_linear_noalloc(ctypes.byref(layer), _dev(x, "x"), _dtype(x, "x"), B,
+                                      _dev(y, "y"), _dtype(y, "y"), _stream(stream)),
+           "lq_linear_noalloc")
 
 
 def lq_linear_workspace_size_ex(layer: LQLayer, B, xtype, algo) -> int:

@@ -18,6 +18,7 @@ LQ_WS_ERROR_WORD = 96
 LQ_ENCODE_MAX_D = 24
 LQ_ENCODE_MAX_SMALL_D = 16
 LQ_MULTI_MAX = 4
+LQ_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 # Every symbol include/lq.h declares.
 EXPORTS = [
@@ -27,7 +28,7 @@ EXPORTS = [
     "lq_linear_workspace_size", "lq_linear", "lq_linear_workspace_size_ex", "lq_linear_ex",
     "lq_linear_algo", "lq_workspace_init", "lq_profile_events", "lq_encode",
     "lq_train_m_step_workspace_size", "lq_train_m_step", "lq_linear_multi_workspace_size",
-    "lq_linear_multi",
+    "lq_linear_multi", "lq_linear_noalloc",
 ]
 
 
@@ -80,6 +81,7 @@ def _load():
                                                    POINTER(sz)]),
         "lq_linear_multi": (c_int, [POINTER(LQLayer), c_int32, vp, c_int, i64, POINTER(vp), c_int,
                                     vp, sz, vp]),
+        "lq_linear_noalloc": (c_int, [POINTER(LQLayer), vp, c_int, i64, vp, c_int, vp]),
         "lq_workspace_init": (c_int, [vp, sz, vp]),
         "lq_profile_events": (c_int, [POINTER(vp), POINTER(vp), i32]),
     }

@@ -409,6 +409,33 @@ lq_status plan_multi(const lq_layer* layers, int32_t n, int64_t B, lq_dtype xtyp
   return LQ_OK;
 }
 
+// Scratch of lq_linear_noalloc: a file-scope device array (one copy per GPU)
+// whose device address is looked up once per device and kept. In host code
+// `scratch` names only a host-side stand-in: kernels get the looked-up address.
+static __device__ __align__(256) uint8_t scratch[LQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// The current device's address of `scratch` (looked up on its first use on
+// that device, with the device current).
+lq_status noalloc_scratch(void** out) {
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return LQ_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (r != hipSuccess || p == nullptr) return hip_status(r != hipSuccess ? r : hipErrorInvalidSymbol);
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return LQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -585,6 +612,30 @@ lq_status lq_linear_ex(const lq_layer* layer, const void* x, lq_dtype xtype, int
 lq_status lq_linear(const lq_layer* layer, const void* x, lq_dtype xtype, int64_t B, void* y,
                     lq_dtype ytype, void* ws, size_t ws_bytes, void* stream) {
   return lq_linear_ex(layer, x, xtype, B, y, ytype, LQ_ALGO_AUTO, ws, ws_bytes, stream);
+}
+
+lq_status lq_linear_noalloc(const lq_layer* layer, const void* x, lq_dtype xtype, int64_t B,
+                            void* y, lq_dtype ytype, void* stream) {
+  if (!valid_dtype(xtype) || !valid_dtype(ytype) || B < 0) return LQ_ERR_INVALID_ARG;
+  int64_t L = 0;
+  lq_status s = check_layer(layer, &L);
+  if (s != LQ_OK) return s;
+  s = check_sign_dims(B, layer->N, L);
+  if (s != LQ_OK) return s;
+  if (!mul_ok(B, layer->K, kMaxElems)) return LQ_ERR_UNSUPPORTED;
+  if (B == 0 || layer->N == 0) return LQ_OK;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(layer->packed) || !aligned16(layer->M) ||
+      !aligned16(layer->c) || !aligned16(layer->row_scale))
+    return LQ_ERR_INVALID_ARG;
+  Exec e;
+  s = plan_exec(B, layer->N, L, layer->K, layer->d, layer->D, xtype, LQ_ALGO_AUTO, true, &e);
+  if (s != LQ_OK) return s;
+  if (e.total > (size_t)LQ_NOALLOC_SCRATCH_BYTES) return LQ_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  s = noalloc_scratch(&ws);
+  if (s != LQ_OK) return s;
+  return run_exec(e, layer->packed, x, xtype, B, layer->N, L, layer->row_scale, y, ytype, ws,
+                  (hipStream_t)stream, layer);
 }
 
 lq_status lq_linear_multi_workspace_size(const lq_layer* layers, int32_t n, int64_t B,

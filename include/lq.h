@@ -274,6 +274,27 @@ lq_status lq_linear_ex(const lq_layer* layer, const void* x, lq_dtype xtype, int
                        lq_dtype ytype, lq_algo algo, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): lq_linear
+ * without a caller workspace. It runs exactly what lq_linear runs (the same
+ * algorithm, kernels and results) with the workspace carved from a
+ * file-scope device array of LQ_NOALLOC_SCRATCH_BYTES bytes inside the
+ * library: one array per GPU, whose address the first call on a GPU looks up
+ * (with that GPU current) and keeps; each GPU holds it until the process
+ * ends. Nothing is allocated and no allocating routine is called.
+ * Every call on a GPU shares that GPU's array, which keeps the last call's
+ * contents (each call rewrites everything it reads from it): calls that
+ * overlap on one GPU race, so order them (one stream, or events between
+ * streams). Errors: as lq_linear; UNSUPPORTED when lq_linear's workspace for
+ * this call would exceed LQ_NOALLOC_SCRATCH_BYTES (checked on the host
+ * before anything is enqueued), LQ_ERR_HIP when the array's address cannot
+ * be looked up.
+ */
+#define LQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+lq_status lq_linear_noalloc(const lq_layer* layer, const void* x, lq_dtype xtype, int64_t B,
+                            void* y, lq_dtype ytype, void* stream);
+
+/*
  * Several layers on the same input (as the gate and up projections of a
  * transformer MLP): ys[i] = lq_linear(&layers[i], x) for i < n, with
  * 1 <= n <= LQ_MULTI_MAX and every layer of the same K (d, D, hb, M, c and N
