@@ -17,7 +17,8 @@ from . import _lib
 from ._lib import (LQ_MULTI_MAX, LQ_ENCODE_MAX_D, LQ_ENCODE_MAX_SMALL_D, LQ_ALGO_AUTO, LQ_ALGO_FUSED, LQ_ALGO_FUSED_LOCAL, LQ_ALGO_MFMA_LARGE, LQ_ALGO_WSPACE, LQ_ALGO_FUSED_SPLIT,
                    LQ_ALGO_MFMA_SMALL,
                    LQ_ALGO_VALU, LQ_BF16, LQ_F32, LQ_MAX_D, LQ_MAX_HB, LQ_WS_CONTROL_BYTES,
-                   LQ_WS_ERROR_WORD, LQ_NOALLOC_SCRATCH_BYTES, LQError, LQLayer)
+                   LQ_WS_ERROR_WORD, LQ_NOALLOC_SCRATCH_BYTES, LQ_ERR_DEVICE, LQ_MAX_L, LQError,
+                   LQLayer, LQPlanInfo)
 
 __all__ = [
     "lq_version", "lq_packed_size", "lq_pack_signs", "lq_unpack_signs", "lq_hadamard_scale",
@@ -30,6 +31,8 @@ __all__ = [
     "LQ_F32", "LQ_BF16", "LQ_ALGO_AUTO", "LQ_ALGO_VALU", "LQ_ALGO_MFMA_SMALL",
     "LQ_ALGO_MFMA_LARGE", "LQ_ALGO_FUSED", "LQ_ALGO_FUSED_LOCAL", "LQ_ALGO_WSPACE", "LQ_ALGO_FUSED_SPLIT", "LQ_MAX_D", "LQ_MAX_HB", "LQ_WS_CONTROL_BYTES",
     "LQ_WS_ERROR_WORD", "library_path", "lq_linear_noalloc", "LQ_NOALLOC_SCRATCH_BYTES",
+    "lq_linear_plan", "lq_sign_gemm_plan", "lq_workspace_status", "lq_debug_fused_timeout",
+    "LQ_ERR_DEVICE", "LQ_MAX_L", "LQPlanInfo",
 ]
 
 _DTYPES = {torch.float32: LQ_F32, torch.bfloat16: LQ_BF16}
@@ -164,6 +167,37 @@ def lq_linear_algo(layer: LQLayer, B, xtype, algo=0) -> int:
     _check(_lib.LIB.lq_linear_algo(ctypes.byref(layer), B, xt, algo, ctypes.byref(out)),
            "lq_linear_algo")
     return out.value
+
+
+def lq_linear_plan(layer: LQLayer, B, xtype, algo=LQ_ALGO_AUTO) -> dict:
+    """Algorithm and sign-product launch shape lq_linear_ex would use."""
+    info = LQPlanInfo()
+    xt = _DTYPES[xtype] if isinstance(xtype, torch.dtype) else int(xtype)
+    _check(_lib.LIB.lq_linear_plan(ctypes.byref(layer), B, xt, algo, ctypes.byref(info)),
+           "lq_linear_plan")
+    return {f: getattr(info, f) for f, _ in LQPlanInfo._fields_}
+
+
+def lq_sign_gemm_plan(B, N, L, ztype, algo=LQ_ALGO_AUTO) -> dict:
+    """Algorithm and launch shape lq_sign_gemm_ex would use."""
+    info = LQPlanInfo()
+    zt = _DTYPES[ztype] if isinstance(ztype, torch.dtype) else int(ztype)
+    _check(_lib.LIB.lq_sign_gemm_plan(B, N, L, zt, algo, ctypes.byref(info)), "lq_sign_gemm_plan")
+    return {f: getattr(info, f) for f, _ in LQPlanInfo._fields_}
+
+
+def lq_workspace_status(ws, stream=None) -> int:
+    """LQ_OK, or LQ_ERR_DEVICE when a call on this workspace reported a
+    failure (waits for the stream). Other errors raise."""
+    st = _lib.LIB.lq_workspace_status(_dev(ws, "ws"), ws.numel() * ws.element_size(),
+                                      _stream(stream))
+    if st not in (0, LQ_ERR_DEVICE):
+        _check(st, "lq_workspace_status")
+    return st
+
+
+def lq_debug_fused_timeout(enable: bool) -> None:
+    _check(_lib.LIB.lq_debug_fused_timeout(1 if enable else 0), "lq_debug_fused_timeout")
 
 
 def lq_linear_ex(layer: LQLayer, x, B, y, algo, ws=None, stream=None) -> None:

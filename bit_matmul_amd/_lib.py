@@ -7,12 +7,13 @@ from pathlib import Path
 
 LIB_PATH = Path(__file__).resolve().parent / "liblq.so"
 
-LQ_OK, LQ_ERR_INVALID_ARG, LQ_ERR_UNSUPPORTED, LQ_ERR_WORKSPACE, LQ_ERR_HIP = range(5)
+LQ_OK, LQ_ERR_INVALID_ARG, LQ_ERR_UNSUPPORTED, LQ_ERR_WORKSPACE, LQ_ERR_HIP, LQ_ERR_DEVICE = range(6)
 LQ_F32, LQ_BF16 = 0, 1
 (LQ_ALGO_AUTO, LQ_ALGO_VALU, LQ_ALGO_MFMA_SMALL, LQ_ALGO_MFMA_LARGE, LQ_ALGO_FUSED,
  LQ_ALGO_FUSED_LOCAL, LQ_ALGO_WSPACE, LQ_ALGO_FUSED_SPLIT) = range(8)
 LQ_MAX_D = 64
 LQ_MAX_HB = 1024
+LQ_MAX_L = 1 << 28
 LQ_WS_CONTROL_BYTES = 20992
 LQ_WS_ERROR_WORD = 96
 LQ_ENCODE_MAX_D = 24
@@ -28,7 +29,8 @@ EXPORTS = [
     "lq_linear_workspace_size", "lq_linear", "lq_linear_workspace_size_ex", "lq_linear_ex",
     "lq_linear_algo", "lq_workspace_init", "lq_profile_events", "lq_encode",
     "lq_train_m_step_workspace_size", "lq_train_m_step", "lq_linear_multi_workspace_size",
-    "lq_linear_multi", "lq_linear_noalloc",
+    "lq_linear_multi", "lq_linear_noalloc", "lq_linear_plan", "lq_sign_gemm_plan",
+    "lq_workspace_status", "lq_debug_fused_timeout",
 ]
 
 
@@ -38,6 +40,14 @@ class LQLayer(ctypes.Structure):
         ("N", c_int64), ("K", c_int64), ("d", c_int32), ("D", c_int32),
         ("hb", c_int32), ("reserved", c_int32),
         ("packed", c_void_p), ("M", c_void_p), ("c", c_void_p), ("row_scale", c_void_p),
+    ]
+
+
+class LQPlanInfo(ctypes.Structure):
+    """Mirror of ``struct lq_plan_info``."""
+    _fields_ = [
+        ("algo", c_int32), ("workgroups", c_int32), ("waves", c_int32), ("panels", c_int32),
+        ("batch_rows", c_int32), ("ksplit", c_int32),
     ]
 
 
@@ -83,6 +93,10 @@ def _load():
                                     vp, sz, vp]),
         "lq_linear_noalloc": (c_int, [POINTER(LQLayer), vp, c_int, i64, vp, c_int, vp]),
         "lq_workspace_init": (c_int, [vp, sz, vp]),
+        "lq_linear_plan": (c_int, [POINTER(LQLayer), i64, c_int, c_int, POINTER(LQPlanInfo)]),
+        "lq_sign_gemm_plan": (c_int, [i64, i64, i64, c_int, c_int, POINTER(LQPlanInfo)]),
+        "lq_workspace_status": (c_int, [vp, sz, vp]),
+        "lq_debug_fused_timeout": (c_int, [i32]),
         "lq_profile_events": (c_int, [POINTER(vp), POINTER(vp), i32]),
     }
     for name, (res, args) in protos.items():

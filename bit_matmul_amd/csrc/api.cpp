@@ -47,14 +47,15 @@ lq_status check_layer_dims(int64_t N, int64_t K, int32_t d, int32_t D, int64_t* 
   if (D > LQ_MAX_D || N > kMaxDim || K > kMaxDim) return LQ_ERR_UNSUPPORTED;
   const int64_t Kb = (K + d - 1) / d;
   *L = Kb * D;
-  if (N % lq::kPanelRows != 0 || *L % 8 != 0 || *L > kMaxDim) return LQ_ERR_UNSUPPORTED;
+  // (L <= LQ_MAX_L keeps every byte offset within a panel, 2 L, in 32 bits)
+  if (N % lq::kPanelRows != 0 || *L % 8 != 0 || *L > LQ_MAX_L) return LQ_ERR_UNSUPPORTED;
   if (!mul_ok(N, *L, kMaxElems * 64)) return LQ_ERR_UNSUPPORTED;
   return LQ_OK;
 }
 
 lq_status check_sign_dims(int64_t B, int64_t N, int64_t L) {
   if (B < 0 || N < 0 || L < 1) return LQ_ERR_INVALID_ARG;
-  if (B > kMaxBatch || N > kMaxDim || L > kMaxDim) return LQ_ERR_UNSUPPORTED;
+  if (B > kMaxBatch || N > kMaxDim || L > LQ_MAX_L) return LQ_ERR_UNSUPPORTED;
   if (N % lq::kPanelRows != 0 || L % 8 != 0) return LQ_ERR_UNSUPPORTED;
   if (!mul_ok(B, L, kMaxElems) || !mul_ok(B, N, kMaxElems)) return LQ_ERR_UNSUPPORTED;
   return LQ_OK;
@@ -137,6 +138,7 @@ struct Exec {
   int tickets;
   size_t off_tickets, off_aop, off_partial, off_zf32, off_xt, off_zp, off_tslots, total;
   int d, D;
+  lq_dtype ztype;
 };
 
 // Plans a sign product of z (ztype) or, when `linear`, the whole operator
@@ -150,6 +152,7 @@ lq_status plan_exec(int64_t B, int64_t N, int64_t L, int64_t K, int d, int D, lq
   e->algo = algo;
   e->d = d;
   e->D = D;
+  e->ztype = ztype;
   if (algo == LQ_ALGO_AUTO) {
     if (B > 16) {
       // W space where it applies: D / d times fewer MACs on the same bf16
@@ -184,7 +187,7 @@ lq_status plan_exec(int64_t B, int64_t N, int64_t L, int64_t K, int d, int D, lq
     case LQ_ALGO_MFMA_SMALL:
       if (B > 16) return LQ_ERR_UNSUPPORTED;
       e->os = lq::operand_shape(B, ztype == LQ_BF16);
-      e->fp = lq::plan_fp6(B, e->g, e->os);
+      e->fp = lq::plan_fp6(B, e->g, e->os, device_cus());
       e->off_aop = take(lq::operand_bytes(L, e->os));
       break;
     case LQ_ALGO_FUSED:
@@ -333,6 +336,65 @@ lq_status run_exec(const Exec& e, const uint8_t* packed, const void* zin, lq_dty
   }
 }
 
+// The launch shape of a planned call's sign-product kernel.
+void fill_plan_info(const Exec& e, int64_t B, lq_plan_info* info) {
+  const int64_t panels = e.g.panels;
+  const int64_t B16 = (B + 15) / 16;
+  lq_plan_info p{};
+  p.algo = e.algo;
+  p.ksplit = 1;
+  p.batch_rows = (int32_t)B;
+  switch (e.algo) {
+    case LQ_ALGO_VALU:
+      p.waves = lq::kValuWaves;
+      p.panels = lq::kValuWaves;
+      p.batch_rows = e.vp.bt;
+      p.ksplit = e.vp.ksplit;
+      p.workgroups = (int32_t)(((panels + 3) / 4) * e.vp.ksplit * ((B + e.vp.bt - 1) / e.vp.bt));
+      break;
+    case LQ_ALGO_MFMA_SMALL:
+      p.waves = e.fp.w + 1;
+      p.panels = e.fp.p;
+      p.workgroups = e.fp.groups;
+      break;
+    case LQ_ALGO_FUSED:
+      p.waves = lq::kOneLaunchWaves;
+      p.panels = e.fu.p;
+      p.workgroups = e.fu.groups;
+      break;
+    case LQ_ALGO_FUSED_LOCAL:
+      p.waves = lq::kOneLaunchWaves;
+      p.panels = e.sp.pw;
+      p.workgroups = e.sp.groups;
+      break;
+    case LQ_ALGO_FUSED_SPLIT:
+      p.waves = lq::kOneLaunchWaves;
+      p.panels = lq::kSplitPanels;
+      p.ksplit = e.spl.kgroups;
+      p.workgroups = e.spl.kgroups * e.spl.pgroups;
+      break;
+    case LQ_ALGO_MFMA_LARGE: {
+      const lq::LargePlan lp = lq::plan_large(B, e.g, e.ztype == LQ_BF16);
+      p.waves = lq::kLargeWaves;
+      p.panels = lq::kLargeWaves * lp.ppw;
+      p.batch_rows = 16 * lp.jb;
+      p.workgroups = (int32_t)(((panels + p.panels - 1) / p.panels) * ((B16 + lp.jb - 1) / lp.jb));
+      break;
+    }
+    case LQ_ALGO_WSPACE: {
+      const int jb = lq::plan_wspace_jb(B, e.g, e.d);
+      p.waves = lq::kLargeWaves;
+      p.panels = lq::kLargeWaves * lq::kWsPanelsPerWave;
+      p.batch_rows = 16 * jb;
+      p.workgroups = (int32_t)(((panels + p.panels - 1) / p.panels) * ((B16 + jb - 1) / jb));
+      break;
+    }
+    default:
+      break;
+  }
+  *info = p;
+}
+
 lq_status check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (need == 0) return LQ_OK;
   if (ws == nullptr || ws_bytes < need) return LQ_ERR_WORKSPACE;
@@ -393,8 +455,9 @@ lq_status plan_multi(const lq_layer* layers, int32_t n, int64_t B, lq_dtype xtyp
     // panels per workgroup chosen for all the layers' panels together
     int64_t panels = 0;
     for (int j = 0; j < mp->n; ++j) panels += mp->e[j].g.panels;
-    const int pp = lq::fp6_panels_per_group(panels, mp->e[0].os);
-    for (int j = 0; j < mp->n; ++j) mp->e[j].fp = lq::plan_fp6(B, mp->e[j].g, mp->e[j].os, pp);
+    const int cus = device_cus();
+    const int pp = lq::fp6_panels_per_group(panels, mp->e[0].os, cus);
+    for (int j = 0; j < mp->n; ++j) mp->e[j].fp = lq::plan_fp6(B, mp->e[j].g, mp->e[j].os, cus, pp);
     for (int j = 1; j < mp->n; ++j)
       if (!lq::fp6_plans_match(mp->e[j].fp, mp->e[0].fp)) mp->grouped = false;
   }
@@ -449,6 +512,7 @@ const char* lq_status_string(lq_status status) {
     case LQ_ERR_UNSUPPORTED: return "LQ_ERR_UNSUPPORTED: outside the library's limits";
     case LQ_ERR_WORKSPACE: return "LQ_ERR_WORKSPACE: workspace missing or too small";
     case LQ_ERR_HIP: return "LQ_ERR_HIP: HIP runtime error";
+    case LQ_ERR_DEVICE: return "LQ_ERR_DEVICE: a kernel reported a failure; the call's output is wrong";
     default: return "unknown lq_status";
   }
 }
@@ -581,6 +645,36 @@ lq_status lq_linear_algo(const lq_layer* layer, int64_t B, lq_dtype xtype, lq_al
   return LQ_OK;
 }
 
+lq_status lq_linear_plan(const lq_layer* layer, int64_t B, lq_dtype xtype, lq_algo algo,
+                         lq_plan_info* info) {
+  if (info == nullptr || !valid_dtype(xtype) || B < 1) return LQ_ERR_INVALID_ARG;
+  if (!valid_algo(algo, true)) return LQ_ERR_INVALID_ARG;
+  int64_t L = 0;
+  lq_status s = check_layer(layer, &L);
+  if (s != LQ_OK) return s;
+  s = check_sign_dims(B, layer->N, L);
+  if (s != LQ_OK) return s;
+  if (!mul_ok(B, layer->K, kMaxElems)) return LQ_ERR_UNSUPPORTED;
+  Exec e;
+  s = plan_exec(B, layer->N, L, layer->K, layer->d, layer->D, xtype, algo, true, &e);
+  if (s != LQ_OK) return s;
+  fill_plan_info(e, B, info);
+  return LQ_OK;
+}
+
+lq_status lq_sign_gemm_plan(int64_t B, int64_t N, int64_t L, lq_dtype ztype, lq_algo algo,
+                            lq_plan_info* info) {
+  if (info == nullptr || !valid_dtype(ztype) || B < 1) return LQ_ERR_INVALID_ARG;
+  if (!valid_algo(algo, false)) return LQ_ERR_INVALID_ARG;
+  lq_status s = check_sign_dims(B, N, L);
+  if (s != LQ_OK) return s;
+  Exec e;
+  s = plan_exec(B, N, L, 0, 1, 1, ztype, algo, false, &e);
+  if (s != LQ_OK) return s;
+  fill_plan_info(e, B, info);
+  return LQ_OK;
+}
+
 lq_status lq_linear_workspace_size(const lq_layer* layer, int64_t B, lq_dtype xtype,
                                    size_t* bytes) {
   return lq_linear_workspace_size_ex(layer, B, xtype, LQ_ALGO_AUTO, bytes);
@@ -697,6 +791,23 @@ lq_status lq_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   const size_t n = std::min(ws_bytes, (size_t)LQ_WS_CONTROL_BYTES) / 4;
   if (n == 0) return LQ_OK;
   return hip_status(lq::launch_zero_u32(static_cast<unsigned*>(ws), (int)n, (hipStream_t)stream));
+}
+
+lq_status lq_workspace_status(const void* ws, size_t ws_bytes, void* stream) {
+  if (ws_bytes < (size_t)LQ_WS_CONTROL_BYTES) return LQ_OK;
+  if (!aligned16(ws)) return LQ_ERR_INVALID_ARG;
+  const hipStream_t st = (hipStream_t)stream;
+  uint32_t word = 0;
+  const uint32_t* src = static_cast<const uint32_t*>(ws) + LQ_WS_ERROR_WORD;
+  hipError_t e = hipMemcpyAsync(&word, src, sizeof(word), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_status(e);
+  return word != 0 ? LQ_ERR_DEVICE : LQ_OK;
+}
+
+lq_status lq_debug_fused_timeout(int32_t enable) {
+  lq::set_fused_forced_timeout(enable != 0);
+  return LQ_OK;
 }
 
 static_assert(LQ_ENCODE_MAX_D == lq::kEncodeMaxD && LQ_ENCODE_MAX_SMALL_D == lq::kEncodeMaxSmallD,

@@ -27,6 +27,7 @@
 // and finish counters and advances the epoch. The control words and flags
 // must be zero before the first launch that uses them.
 #include <algorithm>
+#include <atomic>
 
 #include "lq_fp6_mma.h"
 #include "lq_prep.h"
@@ -65,7 +66,8 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(
     int tail_bytes, const void* __restrict__ x, int B, int K, int d, int D, int lhb, float norm,
     const float* __restrict__ c, const float* __restrict__ M, int L, uint8_t* aop, int rec,
     int ncv, unsigned* ctl, int nch, int chunk_bytes, int producers,
-    const float* __restrict__ row_scale, void* __restrict__ y, int y_bf16, int N) {
+    const float* __restrict__ row_scale, void* __restrict__ y, int y_bf16, int N,
+    unsigned max_polls, unsigned wait_skew) {
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr int W = kW;
   constexpr int CT = W * TPC;
@@ -160,10 +162,10 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(
       bool ok = true;
       for (int i = lane; i < n; i += 64) {
         const int t = t0 + i / B, b = i % B;
-        ok = ok && (load_coherent_u32(flags + t * 16 + b) == epoch);
+        ok = ok && (load_coherent_u32(flags + t * 16 + b) == epoch + wait_skew);
       }
       if (__all(ok)) break;
-      if (it >= kMaxPolls) {
+      if (it >= max_polls) {
         if (lane == 0) store_coherent_u32(ctl + kCtlError, 1u);
         break;
       }
@@ -418,6 +420,12 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(
   }
 }
 
+// The test aid: an epoch offset no producer writes (epochs count launches
+// from zero) and a short bound on the polls.
+std::atomic<bool> g_forced_timeout{false};
+constexpr unsigned kForcedPolls = 4;
+constexpr unsigned kForcedSkew = 0x40000000u;
+
 template <int P, int TPC, int kXKind>
 hipError_t launch_fused_t(const uint8_t* packed, const PackedGeom& g, const void* x, int64_t B,
                           int64_t K, int d, int D, int hb, const float* c, const float* M,
@@ -427,6 +435,7 @@ hipError_t launch_fused_t(const uint8_t* packed, const PackedGeom& g, const void
   while ((1 << lhb) < hb) ++lhb;
   const float norm = (lhb % 2 == 0) ? ldexpf(1.0f, -lhb / 2) : (float)(1.0 / sqrt((double)hb));
   if (plan.lds_bytes > 160 * 1024) return hipErrorInvalidValue;
+  const bool forced = g_forced_timeout.load(std::memory_order_relaxed);
   static size_t allowed = 0;
   if (plan.lds_bytes > allowed) {
     const hipError_t e = hipFuncSetAttribute(
@@ -439,10 +448,13 @@ hipError_t launch_fused_t(const uint8_t* packed, const PackedGeom& g, const void
                       dim3(kFusedThreads), plan.lds_bytes, stream, packed, (int)g.panels,
                       g.panel_bytes, g.full_tiles, g.tail_bytes, x, (int)B, (int)K, d, D, lhb, norm,
                       c, M, (int)g.L, op.aop, op.s.rec, op.s.ncv, ctl, plan.nch, plan.chunk_bytes,
-                      plan.producers, row_scale, y, y_bf16 ? 1 : 0, (int)g.N);
+                      plan.producers, row_scale, y, y_bf16 ? 1 : 0, (int)g.N,
+                      forced ? kForcedPolls : kMaxPolls, forced ? kForcedSkew : 0u);
 }
 
 }  // namespace
+
+void set_fused_forced_timeout(bool on) { g_forced_timeout.store(on, std::memory_order_relaxed); }
 
 FusedPlan plan_fused(int64_t B, const PackedGeom& g, const OperandShape& s, int cus) {
   FusedPlan p{};

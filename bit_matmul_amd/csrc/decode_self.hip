@@ -26,7 +26,7 @@
 namespace lq {
 namespace {
 
-constexpr int kSelfWaves = 8;
+constexpr int kSelfWaves = kOneLaunchWaves;
 constexpr int kSelfThreads = 64 * kSelfWaves;
 constexpr int kSelfMaxTiles = 20;        // full tiles of a panel (registers of its 2 wavefronts)
 

@@ -24,9 +24,10 @@
 namespace lq {
 namespace {
 
-constexpr int kSpWaves = 8;
+constexpr int kSpWaves = kOneLaunchWaves;
 constexpr int kSpThreads = 64 * kSpWaves;
-constexpr int kSpPanels = 2 * kSpWaves;     // panels per workgroup (two per wavefront)
+constexpr int kSpPanels = kSplitPanels;     // panels per workgroup (two per wavefront)
+static_assert(kSpPanels == 2 * kSpWaves, "two panels per wavefront");
 constexpr int kSpMaxXLoads = 10;            // x values per thread (whitened span <= 5120)
 constexpr int kSpMaxTiles = 6;              // tiles per group (slots held in registers)
 

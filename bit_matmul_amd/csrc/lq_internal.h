@@ -177,6 +177,13 @@ hipError_t launch_timed(Kernel kernel, dim3 grid, dim3 block, size_t lds, hipStr
 // ---------------------------------------------------------------- launchers
 // Every launcher enqueues on `stream` and returns hipGetLastError().
 
+// Launch shapes of the product kernels that the plan query reports.
+constexpr int kLargeWaves = 4;         // sign_mfma_large_kernel, wspace_kernel
+constexpr int kWsPanelsPerWave = 4;    // wspace_kernel
+constexpr int kValuWaves = 4;          // sign_valu_kernel (one panel per wavefront)
+constexpr int kOneLaunchWaves = 8;     // decode_fused / decode_self / decode_split kernels
+constexpr int kSplitPanels = 2 * kOneLaunchWaves;   // decode_split_kernel: panels per workgroup
+
 hipError_t launch_pack(const int8_t* signs, int64_t N, int64_t L, uint8_t* packed,
                        hipStream_t stream);
 hipError_t launch_unpack(const uint8_t* packed, int64_t N, int64_t L, int8_t* signs,
@@ -242,9 +249,11 @@ struct Fp6Plan {
   size_t lds_bytes; // dynamic LDS per workgroup
   int groups;       // workgroups
 };
-// panels_per_group 0: chosen for this layer alone (fp6_panels_per_group).
-Fp6Plan plan_fp6(int64_t B, const PackedGeom& g, const OperandShape& s, int panels_per_group = 0);
-int fp6_panels_per_group(int64_t panels, const OperandShape& s);
+// panels_per_group 0: chosen for this layer alone (fp6_panels_per_group);
+// device_cus: compute units of the device (0: unknown, taken as 256).
+Fp6Plan plan_fp6(int64_t B, const PackedGeom& g, const OperandShape& s, int device_cus,
+                 int panels_per_group = 0);
+int fp6_panels_per_group(int64_t panels, const OperandShape& s, int device_cus);
 
 // Fused decode (whitening, lift, operand and product in one launch; the
 // operand record of each (tile, batch row) is produced by one workgroup and
@@ -263,6 +272,10 @@ struct FusedPlan {
 };
 // `cus`: compute units of the device (all producers must be co-resident).
 FusedPlan plan_fused(int64_t B, const PackedGeom& g, const OperandShape& s, int cus);
+// Test aid: while set, the loaders of decode_fused launches wait for a
+// publication no producer makes and give up after a few polls (the error
+// word is set; every kernel still runs to its end).
+void set_fused_forced_timeout(bool on);
 hipError_t launch_decode_fused(const uint8_t* packed, const PackedGeom& g, const void* x,
                                bool x_bf16, int64_t B, int64_t K, int d, int D, int hb,
                                const float* c, const float* M, const OperandPlan& op,

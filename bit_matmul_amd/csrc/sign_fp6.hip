@@ -335,19 +335,20 @@ constexpr int tiles_for(int p, int cs) { return cs == 1 && p <= 4 ? 3 : 1; }
 
 }  // namespace
 
-int fp6_panels_per_group(int64_t panels, const OperandShape& s) {
+int fp6_panels_per_group(int64_t panels, const OperandShape& s, int device_cus) {
   // Panels per workgroup: the fewest that still give at most one workgroup
   // per compute unit (so that none streams more than its share), which also
   // lets as many panels as possible share each activation-operand read.
-  const int64_t cus = 256;
+  const int64_t cus = device_cus > 0 ? device_cus : 256;
   const int most = s.cs >= 3 ? 4 : 8;          // register budget
   return (int)std::min<int64_t>(most, std::max<int64_t>(1, (panels + cus - 1) / cus));
 }
 
-Fp6Plan plan_fp6(int64_t B, const PackedGeom& g, const OperandShape& s, int panels_per_group) {
+Fp6Plan plan_fp6(int64_t B, const PackedGeom& g, const OperandShape& s, int device_cus,
+                 int panels_per_group) {
   (void)B;
   Fp6Plan p;
-  p.p = panels_per_group > 0 ? panels_per_group : fp6_panels_per_group(g.panels, s);
+  p.p = panels_per_group > 0 ? panels_per_group : fp6_panels_per_group(g.panels, s, device_cus);
   p.w = waves_for(p.p, s.cs);
   const int budget = 112 * 1024;   // two chunks of activation records
   p.tpc = 1;

@@ -241,7 +241,7 @@ __global__ __launch_bounds__(256) void xpw_kernel(const void* __restrict__ x,
 // ------------------------------------------------------------ product
 // Workgroup: 4 wavefronts; tile 4 PW panels x 16 JB batch rows; wavefront w
 // owns panels w PW .. w PW + PW - 1 and all JB batch tiles.
-constexpr int kWsPW = 4;
+constexpr int kWsPW = kWsPanelsPerWave;
 
 // The DD A operands of one step from the table entries e[0..7] of its 8
 // blocks (entry j: dwords .x = v0 | v1 << 16, .y = v2 | v3 << 16, zero past

@@ -75,7 +75,10 @@ typedef enum lq_status {
   LQ_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, negative size, d > D, ... */
   LQ_ERR_UNSUPPORTED = 2,   /* valid maths but outside this library's limits */
   LQ_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
-  LQ_ERR_HIP = 4            /* a HIP runtime call failed; see lq_last_hip_error */
+  LQ_ERR_HIP = 4,           /* a HIP runtime call failed; see lq_last_hip_error */
+  LQ_ERR_DEVICE = 5         /* a kernel reported a failure of its own (only the
+                               one-launch decode LQ_ALGO_FUSED can: see
+                               lq_workspace_status); that call's output is wrong */
 } lq_status;
 
 typedef enum lq_dtype {
@@ -145,6 +148,7 @@ typedef enum lq_algo {
 
 /* Limits. d and D are runtime parameters: one operator for every rate. */
 #define LQ_MAX_D 64          /* 1 <= d <= D <= LQ_MAX_D */
+#define LQ_MAX_L (1 << 28)   /* lifted columns per row, L = ceil(K/d) * D */
 #define LQ_MAX_HB 1024       /* hb a power of two, 1 <= hb <= 1024, hb | K */
 
 /* Workspace control area (see the conventions above). */
@@ -272,6 +276,52 @@ lq_status lq_linear_algo(const lq_layer* layer, int64_t B, lq_dtype xtype, lq_al
                          lq_algo* resolved);
 lq_status lq_linear_ex(const lq_layer* layer, const void* x, lq_dtype xtype, int64_t B, void* y,
                        lq_dtype ytype, lq_algo algo, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * How a call would run, without running it (host only, launches nothing):
+ * the algorithm (AUTO resolved) and the shape of its sign-product launch,
+ * the one kernel that streams the packed signs (the decode's INT1 x FP GEMM,
+ * review Method). lq_linear_plan takes lq_linear_ex's arguments,
+ * lq_sign_gemm_plan lq_sign_gemm_ex's. Errors: as lq_linear_algo (and as
+ * lq_sign_gemm_workspace_size for lq_sign_gemm_plan), INVALID_ARG for a NULL
+ * info or B < 1.
+ */
+typedef struct lq_plan_info {
+  int32_t algo;              /* the lq_algo that runs */
+  int32_t workgroups;        /* workgroups of the sign-product launch */
+  int32_t waves;             /* wavefronts per workgroup of that launch */
+  int32_t panels;            /* 16-row panels of S per workgroup */
+  int32_t batch_rows;        /* batch rows per workgroup */
+  int32_t ksplit;            /* workgroups that share the same output rows, each
+                                multiplying a part of the reduction (1 = none) */
+} lq_plan_info;
+lq_status lq_linear_plan(const lq_layer* layer, int64_t B, lq_dtype xtype, lq_algo algo,
+                         lq_plan_info* info);
+lq_status lq_sign_gemm_plan(int64_t B, int64_t N, int64_t L, lq_dtype ztype, lq_algo algo,
+                            lq_plan_info* info);
+
+/*
+ * Whether the calls that used a workspace ran correctly: waits for `stream`
+ * (hipStreamSynchronize; not while it is being captured), then reads the
+ * control area's error word. LQ_ERR_DEVICE when it is set: a one-launch
+ * decode (LQ_ALGO_FUSED, [paper] §3 introduction: the whole operator in one
+ * kernel) gave up waiting for the activation operand, so the output of that
+ * call is wrong; the word stays set until lq_workspace_init. LQ_OK otherwise,
+ * and for workspaces shorter than LQ_WS_CONTROL_BYTES (no call that can fail
+ * this way uses those). Errors: INVALID_ARG for a NULL or unaligned ws with
+ * ws_bytes >= LQ_WS_CONTROL_BYTES; LQ_ERR_HIP if the copy or the wait fails.
+ */
+lq_status lq_workspace_status(const void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Test aid for that failure path: while `enable` is non-zero, the loaders of
+ * LQ_ALGO_FUSED launches wait for a publication that no producer makes,
+ * polling only a few times, so every one of them gives up at once and sets
+ * the error word; every kernel still runs to its end and the control words
+ * stay consistent for the next launch (the outputs of those calls are wrong
+ * by construction). Process-wide; 0 restores the normal waits. Host only.
+ */
+lq_status lq_debug_fused_timeout(int32_t enable);
 
 /*
  * For callers that cannot allocate device memory (code under HIP graph

@@ -65,6 +65,7 @@ class DeviceLayer:
             lq.lq_linear_ex(self.struct, x, B, y, algo, ws)
         torch.cuda.synchronize()
         assert control_error(lq, ws) == 0
+        assert lq.lq_workspace_status(ws) == 0
         return y
 
 

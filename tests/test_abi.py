@@ -313,3 +313,62 @@ def test_linear_multi_plan_and_validation():
     ys = (ctypes.c_void_p * 2)(P, P)
     assert LIB.lq_linear_multi(arr, 2, P, LQ_BF16, 1, ys, LQ_BF16, P, two - 16, None) == LQ_ERR_WORKSPACE
     assert LIB.lq_linear_multi(arr, 2, P, LQ_BF16, 0, ys, LQ_BF16, None, 0, None) == LQ_OK   # B = 0
+
+
+# ------------------------------------------------------------ plan queries
+
+from tests.plan_cases import LARGE_PLAN_CASES, case_id  # noqa: E402
+
+
+@pytest.mark.parametrize("case", LARGE_PLAN_CASES, ids=[case_id(c) for c in LARGE_PLAN_CASES])
+def test_large_batch_plan_of_each_parity_shape(case):
+    """Each shape of the large-batch parity tests selects the tiling it is
+    listed for, so every instantiated tiling is compared with the oracle."""
+    N, L, B, zt, pw, jb = case
+    info = _lib.LQPlanInfo()
+    st = LIB.lq_sign_gemm_plan(B, N, L, LQ_BF16 if zt == "bf16" else LQ_F32, 3, ctypes.byref(info))
+    assert st == LQ_OK
+    assert info.algo == 3 and info.waves == 4
+    assert (info.panels // 4, info.batch_rows // 16) == (pw, jb)
+    assert info.workgroups == -(-N // (16 * 4 * pw)) * -(-(-(-B // 16)) // jb)
+
+
+def test_linear_plan_of_the_benchmarked_layers():
+    """lq_linear's choice on the workloads: the small-batch matrix-core
+    product at B <= 16 (bf16 x), W space for the prefill layers, the lifted
+    large-batch product for the Qwen layers at B = 64."""
+    info = _lib.LQPlanInfo()
+    for wl in WORKLOADS.values():
+        for s in wl.layers:
+            lay = LQLayer(s.N, s.K, s.d, s.D, s.hb, 0, P, P, P, P)
+            for B in wl.batches:
+                xt = LQ_F32 if wl.xdtype == "f32" else LQ_BF16
+                assert LIB.lq_linear_plan(ctypes.byref(lay), B, xt, 0, ctypes.byref(info)) == LQ_OK
+                if B > 16:
+                    want = 6 if s.D in (4, 8) and s.d <= 4 else 3
+                else:
+                    want = 1 if xt == LQ_F32 else 2
+                assert info.algo == want, (wl.name, s.name, B)
+                assert info.workgroups > 0 and info.waves > 0 and info.panels > 0
+    assert LIB.lq_linear_plan(None, 1, LQ_BF16, 0, ctypes.byref(info)) == LQ_ERR_INVALID_ARG
+    lay = LQLayer(16, 64, 2, 8, 64, 0, P, P, P, P)
+    assert LIB.lq_linear_plan(ctypes.byref(lay), 0, LQ_BF16, 0, ctypes.byref(info)) == LQ_ERR_INVALID_ARG
+    assert LIB.lq_linear_plan(ctypes.byref(lay), 1, LQ_BF16, 0, None) == LQ_ERR_INVALID_ARG
+
+
+def test_lifted_length_cap():
+    """L above LQ_MAX_L (2^28 lifted columns per row) is rejected: byte
+    offsets inside a panel (2 L) then stay within 32 bits."""
+    assert size(16, 1 << 28, 1, 1)[0] == LQ_OK
+    assert size(16, (1 << 28) + 8, 1, 1)[0] == LQ_ERR_UNSUPPORTED
+    out = ctypes.c_size_t()
+    assert LIB.lq_sign_gemm_workspace_size(1, 16, (1 << 28) + 8, LQ_BF16, 0,
+                                           ctypes.byref(out)) == LQ_ERR_UNSUPPORTED
+
+
+def test_device_status_code_and_short_workspace_status():
+    assert LIB.lq_status_string(5).decode().startswith("LQ_ERR_DEVICE")
+    # a workspace without a control area cannot hold a failure: no device access
+    assert LIB.lq_workspace_status(P, 16, None) == LQ_OK
+    assert LIB.lq_workspace_status(None, 0, None) == LQ_OK
+    assert LIB.lq_workspace_status(MIS, 1 << 20, None) == LQ_ERR_INVALID_ARG

@@ -10,7 +10,11 @@ CPU oracle and with the two-launch small-batch path, through the C ABI.
   multiple of d, hb = 1, d = 1, D = d with M = I, one 16-row panel.
 * One zero-filled workspace reused by many calls of different layers (the
   control words advance an epoch per launch), graph replays, determinism,
-  and the error word staying clear.
+  and the error word staying clear (lq_workspace_status).
+* The failure path, forced from the host (lq_debug_fused_timeout: the
+  loaders wait for a publication no producer makes and give up after a few
+  polls, every kernel still running to its end): lq_workspace_status reports
+  LQ_ERR_DEVICE; after lq_workspace_init the next calls are right again.
 Tolerances (relative L2): fp32 x 2e-5 (four FP6 terms), bf16 x 5e-4 (three).
 """
 import numpy as np
@@ -396,3 +400,31 @@ def test_split_graph_replay(lq):
                         workspace(lq, lq.lq_linear_workspace_size_ex(layer.struct, 1, torch.bfloat16,
                                                                      lq.LQ_ALGO_MFMA_SMALL)))
         torch.cuda.synchronize()
+
+
+def test_fused_failure_is_reported(lq):
+    inp = make_layer_small(512, 4096, 10, 24, 1024, seed=91, B_max=1, xdtype="bf16")
+    layer = DeviceLayer(inp, lq)
+    x = dev(inp.x(1), torch.bfloat16)
+    nbytes = lq.lq_linear_workspace_size_ex(layer.struct, 1, torch.bfloat16, lq.LQ_ALGO_FUSED)
+    ws = workspace(lq, nbytes)
+    y = torch.empty((1, 512), dtype=torch.float32, device=DEV)
+    lq.lq_linear_ex(layer.struct, x, 1, y, lq.LQ_ALGO_FUSED, ws)
+    assert lq.lq_workspace_status(ws) == 0
+    note("lq_linear_ex FUSED with the forced give-up (test aid)")
+    lq.lq_debug_fused_timeout(True)
+    try:
+        lq.lq_linear_ex(layer.struct, x, 1, y, lq.LQ_ALGO_FUSED, ws)
+        lq.lq_linear_ex(layer.struct, x, 1, y, lq.LQ_ALGO_FUSED, ws)
+    finally:
+        lq.lq_debug_fused_timeout(False)
+    assert lq.lq_workspace_status(ws) == lq.LQ_ERR_DEVICE
+    assert lq.lq_workspace_status(ws) == lq.LQ_ERR_DEVICE     # stays set
+    lq.lq_workspace_init(ws)
+    assert lq.lq_workspace_status(ws) == 0
+    for _ in range(3):                                        # the control words are consistent
+        lq.lq_linear_ex(layer.struct, x, 1, y, lq.LQ_ALGO_FUSED, ws)
+        torch.cuda.synchronize()
+        assert lq.lq_workspace_status(ws) == 0
+        want = ref.linear(inp.x(1), inp.c, 1024, inp.M, inp.signs(), inp.row_scale)
+        assert rel_l2(host(y), want) < TOL[torch.bfloat16]

@@ -2,7 +2,12 @@
 
 * Every layer of every workload at its full size and each of its batch
   sizes, in the launch configuration the benchmark times (lq_linear's own
-  dispatch): sampled output rows, recomputed by the oracle one by one.
+  dispatch): sampled output rows, recomputed by the oracle one by one; at
+  batch 1 every output row (the oracle run over chunks of rows), also for
+  the Llama-3-70B gate and up layers through one lq_linear_multi call as the
+  benchmark's decode step runs them. Besides rel-L2, every element must be
+  within 10 x the tolerance of the output's RMS (a fault confined to a few
+  workgroups would show there).
 * The tiny 2.5-bit layer (fp32 activations) in full.
 * Edge cases: empty batch, every batch size 1..17, K not a multiple of d,
   D = d with M = I, hb = 1, a single 16-row panel, D = 32 (the 2-bit LQ-32/16
@@ -68,6 +73,60 @@ def test_full_size_sampled_rows(lq, wl_name, li):
             err = rel_l2(y[np.ix_(bsel, rows)], want)
             assert err < TOL[xd], (B, yd, err)
             assert np.all(np.isfinite(y))
+
+
+def _rows_oracle(inp, spec, x, chunk=8192):
+    """The oracle's operator for every output row, chunk by chunk of rows."""
+    out = np.empty((x.shape[0], spec.N))
+    for r0 in range(0, spec.N, chunk):
+        rows = np.arange(r0, min(spec.N, r0 + chunk))
+        out[:, rows] = ref.linear(x, inp.c, spec.hb, inp.M, inp.signs_rows(rows), inp.row_scale[rows])
+    return out
+
+
+def _check_all(got, want, tol):
+    err = rel_l2(got, want)
+    rms = float(np.sqrt(np.mean(want ** 2)))
+    worst = float(np.max(np.abs(got.astype(np.float64) - want)))
+    assert err < tol, err
+    assert worst <= 10 * tol * rms, (worst, rms)
+    assert np.all(np.isfinite(got))
+    return err
+
+
+@pytest.mark.parametrize("wl_name,li", FULL, ids=[f"{w}-{WORKLOADS[w].layers[i].name}" for w, i in FULL])
+def test_full_size_every_row_batch1(lq, wl_name, li):
+    wl = WORKLOADS[wl_name]
+    spec = wl.layers[li]
+    inp = make_layer(spec, wl, B_max=1)
+    layer = DeviceLayer(inp, lq)
+    xd = _xdtype(wl)
+    x = inp.x(1)
+    y = host(layer.linear(lq, dev(x, xd), 1, torch.float32))
+    err = _check_all(y, _rows_oracle(inp, spec, x), TOL[xd])
+    if xd == torch.bfloat16:
+        assert err < 5e-4            # three FP6 terms per lifted value: ~4e-5 observed
+
+
+def test_full_size_every_row_70b_gate_up_grouped(lq):
+    """The benchmark's grouped call: gate and up of Llama-3-70B (two layers of
+    the gate/up shape with their own weights) on one input, batch 1."""
+    wl = WORKLOADS["llama3_70b"]
+    spec = wl.layers[0]
+    specs = [spec, type(spec)(spec.name + "_up", spec.K, spec.N, spec.d, spec.D, spec.hb, spec.seed + 1000)]
+    inps = [make_layer(s, wl, B_max=1) for s in specs]
+    layers = [DeviceLayer(i, lq) for i in inps]
+    x = inps[0].x(1)
+    xt = dev(x, torch.bfloat16)
+    structs = [l.struct for l in layers]
+    ys = [torch.empty((1, spec.N), dtype=torch.float32, device=DEV) for _ in layers]
+    from tests.gpu_util import workspace
+    ws = workspace(lq, lq.lq_linear_multi_workspace_size(structs, 1, torch.bfloat16))
+    note("lq_linear_multi Llama-3-70B gate+up B=1")
+    lq.lq_linear_multi(structs, xt, 1, ys, ws)
+    torch.cuda.synchronize()
+    for inp, s, y in zip(inps, specs, ys):
+        _check_all(host(y), _rows_oracle(inp, s, x), 1e-2)
 
 
 EDGE = [
