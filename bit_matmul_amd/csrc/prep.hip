@@ -218,8 +218,10 @@ hipError_t launch_prep_table(const void* x, int xkind, int64_t B, int64_t K, con
 OperandShape operand_shape(int64_t B, bool z_bf16) {
   OperandShape s;
   // 4 terms for fp32 z (3 beyond B = 12, where 4 would need a fourth
-  // 16-column set), 3 for bf16 z: at most 48 columns.
-  s.nt = (z_bf16 || 4 * B > 48) ? 3 : 4;
+  // 16-column set: about 2^-20 / 2^-15 of each 32-value block's largest
+  // magnitude); 2 for bf16 z (about 2^-10: finer than a bf16 rounding of z,
+  // which the large-batch path makes); at most 48 columns.
+  s.nt = z_bf16 ? 2 : (4 * B > 48 ? 3 : 4);
   s.ncv = (int)B * s.nt;
   s.cs = (s.ncv + 15) / 16;
   // Records are 128-byte aligned: a cache line never holds parts of two.

@@ -24,18 +24,24 @@
 // (batch row b, term t), the FP6 codes of the t-th residual term of
 // 32-value blocks, the blocks' E8M0 scales, and the per-row plane sums.
 //
-// Work split: a workgroup owns P 16-row panels over the whole reduction
-// length (no communication between workgroups). Its W compute wavefronts
-// take the full tiles in chunks of W*TPC tiles, TPC consecutive tiles each,
-// all P panels per tile, so one activation-operand read from LDS feeds P
-// MFMAs. An extra loader wavefront copies each chunk's activation records
-// into LDS with global_load_lds (double-buffered, one chunk ahead) and
-// computes the partial tail tile from registers. The compute wavefronts
-// keep the packed slots of two chunks in flight; since a wavefront waits for
-// its loads in issue order and it issues nothing else, every tile's MFMAs
-// start as soon as that tile's 16-byte slots have arrived.
+// Work split. A workgroup owns a rectangle of the packed matrix: P 16-row
+// panels times one range of consecutive column tiles (the reduction is cut
+// into `splits` ranges, chosen so that the workgroups stream equal shares
+// of the weights and each range's activation records fit LDS). At entry it
+// copies its range's records into LDS with global_load_lds (issued before
+// anything else, so they are not queued behind the weight stream), and
+// every wavefront requests the packed slots of its first DEPTH tiles. The
+// wavefronts then take the range's tiles round-robin, each keeping DEPTH
+// tiles of slots (P 16-byte loads per tile) requested: no barrier couples
+// them until the end, so the weight stream never waits for another
+// wavefront. One activation-operand read from LDS feeds P panels' MFMAs.
 // The wavefronts' accumulators are added in LDS in a fixed order, the terms
-// and plane sums combined, and y written: deterministic, no atomics.
+// and plane sums combined; with one range the row scale is applied and y
+// written, with several the range's partial row sums go to the workspace
+// (device-coherent stores) and the last range of the panel group to take
+// the group's ticket adds them in range order and writes y, then resets the
+// ticket (graph replays need no memset). Deterministic: fixed summation
+// orders, no floating-point atomics.
 #include <algorithm>
 
 #include "lq_fp6_mma.h"
@@ -45,11 +51,14 @@ namespace {
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
-template <int P, int CS, int W, int TPC>
-__global__ __launch_bounds__(64 * (W + 1)) void sign_fp6_kernel(SignTable tab, int rec, int ncv,
-                                                                int B, int chunk_bytes, int y_bf16) {
+__device__ __forceinline__ void lds_dma16(const void* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
+template <int P, int CS, int W, int DEPTH>
+__global__ __launch_bounds__(64 * W) void sign_fp6_kernel(SignTable tab, int rec, int ncv, int B,
+                                                          int red_off, int y_bf16) {
   extern __shared__ __align__(16) uint8_t smem[];
-  constexpr int CT = W * TPC;                       // full tiles per chunk
   // this workgroup's layer (a wave-uniform choice among at most kMultiMax)
   int li = 0;
 #pragma unroll
@@ -59,33 +68,88 @@ __global__ __launch_bounds__(64 * (W + 1)) void sign_fp6_kernel(SignTable tab, i
   const uint8_t* __restrict__ packed = ly.packed;
   const uint8_t* __restrict__ aop = ly.aop;
   const float* __restrict__ row_scale = ly.row_scale;
-  void* __restrict__ y = ly.y;
   const int64_t panel_bytes = ly.panel_bytes;
   const int panels = ly.panels, full_tiles = ly.full_tiles, tail_bytes = ly.tail_bytes;
-  const int nch = ly.nch, N = ly.N;
+  const int N = ly.N, splits = ly.splits;
+  const int ext_tiles = full_tiles + (tail_bytes > 0 ? 1 : 0);
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int g = lane >> 4, r = lane & 15;
-  const bool loader = wave == W;
-  const int pbase = ((int)blockIdx.x - ly.group_begin) * P;
+  const int wgi = (int)blockIdx.x - ly.group_begin;
+  const int pg = wgi / splits, sp = wgi - pg * splits;
+  const int pbase = pg * P;
+  const int t0 = sp * ly.tiles;
+  const int t1 = min(ext_tiles, t0 + ly.tiles);
+  const bool has_tail = tail_bytes > 0 && t1 == ext_tiles;
+  const int nfull = t1 - t0 - (has_tail ? 1 : 0);    // full tiles of the range
+  // this wavefront's full tiles: t0 + wave + j W, j < nk
+  const int nk = wave < nfull ? (nfull - wave + W - 1) / W : 0;
+
+  // LDS: row scales (1 KB), the range's records (red_off - 1024 bytes, a
+  // whole number of KB), the tail tile's slots (P KB); the final reduction
+  // reuses everything after the row scales.
+  float* rs_lds = reinterpret_cast<float*>(smem);
+  uint8_t* rec_lds = smem + 1024;
+  uint8_t* tslot_lds = smem + red_off;
 
   // This lane's MFMA column in each column set; unused columns read the
   // set's last column (their products are never read).
-  int boff[CS], soff[CS];
+  int boff[CS], soff[CS], u_str[CS];
 #pragma unroll
   for (int cs = 0; cs < CS; ++cs) {
     const int ncs = max(1, min(16, ncv - 16 * cs));
     const int col = min(r, ncs - 1);
     boff[cs] = aop_data_offset(cs, 0, g, col, ncs);
     soff[cs] = aop_scale_offset(ncv, cs, g, col, ncs);
+    u_str[cs] = aop_u_stride(ncs);
   }
-  int u_str[CS];                                    // bytes between the u blocks of a set
-#pragma unroll
-  for (int cs = 0; cs < CS; ++cs) u_str[cs] = aop_u_stride(max(1, min(16, ncv - 16 * cs)));
   const int tpoff = aop_tpart_offset(ncv) + 4 * min(lane, B - 1);
 
   const uint8_t* prow[P];
 #pragma unroll
   for (int p = 0; p < P; ++p) prow[p] = packed + (int64_t)min(pbase + p, panels - 1) * panel_bytes;
+
+  // ---- 1. the range's activation records, the row scales and the tail
+  // tile's packed bytes into LDS, all landed before any weight is requested:
+  // requested together with the weight stream they would queue behind it
+  // (a compute unit returns its vector-memory requests roughly in order, and
+  // the stream fills every memory queue), and with no copy in flight the
+  // compiler's waits for the slot loads below stay exact.
+  {
+    const uint8_t* src = aop + (int64_t)t0 * rec + 16 * lane;
+    const int bytes = (t1 - t0) * rec;
+    for (int off = wave * 1024; off < bytes; off += W * 1024) lds_dma16(src + off, rec_lds + off);
+    if (wave == 0) {
+      const int n4 = min(pbase * kPanelRows + 4 * lane, N - 4);   // rows past N: never used
+      lds_dma16(row_scale + n4, reinterpret_cast<uint8_t*>(rs_lds));
+    }
+    if (has_tail && wave == W - 1) {
+      const int tb = kPanelRows * tail_bytes;                    // a multiple of 16, <= 1008
+      const int o = min(16 * lane, tb - 16);
+#pragma unroll
+      for (int p = 0; p < P; ++p)
+        lds_dma16(prow[p] + (int64_t)full_tiles * kTileBytes + o, tslot_lds + 1024 * p);
+    }
+  }
+
+  __builtin_amdgcn_s_waitcnt(0);
+  wg_barrier();
+
+  // ---- 2. packed slots, DEPTH tiles ahead. Loads are issued on every path
+  // (past the wavefront's last tile every lane reads the panel's first 16
+  // bytes, unused), so that the count of loads issued after any given one
+  // is fixed and the waits are exact.
+  uint4 A[DEPTH][P];
+  auto issue = [&](int j, uint4 (&S)[P]) {
+    const int off = j < nk ? (t0 + wave + j * W) * kTileBytes + 16 * lane : 0;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      // each weight byte is read once per call: non-temporal
+      const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(prow[p] + off));
+      S[p] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+  };
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) issue(d, A[d]);
 
   f32x4 acc[P][CS];
 #pragma unroll
@@ -93,28 +157,6 @@ __global__ __launch_bounds__(64 * (W + 1)) void sign_fp6_kernel(SignTable tab, i
 #pragma unroll
     for (int cs = 0; cs < CS; ++cs) acc[p][cs] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
   float tacc = 0.0f;
-
-  uint4 A0[TPC][P], A1[TPC][P];
-  const int last_full = max(full_tiles - 1, 0);
-  // Packed slots of chunk c. Past the last chunk every lane reads the same
-  // 16 bytes instead (one cache line; the registers are not used): the loads
-  // are issued on every path, so that no register ever merges two values (a
-  // merge would make the compiler wait for the loads in flight).
-  auto issue_A = [&](int c, uint4 (&A)[TPC][P]) {
-    const bool live = c < nch;
-#pragma unroll
-    for (int q = 0; q < TPC; ++q) {
-      const int t = min(c * CT + wave * TPC + q, last_full);
-      const int off = live ? t * kTileBytes + 16 * lane : 0;
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        // Each weight byte is read once per call: a non-temporal load keeps
-        // the stream from displacing the activation records in the caches.
-        const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(prow[p] + off));
-        A[q][p] = make_uint4(v.x, v.y, v.z, v.w);
-      }
-    }
-  };
   // The MFMAs of one tile whose activation record starts at `recp` (LDS).
   auto tile_mfma = [&](const uint8_t* recp, const uint4 (&S)[P]) {
     i32x8 bop[CS][4];
@@ -126,259 +168,281 @@ __global__ __launch_bounds__(64 * (W + 1)) void sign_fp6_kernel(SignTable tab, i
       for (int u = 0; u < 4; ++u) bop[cs][u] = lds_b_operand(recp + boff[cs] + u * u_str[cs]);
     }
     tacc += *reinterpret_cast<const float*>(recp + tpoff);
+    // Word u of every panel before word u + 1: consecutive MFMAs go to
+    // different accumulators, so none waits for the one before it.
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int cs = 0; cs < CS; ++cs) acc[p][cs] = mfma_fp4_fp6<0>(S[p].x, bop[cs][0], sc[cs], acc[p][cs]);
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int cs = 0; cs < CS; ++cs) acc[p][cs] = mfma_fp4_fp6<1>(S[p].y, bop[cs][1], sc[cs], acc[p][cs]);
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int cs = 0; cs < CS; ++cs) acc[p][cs] = mfma_fp4_fp6<2>(S[p].z, bop[cs][2], sc[cs], acc[p][cs]);
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int cs = 0; cs < CS; ++cs) acc[p][cs] = mfma_fp4_fp6<3>(S[p].w, bop[cs][3], sc[cs], acc[p][cs]);
+  };
+
+
+  // ---- 3. the tail tile first (its slots from the row-major tail bytes),
+  // by the wavefront whose turn it would be, then the full tiles
+  if (has_tail && wave == nfull % W) {
+    uint4 TS[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
+      // slot (g, r): bytes 16u + 4g .. + 3 of row r, zero past the row's tail
+      const uint8_t* row = tslot_lds + 1024 * p + r * tail_bytes;
+      uint32_t w[4];
 #pragma unroll
-      for (int cs = 0; cs < CS; ++cs) {
-        acc[p][cs] = mfma_fp4_fp6<0>(S[p].x, bop[cs][0], sc[cs], acc[p][cs]);
-        acc[p][cs] = mfma_fp4_fp6<1>(S[p].y, bop[cs][1], sc[cs], acc[p][cs]);
-        acc[p][cs] = mfma_fp4_fp6<2>(S[p].z, bop[cs][2], sc[cs], acc[p][cs]);
-        acc[p][cs] = mfma_fp4_fp6<3>(S[p].w, bop[cs][3], sc[cs], acc[p][cs]);
-      }
-    }
-  };
-  auto dma_chunk = [&](int c, uint8_t* dst) {
-    const int t0 = c * CT;
-    const int bytes = min(CT, full_tiles - t0) * rec;
-    const uint8_t* src = aop + (int64_t)t0 * rec + 16 * lane;
-    for (int off = 0; off < bytes; off += 1024)
-      __builtin_amdgcn_global_load_lds((const void*)(src + off),
-                                       (__attribute__((address_space(3))) void*)(dst + off), 16, 0, 0);
-  };
-
-  // LDS: row scales (1 KB), chunk buffers 0 and 1, the tail tile's record
-  // and slots; the final reduction reuses everything after the row scales.
-  float* rs_lds = reinterpret_cast<float*>(smem);
-  uint8_t* buf0 = smem + 1024;
-  uint8_t* buf1 = buf0 + chunk_bytes;
-
-  // ---- Pipeline. A compute unit serves its vector-memory requests roughly
-  // in order, so the activation records (L2 hits) must be requested before
-  // the HBM traffic that would otherwise delay them: the loader requests
-  // chunks 0 and 1, the tail tile and the row scales first; a barrier then
-  // releases the compute wavefronts' requests for the packed slots of chunks
-  // 0 and 1. After multiplying chunk c, the loader requests chunk c + 2 into
-  // the freed buffer before a barrier that releases the slot requests of
-  // chunk c + 2, so each compute wavefront keeps two chunks of slots
-  // requested and each copy lands a chunk ahead of its use.
-  // The two roles run separate code with the same sequence of barriers, so
-  // the compute wavefronts' waits on their slot loads never include the
-  // loader's copies (which the compiler would otherwise have to assume may
-  // still be in flight). The tail tile (its record and the P panels'
-  // row-major tail bytes) is multiplied by the loader while the compute
-  // wavefronts work on the first chunk.
-  const bool tail = tail_bytes > 0;
-  uint8_t* trec_lds = buf1 + chunk_bytes;
-  uint8_t* tslot_lds = trec_lds + ((rec + 1023) / 1024) * 1024;
-
-  if (loader) {
-    // Row scales of the workgroup's rows (16 bytes per lane, clamped to N).
-    const int n4 = min(pbase * kPanelRows + 4 * lane, N - 4);
-    __builtin_amdgcn_global_load_lds((const void*)(row_scale + n4),
-                                     (__attribute__((address_space(3))) void*)rs_lds, 16, 0, 0);
-    if (nch > 0) dma_chunk(0, buf0);
-    if (nch > 1) dma_chunk(1, buf1);
-    if (tail) {
-      const uint8_t* trec = aop + (int64_t)full_tiles * rec + 16 * lane;
-      for (int off = 0; off < rec; off += 1024)
-        __builtin_amdgcn_global_load_lds((const void*)(trec + off),
-                                         (__attribute__((address_space(3))) void*)(trec_lds + off), 16, 0, 0);
-      const int tb = kPanelRows * tail_bytes;         // a multiple of 16, at most 1008
-      const int o = min(16 * lane, tb - 16);
+      for (int u = 0; u < 4; ++u) {
+        uint32_t v = 0;
 #pragma unroll
-      for (int p = 0; p < P; ++p)
-        __builtin_amdgcn_global_load_lds((const void*)(prow[p] + (int64_t)full_tiles * kTileBytes + o),
-                                         (__attribute__((address_space(3))) void*)(tslot_lds + 1024 * p), 16, 0, 0);
-    }
-    wg_barrier();
-    __builtin_amdgcn_s_waitcnt(0);                    // chunks 0, 1, the tail, the row scales
-    wg_barrier();
-    // The tail tile while the compute wavefronts multiply the first chunk
-    // (its record and slots landed with chunk 0): at the end it would delay
-    // the final reduction.
-    if (tail) {
-      // Slot (g, r) of the tail: bytes 16u + 4g .. + 3 of row r (zero past
-      // the row's tail_bytes), as in load_tail_slot.
-      uint4 TS[P];
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        const uint8_t* row = tslot_lds + 1024 * p + r * tail_bytes;
-        uint32_t w[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          uint32_t v = 0;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int t = 16 * u + 4 * g + k;
-            const uint32_t byte = row[min(t, tail_bytes - 1)];       // unconditional read
-            v |= (byte & (t < tail_bytes ? 0xFFu : 0u)) << (8 * k);
-          }
-          w[u] = v;
+        for (int k = 0; k < 4; ++k) {
+          const int t = 16 * u + 4 * g + k;
+          const uint32_t byte = row[min(t, tail_bytes - 1)];      // unconditional read
+          v |= (byte & (t < tail_bytes ? 0xFFu : 0u)) << (8 * k);
         }
-        TS[p] = make_uint4(w[0], w[1], w[2], w[3]);
+        w[u] = v;
       }
-      tile_mfma(trec_lds, TS);
+      TS[p] = make_uint4(w[0], w[1], w[2], w[3]);
     }
-    for (int c = 0; c < nch; c += 2) {
+    tile_mfma(rec_lds + nfull * rec, TS);
+  }
+  for (int j0 = 0; j0 < nk; j0 += DEPTH) {
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {                   // step c + k
-        __builtin_amdgcn_s_waitcnt(0);                // chunk c + k + 1 is in LDS
-        wg_barrier();
-        if (c + k + 2 < nch) dma_chunk(c + k + 2, k == 0 ? buf0 : buf1);
-        wg_barrier();
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-  } else {
-    wg_barrier();
-    issue_A(0, A0);
-    issue_A(1, A1);
-    wg_barrier();
-    // Step c: chunk c is in LDS (`cur`), its slots (A) are requested.
-    auto step = [&](int c, uint4 (&A)[TPC][P], uint8_t* cur) {
-#pragma unroll
-      for (int q = 0; q < TPC; ++q) {
-        const int j = wave * TPC + q;                 // tile within the chunk
-        if (c * CT + j < full_tiles) tile_mfma(cur + j * rec, A[q]);
-      }
-      wg_barrier();                                   // `cur` and A are free
-      wg_barrier();                                   // chunk c + 2 requested
-      issue_A(c + 2, A);
-    };
-    // Unrolled by two for the two register sets; an odd chunk count ends
-    // with one empty step (no tiles).
-    for (int c = 0; c < nch; c += 2) {
-      step(c, A0, buf0);
-      step(c + 1, A1, buf1);
+    for (int d = 0; d < DEPTH; ++d) {
+      const int j = j0 + d;
+      if (j < nk) tile_mfma(rec_lds + (wave + j * W) * rec, A[d]);
+      issue(j + DEPTH, A[d]);
     }
   }
-  wg_barrier();                                      // LDS past the row scales is reused below
+  __builtin_amdgcn_s_waitcnt(0);                     // the unused trailing loads
+  wg_barrier();                                      // records are no longer read
 
-  // ---- add the wavefronts' accumulators in a fixed order and write y.
-  uint8_t* red_base = buf0;
-  f32x4* red = reinterpret_cast<f32x4*>(red_base);                   // [W+1][P][CS][64]
-  float* tred = reinterpret_cast<float*>(red_base + (W + 1) * P * CS * 64 * 16);   // [W+1][16]
+  // ---- 4. add the wavefronts' accumulators in a fixed order. Compact
+  // layout: only the columns that hold a (batch row, term).
+  const int NC = min(16, ncv);
+  f32x4* red = reinterpret_cast<f32x4*>(smem + 1024);               // [W][P][CS][4][NC]
+  float* tred = reinterpret_cast<float*>(smem + 1024 + W * P * CS * 4 * NC * 16);   // [W][16]
 #pragma unroll
   for (int p = 0; p < P; ++p)
 #pragma unroll
-    for (int cs = 0; cs < CS; ++cs) red[((wave * P + p) * CS + cs) * 64 + lane] = acc[p][cs];
+    for (int cs = 0; cs < CS; ++cs)
+      if (r < min(16, ncv - 16 * cs)) red[(((wave * P + p) * CS + cs) * 4 + g) * NC + r] = acc[p][cs];
   if (lane < 16) tred[wave * 16 + lane] = tacc;
   wg_barrier();
 
-  // One output (panel p, row, batch row b) per thread and pass: every LDS
-  // read is issued before the sums (fixed order: terms, then wavefronts).
-  const int nt = ncv / B;                           // 1..4
+  // One output (panel p, row, batch row b) per thread and pass, the terms'
+  // columns read unconditionally (a term index past nt repeats the last,
+  // weighted 0), summed in a fixed order: wavefronts, then terms.
+  const int nt = ncv / B;                           // terms per batch row, 2..4
+  void* __restrict__ y = ly.y;
+  float* __restrict__ partial = ly.partial;
   const int items = P * B * 16;
-  for (int item = threadIdx.x; item < items; item += 64 * (W + 1)) {
+  for (int item = threadIdx.x; item < items; item += 64 * W) {
     const int row = item & 15;
-    const int b = (item >> 4) % B;
-    const int p = (item >> 4) / B;
-    float v[W + 1][4], tv[W + 1];
+    const int pb = item >> 4;
+    const int p = pb / B, b = pb - (pb / B) * B;
+    const int gi = row >> 2, ri = row & 3;
+    float v[W][4], tv[W];
 #pragma unroll
-    for (int w = 0; w <= W; ++w) {
+    for (int w = 0; w < W; ++w) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int cc = b * nt + min(t, nt - 1);
-        const int l = 16 * (row >> 2) + (cc & 15);
-        v[w][t] = red[((w * P + p) * CS + (cc >> 4)) * 64 + l][row & 3];
+        v[w][t] = red[(((w * P + p) * CS + (cc >> 4)) * 4 + gi) * NC + (cc & 15)][ri];
       }
       tv[w] = tred[w * 16 + b];
     }
-    const float rs = rs_lds[p * kPanelRows + row];
     float acc_s = 0.0f, tp = 0.0f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      if (t < nt) {
+      const float keep = t < nt ? 1.0f : 0.0f;
 #pragma unroll
-        for (int w = 0; w <= W; ++w) acc_s += v[w][t];
-      }
+      for (int w = 0; w < W; ++w) acc_s = fmaf(v[w][t], keep, acc_s);
     }
 #pragma unroll
-    for (int w = 0; w <= W; ++w) tp += tv[w];
-    const float out = rs * (acc_s + tp);
+    for (int w = 0; w < W; ++w) tp += tv[w];
+    const float val = acc_s + tp;
     const int n = (pbase + p) * kPanelRows + row;
     if (pbase + p < panels) {
-      if (y_bf16)
-        reinterpret_cast<uint16_t*>(y)[(int64_t)b * N + n] = (uint16_t)f32_to_bf16_bits(out);
-      else
-        reinterpret_cast<float*>(y)[(int64_t)b * N + n] = out;
+      if (splits > 1) {
+        store_coherent(partial + ((int64_t)sp * B + b) * N + n, val);
+      } else {
+        const float out = rs_lds[p * kPanelRows + row] * val;
+        if (y_bf16)
+          reinterpret_cast<uint16_t*>(y)[(int64_t)b * N + n] = (uint16_t)f32_to_bf16_bits(out);
+        else
+          reinterpret_cast<float*>(y)[(int64_t)b * N + n] = out;
+      }
     }
   }
+  if (splits == 1) return;
+
+  // ---- 5. the panel group's last range adds the partials in range order
+  __shared__ int s_last;
+  unsigned* ticket = ly.tickets + pg;
+  if (!last_ticket(ticket, splits, &s_last)) return;
+  for (int item = threadIdx.x; item < items; item += 64 * W) {
+    const int row = item & 15;
+    const int b = (item >> 4) % B;
+    const int p = (item >> 4) / B;
+    const int n = (pbase + p) * kPanelRows + row;
+    if (pbase + p >= panels) continue;
+    float v = 0.0f;
+    for (int q = 0; q < splits; ++q) v += load_coherent(partial + ((int64_t)q * B + b) * N + n);
+    const float out = rs_lds[p * kPanelRows + row] * v;
+    if (y_bf16)
+      reinterpret_cast<uint16_t*>(y)[(int64_t)b * N + n] = (uint16_t)f32_to_bf16_bits(out);
+    else
+      reinterpret_cast<float*>(y)[(int64_t)b * N + n] = out;
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int P, int CS, int W, int TPC>
+constexpr int kRecLdsMax = 128 * 1024;             // LDS for a range's records
+
+// Wavefronts per workgroup, and the slot tiles each keeps requested (P
+// 16-byte loads per tile). Eight wavefronts (two per SIMD, 256 registers
+// each) up to 12 panels; four (one per SIMD) beyond, whose slot and
+// accumulator registers would not fit 256.
+constexpr int waves_for(int p) { return p >= 14 ? 4 : 8; }
+constexpr int depth_for(int p) { return p <= 4 ? 4 : (p <= 8 ? 3 : (p <= 12 ? 2 : 3)); }
+
+template <int P, int CS>
 hipError_t launch_fp6_t(const SignTable& tab, int groups, const OperandShape& s, int64_t B,
                         bool y_bf16, const Fp6Plan& plan, hipStream_t stream) {
+  constexpr int W = waves_for(P), DEPTH = depth_for(P);
+  if (plan.w != W) return hipErrorInvalidValue;
   const dim3 grid((unsigned)groups);
-  const dim3 block(64 * (W + 1));
+  const dim3 block(64 * W);
   if (plan.lds_bytes > 160 * 1024) return hipErrorInvalidValue;   // a compute unit's LDS
   // Dynamic LDS beyond the default 64 KB limit has to be allowed per kernel.
   static size_t allowed = 0;
   if (plan.lds_bytes > allowed) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&sign_fp6_kernel<P, CS, W, TPC>),
+        reinterpret_cast<const void*>(&sign_fp6_kernel<P, CS, W, DEPTH>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)plan.lds_bytes);
     if (e != hipSuccess) return e;
     allowed = plan.lds_bytes;
   }
-  return launch_timed(sign_fp6_kernel<P, CS, W, TPC>, grid, block, plan.lds_bytes, stream, tab,
-                      s.rec, s.ncv, (int)B, plan.chunk_bytes, y_bf16 ? 1 : 0);
+  return launch_timed(sign_fp6_kernel<P, CS, W, DEPTH>, grid, block, plan.lds_bytes, stream, tab,
+                      s.rec, s.ncv, (int)B, plan.red_off, y_bf16 ? 1 : 0);
 }
 
-// Compute wavefronts and tiles per wavefront per chunk for each column-set
-// count: wider operands take fewer tiles per chunk so that two chunks of
-// activation records fit in LDS.
-// (Registers: with W + 1 wavefronts a SIMD runs up to ceil((W + 1) / 4) of
-// them, each with 512 / that many VGPRs.)
-constexpr int waves_for(int p, int cs) { return cs == 1 ? (p >= 4 ? 4 : 8) : (cs == 2 && p < 8 ? 4 : 2); }
-constexpr int tiles_for(int p, int cs) { return cs == 1 && p <= 4 ? 3 : 1; }
+// Panels per workgroup instantiated for each count of 16-column sets
+// (registers: P x CS accumulator quads, DEPTH x P slot quads).
+constexpr int kPanelsCS1[] = {1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16};
+constexpr int kPanelsCS2[] = {1, 2, 3, 4, 6};
+constexpr int kPanelsCS3[] = {1, 2, 3, 4};
 
 }  // namespace
 
-int fp6_panels_per_group(int64_t panels, const OperandShape& s, int device_cus) {
-  // Panels per workgroup: the fewest that still give at most one workgroup
-  // per compute unit (so that none streams more than its share), which also
-  // lets as many panels as possible share each activation-operand read.
-  const int64_t cus = device_cus > 0 ? device_cus : 256;
-  const int most = s.cs >= 3 ? 4 : 8;          // register budget
-  return (int)std::min<int64_t>(most, std::max<int64_t>(1, (panels + cus - 1) / cus));
+// Reduction ranges and LDS of a workgroup of P panels for one layer.
+static void fill_ranges(Fp6Plan* pl, const PackedGeom& g, const OperandShape& s, int S) {
+  const int ext = g.ext_tiles;
+  pl->tiles = (ext + S - 1) / S;
+  pl->splits = (ext + pl->tiles - 1) / pl->tiles;    // no empty range
+  pl->pgroups = (int)((g.panels + pl->p - 1) / pl->p);
+  pl->groups = pl->pgroups * pl->splits;
+  const int recs = ((pl->tiles * s.rec + 1023) / 1024) * 1024;
+  const int nc = std::min(16, s.ncv);
+  pl->w = waves_for(pl->p);
+  const size_t red = (size_t)pl->w * pl->p * s.cs * 4 * nc * 16 + (size_t)pl->w * 16 * 4;
+  pl->red_off = 1024 + recs;
+  pl->lds_bytes = std::max((size_t)pl->red_off + (size_t)1024 * pl->p, 1024 + red);
+  pl->partial_bytes = 0;
 }
 
 Fp6Plan plan_fp6(int64_t B, const PackedGeom& g, const OperandShape& s, int device_cus,
                  int panels_per_group) {
   (void)B;
-  Fp6Plan p;
-  p.p = panels_per_group > 0 ? panels_per_group : fp6_panels_per_group(g.panels, s, device_cus);
-  p.w = waves_for(p.p, s.cs);
-  const int budget = 112 * 1024;   // two chunks of activation records
-  p.tpc = 1;
-  const int tpc = tiles_for(p.p, s.cs);
-  if (tpc > 1 && 2 * p.w * tpc * s.rec + 2048 <= budget) p.tpc = tpc;
-  const int ct = p.w * p.tpc;
-  p.nch = (g.full_tiles + ct - 1) / ct;
-  p.chunk_bytes = ((ct * s.rec + 1023) / 1024) * 1024;
-  const size_t red = (size_t)(p.w + 1) * p.p * s.cs * 64 * 16 + (size_t)(p.w + 1) * 16 * 4;
-  const size_t tail = (size_t)((s.rec + 1023) / 1024) * 1024 + (size_t)1024 * p.p;
-  p.lds_bytes = 1024 + std::max((size_t)2 * p.chunk_bytes + tail, red);
-  p.groups = (int)((g.panels + p.p - 1) / p.p);
-  return p;
+  const int64_t cus = device_cus > 0 ? device_cus : 256;
+  const int* cand = s.cs == 1 ? kPanelsCS1 : (s.cs == 2 ? kPanelsCS2 : kPanelsCS3);
+  const int ncand = s.cs == 1 ? 12 : (s.cs == 2 ? 5 : 4);
+  const int ext = g.ext_tiles;
+  const int smin = std::max(1, (ext * s.rec + kRecLdsMax - 1) / kRecLdsMax);
+  // The rectangle that minimises the packed kilobytes the busiest compute
+  // unit streams (workgroups beyond one per unit queue behind it), counting
+  // a split row as kSplitCost kilobytes more (the hand-off of the partial
+  // sums through device-coherent memory and a ticket: several microseconds
+  // of latency); then the most panels per workgroup (each operand read from
+  // LDS feeds them all, and the records are copied by fewer workgroups);
+  // then the fewest ranges.
+  constexpr int64_t kSplitCost = 128;
+  Fp6Plan best{};
+  int64_t best_load = -1;
+  for (int ci = 0; ci < ncand; ++ci) {
+    const int P = cand[ci];
+    if (panels_per_group > 0 && P != panels_per_group) continue;
+    const int64_t pgroups = (g.panels + P - 1) / P;
+    for (int S = smin; S <= ext; ++S) {
+      const int T = (ext + S - 1) / S;
+      const int Se = (ext + T - 1) / T;
+      if (Se > 1 && pgroups > kSplitTickets) break;
+      const int64_t wgs = pgroups * Se;
+      const int64_t load = ((wgs + cus - 1) / cus) * P * T + (Se > 1 ? kSplitCost : 0);
+      const bool better = best_load < 0 || load < best_load ||
+                          (load == best_load && (P > best.p || (P == best.p && Se < best.splits)));
+      if (better) {
+        best_load = load;
+        best.p = P;
+        fill_ranges(&best, g, s, S);
+      }
+      if (wgs >= cus) break;                       // more ranges only add hand-offs
+    }
+  }
+  if (best_load < 0) {                             // (cannot happen: P = 1, S = smin fits)
+    best.p = 1;
+    fill_ranges(&best, g, s, smin);
+  }
+  return best;
+}
+
+Fp6Plan plan_fp6_group(int64_t B, const PackedGeom* gs, int n, const OperandShape& s,
+                       int device_cus) {
+  // The layers' panels as one matrix of the longest rows: one P and one
+  // count of reduction ranges for all of them.
+  PackedGeom all = gs[0];
+  int64_t panels = 0;
+  for (int i = 0; i < n; ++i) {
+    panels += gs[i].panels;
+    if (gs[i].ext_tiles > all.ext_tiles) all = gs[i];
+  }
+  all.panels = panels;
+  return plan_fp6(B, all, s, device_cus);
+}
+
+Fp6Plan plan_fp6_layer(const Fp6Plan& group, const PackedGeom& g, const OperandShape& s) {
+  Fp6Plan pl = group;
+  fill_ranges(&pl, g, s, group.splits);
+  return pl;
 }
 
 namespace {
 
 SignLayer sign_layer(const uint8_t* packed, const PackedGeom& g, const uint8_t* aop,
-                     const float* row_scale, void* y, int nch, int group_begin) {
+                     const float* row_scale, void* y, const Fp6Plan& plan, float* partial,
+                     unsigned* tickets, int group_begin) {
   SignLayer l;
   l.packed = packed;
   l.aop = aop;
   l.row_scale = row_scale;
   l.y = y;
+  l.partial = partial;
+  l.tickets = tickets;
   l.panel_bytes = g.panel_bytes;
   l.panels = (int)g.panels;
   l.full_tiles = (int)g.full_tiles;
   l.tail_bytes = (int)g.tail_bytes;
-  l.nch = nch;
   l.N = (int)g.N;
+  l.splits = plan.splits;
+  l.tiles = plan.tiles;
   l.group_begin = group_begin;
   return l;
 }
@@ -386,15 +450,13 @@ SignLayer sign_layer(const uint8_t* packed, const PackedGeom& g, const uint8_t* 
 hipError_t launch_fp6_table(const SignTable& tab, int groups, const OperandShape& s, int64_t B,
                             bool y_bf16, const Fp6Plan& plan, hipStream_t stream) {
   (void)hipGetLastError();   // clear a stale error of an earlier runtime call
-#define LQ_FP6_CASE(P_, CS_, TPC_)                                                          \
-  if (plan.p == P_ && s.cs == CS_ && plan.tpc == TPC_ && plan.w == waves_for(P_, CS_))      \
-    return launch_fp6_t<P_, CS_, waves_for(P_, CS_), TPC_>(tab, groups, s, B, y_bf16, plan, stream);
-  LQ_FP6_CASE(1, 1, 3) LQ_FP6_CASE(2, 1, 3) LQ_FP6_CASE(3, 1, 3) LQ_FP6_CASE(4, 1, 3)
-  LQ_FP6_CASE(1, 1, 1) LQ_FP6_CASE(2, 1, 1) LQ_FP6_CASE(3, 1, 1) LQ_FP6_CASE(4, 1, 1)
-  LQ_FP6_CASE(5, 1, 1) LQ_FP6_CASE(6, 1, 1) LQ_FP6_CASE(7, 1, 1) LQ_FP6_CASE(8, 1, 1)
-  LQ_FP6_CASE(1, 2, 1) LQ_FP6_CASE(2, 2, 1) LQ_FP6_CASE(3, 2, 1) LQ_FP6_CASE(4, 2, 1)
-  LQ_FP6_CASE(5, 2, 1) LQ_FP6_CASE(6, 2, 1) LQ_FP6_CASE(7, 2, 1) LQ_FP6_CASE(8, 2, 1)
-  LQ_FP6_CASE(1, 3, 1) LQ_FP6_CASE(2, 3, 1) LQ_FP6_CASE(3, 3, 1) LQ_FP6_CASE(4, 3, 1)
+#define LQ_FP6_CASE(P_, CS_)                                                            \
+  if (plan.p == P_ && s.cs == CS_) return launch_fp6_t<P_, CS_>(tab, groups, s, B, y_bf16, plan, stream);
+  LQ_FP6_CASE(1, 1) LQ_FP6_CASE(2, 1) LQ_FP6_CASE(3, 1) LQ_FP6_CASE(4, 1) LQ_FP6_CASE(5, 1)
+  LQ_FP6_CASE(6, 1) LQ_FP6_CASE(7, 1) LQ_FP6_CASE(8, 1) LQ_FP6_CASE(10, 1) LQ_FP6_CASE(12, 1)
+  LQ_FP6_CASE(14, 1) LQ_FP6_CASE(16, 1)
+  LQ_FP6_CASE(1, 2) LQ_FP6_CASE(2, 2) LQ_FP6_CASE(3, 2) LQ_FP6_CASE(4, 2) LQ_FP6_CASE(6, 2)
+  LQ_FP6_CASE(1, 3) LQ_FP6_CASE(2, 3) LQ_FP6_CASE(3, 3) LQ_FP6_CASE(4, 3)
 #undef LQ_FP6_CASE
   return hipErrorInvalidValue;
 }
@@ -403,33 +465,46 @@ hipError_t launch_fp6_table(const SignTable& tab, int groups, const OperandShape
 
 hipError_t launch_sign_fp6(const uint8_t* packed, const PackedGeom& g, const OperandPlan& op,
                            int64_t B, const float* row_scale, void* y, bool y_bf16,
-                           const Fp6Plan& plan, hipStream_t stream) {
+                           const Fp6Plan& plan, float* partial, unsigned* tickets,
+                           hipStream_t stream) {
+  if (plan.splits > 1 && (partial == nullptr || tickets == nullptr || plan.pgroups > kSplitTickets))
+    return hipErrorInvalidValue;
   SignTable tab;
   tab.n = 1;
-  tab.l[0] = sign_layer(packed, g, op.aop, row_scale, y, plan.nch, 0);
+  tab.l[0] = sign_layer(packed, g, op.aop, row_scale, y, plan, partial, tickets, 0);
   for (int i = 1; i < kMultiMax; ++i) tab.l[i] = tab.l[0];
   return launch_fp6_table(tab, plan.groups, op.s, B, y_bf16, plan, stream);
 }
 
-bool fp6_plans_match(const Fp6Plan& a, const Fp6Plan& b) {
-  return a.p == b.p && a.w == b.w && a.tpc == b.tpc && a.chunk_bytes == b.chunk_bytes;
-}
+bool fp6_plans_match(const Fp6Plan& a, const Fp6Plan& b) { return a.p == b.p && a.w == b.w; }
 
 hipError_t launch_sign_fp6_multi(int n, const SignLayerDesc* layers, const OperandShape& s,
-                                 int64_t B, bool y_bf16, hipStream_t stream) {
+                                 int64_t B, bool y_bf16, unsigned* tickets, hipStream_t stream) {
   if (n < 1 || n > kMultiMax) return hipErrorInvalidValue;
   SignTable tab;
   tab.n = n;
   Fp6Plan plan = layers[0].plan;
-  int groups = 0;
+  int groups = 0, ticket_base = 0;
   for (int i = 0; i < n; ++i) {
     const SignLayerDesc& l = layers[i];
     if (!fp6_plans_match(l.plan, plan)) return hipErrorInvalidValue;
     plan.lds_bytes = std::max(plan.lds_bytes, l.plan.lds_bytes);
-    tab.l[i] = sign_layer(l.packed, l.g, l.aop, l.row_scale, l.y, l.plan.nch, groups);
+    unsigned* t = nullptr;
+    if (l.plan.splits > 1) {
+      if (l.partial == nullptr || tickets == nullptr ||
+          ticket_base + l.plan.pgroups > kSplitTickets)
+        return hipErrorInvalidValue;
+      t = tickets + ticket_base;
+      ticket_base += l.plan.pgroups;
+    }
+    tab.l[i] = sign_layer(l.packed, l.g, l.aop, l.row_scale, l.y, l.plan, l.partial, t, groups);
     groups += l.plan.groups;
   }
   for (int i = n; i < kMultiMax; ++i) tab.l[i] = tab.l[n - 1];
+  // every layer's records, tail slots and reduction must fit the LDS given
+  for (int i = 0; i < n; ++i)
+    if (layers[i].plan.red_off > plan.red_off) plan.red_off = layers[i].plan.red_off;
+  plan.lds_bytes = std::max(plan.lds_bytes, (size_t)plan.red_off + (size_t)1024 * plan.p);
   return launch_fp6_table(tab, groups, s, B, y_bf16, plan, stream);
 }
 

@@ -94,8 +94,9 @@ typedef enum lq_algo {
   LQ_ALGO_MFMA_SMALL = 2,   /* B <= 16: packed signs fed to the FP4 x FP6
                                matrix cores as bit planes; z carried as a sum of
                                FP6 (E2M3) residual terms with a power-of-two
-                               scale per 32-value block (4 terms for fp32 z,
-                               3 for bf16 z; about 2^-20 / 2^-15 relative);
+                               scale per 32-value block (4 terms for fp32 z, 3
+                               beyond B = 12; 2 for bf16 z: about 2^-20, 2^-15
+                               and 2^-10 of the block's largest magnitude);
                                fp32 accumulate */
   LQ_ALGO_MFMA_LARGE = 3,   /* any B: tiled GEMM on bf16 matrix cores, z as bf16
                                (bf16 z) or as a bf16 hi+lo pair (fp32 z) */
@@ -106,7 +107,7 @@ typedef enum lq_algo {
                                publish the activation operand, every workgroup
                                streams its weight panels meanwhile. Applies
                                when the operand fits one 16-column set
-                               (B <= 5 bf16 x, B <= 4 fp32 x) and
+                               (B <= 8 bf16 x, B <= 4 fp32 x) and
                                ceil(L/512)*B is at most both the number of
                                workgroups and of compute units; otherwise
                                UNSUPPORTED */

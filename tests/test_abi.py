@@ -139,7 +139,7 @@ def test_linear_validation():
     out = ctypes.c_size_t()
     assert LIB.lq_linear_workspace_size(ctypes.byref(lay), 1, LQ_BF16, ctypes.byref(out)) == LQ_OK
     need = out.value
-    assert need >= 34416 * 3          # at least three fp8 terms per lifted column
+    assert need >= 34416 * 12 // 8    # at least two 6-bit terms per lifted column
     f = LIB.lq_linear
     assert f(ctypes.byref(lay), P, LQ_BF16, 1, P, LQ_BF16, P, need - 1, None) == LQ_ERR_WORKSPACE
     bad = LQLayer(4096, 14336, 10, 24, 1000, 0, P, P, P, P)
@@ -291,12 +291,16 @@ def test_linear_multi_plan_and_validation():
     down = LQLayer(4096, 14336, 10, 24, 1024, 0, P, P, P, P)
     st, one = linear_ws_size(gate, 1, LQ_BF16, 0)
     assert st == LQ_OK
-    # grouped (bf16 x, batch 1): the control area and one operand per layer
+    # grouped (bf16 x, batch 1): the control area, one operand per layer (20
+    # records of 896 bytes: two terms of one batch row, and 1 KB of slack)
+    # and the partial row sums of the layers whose rows are split into
+    # reduction ranges
+    operand = 20 * 896 + 1024
     st, two = multi_ws_size([gate, gate], 1, LQ_BF16)
     assert st == LQ_OK
-    assert two == _lib.LQ_WS_CONTROL_BYTES + 2 * (one - _lib.LQ_WS_CONTROL_BYTES)
+    assert _lib.LQ_WS_CONTROL_BYTES + 2 * operand <= two <= _lib.LQ_WS_CONTROL_BYTES + 2 * (one - _lib.LQ_WS_CONTROL_BYTES)
     st, four = multi_ws_size([gate] * 4, 1, LQ_BF16)
-    assert st == LQ_OK and four == _lib.LQ_WS_CONTROL_BYTES + 4 * (one - _lib.LQ_WS_CONTROL_BYTES)
+    assert st == LQ_OK and four >= _lib.LQ_WS_CONTROL_BYTES + 4 * operand
     # fp32 x and large batches run the layers one after another: one call's workspace
     assert multi_ws_size([gate, gate], 1, LQ_F32) == linear_ws_size(gate, 1, LQ_F32, 0)
     assert multi_ws_size([gate, gate], 64, LQ_BF16) == linear_ws_size(gate, 64, LQ_BF16, 0)

@@ -105,7 +105,7 @@ def test_full_size_every_row_batch1(lq, wl_name, li):
     y = host(layer.linear(lq, dev(x, xd), 1, torch.float32))
     err = _check_all(y, _rows_oracle(inp, spec, x), TOL[xd])
     if xd == torch.bfloat16:
-        assert err < 5e-4            # three FP6 terms per lifted value: ~4e-5 observed
+        assert err < 3e-3            # two FP6 terms per lifted value: ~8e-4 observed
 
 
 def test_full_size_every_row_70b_gate_up_grouped(lq):
@@ -164,8 +164,8 @@ def test_every_batch_size_small(lq):
         want = ref.linear(x, inp.c, 1024, inp.M, inp.signs(), inp.row_scale)
         err = rel_l2(host(y), want)
         assert err < 1e-2, B
-        if B <= 16:                # three FP6 terms per value; B = 17 rounds z to bf16
-            assert err < 5e-4, (B, err)
+        if B <= 16:                # two FP6 terms per value; B = 17 rounds z to bf16
+            assert err < 3e-3, (B, err)
 
 
 def test_every_batch_size_small_fp32(lq):
