@@ -189,10 +189,6 @@ lq_status plan_exec(int64_t B, int64_t N, int64_t L, int64_t K, int d, int D, lq
       e->os = lq::operand_shape(B, ztype == LQ_BF16);
       e->fp = lq::plan_fp6(B, e->g, e->os, device_cus());
       e->off_aop = take(lq::operand_bytes(L, e->os));
-      if (e->fp.splits > 1) {
-        e->fp.partial_bytes = (size_t)e->fp.splits * B * N * sizeof(float);
-        e->off_partial = take(e->fp.partial_bytes);
-      }
       break;
     case LQ_ALGO_FUSED:
       if (!linear) return LQ_ERR_INVALID_ARG;
@@ -239,12 +235,6 @@ lq_status plan_exec(int64_t B, int64_t N, int64_t L, int64_t K, int d, int D, lq
   return LQ_OK;
 }
 
-// The reduction-range tickets in a workspace's control area (zero between
-// calls; shared by the split one-launch decode and the small-batch product).
-unsigned* split_tickets(void* ws) {
-  return reinterpret_cast<unsigned*>(static_cast<char*>(ws) + lq::kFusedControlBytes);
-}
-
 // Sign product of a prepared input. `zin` is z (sign_gemm) or the raw
 // activations x (linear, whitened and lifted by the preparation launch).
 lq_status run_exec(const Exec& e, const uint8_t* packed, const void* zin, lq_dtype ztype,
@@ -287,8 +277,7 @@ lq_status run_exec(const Exec& e, const uint8_t* packed, const void* zin, lq_dty
                                        &op, tickets, e.tickets, st));
       if (s != LQ_OK) return s;
       return hip_status(profiled(st, [&] {
-        return lq::launch_sign_fp6(packed, e.g, op, B, row_scale, y, yb, e.fp, partial,
-                                   split_tickets(ws), st);
+        return lq::launch_sign_fp6(packed, e.g, op, B, row_scale, y, yb, e.fp, st);
       }));
     }
     case LQ_ALGO_FUSED: {
@@ -364,9 +353,8 @@ void fill_plan_info(const Exec& e, int64_t B, lq_plan_info* info) {
       p.workgroups = (int32_t)(((panels + 3) / 4) * e.vp.ksplit * ((B + e.vp.bt - 1) / e.vp.bt));
       break;
     case LQ_ALGO_MFMA_SMALL:
-      p.waves = e.fp.w;
+      p.waves = e.fp.chunked ? e.fp.w + 1 : e.fp.w;
       p.panels = e.fp.p;
-      p.ksplit = e.fp.splits;
       p.workgroups = e.fp.groups;
       break;
     case LQ_ALGO_FUSED:
@@ -434,7 +422,6 @@ struct MultiPlan {
   int64_t L[LQ_MULTI_MAX];
   bool grouped;
   size_t off_aop[LQ_MULTI_MAX];
-  size_t off_partial[LQ_MULTI_MAX];
   size_t total;
 };
 
@@ -465,30 +452,18 @@ lq_status plan_multi(const lq_layer* layers, int32_t n, int64_t B, lq_dtype xtyp
   }
   if (mp->n < 2) mp->grouped = false;
   if (mp->grouped) {
-    // one plan for all the layers' panels together (same panels per
-    // workgroup, same count of reduction ranges), each layer's ranges under it
+    // one plan for all the layers' panels together (same kernel and panels
+    // per workgroup), each layer's share under it
     lq::PackedGeom gs[LQ_MULTI_MAX];
     for (int j = 0; j < mp->n; ++j) gs[j] = mp->e[j].g;
     const lq::Fp6Plan group = lq::plan_fp6_group(B, gs, mp->n, mp->e[0].os, device_cus());
-    int tickets = 0;
-    for (int j = 0; j < mp->n; ++j) {
-      mp->e[j].fp = lq::plan_fp6_layer(group, mp->e[j].g, mp->e[j].os);
-      if (mp->e[j].fp.splits > 1) tickets += mp->e[j].fp.pgroups;
-    }
-    if (tickets > lq::kSplitTickets) mp->grouped = false;
+    for (int j = 0; j < mp->n; ++j) mp->e[j].fp = lq::plan_fp6_layer(group, mp->e[j].g, mp->e[j].os);
   }
   if (mp->grouped) {
     size_t at = align_up(lq::kControlBytes);
     for (int j = 0; j < mp->n; ++j) {
       mp->off_aop[j] = at;
       at += align_up(lq::operand_bytes(mp->L[j], mp->e[j].os));
-      mp->off_partial[j] = 0;
-      if (mp->e[j].fp.splits > 1) {
-        mp->e[j].fp.partial_bytes =
-            (size_t)mp->e[j].fp.splits * B * layers[mp->idx[j]].N * sizeof(float);
-        mp->off_partial[j] = at;
-        at += align_up(mp->e[j].fp.partial_bytes);
-      }
     }
     mp->total = at;
   }
@@ -799,15 +774,12 @@ lq_status lq_linear_multi(const lq_layer* layers, int32_t n, const void* x, lq_d
     const lq_layer& l = layers[mp.idx[j]];
     uint8_t* aop = base + mp.off_aop[j];
     pd[j] = lq::PrepLayerDesc{l.d, l.D, l.hb, mp.L[j], l.c, l.M, aop};
-    float* partial = mp.e[j].fp.splits > 1 ? reinterpret_cast<float*>(base + mp.off_partial[j]) : nullptr;
-    sd[j] = lq::SignLayerDesc{l.packed, mp.e[j].g, aop, l.row_scale, ys[mp.idx[j]], mp.e[j].fp,
-                              partial};
+    sd[j] = lq::SignLayerDesc{l.packed, mp.e[j].g, aop, l.row_scale, ys[mp.idx[j]], mp.e[j].fp};
   }
   s = hip_status(lq::launch_prep_multi(x, xtype == LQ_BF16, B, layers[0].K, mp.n, pd, mp.e[0].os, st));
   if (s != LQ_OK) return s;
   return hip_status(profiled(st, [&] {
-    return lq::launch_sign_fp6_multi(mp.n, sd, mp.e[0].os, B, ytype == LQ_BF16,
-                                     split_tickets(ws), st);
+    return lq::launch_sign_fp6_multi(mp.n, sd, mp.e[0].os, B, ytype == LQ_BF16, st);
   }));
 }
 

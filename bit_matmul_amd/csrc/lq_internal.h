@@ -240,28 +240,33 @@ struct OperandPlan {
 OperandShape operand_shape(int64_t B, bool z_bf16);
 size_t operand_bytes(int64_t L, const OperandShape& s);
 
-// Small-batch product plan: a workgroup multiplies P panels over one range
-// of `tiles` consecutive column tiles; `splits` ranges cover a row.
+// Small-batch product plan: a workgroup multiplies P panels over the whole
+// row; the row's activation records either all sit in LDS (sign_fp6.hip)
+// or stream through it in chunks (`chunked`, sign_fp6_chunked.hip).
 struct Fp6Plan {
+  bool chunked;
   int p;                  // panels per workgroup
-  int w;                  // wavefronts per workgroup
-  int splits;             // reduction ranges per panel group
-  int tiles;              // column tiles (full or tail) per range
+  int w;                  // wavefronts per workgroup (chunked: compute wavefronts, plus a loader)
   int pgroups;            // panel groups
-  int groups;             // workgroups = pgroups * splits
-  int red_off;            // LDS offset of the tail tile's slots (after the records)
+  int groups;             // workgroups (= pgroups)
+  int red_off;            // resident: LDS offset of the tail tile's slots (after the records)
+  int tpc, nch, chunk_bytes;   // chunked: tiles per wavefront per chunk, chunks, LDS per chunk
   size_t lds_bytes;       // dynamic LDS per workgroup
-  size_t partial_bytes;   // set by the caller: splits > 1 needs splits * B * N floats
 };
 // Chosen for one layer; panels_per_group 0: free; device_cus: compute units
 // of the device (0: unknown, taken as 256).
 Fp6Plan plan_fp6(int64_t B, const PackedGeom& g, const OperandShape& s, int device_cus,
                  int panels_per_group = 0);
-// One plan for n layers launched together (same panels per workgroup, same
-// count of ranges), and each layer's ranges under it.
+// One plan for n layers launched together (same kernel and panels per
+// workgroup), and each layer's share under it.
 Fp6Plan plan_fp6_group(int64_t B, const PackedGeom* gs, int n, const OperandShape& s,
                        int device_cus);
 Fp6Plan plan_fp6_layer(const Fp6Plan& group, const PackedGeom& g, const OperandShape& s);
+// The chunked kernel's plan and instances (sign_fp6_chunked.hip).
+bool fp6_records_fit(const PackedGeom& g, const OperandShape& s);
+Fp6Plan plan_fp6_chunked(const PackedGeom& g, const OperandShape& s, int device_cus,
+                         int panels_per_group);
+void fill_chunks(Fp6Plan* p, const PackedGeom& g, const OperandShape& s);
 
 // Fused decode (whitening, lift, operand and product in one launch; the
 // operand record of each (tile, batch row) is produced by one workgroup and
@@ -361,23 +366,18 @@ hipError_t launch_prep(const void* x, int xkind, int64_t B, int64_t K, int d, in
                        const float* c, const float* M, int64_t L, float* zf32,
                        const OperandPlan* op, unsigned* tickets, int n_tickets,
                        hipStream_t stream);
-// splits > 1: `partial` holds splits * B * N floats and `tickets` pgroups
-// zeroed words (each left zero again by the call).
 hipError_t launch_sign_fp6(const uint8_t* packed, const PackedGeom& g, const OperandPlan& op,
                            int64_t B, const float* row_scale, void* y, bool y_bf16,
-                           const Fp6Plan& plan, float* partial, unsigned* tickets,
-                           hipStream_t stream);
+                           const Fp6Plan& plan, hipStream_t stream);
 // One layer of a small-batch product launch (kernel argument, by value).
 struct SignLayer {
   const uint8_t* packed;
   const uint8_t* aop;
   const float* row_scale;
   void* y;
-  float* partial;      // splits > 1: partial row sums [splits][B][N]
-  unsigned* tickets;   // splits > 1: one per panel group
   int64_t panel_bytes;
   int panels, full_tiles, tail_bytes, N;
-  int splits, tiles;
+  int nch;             // chunked kernel: chunks of full tiles
   int group_begin;     // its first workgroup
 };
 struct SignTable {
@@ -393,13 +393,14 @@ struct SignLayerDesc {
   const float* row_scale;
   void* y;
   Fp6Plan plan;
-  float* partial;      // plan.splits > 1
 };
 // Whether two layers' plans can share one launch (same kernel instance).
 bool fp6_plans_match(const Fp6Plan& a, const Fp6Plan& b);
-// `tickets`: kSplitTickets zeroed words shared by the layers that split.
 hipError_t launch_sign_fp6_multi(int n, const SignLayerDesc* layers, const OperandShape& s,
-                                 int64_t B, bool y_bf16, unsigned* tickets, hipStream_t stream);
+                                 int64_t B, bool y_bf16, hipStream_t stream);
+hipError_t launch_fp6_chunked_table(const SignTable& tab, int groups, const OperandShape& s,
+                                    int64_t B, bool y_bf16, const Fp6Plan& plan,
+                                    hipStream_t stream);
 hipError_t launch_sign_valu(const uint8_t* packed, const PackedGeom& g, const void* z,
                             bool z_bf16, int64_t B, const float* row_scale, void* y, bool y_bf16,
                             const ValuPlan& plan, float* partial, unsigned* tickets,

@@ -24,24 +24,24 @@
 // (batch row b, term t), the FP6 codes of the t-th residual term of
 // 32-value blocks, the blocks' E8M0 scales, and the per-row plane sums.
 //
-// Work split. A workgroup owns a rectangle of the packed matrix: P 16-row
-// panels times one range of consecutive column tiles (the reduction is cut
-// into `splits` ranges, chosen so that the workgroups stream equal shares
-// of the weights and each range's activation records fit LDS). At entry it
-// copies its range's records into LDS with global_load_lds (issued before
-// anything else, so they are not queued behind the weight stream), and
-// every wavefront requests the packed slots of its first DEPTH tiles. The
-// wavefronts then take the range's tiles round-robin, each keeping DEPTH
-// tiles of slots (P 16-byte loads per tile) requested: no barrier couples
-// them until the end, so the weight stream never waits for another
-// wavefront. One activation-operand read from LDS feeds P panels' MFMAs.
-// The wavefronts' accumulators are added in LDS in a fixed order, the terms
-// and plane sums combined; with one range the row scale is applied and y
-// written, with several the range's partial row sums go to the workspace
-// (device-coherent stores) and the last range of the panel group to take
-// the group's ticket adds them in range order and writes y, then resets the
-// ticket (graph replays need no memset). Deterministic: fixed summation
-// orders, no floating-point atomics.
+// Work split. A workgroup owns P 16-row panels over the whole reduction
+// length (no communication between workgroups), for layers whose
+// activation records all fit LDS (the chunked variant in
+// sign_fp6_chunked.hip streams them for the others). At entry it copies
+// the records into LDS with global_load_lds, with the row scales and the
+// tail tile's packed bytes, and waits for them before any weight is
+// requested: requested together with the weight stream they would queue
+// behind it (a compute unit returns its vector-memory requests roughly in
+// order, and the stream fills every memory queue); with no copy in flight
+// the compiler's waits for the slot loads also stay exact. Then every
+// wavefront requests the packed slots of its first DEPTH tiles and takes
+// the row's tiles round-robin, keeping DEPTH tiles of slots (P 16-byte
+// loads per tile) requested: no barrier couples the wavefronts until the
+// end, so the weight stream never waits for another wavefront. One
+// activation-operand read from LDS feeds P panels' MFMAs. The wavefronts'
+// accumulators are added in LDS in a fixed order, the terms and plane sums
+// combined, the row scale applied and y written. Deterministic: fixed
+// summation orders, no floating-point atomics.
 #include <algorithm>
 
 #include "lq_fp6_mma.h"
@@ -70,21 +70,17 @@ __global__ __launch_bounds__(64 * W) void sign_fp6_kernel(SignTable tab, int rec
   const float* __restrict__ row_scale = ly.row_scale;
   const int64_t panel_bytes = ly.panel_bytes;
   const int panels = ly.panels, full_tiles = ly.full_tiles, tail_bytes = ly.tail_bytes;
-  const int N = ly.N, splits = ly.splits;
+  const int N = ly.N;
   const int ext_tiles = full_tiles + (tail_bytes > 0 ? 1 : 0);
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int g = lane >> 4, r = lane & 15;
-  const int wgi = (int)blockIdx.x - ly.group_begin;
-  const int pg = wgi / splits, sp = wgi - pg * splits;
-  const int pbase = pg * P;
-  const int t0 = sp * ly.tiles;
-  const int t1 = min(ext_tiles, t0 + ly.tiles);
-  const bool has_tail = tail_bytes > 0 && t1 == ext_tiles;
-  const int nfull = t1 - t0 - (has_tail ? 1 : 0);    // full tiles of the range
+  const int pbase = ((int)blockIdx.x - ly.group_begin) * P;
+  const bool has_tail = tail_bytes > 0;
+  const int nfull = full_tiles;
   // this wavefront's full tiles: t0 + wave + j W, j < nk
   const int nk = wave < nfull ? (nfull - wave + W - 1) / W : 0;
 
-  // LDS: row scales (1 KB), the range's records (red_off - 1024 bytes, a
+  // LDS: row scales (1 KB), the row's records (red_off - 1024 bytes, a
   // whole number of KB), the tail tile's slots (P KB); the final reduction
   // reuses everything after the row scales.
   float* rs_lds = reinterpret_cast<float*>(smem);
@@ -108,15 +104,11 @@ __global__ __launch_bounds__(64 * W) void sign_fp6_kernel(SignTable tab, int rec
 #pragma unroll
   for (int p = 0; p < P; ++p) prow[p] = packed + (int64_t)min(pbase + p, panels - 1) * panel_bytes;
 
-  // ---- 1. the range's activation records, the row scales and the tail
-  // tile's packed bytes into LDS, all landed before any weight is requested:
-  // requested together with the weight stream they would queue behind it
-  // (a compute unit returns its vector-memory requests roughly in order, and
-  // the stream fills every memory queue), and with no copy in flight the
-  // compiler's waits for the slot loads below stay exact.
+  // ---- 1. the activation records, the row scales and the tail tile's
+  // packed bytes into LDS, all landed before any weight is requested
   {
-    const uint8_t* src = aop + (int64_t)t0 * rec + 16 * lane;
-    const int bytes = (t1 - t0) * rec;
+    const uint8_t* src = aop + 16 * lane;
+    const int bytes = ext_tiles * rec;
     for (int off = wave * 1024; off < bytes; off += W * 1024) lds_dma16(src + off, rec_lds + off);
     if (wave == 0) {
       const int n4 = min(pbase * kPanelRows + 4 * lane, N - 4);   // rows past N: never used
@@ -140,7 +132,7 @@ __global__ __launch_bounds__(64 * W) void sign_fp6_kernel(SignTable tab, int rec
   // is fixed and the waits are exact.
   uint4 A[DEPTH][P];
   auto issue = [&](int j, uint4 (&S)[P]) {
-    const int off = j < nk ? (t0 + wave + j * W) * kTileBytes + 16 * lane : 0;
+    const int off = j < nk ? (wave + j * W) * kTileBytes + 16 * lane : 0;
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       // each weight byte is read once per call: non-temporal
@@ -242,7 +234,6 @@ __global__ __launch_bounds__(64 * W) void sign_fp6_kernel(SignTable tab, int rec
   // weighted 0), summed in a fixed order: wavefronts, then terms.
   const int nt = ncv / B;                           // terms per batch row, 2..4
   void* __restrict__ y = ly.y;
-  float* __restrict__ partial = ly.partial;
   const int items = P * B * 16;
   for (int item = threadIdx.x; item < items; item += 64 * W) {
     const int row = item & 15;
@@ -268,56 +259,30 @@ __global__ __launch_bounds__(64 * W) void sign_fp6_kernel(SignTable tab, int rec
     }
 #pragma unroll
     for (int w = 0; w < W; ++w) tp += tv[w];
-    const float val = acc_s + tp;
+    const float out = rs_lds[p * kPanelRows + row] * (acc_s + tp);
     const int n = (pbase + p) * kPanelRows + row;
     if (pbase + p < panels) {
-      if (splits > 1) {
-        store_coherent(partial + ((int64_t)sp * B + b) * N + n, val);
-      } else {
-        const float out = rs_lds[p * kPanelRows + row] * val;
-        if (y_bf16)
-          reinterpret_cast<uint16_t*>(y)[(int64_t)b * N + n] = (uint16_t)f32_to_bf16_bits(out);
-        else
-          reinterpret_cast<float*>(y)[(int64_t)b * N + n] = out;
-      }
+      if (y_bf16)
+        reinterpret_cast<uint16_t*>(y)[(int64_t)b * N + n] = (uint16_t)f32_to_bf16_bits(out);
+      else
+        reinterpret_cast<float*>(y)[(int64_t)b * N + n] = out;
     }
   }
-  if (splits == 1) return;
-
-  // ---- 5. the panel group's last range adds the partials in range order
-  __shared__ int s_last;
-  unsigned* ticket = ly.tickets + pg;
-  if (!last_ticket(ticket, splits, &s_last)) return;
-  for (int item = threadIdx.x; item < items; item += 64 * W) {
-    const int row = item & 15;
-    const int b = (item >> 4) % B;
-    const int p = (item >> 4) / B;
-    const int n = (pbase + p) * kPanelRows + row;
-    if (pbase + p >= panels) continue;
-    float v = 0.0f;
-    for (int q = 0; q < splits; ++q) v += load_coherent(partial + ((int64_t)q * B + b) * N + n);
-    const float out = rs_lds[p * kPanelRows + row] * v;
-    if (y_bf16)
-      reinterpret_cast<uint16_t*>(y)[(int64_t)b * N + n] = (uint16_t)f32_to_bf16_bits(out);
-    else
-      reinterpret_cast<float*>(y)[(int64_t)b * N + n] = out;
-  }
-  if (threadIdx.x == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-constexpr int kRecLdsMax = 128 * 1024;             // LDS for a range's records
+constexpr int kRecLdsMax = 128 * 1024;             // LDS for the records of a row
 
 // Wavefronts per workgroup, and the slot tiles each keeps requested (P
 // 16-byte loads per tile). Eight wavefronts (two per SIMD, 256 registers
-// each) up to 12 panels; four (one per SIMD) beyond, whose slot and
-// accumulator registers would not fit 256.
-constexpr int waves_for(int p) { return p >= 14 ? 4 : 8; }
+// each) while the slot, accumulator and operand registers fit 256: up to 12
+// panels of one 16-column set, 6 of two; four (one per SIMD, 512) beyond.
+constexpr int waves_for(int p, int cs) { return (cs == 1 ? p >= 14 : p >= 8) ? 4 : 8; }
 constexpr int depth_for(int p) { return p <= 4 ? 4 : (p <= 8 ? 3 : (p <= 12 ? 2 : 3)); }
 
 template <int P, int CS>
 hipError_t launch_fp6_t(const SignTable& tab, int groups, const OperandShape& s, int64_t B,
                         bool y_bf16, const Fp6Plan& plan, hipStream_t stream) {
-  constexpr int W = waves_for(P), DEPTH = depth_for(P);
+  constexpr int W = waves_for(P, CS), DEPTH = depth_for(P);
   if (plan.w != W) return hipErrorInvalidValue;
   const dim3 grid((unsigned)groups);
   const dim3 block(64 * W);
@@ -338,76 +303,61 @@ hipError_t launch_fp6_t(const SignTable& tab, int groups, const OperandShape& s,
 // Panels per workgroup instantiated for each count of 16-column sets
 // (registers: P x CS accumulator quads, DEPTH x P slot quads).
 constexpr int kPanelsCS1[] = {1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16};
-constexpr int kPanelsCS2[] = {1, 2, 3, 4, 6};
+constexpr int kPanelsCS2[] = {1, 2, 3, 4, 6, 8, 12};
 constexpr int kPanelsCS3[] = {1, 2, 3, 4};
 
 }  // namespace
 
-// Reduction ranges and LDS of a workgroup of P panels for one layer.
-static void fill_ranges(Fp6Plan* pl, const PackedGeom& g, const OperandShape& s, int S) {
-  const int ext = g.ext_tiles;
-  pl->tiles = (ext + S - 1) / S;
-  pl->splits = (ext + pl->tiles - 1) / pl->tiles;    // no empty range
-  pl->pgroups = (int)((g.panels + pl->p - 1) / pl->p);
-  pl->groups = pl->pgroups * pl->splits;
-  const int recs = ((pl->tiles * s.rec + 1023) / 1024) * 1024;
+// LDS and workgroups of a plan of P panels per workgroup for one layer.
+static void fill_resident(Fp6Plan* pl, const PackedGeom& g, const OperandShape& s) {
+  const int recs = ((g.ext_tiles * s.rec + 1023) / 1024) * 1024;
   const int nc = std::min(16, s.ncv);
-  pl->w = waves_for(pl->p);
+  pl->w = waves_for(pl->p, s.cs);
   const size_t red = (size_t)pl->w * pl->p * s.cs * 4 * nc * 16 + (size_t)pl->w * 16 * 4;
   pl->red_off = 1024 + recs;
   pl->lds_bytes = std::max((size_t)pl->red_off + (size_t)1024 * pl->p, 1024 + red);
-  pl->partial_bytes = 0;
+  pl->pgroups = (int)((g.panels + pl->p - 1) / pl->p);
+  pl->groups = pl->pgroups;
+}
+
+bool fp6_records_fit(const PackedGeom& g, const OperandShape& s) {
+  return (int64_t)g.ext_tiles * s.rec <= kRecLdsMax;
 }
 
 Fp6Plan plan_fp6(int64_t B, const PackedGeom& g, const OperandShape& s, int device_cus,
                  int panels_per_group) {
   (void)B;
+  if (!fp6_records_fit(g, s)) return plan_fp6_chunked(g, s, device_cus, panels_per_group);
   const int64_t cus = device_cus > 0 ? device_cus : 256;
   const int* cand = s.cs == 1 ? kPanelsCS1 : (s.cs == 2 ? kPanelsCS2 : kPanelsCS3);
-  const int ncand = s.cs == 1 ? 12 : (s.cs == 2 ? 5 : 4);
-  const int ext = g.ext_tiles;
-  const int smin = std::max(1, (ext * s.rec + kRecLdsMax - 1) / kRecLdsMax);
-  // The rectangle that minimises the packed kilobytes the busiest compute
-  // unit streams (workgroups beyond one per unit queue behind it), counting
-  // a split row as kSplitCost kilobytes more (the hand-off of the partial
-  // sums through device-coherent memory and a ticket: several microseconds
-  // of latency); then the most panels per workgroup (each operand read from
-  // LDS feeds them all, and the records are copied by fewer workgroups);
-  // then the fewest ranges.
-  constexpr int64_t kSplitCost = 128;
+  const int ncand = s.cs == 1 ? 12 : (s.cs == 2 ? 7 : 4);
+  // The panels per workgroup that minimise the kilobytes the busiest
+  // compute unit streams (workgroups beyond one per unit queue behind it):
+  // its packed weights from memory, plus its activation records from the L2
+  // cache weighted 1/4 (a compute unit's share of L2 bandwidth is several
+  // times its share of HBM's); then the most panels (each operand read from
+  // LDS feeds them all).
   Fp6Plan best{};
   int64_t best_load = -1;
   for (int ci = 0; ci < ncand; ++ci) {
     const int P = cand[ci];
     if (panels_per_group > 0 && P != panels_per_group) continue;
-    const int64_t pgroups = (g.panels + P - 1) / P;
-    for (int S = smin; S <= ext; ++S) {
-      const int T = (ext + S - 1) / S;
-      const int Se = (ext + T - 1) / T;
-      if (Se > 1 && pgroups > kSplitTickets) break;
-      const int64_t wgs = pgroups * Se;
-      const int64_t load = ((wgs + cus - 1) / cus) * P * T + (Se > 1 ? kSplitCost : 0);
-      const bool better = best_load < 0 || load < best_load ||
-                          (load == best_load && (P > best.p || (P == best.p && Se < best.splits)));
-      if (better) {
-        best_load = load;
-        best.p = P;
-        fill_ranges(&best, g, s, S);
-      }
-      if (wgs >= cus) break;                       // more ranges only add hand-offs
+    const int64_t wgs = (g.panels + P - 1) / P;
+    const int64_t load = ((wgs + cus - 1) / cus) * g.ext_tiles * (4 * P + s.rec / 1024) / 4;
+    if (best_load < 0 || load < best_load || (load == best_load && P > best.p)) {
+      best_load = load;
+      best.p = P;
     }
   }
-  if (best_load < 0) {                             // (cannot happen: P = 1, S = smin fits)
-    best.p = 1;
-    fill_ranges(&best, g, s, smin);
-  }
+  if (best_load < 0) best.p = 1;
+  fill_resident(&best, g, s);
   return best;
 }
 
 Fp6Plan plan_fp6_group(int64_t B, const PackedGeom* gs, int n, const OperandShape& s,
                        int device_cus) {
-  // The layers' panels as one matrix of the longest rows: one P and one
-  // count of reduction ranges for all of them.
+  // The layers' panels as one matrix of the longest rows: one kernel and one
+  // count of panels per workgroup for all of them.
   PackedGeom all = gs[0];
   int64_t panels = 0;
   for (int i = 0; i < n; ++i) {
@@ -420,35 +370,33 @@ Fp6Plan plan_fp6_group(int64_t B, const PackedGeom* gs, int n, const OperandShap
 
 Fp6Plan plan_fp6_layer(const Fp6Plan& group, const PackedGeom& g, const OperandShape& s) {
   Fp6Plan pl = group;
-  fill_ranges(&pl, g, s, group.splits);
+  if (pl.chunked) fill_chunks(&pl, g, s);
+  else fill_resident(&pl, g, s);
   return pl;
 }
 
 namespace {
 
 SignLayer sign_layer(const uint8_t* packed, const PackedGeom& g, const uint8_t* aop,
-                     const float* row_scale, void* y, const Fp6Plan& plan, float* partial,
-                     unsigned* tickets, int group_begin) {
+                     const float* row_scale, void* y, const Fp6Plan& plan, int group_begin) {
   SignLayer l;
   l.packed = packed;
   l.aop = aop;
   l.row_scale = row_scale;
   l.y = y;
-  l.partial = partial;
-  l.tickets = tickets;
   l.panel_bytes = g.panel_bytes;
   l.panels = (int)g.panels;
   l.full_tiles = (int)g.full_tiles;
   l.tail_bytes = (int)g.tail_bytes;
   l.N = (int)g.N;
-  l.splits = plan.splits;
-  l.tiles = plan.tiles;
+  l.nch = plan.chunked ? plan.nch : 0;
   l.group_begin = group_begin;
   return l;
 }
 
 hipError_t launch_fp6_table(const SignTable& tab, int groups, const OperandShape& s, int64_t B,
                             bool y_bf16, const Fp6Plan& plan, hipStream_t stream) {
+  if (plan.chunked) return launch_fp6_chunked_table(tab, groups, s, B, y_bf16, plan, stream);
   (void)hipGetLastError();   // clear a stale error of an earlier runtime call
 #define LQ_FP6_CASE(P_, CS_)                                                            \
   if (plan.p == P_ && s.cs == CS_) return launch_fp6_t<P_, CS_>(tab, groups, s, B, y_bf16, plan, stream);
@@ -456,6 +404,7 @@ hipError_t launch_fp6_table(const SignTable& tab, int groups, const OperandShape
   LQ_FP6_CASE(6, 1) LQ_FP6_CASE(7, 1) LQ_FP6_CASE(8, 1) LQ_FP6_CASE(10, 1) LQ_FP6_CASE(12, 1)
   LQ_FP6_CASE(14, 1) LQ_FP6_CASE(16, 1)
   LQ_FP6_CASE(1, 2) LQ_FP6_CASE(2, 2) LQ_FP6_CASE(3, 2) LQ_FP6_CASE(4, 2) LQ_FP6_CASE(6, 2)
+  LQ_FP6_CASE(8, 2) LQ_FP6_CASE(12, 2)
   LQ_FP6_CASE(1, 3) LQ_FP6_CASE(2, 3) LQ_FP6_CASE(3, 3) LQ_FP6_CASE(4, 3)
 #undef LQ_FP6_CASE
   return hipErrorInvalidValue;
@@ -465,46 +414,38 @@ hipError_t launch_fp6_table(const SignTable& tab, int groups, const OperandShape
 
 hipError_t launch_sign_fp6(const uint8_t* packed, const PackedGeom& g, const OperandPlan& op,
                            int64_t B, const float* row_scale, void* y, bool y_bf16,
-                           const Fp6Plan& plan, float* partial, unsigned* tickets,
-                           hipStream_t stream) {
-  if (plan.splits > 1 && (partial == nullptr || tickets == nullptr || plan.pgroups > kSplitTickets))
-    return hipErrorInvalidValue;
+                           const Fp6Plan& plan, hipStream_t stream) {
   SignTable tab;
   tab.n = 1;
-  tab.l[0] = sign_layer(packed, g, op.aop, row_scale, y, plan, partial, tickets, 0);
+  tab.l[0] = sign_layer(packed, g, op.aop, row_scale, y, plan, 0);
   for (int i = 1; i < kMultiMax; ++i) tab.l[i] = tab.l[0];
   return launch_fp6_table(tab, plan.groups, op.s, B, y_bf16, plan, stream);
 }
 
-bool fp6_plans_match(const Fp6Plan& a, const Fp6Plan& b) { return a.p == b.p && a.w == b.w; }
+bool fp6_plans_match(const Fp6Plan& a, const Fp6Plan& b) {
+  return a.chunked == b.chunked && a.p == b.p && a.w == b.w &&
+         (!a.chunked || (a.tpc == b.tpc && a.chunk_bytes == b.chunk_bytes));
+}
 
 hipError_t launch_sign_fp6_multi(int n, const SignLayerDesc* layers, const OperandShape& s,
-                                 int64_t B, bool y_bf16, unsigned* tickets, hipStream_t stream) {
+                                 int64_t B, bool y_bf16, hipStream_t stream) {
   if (n < 1 || n > kMultiMax) return hipErrorInvalidValue;
   SignTable tab;
   tab.n = n;
   Fp6Plan plan = layers[0].plan;
-  int groups = 0, ticket_base = 0;
+  int groups = 0;
   for (int i = 0; i < n; ++i) {
     const SignLayerDesc& l = layers[i];
     if (!fp6_plans_match(l.plan, plan)) return hipErrorInvalidValue;
     plan.lds_bytes = std::max(plan.lds_bytes, l.plan.lds_bytes);
-    unsigned* t = nullptr;
-    if (l.plan.splits > 1) {
-      if (l.partial == nullptr || tickets == nullptr ||
-          ticket_base + l.plan.pgroups > kSplitTickets)
-        return hipErrorInvalidValue;
-      t = tickets + ticket_base;
-      ticket_base += l.plan.pgroups;
-    }
-    tab.l[i] = sign_layer(l.packed, l.g, l.aop, l.row_scale, l.y, l.plan, l.partial, t, groups);
+    plan.red_off = std::max(plan.red_off, l.plan.red_off);
+    tab.l[i] = sign_layer(l.packed, l.g, l.aop, l.row_scale, l.y, l.plan, groups);
     groups += l.plan.groups;
   }
   for (int i = n; i < kMultiMax; ++i) tab.l[i] = tab.l[n - 1];
   // every layer's records, tail slots and reduction must fit the LDS given
-  for (int i = 0; i < n; ++i)
-    if (layers[i].plan.red_off > plan.red_off) plan.red_off = layers[i].plan.red_off;
-  plan.lds_bytes = std::max(plan.lds_bytes, (size_t)plan.red_off + (size_t)1024 * plan.p);
+  if (!plan.chunked)
+    plan.lds_bytes = std::max(plan.lds_bytes, (size_t)plan.red_off + (size_t)1024 * plan.p);
   return launch_fp6_table(tab, groups, s, B, y_bf16, plan, stream);
 }
 
