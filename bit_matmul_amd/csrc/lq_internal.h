@@ -341,7 +341,7 @@ struct PrepLayer {
   uint8_t* aop;
   int d, D, lhb, L;
   float norm;
-  int tile_begin;   // its first workgroup along the grid's x dimension
+  int tiles;        // its 512-column lifted tiles (workgroups along the grid's x dimension)
 };
 struct PrepTable {
   int n;

@@ -32,15 +32,29 @@ __device__ __forceinline__ TileSpan tile_span(int q, int K, int d, int D, int lh
   return t;
 }
 
-// Value of lane ^ X (X a power of two up to 32): DPP for 1 and 2, a
-// swizzle for 4..16 (within 32 lanes), a permute for 32.
+// Value of lane ^ X (X a power of two up to 32), all on the vector ALU:
+// DPP quad permutations for 1 and 2, a half-row mirror (lane ^ 7) then a
+// quad reversal (lane ^ 3) for 4, a rotation of the 16-lane row by 8 for 8,
+// and the gfx950 row-swap permutes for 16 and 32 (each returns the two
+// halves of the exchange; a lane keeps the one that came from its partner).
 template <int X>
 __device__ __forceinline__ float lane_xor(float v) {
   const int i = __float_as_int(v);
   if constexpr (X == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, i, 0xB1, 0xF, 0xF, false));
   else if constexpr (X == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, i, 0x4E, 0xF, 0xF, false));
-  else if constexpr (X <= 16) return __int_as_float(__builtin_amdgcn_ds_swizzle(i, 0x1F | (X << 10)));
-  else return __shfl_xor(v, X, 64);
+  else if constexpr (X == 4) {
+    const int h = __builtin_amdgcn_update_dpp(0, i, 0x141, 0xF, 0xF, false);
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, h, 0x1B, 0xF, 0xF, false));
+  } else if constexpr (X == 8) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, i, 0x128, 0xF, 0xF, false));
+  } else if constexpr (X == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(i, i, false, false);
+    return __int_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+  } else {
+    static_assert(X == 32, "lane_xor: X is a power of two up to 32");
+    const auto r = __builtin_amdgcn_permlane32_swap(i, i, false, false);
+    return __int_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+  }
 }
 
 // One cross-lane butterfly stage over the 16 registers: all exchanges are
@@ -112,15 +126,17 @@ __device__ __forceinline__ void wave_fwht_1024(float* xs, int lhb, int lane) {
   }
 }
 
-// The same transform of the 1024 values xs[0..1023] by 256 threads (four
-// wavefronts; t = 0..255 within the group), every thread of the workgroup
-// calling it the same number of times (it holds two workgroup barriers);
-// `active` false: the thread only takes part in the barriers. Thread t holds
-// xs[4t + i]: bits 0 and 1 pair registers, bits 2..7 pair lanes t ^ 1 ..
-// t ^ 32 (DPP, swizzles, a permute for 32); then, through LDS, thread t holds
-// xs[t + 256j] and bits 8 and 9 pair registers. The stages run in the order
+// The same transform of 1024 values by 256 threads (four wavefronts; t =
+// 0..255 within the group), every thread of the workgroup calling it (it
+// holds workgroup barriers). Thread t brings v[j] = value (t % 64) + 64 j +
+// 256 (t / 64): bits 0..5 of the index pair lanes t ^ 1 .. t ^ 32
+// (vector-ALU exchanges), bits 6 and 7 pair registers. Through LDS, thread
+// t then holds values (t % 64) + 64 (t / 64) + 256 j, where bits 8 and 9
+// pair registers. Results land in xs[0..1023]. The stages run in the order
 // of their bit and every butterfly is the same single add or subtract as in
-// wave_fwht_1024, so both give identical results.
+// wave_fwht_1024, so both give identical results. A group past the values
+// in use transforms whatever it holds (no branch, so the loads feeding v
+// stay ahead of every wait).
 template <int X>
 __device__ __forceinline__ void lane_stage4(float (&v)[4], int t, int lhb, int bit) {
   if (bit < lhb) {
@@ -132,44 +148,37 @@ __device__ __forceinline__ void lane_stage4(float (&v)[4], int t, int lhb, int b
     for (int i = 0; i < 4; ++i) v[i] = fmaf(v[i], sgn, o[i]);
   }
 }
-__device__ __forceinline__ void block_fwht_1024(float* xs, int lhb, int t, bool active) {
-  if (active) {
-    float v[4];
-    const float4 q = *reinterpret_cast<const float4*>(xs + 4 * t);
-    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
-    if (lhb > 0) {
-      float a = v[0], b = v[1]; v[0] = a + b; v[1] = a - b;
-      a = v[2]; b = v[3]; v[2] = a + b; v[3] = a - b;
-    }
-    if (lhb > 1) {
-      float a = v[0], b = v[2]; v[0] = a + b; v[2] = a - b;
-      a = v[1]; b = v[3]; v[1] = a + b; v[3] = a - b;
-    }
-    lane_stage4<1>(v, t, lhb, 2);
-    lane_stage4<2>(v, t, lhb, 3);
-    lane_stage4<4>(v, t, lhb, 4);
-    lane_stage4<8>(v, t, lhb, 5);
-    lane_stage4<16>(v, t, lhb, 6);
-    lane_stage4<32>(v, t, lhb, 7);
-    *reinterpret_cast<float4*>(xs + 4 * t) = make_float4(v[0], v[1], v[2], v[3]);
+__device__ __forceinline__ void reg_stages4(float (&v)[4], bool b0, bool b1) {
+  if (b0) {
+    float a = v[0], b = v[1]; v[0] = a + b; v[1] = a - b;
+    a = v[2]; b = v[3]; v[2] = a + b; v[3] = a - b;
   }
+  if (b1) {
+    float a = v[0], b = v[2]; v[0] = a + b; v[2] = a - b;
+    a = v[1]; b = v[3]; v[1] = a + b; v[3] = a - b;
+  }
+}
+__device__ __forceinline__ void block_fwht_1024_regs(float* xs, float (&v)[4], int lhb, int t) {
+  lane_stage4<1>(v, t, lhb, 0);
+  lane_stage4<2>(v, t, lhb, 1);
+  lane_stage4<4>(v, t, lhb, 2);
+  lane_stage4<8>(v, t, lhb, 3);
+  lane_stage4<16>(v, t, lhb, 4);
+  lane_stage4<32>(v, t, lhb, 5);
+  reg_stages4(v, lhb > 6, lhb > 7);
+  const int lo = t & 63, hi = t >> 6;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) xs[lo + 64 * j + 256 * hi] = v[j];
   __syncthreads();
-  if (active && lhb > 8) {
+  if (lhb > 8) {
     float w[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = xs[t + 256 * j];
-    {
-      float a = w[0], b = w[1]; w[0] = a + b; w[1] = a - b;
-      a = w[2]; b = w[3]; w[2] = a + b; w[3] = a - b;
-    }
-    if (lhb > 9) {
-      float a = w[0], b = w[2]; w[0] = a + b; w[2] = a - b;
-      a = w[1]; b = w[3]; w[1] = a + b; w[3] = a - b;
-    }
+    for (int j = 0; j < 4; ++j) w[j] = xs[lo + 64 * hi + 256 * j];
+    reg_stages4(w, true, lhb > 9);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xs[t + 256 * j] = w[j];
+    for (int j = 0; j < 4; ++j) xs[lo + 64 * hi + 256 * j] = w[j];
+    __syncthreads();
   }
-  __syncthreads();
 }
 
 // One lifted value z[col] = sum_{i < min(d, K - kb)} Ms[i * D + e] *
