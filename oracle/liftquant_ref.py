@@ -47,7 +47,7 @@ import numpy as np
 __all__ = [
     "hadamard", "whitening_block", "whiten", "pad_blocks", "decode_weight",
     "linear", "lift", "sign_matmul", "packed_bits", "bits_per_weight",
-    "codebook", "sign_pattern", "encode_nn", "train_m_step", "orthonormal_rows",
+    "codebook", "sign_pattern", "encode_nn", "encode_pinv", "train_m_step", "orthonormal_rows",
 ]
 
 
@@ -238,6 +238,53 @@ def encode_nn(w: np.ndarray, M: np.ndarray):
             best[a:a + 64] = np.where(take, v, best[a:a + 64])
             idx[a:a + 64] = np.where(take, p0 + i, idx[a:a + 64])
     signs = np.where((idx[:, None] >> np.arange(D)[None, :]) & 1, -1.0, 1.0)
+    return signs, best
+
+
+def encode_pinv(w: np.ndarray, M: np.ndarray):
+    """The nearest-neighbour search reduced from 2^D to 2^(D-d) sign vectors by
+    pseudo-inverse initialisation ([review] Method: "accelerated from 2^D to
+    2^(D-d) by pseudo-inverse initialization"; [review] Limitations: the exact
+    search is practically capped at D - d <= 20). The pages give no more; the
+    reading taken here:
+
+    * M = [M_a | M_f]: the first d columns M_a (d x d) are solved for, the
+      other D - d columns M_f are enumerated.
+    * For each of the 2^(D-d) sign vectors s_f of the enumerated columns, the
+      solved signs are the signs of the pseudo-inverse solution
+      u = pinv(M_a) (w - M_f s_f) (the least-squares lifted coordinates given
+      s_f), s_a = sgn(u) with sgn(0) = +1; the candidate is s = (s_a, s_f).
+    * The candidate closest to w in Euclidean distance wins; among equally
+      close ones, the lowest pattern index (bit e set meaning s_e = -1, as in
+      ``sign_pattern``).
+
+    Where M_a is diagonal (a multiple of the identity in particular) the
+    minimisation over s_a separates per coordinate and sgn(u) is its exact
+    minimiser, so the result is the exhaustive search's (``encode_nn``); in
+    general it visits a subset of the sign vectors, so its distance is never
+    below the exhaustive one.
+
+    Returns (signs (n, D) of +-1, squared distances (n,))."""
+    M = np.asarray(M, dtype=np.float64)
+    d, D = M.shape
+    F = D - d
+    w = np.asarray(w, dtype=np.float64).reshape(-1, d)
+    n = w.shape[0]
+    Ma, Mf = M[:, :d], M[:, d:]
+    A = np.linalg.pinv(Ma)
+    q = np.arange(1 << F, dtype=np.int64)                                   # free-sign patterns
+    Sf = np.where((q[:, None] >> np.arange(F)[None, :]) & 1, -1.0, 1.0)    # (2^F, F)
+    signs = np.zeros((n, D))
+    best = np.zeros(n)
+    for b in range(n):
+        U = (A @ (w[b][:, None] - Mf @ Sf.T)).T                             # (2^F, d): pinv(M_a)(w - M_f s_f)
+        Sa = np.where(U >= 0.0, 1.0, -1.0)
+        R = w[b][None, :] - Sa @ Ma.T - Sf @ Mf.T                           # w - M s
+        dist = (R * R).sum(axis=1)
+        idx = ((Sa < 0) * (1 << np.arange(d))[None, :]).sum(axis=1) + (q << d)
+        k = np.lexsort((idx, dist))[0]                                      # least distance, then index
+        signs[b, :d], signs[b, d:] = Sa[k], Sf[k]
+        best[b] = dist[k]
     return signs, best
 
 

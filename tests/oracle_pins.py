@@ -352,6 +352,89 @@ def pin_encode_symmetry(o, rp):
     assert np.allclose(dist2, 4.0 * dist, rtol=1e-12, atol=0)
 
 
+def _pinv_bruteforce(w, M):
+    """The partial search written out candidate by candidate: for every sign
+    vector of the last D - d columns (in pattern order), the first d signs
+    from a linear solve (not a pseudo-inverse), the distance from a plain
+    loop, ties to the lower full pattern index."""
+    d, D = M.shape
+    F = D - d
+    best, arg, bidx = None, None, None
+    for q in range(1 << F):
+        sf = [(-1.0 if (q >> k) & 1 else 1.0) for k in range(F)]
+        rhs = w - M[:, d:] @ np.array(sf) if F else w.copy()
+        u = np.linalg.solve(M[:, :d], rhs)
+        sa = [1.0 if v >= 0.0 else -1.0 for v in u]
+        s = sa + sf
+        acc = 0.0
+        for i in range(d):
+            v = w[i]
+            for e in range(D):
+                v -= M[i, e] * s[e]
+            acc += v * v
+        idx = sum(1 << e for e in range(D) if s[e] < 0)
+        if best is None or acc < best or (acc == best and idx < bidx):
+            best, arg, bidx = acc, s, idx
+    return np.array(arg), best
+
+
+def pin_encode_pinv_bruteforce(o, rp):
+    rng = np.random.default_rng(47)
+    for (d, D) in [(1, 1), (1, 4), (2, 5), (3, 6), (2, 2), (3, 8)]:
+        M = rng.standard_normal((d, D)) / np.sqrt(D)
+        w = rng.standard_normal((7, d))
+        signs, dist = o.encode_pinv(w, M)
+        assert signs.shape == (7, D) and dist.shape == (7,)
+        for b in range(7):
+            s, best = _pinv_bruteforce(w[b], M)
+            assert np.array_equal(signs[b], s), (d, D, b)
+            assert abs(dist[b] - best) <= 1e-12 * max(1.0, best)
+
+
+def pin_encode_pinv_diagonal_exact(o, rp):
+    """M_a diagonal: the per-coordinate signs of pinv(M_a) (w - M_f s_f) are
+    the exact minimiser over s_a, so the partial search is the exhaustive one."""
+    rng = np.random.default_rng(53)
+    for (d, D) in [(1, 6), (2, 7), (3, 9), (4, 12), (5, 5)]:
+        Ma = np.diag(rng.uniform(0.3, 1.5, d) * rng.choice([-1.0, 1.0], d))
+        M = np.hstack([Ma, rng.standard_normal((d, D - d)) / np.sqrt(D)])
+        w = rng.standard_normal((25, d))
+        s1, d1 = o.encode_pinv(w, M)
+        s2, d2 = o.encode_nn(w, M)
+        assert np.array_equal(s1, s2), (d, D)
+        assert np.allclose(d1, d2, rtol=1e-12, atol=1e-14)
+
+
+def pin_encode_pinv_subset(o, rp):
+    """Gaussian M: never closer than the exhaustive search, and the distance
+    returned is that of the signs returned."""
+    rng = np.random.default_rng(59)
+    for (d, D) in [(2, 6), (4, 12), (3, 11)]:
+        M = rng.standard_normal((d, D)) / np.sqrt(D)
+        w = rng.standard_normal((40, d))
+        s1, d1 = o.encode_pinv(w, M)
+        _, d2 = o.encode_nn(w, M)
+        assert np.all(d1 >= d2 - 1e-12)
+        r = w - s1 @ M.T
+        assert np.allclose(d1, (r * r).sum(axis=1), rtol=1e-12, atol=1e-14)
+        assert np.all(np.abs(s1) == 1.0)
+
+
+def pin_encode_pinv_square(o, rp):
+    """D = d: a single candidate, the signs of the solution of M s = w (+1 at
+    an exact zero)."""
+    rng = np.random.default_rng(61)
+    for d in (1, 3, 6):
+        M = np.diag(rng.uniform(0.5, 2.0, d))
+        w = rng.standard_normal((12, d))
+        w[rng.random((12, d)) < 0.25] = 0.0
+        s, dist = o.encode_pinv(w, M)
+        assert np.array_equal(s, np.where(w >= 0.0, 1.0, -1.0))
+        G = rng.standard_normal((d, d))
+        s, _ = o.encode_pinv(w, G)
+        assert np.array_equal(s, np.where(np.linalg.solve(G, w.T).T >= 0.0, 1.0, -1.0))
+
+
 def _eq1_loss(o, M, w):
     """mean_b min_s ||w_b - M s|| evaluated from scratch (codebook distances)."""
     cb = o.codebook(M)
@@ -411,5 +494,7 @@ ALL_PINS = [
     pin_sign_matmul_integer, pin_row_scale, pin_zero_pad, pin_rates,
     pin_memory_fit, pin_storage_exact, pin_pack_layout_bijective,
     pin_encode_bruteforce, pin_encode_identity, pin_encode_symmetry,
+    pin_encode_pinv_bruteforce, pin_encode_pinv_diagonal_exact, pin_encode_pinv_subset,
+    pin_encode_pinv_square,
     pin_train_gradient_fd, pin_train_descends, pin_orthonormal_rows,
 ]

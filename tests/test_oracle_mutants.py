@@ -208,6 +208,72 @@ def _mutants():
             return np.stack([o.sign_pattern(int(k), D) for k in i]), dist[np.arange(len(i)), i]
         o.encode_nn = enc
 
+    @m("partial search solves for the last d columns")
+    def _(o, rp):
+        orig = o.encode_pinv
+
+        def enc(w, M):
+            M = np.asarray(M, float)
+            d, D = M.shape
+            perm = list(range(D - d, D)) + list(range(D - d))
+            s, dist = orig(w, M[:, perm])
+            out = np.zeros_like(s)
+            out[:, perm] = s
+            return out, dist
+        o.encode_pinv = enc
+
+    @m("partial search rounds the solved coordinates with sgn(0) = -1")
+    def _(o, rp):
+        orig = o.encode_pinv
+
+        def enc(w, M):
+            w = np.asarray(w, float)
+            M = np.asarray(M, float)
+            d = M.shape[0]
+            return orig(np.where(w.reshape(-1, d) == 0.0, -1e-300, w), M)
+        o.encode_pinv = enc
+
+    @m("partial search keeps the farthest candidate")
+    def _(o, rp):
+        def enc(w, M):
+            M = np.asarray(M, float)
+            d, D = M.shape
+            F = D - d
+            w = np.asarray(w, float).reshape(-1, d)
+            A = np.linalg.pinv(M[:, :d])
+            q = np.arange(1 << F)
+            Sf = np.where((q[:, None] >> np.arange(F)[None, :]) & 1, -1.0, 1.0)
+            out, dd = np.zeros((len(w), D)), np.zeros(len(w))
+            for b in range(len(w)):
+                U = (A @ (w[b][:, None] - M[:, d:] @ Sf.T)).T
+                Sa = np.where(U >= 0, 1.0, -1.0)
+                R = w[b] - Sa @ M[:, :d].T - Sf @ M[:, d:].T
+                dist = (R * R).sum(axis=1)
+                k = int(dist.argmax())
+                out[b, :d], out[b, d:], dd[b] = Sa[k], Sf[k], dist[k]
+            return out, dd
+        o.encode_pinv = enc
+
+    @m("partial search leaves the enumerated columns out of the solve")
+    def _(o, rp):
+        def enc(w, M):
+            M = np.asarray(M, float)
+            d, D = M.shape
+            F = D - d
+            w = np.asarray(w, float).reshape(-1, d)
+            A = np.linalg.pinv(M[:, :d])
+            q = np.arange(1 << F)
+            Sf = np.where((q[:, None] >> np.arange(F)[None, :]) & 1, -1.0, 1.0)
+            out, dd = np.zeros((len(w), D)), np.zeros(len(w))
+            for b in range(len(w)):
+                sa = np.where(A @ w[b] >= 0, 1.0, -1.0)
+                R = w[b] - sa @ M[:, :d].T - Sf @ M[:, d:].T
+                dist = (R * R).sum(axis=1)
+                k = int(dist.argmin())
+                out[b, :d], out[b, d:], dd[b] = sa, Sf[k], dist[k]
+            return out, dd
+        o.encode_pinv = enc
+
     @m("training step ascends")
     def _(o, rp):
         orig = o.train_m_step
