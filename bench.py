@@ -658,6 +658,20 @@ def run_encode(torch, lq, reps=3):
         flops = float(n) * (1 << D) * 4 * d        # per visited vector: d updates + d distance FMAs
         out.append(dict(workload=label, d=d, D=D, blocks=n, ms=ms, blocks_per_s=n / (ms * 1e-3),
                         tflops=flops / (ms * 1e-3) / 1e12))
+    # the 2^(D-d) pseudo-inverse-initialised search: LQ-24/10 and LQ-32/16
+    for d, D, n, label in ((10, 24, 65536, "pseudo-inverse search, 2.4-bit rate (d=10, D=24: 2^14 "
+                                           "candidates per block), 65536 blocks"),
+                           (16, 32, 16384, "pseudo-inverse search, 2-bit LQ-32/16 (2^16 candidates "
+                                           "per block), 16384 blocks")):
+        M = orth(d, D)
+        w = torch.randn(n, d, device=dev, generator=gen)
+        signs = torch.empty(n, D, dtype=torch.int8, device=dev)
+        ws = torch.zeros(lq.lq_encode_pinv_workspace_size(d, D), dtype=torch.uint8, device=dev)
+        ms = timed(lambda: lq.lq_encode_pinv(w, n, d, D, M, signs, None, ws))
+        # per candidate: 2d updates, d^2 residual and d distance FMAs
+        flops = float(n) * (1 << (D - d)) * 2 * (d * d + 3 * d)
+        out.append(dict(workload=label, d=d, D=D, blocks=n, ms=ms, blocks_per_s=n / (ms * 1e-3),
+                        tflops=flops / (ms * 1e-3) / 1e12, search="pinv"))
     d, D, n = 3, 8, 65536
     M = orth(d, D)
     w = torch.randn(n, d, device=dev, generator=gen)
@@ -673,13 +687,17 @@ def encode_cpu_baseline():
     from oracle import liftquant_ref as ref
     rng = np.random.default_rng(3)
     res = []
-    for d, D, n in ((10, 24, 1), (3, 8, 20000)):
+    for d, D, n, fn, search in ((10, 24, 1, ref.encode_nn, "exhaustive"),
+                                (3, 8, 20000, ref.encode_nn, "exhaustive"),
+                                (10, 24, 20, ref.encode_pinv, "pinv"),
+                                (16, 32, 8, ref.encode_pinv, "pinv")):
         M = ref.orthonormal_rows(rng.standard_normal((D, D)), d)
         w = rng.standard_normal((n, d))
         t0 = time.perf_counter()
-        ref.encode_nn(w, M)
+        fn(w, M)
         dt = time.perf_counter() - t0
-        res.append(dict(d=d, D=D, blocks=n, seconds=round(dt, 3), blocks_per_s=round(n / dt, 3)))
+        res.append(dict(d=d, D=D, blocks=n, search=search, seconds=round(dt, 3),
+                        blocks_per_s=round(n / dt, 3)))
     return res
 
 
@@ -923,7 +941,8 @@ def main():
         enc, train = run_encode(torch, lq)
         big = enc[0]
         out["encode"] = {
-            "metric": "blocks/s encoded (exhaustive nearest-neighbour search, Eq. (1) inner minimisation)",
+            "metric": "blocks/s encoded (the nearest-neighbour search of Eq. (1)'s inner minimisation: "
+                      "exhaustive over 2^D, or the 2^(D-d) pseudo-inverse-initialised search)",
             "workloads": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in e.items()}
                           for e in enc],
             "kernel": "encode_kernel",

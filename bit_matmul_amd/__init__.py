@@ -14,7 +14,8 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import (LQ_MULTI_MAX, LQ_ENCODE_MAX_D, LQ_ENCODE_MAX_SMALL_D, LQ_ALGO_AUTO, LQ_ALGO_FUSED, LQ_ALGO_FUSED_LOCAL, LQ_ALGO_MFMA_LARGE, LQ_ALGO_WSPACE, LQ_ALGO_FUSED_SPLIT,
+from ._lib import (LQ_MULTI_MAX, LQ_ENCODE_MAX_D, LQ_ENCODE_MAX_SMALL_D, LQ_ENCODE_PINV_MAX_D,
+                   LQ_ENCODE_PINV_MAX_FREE, LQ_ALGO_AUTO, LQ_ALGO_FUSED, LQ_ALGO_FUSED_LOCAL, LQ_ALGO_MFMA_LARGE, LQ_ALGO_WSPACE, LQ_ALGO_FUSED_SPLIT,
                    LQ_ALGO_MFMA_SMALL,
                    LQ_ALGO_VALU, LQ_BF16, LQ_F32, LQ_MAX_D, LQ_MAX_HB, LQ_WS_CONTROL_BYTES,
                    LQ_WS_ERROR_WORD, LQ_NOALLOC_SCRATCH_BYTES, LQ_ERR_DEVICE, LQ_MAX_L, LQError,
@@ -26,7 +27,8 @@ __all__ = [
     "lq_linear_workspace_size", "lq_linear", "lq_linear_workspace_size_ex", "lq_linear_ex",
     "lq_linear_algo", "lq_linear_multi_workspace_size", "lq_linear_multi", "LQ_MULTI_MAX",
     "lq_encode", "lq_train_m_step_workspace_size", "lq_train_m_step",
-    "LQ_ENCODE_MAX_D", "LQ_ENCODE_MAX_SMALL_D",
+    "LQ_ENCODE_MAX_D", "LQ_ENCODE_MAX_SMALL_D", "LQ_ENCODE_PINV_MAX_D", "LQ_ENCODE_PINV_MAX_FREE",
+    "lq_encode_pinv_workspace_size", "lq_encode_pinv",
     "lq_workspace_init", "lq_profile_events", "layer_struct", "LQError", "LQLayer",
     "LQ_F32", "LQ_BF16", "LQ_ALGO_AUTO", "LQ_ALGO_VALU", "LQ_ALGO_MFMA_SMALL",
     "LQ_ALGO_MFMA_LARGE", "LQ_ALGO_FUSED", "LQ_ALGO_FUSED_LOCAL", "LQ_ALGO_WSPACE", "LQ_ALGO_FUSED_SPLIT", "LQ_MAX_D", "LQ_MAX_HB", "LQ_WS_CONTROL_BYTES",
@@ -252,6 +254,28 @@ def lq_encode(w, nblocks, d, D, M, signs, dist2=None, stream=None) -> None:
         raise ValueError("dist2 must be float32")
     _check(_lib.LIB.lq_encode(_dev(w, "w"), nblocks, d, D, _dev(M, "M"), _dev(signs, "signs"),
                               _opt(dist2, "dist2"), _stream(stream)), "lq_encode")
+
+
+def lq_encode_pinv_workspace_size(d, D) -> int:
+    out = ctypes.c_size_t()
+    _check(_lib.LIB.lq_encode_pinv_workspace_size(d, D, ctypes.byref(out)),
+           "lq_encode_pinv_workspace_size")
+    return out.value
+
+
+def lq_encode_pinv(w, nblocks, d, D, M, signs, dist2=None, ws=None, stream=None) -> None:
+    """The 2^(D-d) pseudo-inverse-initialised search (float32 w, M; int8
+    signs; optional float32 squared distances; ws: uint8 device tensor of
+    lq_encode_pinv_workspace_size bytes)."""
+    for t, name, dt in ((w, "w", torch.float32), (M, "M", torch.float32), (signs, "signs", torch.int8)):
+        if t.dtype != dt:
+            raise ValueError(f"{name} must be {dt}")
+    if dist2 is not None and dist2.dtype != torch.float32:
+        raise ValueError("dist2 must be float32")
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.LIB.lq_encode_pinv(_dev(w, "w"), nblocks, d, D, _dev(M, "M"), _dev(signs, "signs"),
+                                   _opt(dist2, "dist2"), _opt(ws, "ws"), ws_bytes, _stream(stream)),
+           "lq_encode_pinv")
 
 
 def lq_train_m_step_workspace_size(n, d, D) -> int:

@@ -18,6 +18,8 @@ LQ_WS_CONTROL_BYTES = 20992
 LQ_WS_ERROR_WORD = 96
 LQ_ENCODE_MAX_D = 24
 LQ_ENCODE_MAX_SMALL_D = 16
+LQ_ENCODE_PINV_MAX_D = 32
+LQ_ENCODE_PINV_MAX_FREE = 24
 LQ_MULTI_MAX = 4
 LQ_NOALLOC_SCRATCH_BYTES = 16 << 20
 
@@ -30,7 +32,8 @@ EXPORTS = [
     "lq_linear_algo", "lq_workspace_init", "lq_profile_events", "lq_encode",
     "lq_train_m_step_workspace_size", "lq_train_m_step", "lq_linear_multi_workspace_size",
     "lq_linear_multi", "lq_linear_noalloc", "lq_linear_plan", "lq_sign_gemm_plan",
-    "lq_workspace_status", "lq_debug_fused_timeout",
+    "lq_workspace_status", "lq_debug_fused_timeout", "lq_encode_pinv_workspace_size",
+    "lq_encode_pinv",
 ]
 
 
@@ -84,6 +87,8 @@ def _load():
         "lq_linear_workspace_size_ex": (c_int, [POINTER(LQLayer), i64, c_int, c_int, POINTER(sz)]),
         "lq_linear_algo": (c_int, [POINTER(LQLayer), i64, c_int, c_int, POINTER(c_int)]),
         "lq_encode": (c_int, [vp, i64, c_int32, c_int32, vp, vp, vp, vp]),
+        "lq_encode_pinv_workspace_size": (c_int, [c_int32, c_int32, POINTER(sz)]),
+        "lq_encode_pinv": (c_int, [vp, i64, c_int32, c_int32, vp, vp, vp, vp, sz, vp]),
         "lq_train_m_step_workspace_size": (c_int, [i64, c_int32, c_int32, POINTER(sz)]),
         "lq_train_m_step": (c_int, [vp, vp, i64, c_int32, c_int32, c_float, vp, vp, sz, vp]),
         "lq_linear_ex": (c_int, [POINTER(LQLayer), vp, c_int, i64, vp, c_int, c_int, vp, sz, vp]),

@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstdint>
+#include <cmath>
 #include <mutex>
 #include <vector>
 
@@ -829,6 +830,98 @@ lq_status lq_encode(const float* w, int64_t nblocks, int32_t d, int32_t D, const
   if (w == nullptr || M == nullptr || signs == nullptr) return LQ_ERR_INVALID_ARG;
   if (!aligned4(w) || !aligned4(M) || !aligned4(dist2)) return LQ_ERR_INVALID_ARG;
   return hip_status(lq::launch_encode(w, nblocks, d, D, M, signs, dist2, (hipStream_t)stream));
+}
+
+static_assert(LQ_ENCODE_PINV_MAX_D == lq::kEncodePinvMaxD &&
+              LQ_ENCODE_PINV_MAX_FREE == lq::kEncodePinvMaxFree, "partial search limits");
+
+static lq_status check_pinv_dims(int64_t n, int32_t d, int32_t D) {
+  if (n < 0 || d < 1 || D < 1) return LQ_ERR_INVALID_ARG;
+  if (d > D) return LQ_ERR_INVALID_ARG;
+  if (d > LQ_ENCODE_MAX_SMALL_D || D > LQ_ENCODE_PINV_MAX_D || D - d > LQ_ENCODE_PINV_MAX_FREE)
+    return LQ_ERR_UNSUPPORTED;
+  if (!mul_ok(n, D, kMaxElems) || !mul_ok(n, d, kMaxElems)) return LQ_ERR_UNSUPPORTED;
+  return LQ_OK;
+}
+
+static size_t pinv_table_bytes(int32_t d, int32_t D) {
+  return ((size_t)d * (size_t)D * sizeof(double) + 255) / 256 * 256;
+}
+
+lq_status lq_encode_pinv_workspace_size(int32_t d, int32_t D, size_t* bytes) {
+  if (bytes == nullptr) return LQ_ERR_INVALID_ARG;
+  const lq_status s = check_pinv_dims(0, d, D);
+  if (s != LQ_OK) return s;
+  *bytes = pinv_table_bytes(d, D);
+  return LQ_OK;
+}
+
+// A = M_a^-1 by Gauss-Jordan elimination with partial pivoting (fp64), then
+// B = A M_f; false when a pivot is at most 2^-40 of M_a's largest magnitude.
+static bool pinv_tables(const std::vector<float>& M, int d, int D, std::vector<double>& AB) {
+  const int W = 2 * d;
+  std::vector<double> a((size_t)d * W, 0.0);
+  double amax = 0.0;
+  for (int i = 0; i < d; ++i) {
+    for (int e = 0; e < d; ++e) {
+      a[(size_t)i * W + e] = (double)M[(size_t)i * D + e];
+      amax = std::max(amax, std::fabs((double)M[(size_t)i * D + e]));
+    }
+    a[(size_t)i * W + d + i] = 1.0;
+  }
+  const double tol = std::ldexp(amax, -40);
+  if (!(amax > 0.0)) return false;
+  for (int c = 0; c < d; ++c) {
+    int p = c;
+    for (int r = c + 1; r < d; ++r)
+      if (std::fabs(a[(size_t)r * W + c]) > std::fabs(a[(size_t)p * W + c])) p = r;
+    if (!(std::fabs(a[(size_t)p * W + c]) > tol)) return false;
+    if (p != c)
+      for (int k = 0; k < W; ++k) std::swap(a[(size_t)p * W + k], a[(size_t)c * W + k]);
+    const double piv = a[(size_t)c * W + c];
+    for (int k = 0; k < W; ++k) a[(size_t)c * W + k] /= piv;
+    for (int r = 0; r < d; ++r) {
+      if (r == c) continue;
+      const double f = a[(size_t)r * W + c];
+      if (f == 0.0) continue;
+      for (int k = 0; k < W; ++k) a[(size_t)r * W + k] -= f * a[(size_t)c * W + k];
+    }
+  }
+  const int F = D - d;
+  AB.assign((size_t)d * D, 0.0);
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j) AB[(size_t)i * d + j] = a[(size_t)i * W + d + j];
+  for (int i = 0; i < d; ++i)
+    for (int k = 0; k < F; ++k) {
+      double acc = 0.0;
+      for (int j = 0; j < d; ++j) acc += AB[(size_t)i * d + j] * (double)M[(size_t)j * D + d + k];
+      AB[(size_t)d * d + (size_t)i * F + k] = acc;
+    }
+  return true;
+}
+
+lq_status lq_encode_pinv(const float* w, int64_t nblocks, int32_t d, int32_t D, const float* M,
+                         int8_t* signs, float* dist2, void* ws, size_t ws_bytes, void* stream) {
+  lq_status s = check_pinv_dims(nblocks, d, D);
+  if (s != LQ_OK) return s;
+  if (nblocks == 0) return LQ_OK;
+  if (w == nullptr || M == nullptr || signs == nullptr) return LQ_ERR_INVALID_ARG;
+  if (!aligned4(w) || !aligned4(M) || !aligned4(dist2)) return LQ_ERR_INVALID_ARG;
+  if (ws == nullptr || ws_bytes < pinv_table_bytes(d, D)) return LQ_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 15u) != 0) return LQ_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  // M to the host (the stream's earlier work first), the tables back
+  std::vector<float> hm((size_t)d * D);
+  hipError_t e = hipMemcpyAsync(hm.data(), M, hm.size() * sizeof(float), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_status(e);
+  std::vector<double> ab;
+  if (!pinv_tables(hm, d, D, ab)) return LQ_ERR_INVALID_ARG;
+  e = hipMemcpyAsync(ws, ab.data(), ab.size() * sizeof(double), hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);   // the host copy of the tables goes away
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(lq::launch_encode_pinv(w, nblocks, d, D, M, static_cast<const double*>(ws),
+                                           signs, dist2, st));
 }
 
 lq_status lq_train_m_step_workspace_size(int64_t n, int32_t d, int32_t D, size_t* bytes) {

@@ -11,6 +11,17 @@
 // D <= 10 one lane walks all 2^D vectors of its block; beyond, a wavefront
 // shares a block: lane l walks the 2^(D-6) vectors whose top six bits are l,
 // and the wavefront reduces.
+//
+// Pseudo-inverse-initialised search (lq_encode_pinv): M = [M_a | M_f], the
+// first d columns solved for, the other F = D - d enumerated. For each of the
+// 2^F sign vectors s_f of M_f, visited in Gray-code order, the lane carries
+// u = A (w - M_f s_f) (A = M_a^-1, computed on the host) and r_f = w - M_f s_f
+// in fp64 (a flip moves them by +-2 A M_f[:, k] and +-2 M_f[:, k]); the
+// solved signs are s_a = sgn(u) (+1 at 0), the candidate's residual
+// r = r_f - M_a s_a (d^2 fused multiply-adds). The minimum is taken on
+// (distance, index of the whole pattern). F <= 10: one lane per block;
+// beyond, a wavefront per block, lane l walking the 2^(F-6) vectors whose
+// top six free bits are l.
 #include "lq_internal.h"
 
 namespace lq {
@@ -119,6 +130,165 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(const float* __rest
   }
 }
 
+// ------------------------------------------------- pseudo-inverse search
+// LDS tables (doubles, rows past d zero): ma[e][DM] = column e of M_a,
+// al[i][DM] = row i of A, b2[k][DM] = 2 (A M_f)[:, k], mf2[k][DM] = 2 M_f[:, k].
+template <int DM>
+struct PinvTables {
+  double ma[DM * DM];
+  double al[DM * DM];
+  double b2[kEncodePinvMaxFree * DM];
+  double mf2[kEncodePinvMaxFree * DM];
+};
+
+template <int DM>
+__device__ __forceinline__ void stage_pinv(PinvTables<DM>& t, const float* __restrict__ M,
+                                           const double* __restrict__ AB, int d, int D) {
+  const int F = D - d;
+  for (int j = threadIdx.x; j < DM * DM; j += kEncThreads) {
+    const int e = j / DM, i = j - e * DM;
+    t.ma[j] = (i < d && e < d) ? (double)M[i * D + e] : 0.0;
+    t.al[j] = (i < d && e < d) ? AB[e * d + i] : 0.0;     // al[e][i] = A[e][i]
+  }
+  for (int j = threadIdx.x; j < kEncodePinvMaxFree * DM; j += kEncThreads) {
+    const int k = j / DM, i = j - k * DM;
+    const bool in = i < d && k < F;
+    t.b2[j] = in ? 2.0 * AB[d * d + i * F + k] : 0.0;
+    t.mf2[j] = in ? 2.0 * (double)M[i * D + d + k] : 0.0;
+  }
+}
+
+// Zero, opaque to the compiler: a table address offset by it is a new
+// address on every visit, so the d^2 M_a entries are read from LDS where they
+// are used instead of being hoisted into (far too many) registers.
+__device__ __forceinline__ int opaque_zero() {
+  int z;
+  asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+  return z;
+}
+
+// The candidate of free pattern q: s_a = sgn(u), r = r_f - M_a s_a.
+template <int DM>
+__device__ __forceinline__ void pinv_candidate(const PinvTables<DM>& t, const double (&u)[DM],
+                                               const double (&rf)[DM], int d, uint32_t q,
+                                               double& best, uint32_t& bidx, bool first) {
+  const double* ma = t.ma + opaque_zero();
+  double r[DM];
+#pragma unroll
+  for (int i = 0; i < DM; ++i) r[i] = rf[i];
+  uint32_t sab = 0;
+#pragma unroll
+  for (int e = 0; e < DM; ++e) {
+    const bool neg = u[e] < 0.0;                      // rows past d: u = 0, +1, a zero column
+    sab |= (neg ? 1u : 0u) << e;
+    const double ms = neg ? 1.0 : -1.0;               // -s_e
+#pragma unroll
+    for (int i = 0; i < DM; ++i) r[i] = fma(ms, ma[e * DM + i], r[i]);
+  }
+  double d0 = 0.0, d1 = 0.0;
+#pragma unroll
+  for (int i = 0; i < DM; ++i) {
+    if (i & 1) d1 = fma(r[i], r[i], d1);
+    else d0 = fma(r[i], r[i], d0);
+  }
+  const double dd = d0 + d1;
+  const uint32_t idx = sab | (q << d);
+  if (first || dd < best || (dd == best && idx < bidx)) {
+    best = dd;
+    bidx = idx;
+  }
+}
+
+// The walk over free patterns q = prefix | g, g < 2^nfree, for one block.
+template <int DM>
+__device__ __forceinline__ void pinv_walk(const PinvTables<DM>& t, const double (&wv)[DM], int d,
+                                          int F, uint32_t prefix, int nfree, double& best,
+                                          uint32_t& bidx) {
+  // u = A w - A M_f s_f and r_f = w - M_f s_f at the first pattern
+  double u[DM], rf[DM];
+#pragma unroll
+  for (int i = 0; i < DM; ++i) {
+    double acc = 0.0;
+#pragma unroll
+    for (int j = 0; j < DM; ++j) acc = fma(t.al[i * DM + j], wv[j], acc);
+    u[i] = acc;
+    rf[i] = wv[i];
+  }
+  for (int k = 0; k < F; ++k) {
+    const double h = ((prefix >> k) & 1) ? 0.5 : -0.5;   // -s_k / 2 (the tables hold 2x)
+#pragma unroll
+    for (int i = 0; i < DM; ++i) {
+      u[i] = fma(h, t.b2[k * DM + i], u[i]);
+      rf[i] = fma(h, t.mf2[k * DM + i], rf[i]);
+    }
+  }
+  uint32_t q = prefix;
+  pinv_candidate<DM>(t, u, rf, d, q, best, bidx, true);
+  const uint32_t count = 1u << nfree;
+  for (uint32_t k = 1; k < count; ++k) {
+    const int e = __builtin_ctz(k);
+    q ^= 1u << e;
+    // s_e became -1: M_f s_f lost 2 M_f[:, e], u and r_f gain it; became +1: they lose it
+    const double sg = ((q >> e) & 1) ? 1.0 : -1.0;
+#pragma unroll
+    for (int i = 0; i < DM; ++i) {
+      u[i] = fma(sg, t.b2[e * DM + i], u[i]);
+      rf[i] = fma(sg, t.mf2[e * DM + i], rf[i]);
+    }
+    pinv_candidate<DM>(t, u, rf, d, q, best, bidx, false);
+  }
+}
+
+template <int DM, bool kWave>
+__global__ __launch_bounds__(kEncThreads) void encode_pinv_kernel(
+    const float* __restrict__ w, int64_t nblocks, int d, int D, const float* __restrict__ M,
+    const double* __restrict__ AB, int8_t* __restrict__ signs, float* __restrict__ dist2) {
+  __shared__ PinvTables<DM> t;
+  stage_pinv<DM>(t, M, AB, d, D);
+  __syncthreads();
+  const int F = D - d;
+  const int lane = threadIdx.x & 63;
+  const int64_t b = kWave ? (int64_t)blockIdx.x * (kEncThreads / 64) + (threadIdx.x >> 6)
+                          : (int64_t)blockIdx.x * kEncThreads + threadIdx.x;
+  if (b >= nblocks) return;                    // (after the only barrier)
+  double wv[DM];
+#pragma unroll
+  for (int i = 0; i < DM; ++i) wv[i] = i < d ? (double)w[b * d + i] : 0.0;
+  double best = 0.0;
+  uint32_t bidx = 0;
+  if (kWave) {
+    const int nfree = F - 6;
+    pinv_walk<DM>(t, wv, d, F, (uint32_t)lane << nfree, nfree, best, bidx);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const double ob = __shfl_xor(best, o, 64);
+      const uint32_t oi = (uint32_t)__shfl_xor((int)bidx, o, 64);
+      better(best, bidx, ob, oi);
+    }
+    if (lane < D) signs[b * D + lane] = ((bidx >> lane) & 1) ? (int8_t)-1 : (int8_t)1;
+    if (lane == 0 && dist2 != nullptr) dist2[b] = (float)best;
+  } else {
+    pinv_walk<DM>(t, wv, d, F, 0u, F, best, bidx);
+    for (int e = 0; e < D; ++e) signs[b * D + e] = ((bidx >> e) & 1) ? (int8_t)-1 : (int8_t)1;
+    if (dist2 != nullptr) dist2[b] = (float)best;
+  }
+}
+
+template <int DM>
+hipError_t launch_encode_pinv_t(const float* w, int64_t nblocks, int d, int D, const float* M,
+                                const double* AB, int8_t* signs, float* dist2, hipStream_t stream) {
+  if (D - d > 10) {
+    const int64_t groups = (nblocks + 3) / 4;
+    hipLaunchKernelGGL((encode_pinv_kernel<DM, true>), dim3((unsigned)groups), dim3(kEncThreads), 0,
+                       stream, w, nblocks, d, D, M, AB, signs, dist2);
+  } else {
+    const int64_t groups = (nblocks + kEncThreads - 1) / kEncThreads;
+    hipLaunchKernelGGL((encode_pinv_kernel<DM, false>), dim3((unsigned)groups), dim3(kEncThreads),
+                       0, stream, w, nblocks, d, D, M, AB, signs, dist2);
+  }
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------ training step
 // Workgroup g takes samples 256 g .. 256 g + 255. Phase 1, thread = sample:
 // r = w - M s* and u = r / ||r|| (zero where r = 0) in fp64, into LDS with
@@ -216,6 +386,18 @@ hipError_t launch_encode(const float* w, int64_t nblocks, int d, int D, const fl
   if (d <= 8) return launch_encode_t<8>(w, nblocks, d, D, M, signs, dist2, stream);
   if (d <= 12) return launch_encode_t<12>(w, nblocks, d, D, M, signs, dist2, stream);
   return launch_encode_t<16>(w, nblocks, d, D, M, signs, dist2, stream);
+}
+
+hipError_t launch_encode_pinv(const float* w, int64_t nblocks, int d, int D, const float* M,
+                              const double* AB, int8_t* signs, float* dist2, hipStream_t stream) {
+  (void)hipGetLastError();
+  if (d < 1 || d > D || D > kEncodePinvMaxD || D - d > kEncodePinvMaxFree || d > kEncodeMaxSmallD)
+    return hipErrorInvalidValue;
+  if (nblocks == 0) return hipSuccess;
+  if (d <= 4) return launch_encode_pinv_t<4>(w, nblocks, d, D, M, AB, signs, dist2, stream);
+  if (d <= 8) return launch_encode_pinv_t<8>(w, nblocks, d, D, M, AB, signs, dist2, stream);
+  if (d <= 12) return launch_encode_pinv_t<12>(w, nblocks, d, D, M, AB, signs, dist2, stream);
+  return launch_encode_pinv_t<16>(w, nblocks, d, D, M, AB, signs, dist2, stream);
 }
 
 int train_groups(int64_t n) { return (int)((n + kEncThreads - 1) / kEncThreads); }

@@ -447,10 +447,15 @@ XpGeom xp_geom(int64_t B, const PackedGeom& g, int d, int D);
 int plan_wspace_jb(int64_t B, const PackedGeom& g, int d);   // 16-row batch tiles per workgroup
 // ---- nearest-neighbour encoding and the training step of M (encode.hip)
 constexpr int kEncodeMaxD = 24;        // exhaustive search: 2^D sign vectors per block
+constexpr int kEncodePinvMaxD = 32;    // pseudo-inverse search: D
+constexpr int kEncodePinvMaxFree = 24; // ... and 2^(D - d) sign vectors per block
 constexpr int kEncodeMaxSmallD = 16;   // d (the residual lives in registers)
 constexpr int kTrainMaxD = 24;
 hipError_t launch_encode(const float* w, int64_t nblocks, int d, int D, const float* M,
                          int8_t* signs, float* dist2, hipStream_t stream);
+// AB: device doubles, A = M_a^-1 (d x d, row-major) then A M_f (d x (D - d), row-major).
+hipError_t launch_encode_pinv(const float* w, int64_t nblocks, int d, int D, const float* M,
+                              const double* AB, int8_t* signs, float* dist2, hipStream_t stream);
 int train_groups(int64_t n);
 size_t train_workspace_bytes(int64_t n, int d, int D);
 hipError_t launch_train_step(float* M, const float* w, int64_t n, int d, int D, float lr,

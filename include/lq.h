@@ -399,6 +399,34 @@ lq_status lq_encode(const float* w, int64_t nblocks, int32_t d, int32_t D, const
                     int8_t* signs, float* dist2, void* stream);
 
 /*
+ * The nearest-neighbour search of lq_encode reduced from 2^D to 2^(D-d) sign
+ * vectors by pseudo-inverse initialisation ([review] Method: encoding
+ * "accelerated from 2^D to 2^(D-d)"; [review] Limitations: the exhaustive
+ * search is practically capped at D - d <= 20). Reading: M = [M_a | M_f],
+ * the first d columns solved for, the other D - d enumerated; for every sign
+ * vector s_f of M_f, s_a = sgn(M_a^-1 (w - M_f s_f)) (+1 at 0), the candidate
+ * s = (s_a, s_f); the candidate closest to w_b wins (fp64 residuals), among
+ * equally close ones the lowest index (index bit e set meaning s_e = -1).
+ * Exact (lq_encode's result) when M_a is diagonal; otherwise never closer
+ * than lq_encode. Makes LQ-32/16 (2^16 candidates per block) encodable.
+ * w, M, signs, dist2: as lq_encode. ws: device workspace of
+ * lq_encode_pinv_workspace_size bytes (16-byte aligned): the tables
+ * M_a^-1 and M_a^-1 M_f (fp64), computed on the host: the call copies M to
+ * the host and synchronizes `stream` twice (M read, tables written) before
+ * the search kernel is enqueued.
+ * Limits: 1 <= d <= LQ_ENCODE_MAX_SMALL_D, d <= D <= LQ_ENCODE_PINV_MAX_D,
+ * D - d <= LQ_ENCODE_PINV_MAX_FREE (UNSUPPORTED beyond). Errors: as
+ * lq_encode; INVALID_ARG also when M_a is singular (a pivot of its
+ * elimination at most 2^-40 of its largest magnitude) or ws is not 16-byte
+ * aligned; WORKSPACE for a missing or short workspace.
+ */
+#define LQ_ENCODE_PINV_MAX_D 32
+#define LQ_ENCODE_PINV_MAX_FREE 24
+lq_status lq_encode_pinv_workspace_size(int32_t d, int32_t D, size_t* bytes);
+lq_status lq_encode_pinv(const float* w, int64_t nblocks, int32_t d, int32_t D, const float* M,
+                         int8_t* signs, float* dist2, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * One gradient step on M of the objective of [paper] §3.1 Eq. (1), on the
  * caller's samples w (n x d floats on the device, drawn from N(0, I_d)):
  *     loss(M) = mean_b min_s || w_b - M s ||_2     (the norm as printed).

@@ -278,6 +278,30 @@ def test_encode_and_train_validation():
     assert t(P, P, 0, 3, 8, ctypes.c_float(0.1), None, None, 0, None) == LQ_OK
 
 
+def test_encode_pinv_validation():
+    f = LIB.lq_encode_pinv
+    g = LIB.lq_encode_pinv_workspace_size
+    out = ctypes.c_size_t()
+    assert g(16, 32, ctypes.byref(out)) == LQ_OK and out.value == 16 * 32 * 8   # M_a^-1, M_a^-1 M_f
+    assert g(3, 8, ctypes.byref(out)) == LQ_OK and out.value == 256              # (192 rounded up)
+    assert g(3, 8, None) == LQ_ERR_INVALID_ARG
+    assert g(3, 33, ctypes.byref(out)) == LQ_ERR_UNSUPPORTED                     # D > 32
+    assert g(2, 27, ctypes.byref(out)) == LQ_ERR_UNSUPPORTED                     # 2^25 per block
+    assert g(17, 32, ctypes.byref(out)) == LQ_ERR_UNSUPPORTED                    # d > 16
+    assert g(9, 8, ctypes.byref(out)) == LQ_ERR_INVALID_ARG                      # d > D
+    ws = 4096
+    assert f(P, 0, 16, 32, P, P, None, None, 0, None) == LQ_OK                   # nothing to do
+    assert f(None, 4, 16, 32, P, P, None, P, ws, None) == LQ_ERR_INVALID_ARG
+    assert f(P, 4, 16, 32, None, P, None, P, ws, None) == LQ_ERR_INVALID_ARG
+    assert f(P, 4, 16, 32, P, None, None, P, ws, None) == LQ_ERR_INVALID_ARG
+    assert f(P, -1, 16, 32, P, P, None, P, ws, None) == LQ_ERR_INVALID_ARG
+    assert f(P, 4, 16, 32, P, P, None, None, 0, None) == LQ_ERR_WORKSPACE
+    assert f(P, 4, 16, 32, P, P, None, P, ws - 1, None) == LQ_ERR_WORKSPACE
+    assert f(P, 4, 16, 32, P, P, None, P + 8, ws, None) == LQ_ERR_INVALID_ARG    # ws not 16-aligned
+    assert f(P, 4, 2, 27, P, P, None, P, ws, None) == LQ_ERR_UNSUPPORTED
+    assert f(P + 2, 4, 16, 32, P, P, None, P, ws, None) == LQ_ERR_INVALID_ARG   # w not 4-aligned
+
+
 def multi_ws_size(layers, B, xt, n=None):
     arr = (LQLayer * max(1, len(layers)))(*layers)
     out = ctypes.c_size_t()

@@ -16,6 +16,12 @@ step of M (lq_train_m_step) with the CPU oracle.
 * Training: one step of M against the oracle's step (fp64 on both sides,
   M stored as fp32), the loss, several steps decreasing the loss, and
   determinism.
+* The 2^(D-d) pseudo-inverse-initialised search (lq_encode_pinv) against the
+  oracle's ``encode_pinv``: both layouts (a lane per block for D - d <= 10, a
+  wavefront beyond), LQ-24/10 and LQ-32/16 (2^16 candidates per block),
+  D = d; the chosen sign vectors must be the oracle's and the distances agree
+  to float rounding. With a diagonal M_a it is the exhaustive search, so it
+  must equal lq_encode. A singular M_a and a short workspace are errors.
 """
 import numpy as np
 import pytest
@@ -172,3 +178,68 @@ def test_train_descends_and_is_deterministic(lq):
         Mr, _ = ref.train_m_step(Mr, wr, 0.05)
         Mr = Mr.astype(np.float32).astype(np.float64)
     assert np.allclose(M1, Mr, rtol=0, atol=1e-5)
+
+
+def _gpu_encode_pinv(lq, w, M):
+    n, d = w.shape
+    D = M.shape[1]
+    wd = dev(w.astype(np.float32))
+    Md = dev(M.astype(np.float32))
+    signs = torch.zeros((n, D), dtype=torch.int8, device="cuda")
+    dist = torch.zeros(n, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(lq.lq_encode_pinv_workspace_size(d, D), dtype=torch.uint8, device="cuda")
+    note(f"lq_encode_pinv n={n} d={d} D={D}")
+    lq.lq_encode_pinv(wd, n, d, D, Md, signs, dist, ws)
+    torch.cuda.synchronize()
+    return signs.cpu().numpy().astype(np.float64), dist.cpu().numpy().astype(np.float64)
+
+
+PINV_CASES = [
+    # (d, D, n): D - d <= 10 a lane per block, beyond a wavefront per block
+    (1, 1, 20), (1, 6, 37), (2, 5, 300), (3, 8, 129), (4, 4, 50), (2, 12, 65),
+    (2, 13, 33), (12, 16, 17), (5, 20, 5), (10, 24, 9), (16, 32, 4),
+]
+
+
+@pytest.mark.parametrize("d,D,n", PINV_CASES, ids=[f"d{c[0]}-D{c[1]}" for c in PINV_CASES])
+@pytest.mark.parametrize("init", ["orthonormal", "gaussian"])
+def test_encode_pinv_matches_oracle(lq, d, D, n, init):
+    rng = np.random.default_rng(7000 + 100 * d + D)
+    if init == "orthonormal":
+        M = ref.orthonormal_rows(rng.standard_normal((D, D)), d)
+    else:
+        M = rng.standard_normal((d, D)) / np.sqrt(D)
+    M = M.astype(np.float32).astype(np.float64)
+    w = rng.standard_normal((n, d)).astype(np.float32).astype(np.float64)
+    s_gpu, d_gpu = _gpu_encode_pinv(lq, w, M)
+    s_ref, d_ref = ref.encode_pinv(w, M)
+    assert np.array_equal(s_gpu, s_ref)
+    assert np.allclose(d_gpu, d_ref, rtol=1e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("d,D", [(3, 12), (10, 20), (4, 16), (1, 9)])
+def test_encode_pinv_diagonal_is_exhaustive(lq, d, D):
+    rng = np.random.default_rng(8000 + 100 * d + D)
+    Ma = np.diag(rng.uniform(0.3, 1.5, d) * rng.choice([-1.0, 1.0], d))
+    M = np.hstack([Ma, rng.standard_normal((d, D - d)) / np.sqrt(D)]).astype(np.float32).astype(np.float64)
+    w = rng.standard_normal((33, d)).astype(np.float32).astype(np.float64)
+    s_p, d_p = _gpu_encode_pinv(lq, w, M)
+    s_e, d_e = _gpu_encode(lq, w, M)
+    assert np.array_equal(s_p, s_e)
+    assert np.allclose(d_p, d_e, rtol=1e-6, atol=1e-7)
+
+
+def test_encode_pinv_errors(lq):
+    d, D = 3, 8
+    M = np.ones((d, D))                                  # M_a of rank 1
+    w = np.zeros((4, d))
+    with pytest.raises(lq.LQError) as e:
+        _gpu_encode_pinv(lq, w, M)
+    assert e.value.status == lq._lib.LQ_ERR_INVALID_ARG
+    wd = dev(w.astype(np.float32))
+    Md = dev(np.eye(d, D).astype(np.float32))
+    signs = torch.zeros((4, D), dtype=torch.int8, device="cuda")
+    short = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(lq.LQError) as e:
+        lq.lq_encode_pinv(wd, 4, d, D, Md, signs, None, short)
+    assert e.value.status == lq._lib.LQ_ERR_WORKSPACE
