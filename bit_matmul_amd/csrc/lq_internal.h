@@ -245,6 +245,7 @@ size_t operand_bytes(int64_t L, const OperandShape& s);
 // or stream through it in chunks (`chunked`, sign_fp6_chunked.hip).
 struct Fp6Plan {
   bool chunked;
+  bool stream;            // resident: each tile's record (<= 1 KB) loaded with its slots
   int p;                  // panels per workgroup
   int w;                  // wavefronts per workgroup (chunked: compute wavefronts, plus a loader)
   int pgroups;            // panel groups

@@ -27,21 +27,28 @@
 // Work split. A workgroup owns P 16-row panels over the whole reduction
 // length (no communication between workgroups), for layers whose
 // activation records all fit LDS (the chunked variant in
-// sign_fp6_chunked.hip streams them for the others). At entry it copies
-// the records into LDS with global_load_lds, with the row scales and the
-// tail tile's packed bytes, and waits for them before any weight is
-// requested: requested together with the weight stream they would queue
-// behind it (a compute unit returns its vector-memory requests roughly in
-// order, and the stream fills every memory queue); with no copy in flight
-// the compiler's waits for the slot loads also stay exact. Then every
-// wavefront requests the packed slots of its first DEPTH tiles and takes
+// sign_fp6_chunked.hip streams them for the others). Every wavefront takes
 // the row's tiles round-robin, keeping DEPTH tiles of slots (P 16-byte
 // loads per tile) requested: no barrier couples the wavefronts until the
 // end, so the weight stream never waits for another wavefront. One
-// activation-operand read from LDS feeds P panels' MFMAs. The wavefronts'
-// accumulators are added in LDS in a fixed order, the terms and plane sums
-// combined, the row scale applied and y written. Deterministic: fixed
-// summation orders, no floating-point atomics.
+// activation-operand read from LDS feeds P panels' MFMAs. Records:
+//   - copied first: at entry the records go to LDS with global_load_lds,
+//     with the row scales and the tail tile's packed bytes, and land before
+//     any weight is requested (requested together with the weight stream
+//     they would queue behind it: a compute unit returns its vector-memory
+//     requests roughly in order, and the stream fills every memory queue;
+//     with no copy in flight the compiler's waits for the slot loads also
+//     stay exact);
+//   - streamed, where that copy is long (records of at most 1 KB, as at
+//     batch 1 with bf16 activations, but more than 64 KB of them: the long
+//     reductions): each tile's record is requested with its slots, 16 bytes
+//     per lane, into the wavefront's registers, and copied to the
+//     wavefront's own 1 KB of LDS just before the tile's MFMAs read it. No
+//     copy precedes the first weight request, and the waits stay exact
+//     (every request is a plain load into registers).
+// The wavefronts' accumulators are added in LDS in a fixed order, the terms
+// and plane sums combined, the row scale applied and y written.
+// Deterministic: fixed summation orders, no floating-point atomics.
 #include <algorithm>
 
 #include "lq_fp6_mma.h"
@@ -55,7 +62,7 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint8_t* dst) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
 }
 
-template <int P, int CS, int W, int DEPTH>
+template <int P, int CS, int W, int DEPTH, bool kStream>
 __global__ __launch_bounds__(64 * W) void sign_fp6_kernel(SignTable tab, int rec, int ncv, int B,
                                                           int red_off, int y_bf16) {
   extern __shared__ __align__(16) uint8_t smem[];
@@ -81,11 +88,12 @@ __global__ __launch_bounds__(64 * W) void sign_fp6_kernel(SignTable tab, int rec
   const int nk = wave < nfull ? (nfull - wave + W - 1) / W : 0;
 
   // LDS: row scales (1 KB), the row's records (red_off - 1024 bytes, a
-  // whole number of KB), the tail tile's slots (P KB); the final reduction
-  // reuses everything after the row scales.
+  // whole number of KB; streamed: 1 KB per wavefront), the tail tile's slots
+  // (P KB); the final reduction reuses everything after the row scales.
   float* rs_lds = reinterpret_cast<float*>(smem);
   uint8_t* rec_lds = smem + 1024;
   uint8_t* tslot_lds = smem + red_off;
+  uint8_t* wrec = rec_lds + 1024 * wave;           // streamed: this wavefront's record
 
   // This lane's MFMA column in each column set; unused columns read the
   // set's last column (their products are never read).
@@ -104,9 +112,14 @@ __global__ __launch_bounds__(64 * W) void sign_fp6_kernel(SignTable tab, int rec
 #pragma unroll
   for (int p = 0; p < P; ++p) prow[p] = packed + (int64_t)min(pbase + p, panels - 1) * panel_bytes;
 
-  // ---- 1. the activation records, the row scales and the tail tile's
-  // packed bytes into LDS, all landed before any weight is requested
-  {
+  const int tail_wave = nfull % W;                 // takes the tail tile first
+  const int tb = kPanelRows * tail_bytes;           // tail bytes of a panel: a multiple of 16, <= 1008
+  const int tail_o = min(16 * lane, max(tb, 16) - 16);
+  v4u rsv = {0u, 0u, 0u, 0u};                       // streamed: row scales (wavefront 0)
+  v4u tr_rec = {0u, 0u, 0u, 0u}, tr_raw[P];         // streamed: the tail tile's record and bytes
+  if (!kStream) {
+    // ---- 1. the activation records, the row scales and the tail tile's
+    // packed bytes into LDS, all landed before any weight is requested
     const uint8_t* src = aop + 16 * lane;
     const int bytes = ext_tiles * rec;
     for (int off = wave * 1024; off < bytes; off += W * 1024) lds_dma16(src + off, rec_lds + off);
@@ -115,33 +128,49 @@ __global__ __launch_bounds__(64 * W) void sign_fp6_kernel(SignTable tab, int rec
       lds_dma16(row_scale + n4, reinterpret_cast<uint8_t*>(rs_lds));
     }
     if (has_tail && wave == W - 1) {
-      const int tb = kPanelRows * tail_bytes;                    // a multiple of 16, <= 1008
-      const int o = min(16 * lane, tb - 16);
 #pragma unroll
       for (int p = 0; p < P; ++p)
-        lds_dma16(prow[p] + (int64_t)full_tiles * kTileBytes + o, tslot_lds + 1024 * p);
+        lds_dma16(prow[p] + (int64_t)full_tiles * kTileBytes + tail_o, tslot_lds + 1024 * p);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    wg_barrier();
+  } else {
+    // ---- 1'. requested ahead of the weights, into registers: the row
+    // scales (used after the loop) and the tail tile's record and bytes
+    if (wave == 0) {
+      const int n4 = min(pbase * kPanelRows + 4 * lane, N - 4);
+      rsv = *reinterpret_cast<const v4u*>(row_scale + n4);
+    }
+    if (has_tail && wave == tail_wave) {
+      tr_rec = *reinterpret_cast<const v4u*>(aop + (int64_t)nfull * rec + 16 * lane);
+#pragma unroll
+      for (int p = 0; p < P; ++p)
+        tr_raw[p] = *reinterpret_cast<const v4u*>(prow[p] + (int64_t)full_tiles * kTileBytes + tail_o);
     }
   }
 
-  __builtin_amdgcn_s_waitcnt(0);
-  wg_barrier();
-
-  // ---- 2. packed slots, DEPTH tiles ahead. Loads are issued on every path
-  // (past the wavefront's last tile every lane reads the panel's first 16
-  // bytes, unused), so that the count of loads issued after any given one
-  // is fixed and the waits are exact.
+  // ---- 2. packed slots, DEPTH tiles ahead (streamed: with the tile's
+  // record). Loads are issued on every path (past the wavefront's last tile
+  // every lane reads the panel's first 16 bytes and the first record,
+  // unused), so that the count of loads issued after any given one is fixed
+  // and the waits are exact.
   uint4 A[DEPTH][P];
-  auto issue = [&](int j, uint4 (&S)[P]) {
-    const int off = j < nk ? (wave + j * W) * kTileBytes + 16 * lane : 0;
+  v4u R[DEPTH];
+  auto issue = [&](int j, uint4 (&S)[P], v4u& Rj) {
+    const int tile = j < nk ? wave + j * W : 0;
+    const int off = j < nk ? tile * kTileBytes + 16 * lane : 0;
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       // each weight byte is read once per call: non-temporal
       const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(prow[p] + off));
       S[p] = make_uint4(v.x, v.y, v.z, v.w);
     }
+    // (a record of <= 1 KB: the 1 KB read from its start stays within the
+    // operand's slack)
+    if (kStream) Rj = *reinterpret_cast<const v4u*>(aop + (int64_t)tile * rec + 16 * lane);
   };
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d) issue(d, A[d]);
+  for (int d = 0; d < DEPTH; ++d) issue(d, A[d], R[d]);
 
   f32x4 acc[P][CS];
 #pragma unroll
@@ -183,7 +212,13 @@ __global__ __launch_bounds__(64 * W) void sign_fp6_kernel(SignTable tab, int rec
 
   // ---- 3. the tail tile first (its slots from the row-major tail bytes),
   // by the wavefront whose turn it would be, then the full tiles
-  if (has_tail && wave == nfull % W) {
+  if (has_tail && wave == tail_wave) {
+    if (kStream) {
+      // the wavefront's own LDS: its later reads follow these writes
+      *reinterpret_cast<v4u*>(wrec + 16 * lane) = tr_rec;
+#pragma unroll
+      for (int p = 0; p < P; ++p) *reinterpret_cast<v4u*>(tslot_lds + 1024 * p + 16 * lane) = tr_raw[p];
+    }
     uint4 TS[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
@@ -203,16 +238,20 @@ __global__ __launch_bounds__(64 * W) void sign_fp6_kernel(SignTable tab, int rec
       }
       TS[p] = make_uint4(w[0], w[1], w[2], w[3]);
     }
-    tile_mfma(rec_lds + nfull * rec, TS);
+    tile_mfma(kStream ? wrec : rec_lds + nfull * rec, TS);
   }
   for (int j0 = 0; j0 < nk; j0 += DEPTH) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       const int j = j0 + d;
-      if (j < nk) tile_mfma(rec_lds + (wave + j * W) * rec, A[d]);
-      issue(j + DEPTH, A[d]);
+      if (j < nk) {
+        if (kStream) *reinterpret_cast<v4u*>(wrec + 16 * lane) = R[d];
+        tile_mfma(kStream ? wrec : rec_lds + (wave + j * W) * rec, A[d]);
+      }
+      issue(j + DEPTH, A[d], R[d]);
     }
   }
+  if (kStream && wave == 0) *reinterpret_cast<v4u*>(smem + 16 * lane) = rsv;   // rs_lds
   __builtin_amdgcn_s_waitcnt(0);                     // the unused trailing loads
   wg_barrier();                                      // records are no longer read
 
@@ -275,15 +314,19 @@ constexpr int kRecLdsMax = 128 * 1024;             // LDS for the records of a r
 // Wavefronts per workgroup, and the slot tiles each keeps requested (P
 // 16-byte loads per tile). Eight wavefronts (two per SIMD, 256 registers
 // each) while the slot, accumulator and operand registers fit 256: up to 12
-// panels of one 16-column set, 6 of two; four (one per SIMD, 512) beyond.
-constexpr int waves_for(int p, int cs) { return (cs == 1 ? p >= 14 : p >= 8) ? 4 : 8; }
+// panels of one 16-column set (10 with streamed records, which hold DEPTH
+// more quads), 6 of two; four (one per SIMD, 512) beyond.
+constexpr int waves_for(int p, int cs, bool stream) {
+  return (cs == 1 ? p >= (stream ? 12 : 14) : p >= 8) ? 4 : 8;
+}
 constexpr int depth_for(int p) { return p <= 4 ? 4 : (p <= 8 ? 3 : (p <= 12 ? 2 : 3)); }
 
-template <int P, int CS>
+template <int P, int CS, bool kStream>
 hipError_t launch_fp6_t(const SignTable& tab, int groups, const OperandShape& s, int64_t B,
                         bool y_bf16, const Fp6Plan& plan, hipStream_t stream) {
-  constexpr int W = waves_for(P, CS), DEPTH = depth_for(P);
+  constexpr int W = waves_for(P, CS, kStream), DEPTH = depth_for(P);
   if (plan.w != W) return hipErrorInvalidValue;
+  if (kStream && s.rec > 1024) return hipErrorInvalidValue;
   const dim3 grid((unsigned)groups);
   const dim3 block(64 * W);
   if (plan.lds_bytes > 160 * 1024) return hipErrorInvalidValue;   // a compute unit's LDS
@@ -291,12 +334,12 @@ hipError_t launch_fp6_t(const SignTable& tab, int groups, const OperandShape& s,
   static size_t allowed = 0;
   if (plan.lds_bytes > allowed) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&sign_fp6_kernel<P, CS, W, DEPTH>),
+        reinterpret_cast<const void*>(&sign_fp6_kernel<P, CS, W, DEPTH, kStream>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)plan.lds_bytes);
     if (e != hipSuccess) return e;
     allowed = plan.lds_bytes;
   }
-  return launch_timed(sign_fp6_kernel<P, CS, W, DEPTH>, grid, block, plan.lds_bytes, stream, tab,
+  return launch_timed(sign_fp6_kernel<P, CS, W, DEPTH, kStream>, grid, block, plan.lds_bytes, stream, tab,
                       s.rec, s.ncv, (int)B, plan.red_off, y_bf16 ? 1 : 0);
 }
 
@@ -309,10 +352,20 @@ constexpr int kPanelsCS3[] = {1, 2, 3, 4};
 }  // namespace
 
 // LDS and workgroups of a plan of P panels per workgroup for one layer.
+constexpr int kStreamRecordsAbove = 64 * 1024;     // records streamed beyond this copy
+
+// Whether a layer's records are streamed (decided once for a group of layers
+// sharing one launch, on its longest rows).
+static bool stream_records(const PackedGeom& g, const OperandShape& s) {
+  return s.rec <= 1024 && (int64_t)g.ext_tiles * s.rec > kStreamRecordsAbove;
+}
+
+// LDS, wavefronts and workgroups of a plan of P panels per workgroup (and
+// the record mode pl->stream) for one layer.
 static void fill_resident(Fp6Plan* pl, const PackedGeom& g, const OperandShape& s) {
-  const int recs = ((g.ext_tiles * s.rec + 1023) / 1024) * 1024;
+  pl->w = waves_for(pl->p, s.cs, pl->stream);
+  const int recs = pl->stream ? 1024 * pl->w : ((g.ext_tiles * s.rec + 1023) / 1024) * 1024;
   const int nc = std::min(16, s.ncv);
-  pl->w = waves_for(pl->p, s.cs);
   const size_t red = (size_t)pl->w * pl->p * s.cs * 4 * nc * 16 + (size_t)pl->w * 16 * 4;
   pl->red_off = 1024 + recs;
   pl->lds_bytes = std::max((size_t)pl->red_off + (size_t)1024 * pl->p, 1024 + red);
@@ -327,7 +380,8 @@ bool fp6_records_fit(const PackedGeom& g, const OperandShape& s) {
 Fp6Plan plan_fp6(int64_t B, const PackedGeom& g, const OperandShape& s, int device_cus,
                  int panels_per_group) {
   (void)B;
-  if (!fp6_records_fit(g, s)) return plan_fp6_chunked(g, s, device_cus, panels_per_group);
+  if (!fp6_records_fit(g, s) && !stream_records(g, s))
+    return plan_fp6_chunked(g, s, device_cus, panels_per_group);
   const int64_t cus = device_cus > 0 ? device_cus : 256;
   const int* cand = s.cs == 1 ? kPanelsCS1 : (s.cs == 2 ? kPanelsCS2 : kPanelsCS3);
   const int ncand = s.cs == 1 ? 12 : (s.cs == 2 ? 7 : 4);
@@ -350,6 +404,7 @@ Fp6Plan plan_fp6(int64_t B, const PackedGeom& g, const OperandShape& s, int devi
     }
   }
   if (best_load < 0) best.p = 1;
+  best.stream = stream_records(g, s);
   fill_resident(&best, g, s);
   return best;
 }
@@ -399,14 +454,19 @@ hipError_t launch_fp6_table(const SignTable& tab, int groups, const OperandShape
   if (plan.chunked) return launch_fp6_chunked_table(tab, groups, s, B, y_bf16, plan, stream);
   (void)hipGetLastError();   // clear a stale error of an earlier runtime call
 #define LQ_FP6_CASE(P_, CS_)                                                            \
-  if (plan.p == P_ && s.cs == CS_) return launch_fp6_t<P_, CS_>(tab, groups, s, B, y_bf16, plan, stream);
-  LQ_FP6_CASE(1, 1) LQ_FP6_CASE(2, 1) LQ_FP6_CASE(3, 1) LQ_FP6_CASE(4, 1) LQ_FP6_CASE(5, 1)
-  LQ_FP6_CASE(6, 1) LQ_FP6_CASE(7, 1) LQ_FP6_CASE(8, 1) LQ_FP6_CASE(10, 1) LQ_FP6_CASE(12, 1)
-  LQ_FP6_CASE(14, 1) LQ_FP6_CASE(16, 1)
+  if (plan.p == P_ && s.cs == CS_) return launch_fp6_t<P_, CS_, false>(tab, groups, s, B, y_bf16, plan, stream);
+#define LQ_FP6_CASE_S(P_)                                                                \
+  if (plan.p == P_ && s.cs == 1)                                                         \
+    return plan.stream ? launch_fp6_t<P_, 1, true>(tab, groups, s, B, y_bf16, plan, stream) \
+                       : launch_fp6_t<P_, 1, false>(tab, groups, s, B, y_bf16, plan, stream);
+  LQ_FP6_CASE_S(1) LQ_FP6_CASE_S(2) LQ_FP6_CASE_S(3) LQ_FP6_CASE_S(4) LQ_FP6_CASE_S(5)
+  LQ_FP6_CASE_S(6) LQ_FP6_CASE_S(7) LQ_FP6_CASE_S(8) LQ_FP6_CASE_S(10) LQ_FP6_CASE_S(12)
+  LQ_FP6_CASE_S(14) LQ_FP6_CASE_S(16)
   LQ_FP6_CASE(1, 2) LQ_FP6_CASE(2, 2) LQ_FP6_CASE(3, 2) LQ_FP6_CASE(4, 2) LQ_FP6_CASE(6, 2)
   LQ_FP6_CASE(8, 2) LQ_FP6_CASE(12, 2)
   LQ_FP6_CASE(1, 3) LQ_FP6_CASE(2, 3) LQ_FP6_CASE(3, 3) LQ_FP6_CASE(4, 3)
 #undef LQ_FP6_CASE
+#undef LQ_FP6_CASE_S
   return hipErrorInvalidValue;
 }
 
@@ -423,7 +483,7 @@ hipError_t launch_sign_fp6(const uint8_t* packed, const PackedGeom& g, const Ope
 }
 
 bool fp6_plans_match(const Fp6Plan& a, const Fp6Plan& b) {
-  return a.chunked == b.chunked && a.p == b.p && a.w == b.w &&
+  return a.chunked == b.chunked && a.stream == b.stream && a.p == b.p && a.w == b.w &&
          (!a.chunked || (a.tpc == b.tpc && a.chunk_bytes == b.chunk_bytes));
 }
 

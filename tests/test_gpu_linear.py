@@ -155,6 +155,30 @@ def test_edge_shapes(lq, N, K, d, D, hb, xd, label, B):
     assert rel_l2(host(y), want) < TOL[xd]
 
 
+# Batch 1, bf16: records of at most 1 KB, more than 64 KB of them, so the
+# small-batch product streams each tile's record with its slots.
+STREAM = [
+    # (N, K, d, D, hb, label): panels per workgroup as planned on 256 units
+    (256, 16010, 10, 24, 2, "76 tiles with a 3-byte tail, 1 panel per workgroup"),
+    (8192, 20000, 10, 24, 32, "94 tiles with a tail, 2 panels"),
+    (10240, 16010, 10, 24, 2, "76 tiles with a tail, 3 panels"),
+    (1040, 28672, 10, 24, 1024, "135 tiles, 65 panels"),
+    (64, 40000, 2, 5, 64, "2.5 bit, 196 tiles: more records than LDS holds"),
+]
+
+
+@pytest.mark.parametrize("N,K,d,D,hb,label", STREAM, ids=[e[-1] for e in STREAM])
+def test_streamed_records_batch1(lq, N, K, d, D, hb, label):
+    inp = make_layer_small(N, K, d, D, hb, seed=N + K + 3, B_max=1, xdtype="bf16")
+    L = -(-K // d) * D
+    assert -(-L // 512) * 896 > 65536
+    layer = DeviceLayer(inp, lq)
+    x = inp.x(1)
+    y = layer.linear(lq, dev(x, torch.bfloat16), 1, torch.float32)
+    want = ref.linear(x, inp.c, hb, inp.M, inp.signs(), inp.row_scale)
+    _check_all(host(y), want, 3e-3)
+
+
 def test_every_batch_size_small(lq):
     inp = make_layer_small(64, 2048, 10, 24, 1024, seed=77, B_max=17, xdtype="bf16")
     layer = DeviceLayer(inp, lq)
