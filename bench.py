@@ -66,7 +66,8 @@ SIGN_KERNEL = "sign_fp6_kernel"
 LARGE_KERNEL = "sign_mfma_large_kernel"
 WSPACE_KERNEL = "wspace_kernel"
 # Kernels that carry the sign product of one lq_linear call (one per call).
-PRODUCT_KERNELS = ("sign_fp6_kernel", "sign_valu_kernel", "sign_mfma_large_kernel",
+PRODUCT_KERNELS = ("sign_fp6_kernel", "sign_fp6_chunked_kernel", "sign_valu_kernel",
+                   "sign_mfma_large_kernel",
                    "wspace_kernel", "decode_fused_kernel", "decode_self_kernel",
                    "decode_split_kernel")
 # The files of the kernels whose HBM traffic the committed summary holds.

@@ -218,6 +218,7 @@ lq_status plan_exec(int64_t B, int64_t N, int64_t L, int64_t K, int d, int D, lq
         const lq::ZpGeom zg = lq::zp_geom(B, e->g, ztype == LQ_BF16);
         e->off_zp = take(zg.bytes);
         e->off_tslots = take(zg.tail_bytes);
+        e->off_partial = take(lq::plan_large(B, e->g, ztype == LQ_BF16).partial_bytes);
       }
       break;
     case LQ_ALGO_WSPACE:
@@ -320,7 +321,7 @@ lq_status run_exec(const Exec& e, const uint8_t* packed, const void* zin, lq_dty
       if (s != LQ_OK) return s;
       return hip_status(profiled(st, [&] {
         return lq::launch_sign_mfma_large(packed, e.g, zp, base + e.off_tslots, zb, B, row_scale, y,
-                                          yb, st);
+                                          yb, reinterpret_cast<float*>(base + e.off_partial), st);
       }));
     }
     case LQ_ALGO_WSPACE: {
@@ -379,7 +380,9 @@ void fill_plan_info(const Exec& e, int64_t B, lq_plan_info* info) {
       p.waves = lq::kLargeWaves;
       p.panels = lq::kLargeWaves * lp.ppw;
       p.batch_rows = 16 * lp.jb;
-      p.workgroups = (int32_t)(((panels + p.panels - 1) / p.panels) * ((B16 + lp.jb - 1) / lp.jb));
+      p.ksplit = lp.ksplit;
+      p.workgroups = (int32_t)(((panels + p.panels - 1) / p.panels) * ((B16 + lp.jb - 1) / lp.jb) *
+                               lp.ksplit);
       break;
     }
     case LQ_ALGO_WSPACE: {

@@ -420,15 +420,18 @@ struct ZpGeom {
 ZpGeom zp_geom(int64_t B, const PackedGeom& g, bool z_bf16);
 struct LargePlan {
   int ppw, jb;      // panels per compute wavefront, 16-row batch tiles per workgroup
+  int ksplit, tps;  // reduction ranges (1: none) and tiles per range
+  size_t partial_bytes;   // ksplit > 1: fp32 partial sums, ksplit x B x N
 };
 LargePlan plan_large(int64_t B, const PackedGeom& g, bool z_bf16);
 // kind 0: z fp32, 1: z bf16 (both B x L); 2: lift xt (B x K fp32) with M into
 // fp32-precision zp (two planes), 3: the same into bf16 zp (one plane).
 hipError_t launch_zp(const void* src, int kind, int64_t B, int64_t L, int64_t K, int d, int D,
                      const float* M, const PackedGeom& g, void* zp, hipStream_t stream);
+// partial: LargePlan::partial_bytes of workspace (unused when ksplit is 1).
 hipError_t launch_sign_mfma_large(const uint8_t* packed, const PackedGeom& g, const void* zp,
                                   void* tail_slots, bool z_bf16, int64_t B,
-                                  const float* row_scale, void* y, bool y_bf16,
+                                  const float* row_scale, void* y, bool y_bf16, float* partial,
                                   hipStream_t stream);
 // The tail tile's slots of every panel in full-tile form (1 KB per panel;
 // columns past L read as +1 signs).

@@ -20,6 +20,8 @@
 // one conflict-free 1 KB wavefront read. fp32 z is carried as two bf16
 // terms, hi = bf16(z) and lo = bf16(z - hi), in two zp planes; bf16 z as is.
 // Accumulation is fp32.
+#include <algorithm>
+
 #include "lq_internal.h"
 #include "lq_prep.h"
 
@@ -194,12 +196,16 @@ __global__ __launch_bounds__(256) void tail_slots_kernel(const uint8_t* __restri
 // still be in flight: memory operations complete in order) and is done
 // with step t - 1, whose stage the next copy overwrites. The packed slots
 // go from memory straight into registers, one tile (4 steps) ahead.
+// Reduction ranges: workgroup z takes tiles [z tps, min((z + 1) tps,
+// ext_tiles)); with more than one range (a layer with too few panel and
+// batch groups to fill the chip), each writes its fp32 sums, unscaled, to
+// partial[z][b][n] and large_reduce_kernel adds the ranges in order.
 template <int NTERM, int PW, int JB, bool kYBF16>
 __global__ __launch_bounds__(256) void sign_mfma_large_kernel(
     const uint8_t* __restrict__ packed, int64_t panels, int64_t panel_bytes, int full_tiles,
     int tail_bytes, int ext_tiles, const uint4* __restrict__ zp, int64_t B16, int64_t B,
     const uint4* __restrict__ tail_slots, const float* __restrict__ row_scale,
-    void* __restrict__ y, int64_t N) {
+    void* __restrict__ y, int64_t N, int tps, float* __restrict__ partial) {
   constexpr int kStageUnits = NTERM * JB * (kZpBlock / 16);   // [term][jb][s][g][r]
   constexpr int kSlotUnits = 4 * PW * 64;                      // [wave][panel][lane]
   __shared__ uint4 stage0[kStageUnits];
@@ -210,7 +216,9 @@ __global__ __launch_bounds__(256) void sign_mfma_large_kernel(
   __shared__ uint4 slotB[kSlotUnits];
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int64_t steps = 4 * (int64_t)ext_tiles;
-  const int64_t last = steps - 1;
+  const int q_lo = (int)blockIdx.z * tps;
+  const int q_hi = min(q_lo + tps, ext_tiles);    // never empty (checked on the host)
+  const int64_t last = 4 * (int64_t)q_hi - 1;      // the last step of this range
   const int64_t jb0 = (int64_t)blockIdx.y * JB;
   const int64_t pbase = (int64_t)blockIdx.x * 4 * PW + wave * PW;
 
@@ -303,10 +311,11 @@ __global__ __launch_bounds__(256) void sign_mfma_large_kernel(
   constexpr int kCopies = NTERM * JB;
   constexpr int kWait1 = (7 << 4) | (15 << 8) | (kCopies & 15) | ((kCopies >> 4) << 14);
   static_assert(kCopies <= 63, "vmcnt range");
-  copy_slots(0, slotA);
-  copy_step(0, stage0);
-  copy_step(min((int64_t)1, last), stage1);
-  copy_step(min((int64_t)2, last), stage2);
+  const int64_t t_lo = 4 * (int64_t)q_lo;
+  copy_slots(q_lo, slotA);
+  copy_step(t_lo, stage0);
+  copy_step(min(t_lo + 1, last), stage1);
+  copy_step(min(t_lo + 2, last), stage2);
   uint4 bcur[NB];
   u32x4 acur[PW];
 
@@ -323,7 +332,7 @@ __global__ __launch_bounds__(256) void sign_mfma_large_kernel(
           const uint4 v = slot_cur[(wave * PW + i) * 64 + lane];
           w[i][0] = v.x; w[i][1] = v.y; w[i][2] = v.z; w[i][3] = v.w;
         }
-        if (q == 0) {
+        if (q == q_lo) {
 #pragma unroll
           for (int c = 0; c < NB; ++c) bcur[c] = stage0[(c * 4) * 64 + lane];
         }
@@ -331,14 +340,14 @@ __global__ __launch_bounds__(256) void sign_mfma_large_kernel(
         for (int i = 0; i < PW; ++i) acur[i] = sign_operand(w[i][0], 0, kMask, kOne);
       }
       copy_step(min(t0 + u + 3, last), u == 0 ? stage3 : (u == 1 ? stage0 : (u == 2 ? stage1 : stage2)));
-      if (u == 0) copy_slots(min(q + 1, ext_tiles - 1), slot_next);
+      if (u == 0) copy_slots(min(q + 1, q_hi - 1), slot_next);
       mult(u == 0 ? stage0 : (u == 1 ? stage1 : (u == 2 ? stage2 : stage3)),
            u == 0 ? stage1 : (u == 1 ? stage2 : (u == 2 ? stage3 : stage0)), w, u, bcur, acur);
     }
   };
-  for (int q = 0; q < ext_tiles; q += 2) {
+  for (int q = q_lo; q < q_hi; q += 2) {
     tile(q, slotA, slotB);
-    if (q + 1 < ext_tiles) tile(q + 1, slotB, slotA);
+    if (q + 1 < q_hi) tile(q + 1, slotB, slotA);
   }
 
   // No copy may still be writing LDS when the workgroup ends.
@@ -346,6 +355,23 @@ __global__ __launch_bounds__(256) void sign_mfma_large_kernel(
   // Epilogue: lane (g, r) of tile (i, j) holds rows 4g..4g+3 of panel
   // pbase + i for batch row 16 (jb0 + j) + r.
   const int g = lane >> 4, r = lane & 15;
+  if (gridDim.z > 1) {
+    float* part = partial + (int64_t)blockIdx.z * B * N;
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      const int64_t pnl = pbase + i;
+      if (pnl >= panels) continue;
+      const int64_t n0 = pnl * kPanelRows + 4 * g;
+#pragma unroll
+      for (int j = 0; j < JB; ++j) {
+        const int64_t b = 16 * (jb0 + j) + r;
+        if (b >= B) continue;
+        *reinterpret_cast<float4*>(part + b * N + n0) =
+            make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
     const int64_t pnl = pbase + i;
@@ -370,27 +396,71 @@ __global__ __launch_bounds__(256) void sign_mfma_large_kernel(
   }
 }
 
+// y[b][n] = r[n] * (the reduction ranges' partial sums added in order), four
+// outputs per thread (N is a multiple of 16).
+__global__ __launch_bounds__(256) void large_reduce_kernel(const float* __restrict__ partial,
+                                                           int ksplit, int64_t B, int64_t N,
+                                                           const float* __restrict__ row_scale,
+                                                           void* __restrict__ y, int y_bf16) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;   // b * N + n
+  if (i >= B * N) return;
+  const int64_t n = i % N;
+  float4 s = *reinterpret_cast<const float4*>(partial + i);
+  for (int k = 1; k < ksplit; ++k) {
+    const float4 v = *reinterpret_cast<const float4*>(partial + (int64_t)k * B * N + i);
+    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  }
+  const float4 rs = *reinterpret_cast<const float4*>(row_scale + n);
+  const float v0 = rs.x * s.x, v1 = rs.y * s.y, v2 = rs.z * s.z, v3 = rs.w * s.w;
+  if (y_bf16) {
+    const uint32_t lo = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
+    const uint32_t hi = f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + i) = make_uint2(lo, hi);
+  } else {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + i) = make_float4(v0, v1, v2, v3);
+  }
+}
+
 template <int NTERM, int PW, int JB, bool kYBF16>
 hipError_t launch_large_t(const uint8_t* packed, const PackedGeom& g, const uint4* zp, int64_t B,
                           const uint4* tail_slots, const float* row_scale, void* y,
-                          hipStream_t stream) {
+                          const LargePlan& p, float* partial, hipStream_t stream) {
   const int64_t B16 = (B + 15) / 16;
-  const dim3 grid((unsigned)((g.panels + 4 * PW - 1) / (4 * PW)), (unsigned)((B16 + JB - 1) / JB));
-  return launch_timed(sign_mfma_large_kernel<NTERM, PW, JB, kYBF16>, grid, dim3(256), 0, stream,
-                      packed, g.panels, g.panel_bytes, g.full_tiles, g.tail_bytes, g.ext_tiles, zp,
-                      B16, B, tail_slots, row_scale, y, g.N);
+  const dim3 grid((unsigned)((g.panels + 4 * PW - 1) / (4 * PW)), (unsigned)((B16 + JB - 1) / JB),
+                  (unsigned)p.ksplit);
+  if (p.ksplit > 1 && partial == nullptr) return hipErrorInvalidValue;
+  if ((int64_t)(p.ksplit - 1) * p.tps >= g.ext_tiles) return hipErrorInvalidValue;   // an empty range
+  // Timed as one product: the first kernel records the start event, the
+  // reduction the stop.
+  LaunchEvents& ev = launch_events();
+  const LaunchEvents taken = ev;
+  if (p.ksplit > 1) ev.stop = nullptr;
+  const hipError_t e = launch_timed(sign_mfma_large_kernel<NTERM, PW, JB, kYBF16>, grid, dim3(256), 0,
+                                    stream, packed, g.panels, g.panel_bytes, g.full_tiles,
+                                    g.tail_bytes, g.ext_tiles, zp, B16, B, tail_slots, row_scale, y,
+                                    g.N, p.tps, partial);
+  if (e != hipSuccess || p.ksplit == 1) return e;
+  const int64_t quads = B * g.N / 4;
+  const dim3 rgrid((unsigned)((quads + 255) / 256));
+  if (taken.start != nullptr)
+    hipExtLaunchKernelGGL(large_reduce_kernel, rgrid, dim3(256), 0u, stream, nullptr, taken.stop, 0u,
+                          (const float*)partial, p.ksplit, B, g.N, row_scale, y, kYBF16 ? 1 : 0);
+  else
+    hipLaunchKernelGGL(large_reduce_kernel, rgrid, dim3(256), 0, stream, (const float*)partial,
+                       p.ksplit, B, g.N, row_scale, y, kYBF16 ? 1 : 0);
+  return hipGetLastError();
 }
 
 template <int NTERM, bool kYBF16>
 hipError_t launch_large_y(const uint8_t* packed, const PackedGeom& g, const uint4* zp, int64_t B,
                           const uint4* tail_slots, const float* row_scale, void* y,
-                          const LargePlan& p, hipStream_t stream) {
+                          const LargePlan& p, float* partial, hipStream_t stream) {
   // (fp32 z: at most 2 batch tiles, or the LDS stages would not fit)
 #define LQ_LARGE_CASE(PW_, JB_)                                                                    \
   if constexpr (NTERM * JB_ <= 4 || (NTERM == 1 && JB_ == 8 && PW_ == 4)) {                        \
     if (p.ppw == PW_ && p.jb == JB_)                                                               \
       return launch_large_t<NTERM, PW_, JB_, kYBF16>(packed, g, zp, B, tail_slots, row_scale, y,  \
-                                                     stream);                                      \
+                                                     p, partial, stream);                          \
   }
   LQ_LARGE_CASE(8, 4) LQ_LARGE_CASE(8, 2) LQ_LARGE_CASE(8, 1)
   LQ_LARGE_CASE(4, 8) LQ_LARGE_CASE(4, 4) LQ_LARGE_CASE(4, 2) LQ_LARGE_CASE(4, 1)
@@ -414,6 +484,9 @@ ZpGeom zp_geom(int64_t B, const PackedGeom& g, bool z_bf16) {
 
 LargePlan plan_large(int64_t B, const PackedGeom& g, bool z_bf16) {
   LargePlan p;
+  p.ksplit = 1;
+  p.tps = g.ext_tiles;
+  p.partial_bytes = 0;
   const int64_t B16 = (B + 15) / 16;
   // bf16 z with >= 128 batch rows: 4 panels x 8 batch tiles per wavefront
   // (each sign operand feeds 8 MFMAs), when that still gives >= 512
@@ -431,6 +504,16 @@ LargePlan plan_large(int64_t B, const PackedGeom& g, bool z_bf16) {
   p.ppw = 1;
   for (int c : {8, 4, 2}) {
     if (((g.panels + 4 * c - 1) / (4 * c)) * bt >= 512) { p.ppw = c; break; }
+  }
+  // Still fewer than 512 (two per compute unit fit its LDS at these
+  // tilings): split the reduction into ranges of at least 8 tiles, as many
+  // as keep the workgroups within 512.
+  const int64_t wgs = ((g.panels + 4 * p.ppw - 1) / (4 * p.ppw)) * bt;
+  const int64_t ks = std::min<int64_t>(512 / std::max<int64_t>(wgs, 1), g.ext_tiles / 8);
+  if (ks >= 2) {
+    p.tps = (int)((g.ext_tiles + ks - 1) / ks);
+    p.ksplit = (int)((g.ext_tiles + p.tps - 1) / p.tps);    // no empty range
+    p.partial_bytes = (size_t)p.ksplit * (size_t)B * (size_t)g.N * sizeof(float);
   }
   return p;
 }
@@ -470,7 +553,7 @@ hipError_t launch_tail_slots(const uint8_t* packed, const PackedGeom& g, void* o
 
 hipError_t launch_sign_mfma_large(const uint8_t* packed, const PackedGeom& g, const void* zp,
                                   void* tail_slots, bool z_bf16, int64_t B,
-                                  const float* row_scale, void* y, bool y_bf16,
+                                  const float* row_scale, void* y, bool y_bf16, float* partial,
                                   hipStream_t stream) {
   (void)hipGetLastError();   // clear a stale error of an earlier runtime call
   const LargePlan p = plan_large(B, g, z_bf16);
@@ -481,10 +564,10 @@ hipError_t launch_sign_mfma_large(const uint8_t* packed, const PackedGeom& g, co
     if (e != hipSuccess) return e;
   }
   if (z_bf16)
-    return y_bf16 ? launch_large_y<1, true>(packed, g, z, B, ts, row_scale, y, p, stream)
-                  : launch_large_y<1, false>(packed, g, z, B, ts, row_scale, y, p, stream);
-  return y_bf16 ? launch_large_y<2, true>(packed, g, z, B, ts, row_scale, y, p, stream)
-                : launch_large_y<2, false>(packed, g, z, B, ts, row_scale, y, p, stream);
+    return y_bf16 ? launch_large_y<1, true>(packed, g, z, B, ts, row_scale, y, p, partial, stream)
+                  : launch_large_y<1, false>(packed, g, z, B, ts, row_scale, y, p, partial, stream);
+  return y_bf16 ? launch_large_y<2, true>(packed, g, z, B, ts, row_scale, y, p, partial, stream)
+                : launch_large_y<2, false>(packed, g, z, B, ts, row_scale, y, p, partial, stream);
 }
 
 }  // namespace lq

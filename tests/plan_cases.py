@@ -39,3 +39,19 @@ LARGE_PLAN_CASES = [
 def case_id(c):
     N, L, B, zt, pw, jb = c
     return f"N{N}-L{L}-B{B}-{zt}-pw{pw}-jb{jb}"
+
+
+# Shapes with too few panel and batch groups to fill the chip, on which the
+# plan splits the reduction into ranges of >= 8 tiles (as many as keep the
+# workgroups within 512): (N, L, B, z dtype, panels per wavefront, batch
+# tiles, ranges).
+LARGE_SPLIT_CASES = [
+    (1024, 8200, 64, "bf16", 1, 4, 2),       # 16 workgroups, 17 tiles (ragged)
+    (512, 40000, 48, "bf16", 1, 2, 9),       # 16 workgroups, 79 tiles
+    (256, 20000, 200, "f32", 1, 2, 5),       # 28 workgroups, 40 tiles
+]
+
+
+def split_case_id(c):
+    N, L, B, zt, pw, jb, ks = c
+    return f"N{N}-L{L}-B{B}-{zt}-pw{pw}-jb{jb}-k{ks}"

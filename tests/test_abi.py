@@ -345,7 +345,7 @@ def test_linear_multi_plan_and_validation():
 
 # ------------------------------------------------------------ plan queries
 
-from tests.plan_cases import LARGE_PLAN_CASES, case_id  # noqa: E402
+from tests.plan_cases import LARGE_PLAN_CASES, LARGE_SPLIT_CASES, case_id, split_case_id  # noqa: E402
 
 
 @pytest.mark.parametrize("case", LARGE_PLAN_CASES, ids=[case_id(c) for c in LARGE_PLAN_CASES])
@@ -358,7 +358,31 @@ def test_large_batch_plan_of_each_parity_shape(case):
     assert st == LQ_OK
     assert info.algo == 3 and info.waves == 4
     assert (info.panels // 4, info.batch_rows // 16) == (pw, jb)
+    assert info.ksplit == 1
     assert info.workgroups == -(-N // (16 * 4 * pw)) * -(-(-(-B // 16)) // jb)
+
+
+@pytest.mark.parametrize("case", LARGE_SPLIT_CASES, ids=[split_case_id(c) for c in LARGE_SPLIT_CASES])
+def test_large_batch_plan_splits_the_reduction(case):
+    """Too few panel and batch groups for the chip: reduction ranges of >= 8
+    tiles, as many as keep the workgroups within 512, none empty."""
+    N, L, B, zt, pw, jb, ks = case
+    info = _lib.LQPlanInfo()
+    zdt = LQ_BF16 if zt == "bf16" else LQ_F32
+    assert LIB.lq_sign_gemm_plan(B, N, L, zdt, 3, ctypes.byref(info)) == LQ_OK
+    assert (info.panels // 4, info.batch_rows // 16, info.ksplit) == (pw, jb, ks)
+    groups = -(-N // (16 * 4 * pw)) * -(-(-(-B // 16)) // jb)
+    assert info.workgroups == groups * ks and info.workgroups <= 512
+    ext = -(-L // 512)
+    tps = -(-ext // ks)
+    assert tps >= 8 and (ks - 1) * tps < ext
+    # the workspace holds the operand in product order and the fp32 partial
+    # sums of every range
+    size = ctypes.c_size_t()
+    assert LIB.lq_sign_gemm_workspace_size(B, N, L, zdt, 3, ctypes.byref(size)) == LQ_OK
+    nterm = 1 if zt == "bf16" else 2
+    zp = nterm * -(-B // 16) * 4 * ext * 4096
+    assert size.value >= zp + ks * B * N * 4
 
 
 def test_linear_plan_of_the_benchmarked_layers():

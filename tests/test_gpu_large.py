@@ -21,7 +21,7 @@ import torch
 
 from oracle import liftquant_ref as ref
 from tests.gpu_util import DEV, DeviceLayer, dev, host, note, rel_l2, sign_gemm
-from tests.plan_cases import LARGE_PLAN_CASES, case_id
+from tests.plan_cases import LARGE_PLAN_CASES, LARGE_SPLIT_CASES, case_id, split_case_id
 from workloads import WORKLOADS, bf16_round, make_layer
 
 pytestmark = pytest.mark.gpu
@@ -67,6 +67,34 @@ def test_large_product_every_tiling(lq, case):
         _check(host(y), want, 2e-5, 1e-4)
     else:
         _check(host(y), want, 1e-4, 1e-3)
+
+
+@pytest.mark.parametrize("case", LARGE_SPLIT_CASES, ids=[split_case_id(c) for c in LARGE_SPLIT_CASES])
+def test_large_product_split_reduction(lq, case):
+    """Reduction ranges added by the reduce kernel (fp32 partial sums in the
+    workspace), bf16 and fp32 y, every output against the oracle."""
+    N, L, B, zt, pw, jb, ks = case
+    zd = torch.bfloat16 if zt == "bf16" else torch.float32
+    plan = lq.lq_sign_gemm_plan(B, N, L, zd, LARGE)
+    assert (plan["panels"] // 4, plan["batch_rows"] // 16, plan["ksplit"]) == (pw, jb, ks)
+    rng = np.random.default_rng(N + 5 * L + 11 * B)
+    S = np.where(rng.random((N, L), dtype=np.float32) < 0.5, -1, 1).astype(np.int8)
+    z = rng.standard_normal((B, L)).astype(np.float32)
+    if zd == torch.bfloat16:
+        z = bf16_round(z)
+    r = rng.uniform(0.5, 1.5, N).astype(np.float32)
+    packed = torch.empty(N * L // 8, dtype=torch.uint8, device=DEV)
+    note(f"lq_pack_signs N={N} L={L}")
+    lq.lq_pack_signs(dev(S), N, L, 1, 1, packed)
+    torch.cuda.synchronize()
+    want = ref.sign_matmul(S, z, r)
+    y = sign_gemm(lq, packed, dev(z, zd), B, N, L, dev(r), torch.float32, LARGE)
+    if zd == torch.bfloat16:
+        _check(host(y), want, 2e-5, 1e-4)
+    else:
+        _check(host(y), want, 1e-4, 1e-3)
+    yb = sign_gemm(lq, packed, dev(z, zd), B, N, L, dev(r), torch.bfloat16, LARGE)
+    _check(host(yb).astype(np.float64), want, 1e-2, 2e-2)
 
 
 @pytest.mark.parametrize("B", [2048, 2103])
