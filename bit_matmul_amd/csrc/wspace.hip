@@ -373,14 +373,29 @@ __global__ __launch_bounds__(256) void wspace_kernel(
   // last one, sub-step 0 of the next step, whose stage is complete by then)
   // are read before the MFMAs of this one; the A operands of the next step
   // are packed from its table entries e between the last sub-step's MFMAs.
+  // The table entries of the next step are looked up in DD parts, part f
+  // right after sub-step f's B-operand reads: a wait for those reads then
+  // covers at most one part's lookups issued after them (the LDS counter
+  // counts only 15), not all 8 PW.
   auto mult = [&](const uint4* st, const uint4* st_next, u32x4 (&a)[PW][DD], uint4 (&bcur)[JB],
-                  const uint2 (&e)[PW][8]) __attribute__((always_inline)) {
+                  const uint32_t (&w)[PW][4], int sg_next, uint2 (&e)[PW][8])
+                  __attribute__((always_inline)) {
     uint4 bnext[JB];
 #pragma unroll
     for (int f = 0; f < DD; ++f) {
 #pragma unroll
       for (int c = 0; c < JB; ++c)
         bnext[c] = f < DD - 1 ? st[(c * DD + f + 1) * 64 + lane] : st_next[(c * DD) * 64 + lane];
+      // this part's table entries: entries lam of every panel with
+      // lam * DD / 8 == f
+#pragma unroll
+      for (int i = 0; i < PW; ++i)
+#pragma unroll
+        for (int lam = 0; lam < 8; ++lam)
+          if ((lam * DD) / 8 == f) {
+            const uint32_t word = w[i][sg_next * WPS + lam / BPW];
+            e[i][lam] = lut[(word >> (D * (lam % BPW))) & (kLut - 1)];
+          }
       // Keep those reads here: the scheduler would otherwise sink each one
       // next to its first use.
       __builtin_amdgcn_sched_barrier(0);
@@ -451,16 +466,11 @@ __global__ __launch_bounds__(256) void wspace_kernel(
     __builtin_amdgcn_s_waitcnt(kWait1);
     wg_barrier();
     uint2 e[PW][8];
-    if constexpr (sg + 1 < SPT) {
-      lut_step(w, sg + 1, e);
-    } else {
-      read_words(slot_next, w);
-      lut_step(w, 0, e);
-    }
+    if constexpr (sg + 1 == SPT) read_words(slot_next, w);   // the next tile's words
     if constexpr (sg == 0) copy_slots(min(q + 1, ext_tiles - 1), slot_next);
     copy_step(min(t + 3, last), stage_c(std::integral_constant<int, su + 3>{}));
     mult(stage_c(std::integral_constant<int, su>{}), stage_c(std::integral_constant<int, su + 1>{}),
-         a, bcur, e);
+         a, bcur, w, sg + 1 < SPT ? sg + 1 : 0, e);
   };
   auto tile = [&](auto offc, int q, uint4* slot_next) __attribute__((always_inline)) {
     do_step(std::integral_constant<int, 0>{}, offc, q, slot_next);
