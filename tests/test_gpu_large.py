@@ -114,6 +114,29 @@ def test_large_linear_prefill_layer_every_output(lq, B):
     _check(y, want, 1e-2, 0.1)
 
 
+def test_large_linear_wide_prefill_layer(lq):
+    """The 8192 -> 28672 prefill layer on the lifted product (the tiling of
+    the benchmark's `large` object: 4 panels x 8 batch tiles per wavefront
+    group), every output row for 64 sampled batch rows, both ends included."""
+    wl = WORKLOADS["prefill"]
+    spec = wl.layers[1]                                   # 8192 -> 28672, d = 3, D = 8
+    inp = make_layer(spec, wl, B_max=2048)
+    layer = DeviceLayer(inp, lq)
+    B = 2048
+    x = inp.x(B)
+    plan = lq.lq_linear_plan(layer.struct, B, torch.bfloat16, LARGE)
+    assert (plan["panels"] // 4, plan["batch_rows"] // 16, plan["ksplit"]) == (4, 8, 1)
+    y = host(layer.linear(lq, dev(x, torch.bfloat16), B, torch.bfloat16, algo=LARGE))
+    rng = np.random.default_rng(5)
+    bsel = np.sort(rng.choice(B, 64, replace=False))
+    bsel[0], bsel[-1] = 0, B - 1
+    want = np.empty((len(bsel), spec.N))
+    for r0 in range(0, spec.N, 8192):
+        rows = np.arange(r0, min(spec.N, r0 + 8192))
+        want[:, rows] = ref.linear(x[bsel], inp.c, spec.hb, inp.M, inp.signs_rows(rows), inp.row_scale[rows])
+    _check(y[bsel].astype(np.float64), want, 1e-2, 0.1)
+
+
 def test_large_linear_fp32_activations(lq):
     """lq_linear's default for fp32 activations beyond batch 16: the lifted
     product on a bf16 hi + lo pair of z (two panels per wavefront, two batch
