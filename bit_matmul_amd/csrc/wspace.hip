@@ -292,8 +292,10 @@ __global__ __launch_bounds__(256) void wspace_kernel(
   __shared__ uint4 stage1[kStageUnits];
   __shared__ uint4 stage2[kStageUnits];
   __shared__ uint4 stage3[kStageUnits];
-  __shared__ uint4 slotA[kSlotUnits];
-  __shared__ uint4 slotB[kSlotUnits];
+  // Each wavefront copies and reads only its own part of the slots, and
+  // reads a tile's words (at the tile's last step) before it copies the next
+  // tile's (at the first step of that tile), so one buffer serves.
+  __shared__ uint4 slots[kSlotUnits];
   __shared__ uint2 lut[kLut];
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int64_t steps = SPT * (int64_t)ext_tiles;
@@ -437,7 +439,7 @@ __global__ __launch_bounds__(256) void wspace_kernel(
   constexpr int kWait2 = (7 << 4) | (15 << 8) | ((2 * kCopies) & 15) | (((2 * kCopies) >> 4) << 14);
   static_assert(2 * kCopies <= 63, "vmcnt range");
   static_assert(SPT >= 2, "the next tile's words are read in a tile's second step or later");
-  copy_slots(0, slotA);
+  copy_slots(0, slots);
   copy_step(0, stage0);
   copy_step(min((int64_t)1, last), stage1);
   copy_step(min((int64_t)2, last), stage2);
@@ -455,29 +457,29 @@ __global__ __launch_bounds__(256) void wspace_kernel(
     else if constexpr (i == 2) return stage2;
     else return stage3;
   };
-  // Step sg of tile q, whose first step uses stage `off` (tiles alternate
-  // between the slot buffers and, for D = 8, between stages 0-1 and 2-3).
+  // Step sg of tile q, whose first step uses stage `off` (for D = 8 tiles
+  // alternate between stages 0-1 and 2-3).
   // On entry a holds the step's A operands; the step looks up the next
   // step's table entries (in its last step, from the next tile's words).
-  auto do_step = [&](auto sgc, auto offc, int q, uint4* slot_next) __attribute__((always_inline)) {
+  auto do_step = [&](auto sgc, auto offc, int q) __attribute__((always_inline)) {
     constexpr int sg = decltype(sgc)::value;
     constexpr int su = (decltype(offc)::value + sg) & 3;
     const int64_t t = (int64_t)q * SPT + sg;
     __builtin_amdgcn_s_waitcnt(kWait1);
     wg_barrier();
     uint2 e[PW][8];
-    if constexpr (sg + 1 == SPT) read_words(slot_next, w);   // the next tile's words
-    if constexpr (sg == 0) copy_slots(min(q + 1, ext_tiles - 1), slot_next);
+    if constexpr (sg + 1 == SPT) read_words(slots, w);   // the next tile's words
+    if constexpr (sg == 0) copy_slots(min(q + 1, ext_tiles - 1), slots);
     copy_step(min(t + 3, last), stage_c(std::integral_constant<int, su + 3>{}));
     mult(stage_c(std::integral_constant<int, su>{}), stage_c(std::integral_constant<int, su + 1>{}),
          a, bcur, w, sg + 1 < SPT ? sg + 1 : 0, e);
   };
-  auto tile = [&](auto offc, int q, uint4* slot_next) __attribute__((always_inline)) {
-    do_step(std::integral_constant<int, 0>{}, offc, q, slot_next);
-    do_step(std::integral_constant<int, 1>{}, offc, q, slot_next);
+  auto tile = [&](auto offc, int q) __attribute__((always_inline)) {
+    do_step(std::integral_constant<int, 0>{}, offc, q);
+    do_step(std::integral_constant<int, 1>{}, offc, q);
     if constexpr (SPT > 2) {
-      do_step(std::integral_constant<int, 2>{}, offc, q, slot_next);
-      do_step(std::integral_constant<int, 3>{}, offc, q, slot_next);
+      do_step(std::integral_constant<int, 2>{}, offc, q);
+      do_step(std::integral_constant<int, 3>{}, offc, q);
     }
   };
   // Before the loop: the first tile's words, step 0's A operands and
@@ -487,7 +489,7 @@ __global__ __launch_bounds__(256) void wspace_kernel(
   wg_barrier();
   {
     uint2 e[PW][8];
-    read_words(slotA, w);
+    read_words(slots, w);
     lut_step(w, 0, e);
 #pragma unroll
     for (int i = 0; i < PW; ++i) pack_step<DD>(e[i], a[i]);
@@ -496,10 +498,10 @@ __global__ __launch_bounds__(256) void wspace_kernel(
   for (int c = 0; c < JB; ++c) bcur[c] = stage0[(c * DD) * 64 + lane];
   int q = 0;
   for (; q + 1 < ext_tiles; q += 2) {
-    tile(std::integral_constant<int, 0>{}, q, slotB);
-    tile(std::integral_constant<int, SPT & 3>{}, q + 1, slotA);
+    tile(std::integral_constant<int, 0>{}, q);
+    tile(std::integral_constant<int, SPT & 3>{}, q + 1);
   }
-  if (q < ext_tiles) tile(std::integral_constant<int, 0>{}, q, slotB);
+  if (q < ext_tiles) tile(std::integral_constant<int, 0>{}, q);
 
   // No copy may still be writing LDS when the workgroup ends.
   __builtin_amdgcn_s_waitcnt(0);
