@@ -402,6 +402,9 @@ def test_linear_plan_of_the_benchmarked_layers():
                     want = 1 if xt == LQ_F32 else 2
                 assert info.algo == want, (wl.name, s.name, B)
                 assert info.workgroups > 0 and info.waves > 0 and info.panels > 0
+                if want == 6 and B >= 2048:
+                    # 4 panels per wavefront, 8 batch tiles per workgroup
+                    assert (info.panels, info.batch_rows) == (16, 128), (s.name, B)
     assert LIB.lq_linear_plan(None, 1, LQ_BF16, 0, ctypes.byref(info)) == LQ_ERR_INVALID_ARG
     lay = LQLayer(16, 64, 2, 8, 64, 0, P, P, P, P)
     assert LIB.lq_linear_plan(ctypes.byref(lay), 0, LQ_BF16, 0, ctypes.byref(info)) == LQ_ERR_INVALID_ARG

@@ -2,8 +2,8 @@
 
 * Every layer of every workload at its full size and each of its batch
   sizes, in the launch configuration the benchmark times (lq_linear's own
-  dispatch): sampled output rows, recomputed by the oracle one by one; at
-  batch 1 every output row (the oracle run over chunks of rows), also for
+  dispatch): every output row at every batch size (the oracle run over
+  chunks of rows), and sampled rows with bf16 outputs too; at batch 1 also
   the Llama-3-70B gate and up layers through one lq_linear_multi call as the
   benchmark's decode step runs them. Besides rel-L2, every element must be
   within 10 x the tolerance of the output's RMS (a fault confined to a few
@@ -95,17 +95,21 @@ def _check_all(got, want, tol):
 
 
 @pytest.mark.parametrize("wl_name,li", FULL, ids=[f"{w}-{WORKLOADS[w].layers[i].name}" for w, i in FULL])
-def test_full_size_every_row_batch1(lq, wl_name, li):
+def test_full_size_every_row(lq, wl_name, li):
+    """Every output row at every batch size of the workload (the oracle run
+    once on the largest batch; a smaller batch is its leading rows)."""
     wl = WORKLOADS[wl_name]
     spec = wl.layers[li]
-    inp = make_layer(spec, wl, B_max=1)
+    inp = make_layer(spec, wl)
     layer = DeviceLayer(inp, lq)
     xd = _xdtype(wl)
-    x = inp.x(1)
-    y = host(layer.linear(lq, dev(x, xd), 1, torch.float32))
-    err = _check_all(y, _rows_oracle(inp, spec, x), TOL[xd])
-    if xd == torch.bfloat16:
-        assert err < 3e-3            # two FP6 terms per lifted value: ~8e-4 observed
+    x = inp.x(max(wl.batches))
+    want = _rows_oracle(inp, spec, x)
+    for B in wl.batches:
+        y = host(layer.linear(lq, dev(x[:B], xd), B, torch.float32))
+        err = _check_all(y, want[:B], TOL[xd])
+        if xd == torch.bfloat16 and B <= 16:
+            assert err < 3e-3, (B, err)   # two FP6 terms per lifted value: ~8e-4 observed
 
 
 def test_full_size_every_row_70b_gate_up_grouped(lq):

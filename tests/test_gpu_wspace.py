@@ -9,7 +9,9 @@ takes).
 * The prefill layers at their full size and batch (2048 rows), in the launch
   configuration the benchmark times: sampled output rows and batch rows,
   recomputed by the oracle one by one; and the whole output against the
-  lifted large-batch product (both bf16-operand paths).
+  lifted large-batch product (both bf16-operand paths). (lq_linear's own
+  dispatch takes this product for these layers; tests/test_gpu_linear.py
+  compares its every output with the oracle's.)
 * Small shapes spanning several tiles with a ragged tail: every batch size
   1..17 and 33, d = 1..4, D = 4 and 8, K not a multiple of d, hb = 1,
   bf16 and fp32 outputs, a single panel, many panels.
