@@ -240,19 +240,34 @@ __global__ __launch_bounds__(64 * W) void sign_fp6_kernel(SignTable tab, int rec
     }
     tile_mfma(kStream ? wrec : rec_lds + nfull * rec, TS);
   }
-  for (int j0 = 0; j0 < nk; j0 += DEPTH) {
+  // While a later block of tiles follows, each tile's slots are replaced by
+  // those DEPTH tiles on; the last block requests nothing, so that no load
+  // is issued after the wavefront's last MFMAs (a request there would be
+  // waited for, a whole memory round trip, before the epilogue).
+  int j0 = 0;
+  for (; j0 + DEPTH < nk; j0 += DEPTH) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       const int j = j0 + d;
-      if (j < nk) {
-        if (kStream) *reinterpret_cast<v4u*>(wrec + 16 * lane) = R[d];
-        tile_mfma(kStream ? wrec : rec_lds + (wave + j * W) * rec, A[d]);
-      }
+      if (kStream) *reinterpret_cast<v4u*>(wrec + 16 * lane) = R[d];
+      tile_mfma(kStream ? wrec : rec_lds + (wave + j * W) * rec, A[d]);
+      // the tile's MFMAs read A[d] before the next request overwrites it
+      __builtin_amdgcn_sched_barrier(0);
       issue(j + DEPTH, A[d], R[d]);
     }
   }
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) {
+    const int j = j0 + d;
+    if (j < nk) {
+      if (kStream) *reinterpret_cast<v4u*>(wrec + 16 * lane) = R[d];
+      tile_mfma(kStream ? wrec : rec_lds + (wave + j * W) * rec, A[d]);
+    }
+    // one tile's operands live at a time, as in the loop
+    __builtin_amdgcn_sched_barrier(0);
+  }
   if (kStream && wave == 0) *reinterpret_cast<v4u*>(smem + 16 * lane) = rsv;   // rs_lds
-  __builtin_amdgcn_s_waitcnt(0);                     // the unused trailing loads
+  __builtin_amdgcn_s_waitcnt(0);                     // loads of tiles past the last, unused
   wg_barrier();                                      // records are no longer read
 
   // ---- 4. add the wavefronts' accumulators in a fixed order. Compact
@@ -313,12 +328,9 @@ constexpr int kRecLdsMax = 128 * 1024;             // LDS for the records of a r
 
 // Wavefronts per workgroup, and the slot tiles each keeps requested (P
 // 16-byte loads per tile). Eight wavefronts (two per SIMD, 256 registers
-// each) while the slot, accumulator and operand registers fit 256: up to 12
-// panels of one 16-column set (10 with streamed records, which hold DEPTH
-// more quads), 6 of two; four (one per SIMD, 512) beyond.
-constexpr int waves_for(int p, int cs, bool stream) {
-  return (cs == 1 ? p >= (stream ? 12 : 14) : p >= 8) ? 4 : 8;
-}
+// each) while the slot, accumulator and operand registers fit 256: up to 11
+// panels of one 16-column set, 7 of two; four (one per SIMD, 512) beyond.
+constexpr int waves_for(int p, int cs, bool) { return (cs == 1 ? p >= 12 : p >= 8) ? 4 : 8; }
 // Two tiles of slots in flight per wavefront at every width: on the 70B
 // batch-1 step (one box, interleaved runs) 65.3 µs per step against 67.1
 // with three and 67.7 with two to four chosen by width.
