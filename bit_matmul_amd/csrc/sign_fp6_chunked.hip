@@ -16,6 +16,7 @@
 // accumulators are added in LDS in a fixed order, the terms and plane sums
 // combined, and y written: deterministic, no atomics.
 #include <algorithm>
+#include <type_traits>
 
 #include "lq_fp6_mma.h"
 
@@ -220,8 +221,11 @@ __global__ __launch_bounds__(64 * (W + 1)) void sign_fp6_chunked_kernel(SignTabl
     issue_A(0, A0);
     issue_A(1, A1);
     wg_barrier();
-    // Step c: chunk c is in LDS (`cur`), its slots (A) are requested.
-    auto step = [&](int c, uint4 (&A)[TPC][P], uint8_t* cur) {
+    // Step c: chunk c is in LDS (`cur`), its slots (A) are requested; the
+    // slots of chunk c + 2 are requested after its MFMAs unless it is one
+    // of the last two steps (a request there would be waited for, a whole
+    // memory round trip, before the epilogue).
+    auto step = [&](int c, uint4 (&A)[TPC][P], uint8_t* cur, auto more) {
 #pragma unroll
       for (int q = 0; q < TPC; ++q) {
         const int j = wave * TPC + q;                 // tile within the chunk
@@ -229,13 +233,18 @@ __global__ __launch_bounds__(64 * (W + 1)) void sign_fp6_chunked_kernel(SignTabl
       }
       wg_barrier();                                   // `cur` and A are free
       wg_barrier();                                   // chunk c + 2 requested
-      issue_A(c + 2, A);
+      if constexpr (decltype(more)::value) issue_A(c + 2, A);
     };
     // Unrolled by two for the two register sets; an odd chunk count ends
-    // with one empty step (no tiles).
-    for (int c = 0; c < nch; c += 2) {
-      step(c, A0, buf0);
-      step(c + 1, A1, buf1);
+    // with one empty step (no tiles). As many steps as the loader's loop.
+    int c = 0;
+    for (; c + 2 < nch; c += 2) {
+      step(c, A0, buf0, std::true_type{});
+      step(c + 1, A1, buf1, std::true_type{});
+    }
+    if (c < nch) {
+      step(c, A0, buf0, std::false_type{});
+      step(c + 1, A1, buf1, std::false_type{});
     }
   }
   wg_barrier();                                      // LDS past the row scales is reused below
