@@ -119,7 +119,8 @@ __global__ __launch_bounds__(64 * W) void sign_fp6_kernel(SignTable tab, int rec
   v4u tr_rec = {0u, 0u, 0u, 0u}, tr_raw[P];         // streamed: the tail tile's record and bytes
   if (!kStream) {
     // ---- 1. the activation records, the row scales and the tail tile's
-    // packed bytes into LDS, all landed before any weight is requested
+    // packed bytes into LDS, requested before any weight (a compute unit
+    // returns vector-memory requests about in order, so they land first)
     const uint8_t* src = aop + 16 * lane;
     const int bytes = ext_tiles * rec;
     for (int off = wave * 1024; off < bytes; off += W * 1024) lds_dma16(src + off, rec_lds + off);
@@ -132,8 +133,6 @@ __global__ __launch_bounds__(64 * W) void sign_fp6_kernel(SignTable tab, int rec
       for (int p = 0; p < P; ++p)
         lds_dma16(prow[p] + (int64_t)full_tiles * kTileBytes + tail_o, tslot_lds + 1024 * p);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    wg_barrier();
   } else {
     // ---- 1'. requested ahead of the weights, into registers: the row
     // scales (used after the loop) and the tail tile's record and bytes
@@ -169,8 +168,18 @@ __global__ __launch_bounds__(64 * W) void sign_fp6_kernel(SignTable tab, int rec
     // operand's slack)
     if (kStream) Rj = *reinterpret_cast<const v4u*>(aop + (int64_t)tile * rec + 16 * lane);
   };
+  // the copies above stay ahead of these requests
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) issue(d, A[d], R[d]);
+  if (!kStream) {
+    // The copies have landed once no more than the DEPTH tiles' P loads
+    // each are outstanding; those stay in flight across the barrier.
+    constexpr int n = DEPTH * P;
+    static_assert(n <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8) | (n & 15) | ((n >> 4) << 14));
+    wg_barrier();
+  }
 
   f32x4 acc[P][CS];
 #pragma unroll
@@ -244,17 +253,28 @@ __global__ __launch_bounds__(64 * W) void sign_fp6_kernel(SignTable tab, int rec
   // those DEPTH tiles on; the last block requests nothing, so that no load
   // is issued after the wavefront's last MFMAs (a request there would be
   // waited for, a whole memory round trip, before the epilogue).
-  int j0 = 0;
-  for (; j0 + DEPTH < nk; j0 += DEPTH) {
+  auto block = [&](int j0) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       const int j = j0 + d;
       if (kStream) *reinterpret_cast<v4u*>(wrec + 16 * lane) = R[d];
       tile_mfma(kStream ? wrec : rec_lds + (wave + j * W) * rec, A[d]);
-      // the tile's MFMAs read A[d] before the next request overwrites it
+      // the tile's MFMAs read A[d] before the next request overwrites it,
+      // and the request goes out before the next tile's work (the scheduler
+      // would otherwise hold it back to spare registers)
       __builtin_amdgcn_sched_barrier(0);
       issue(j + DEPTH, A[d], R[d]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  int j0 = 0;
+  if (DEPTH < nk) {
+    // The first block apart from the loop: the compiler cannot tell that the
+    // LDS copies have landed, and waits for every load once, here, before
+    // the first record read; the loop, entered only after it, keeps exact
+    // waits.
+    block(0);
+    for (j0 = DEPTH; j0 + DEPTH < nk; j0 += DEPTH) block(j0);
   }
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) {
