@@ -382,8 +382,13 @@ hipError_t launch_encode(const float* w, int64_t nblocks, int d, int D, const fl
   (void)hipGetLastError();   // clear a stale error of an earlier runtime call
   if (d < 1 || d > D || D > kEncodeMaxD || d > kEncodeMaxSmallD) return hipErrorInvalidValue;
   if (nblocks == 0) return hipSuccess;
+  // d in registers, padded with zeros to the next width instantiated (the
+  // pages' configurations, d = 2, 3, 10 and 16, run unpadded)
+  if (d <= 2) return launch_encode_t<2>(w, nblocks, d, D, M, signs, dist2, stream);
+  if (d <= 3) return launch_encode_t<3>(w, nblocks, d, D, M, signs, dist2, stream);
   if (d <= 4) return launch_encode_t<4>(w, nblocks, d, D, M, signs, dist2, stream);
   if (d <= 8) return launch_encode_t<8>(w, nblocks, d, D, M, signs, dist2, stream);
+  if (d <= 10) return launch_encode_t<10>(w, nblocks, d, D, M, signs, dist2, stream);
   if (d <= 12) return launch_encode_t<12>(w, nblocks, d, D, M, signs, dist2, stream);
   return launch_encode_t<16>(w, nblocks, d, D, M, signs, dist2, stream);
 }
@@ -394,8 +399,11 @@ hipError_t launch_encode_pinv(const float* w, int64_t nblocks, int d, int D, con
   if (d < 1 || d > D || D > kEncodePinvMaxD || D - d > kEncodePinvMaxFree || d > kEncodeMaxSmallD)
     return hipErrorInvalidValue;
   if (nblocks == 0) return hipSuccess;
+  if (d <= 2) return launch_encode_pinv_t<2>(w, nblocks, d, D, M, AB, signs, dist2, stream);
+  if (d <= 3) return launch_encode_pinv_t<3>(w, nblocks, d, D, M, AB, signs, dist2, stream);
   if (d <= 4) return launch_encode_pinv_t<4>(w, nblocks, d, D, M, AB, signs, dist2, stream);
   if (d <= 8) return launch_encode_pinv_t<8>(w, nblocks, d, D, M, AB, signs, dist2, stream);
+  if (d <= 10) return launch_encode_pinv_t<10>(w, nblocks, d, D, M, AB, signs, dist2, stream);
   if (d <= 12) return launch_encode_pinv_t<12>(w, nblocks, d, D, M, AB, signs, dist2, stream);
   return launch_encode_pinv_t<16>(w, nblocks, d, D, M, AB, signs, dist2, stream);
 }
