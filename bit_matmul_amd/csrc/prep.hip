@@ -73,23 +73,46 @@ __device__ __forceinline__ uint32_t e2m3_round(float a, float& rep) {
   return (a < 0.0f ? 32u : 0u) | mag;
 }
 
+// The lift of one column from M's entries in registers: z = sum over
+// i < min(d, K - kb) of (M[i][e] / sqrt(hb)) * xs[kb + i - h_lo], kb = blk d,
+// added in order of i (mr[i] holds M[i][e] / sqrt(hb), d <= 16); the LDS
+// reads are issued before any is used.
+__device__ __forceinline__ float lift_regs(const float (&mr)[16], const float* xs, int blk, int d,
+                                           int K, int h_lo) {
+  const int kb = blk * d;
+  const int nk = min(d, K - kb);
+  float xv[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) xv[u] = u < nk ? xs[kb + u - h_lo] : 0.0f;
+  float acc = 0.0f;
+#pragma unroll
+  for (int u = 0; u < 16; ++u)
+    if (u < nk) acc = fmaf(mr[u], xv[u], acc);
+  return acc;
+}
+
 // kMode 0: write fp32 z. kMode 1: write the FP6 operand.
 // kXKind 0: x fp32, 1: x bf16, 2: input is already-lifted z in fp32,
 // 3: already-lifted z in bf16 (whitening and lift skipped).
+// kFast (every layer with hb = 1024 and d <= 16, the LLM rates): the
+// transform's size is fixed at compile time, and each thread loads the d
+// entries of M its column needs into registers with the other loads, so the
+// lift reads only the transformed values from LDS; otherwise M is staged in
+// LDS for any d <= 64.
 // Index arithmetic is 32-bit (K, L < 2^31 is checked on the host).
-template <int kMode, int kXKind>
+template <int kMode, int kXKind, bool kFast>
 __global__ __launch_bounds__(kThreads) void prep_kernel(
     const void* __restrict__ x, int B, int K, PrepTable tab,
     float* __restrict__ zf32,                      // kMode 0: B x L
     int nt, int ncv, int rec, unsigned* __restrict__ tickets, int n_tickets) {
   __shared__ __align__(16) float xs[kSpanMax];
-  __shared__ float Ms[64 * 64];
+  __shared__ float Ms[kFast ? 1 : 64 * 64];
   __shared__ __align__(16) uint8_t codes[4][kTileCols];   // [term][block * 32 + code index]
   __shared__ float tp_wave[kThreads / 64];
   // grid: (tile q, layer, batch row b); layers with fewer tiles than the
   // grid's x dimension leave the rest idle
   const PrepLayer& ly = tab.l[blockIdx.y];
-  const int d = ly.d, D = ly.D, lhb = ly.lhb, L = ly.L, tiles = ly.tiles;
+  const int d = ly.d, D = ly.D, lhb = kFast ? 10 : ly.lhb, L = ly.L, tiles = ly.tiles;
   const float norm = ly.norm;
   const float* __restrict__ cvec = ly.c;
   const float* __restrict__ M = ly.M;
@@ -126,22 +149,46 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
       else xb[j] = reinterpret_cast<const uint32_t*>(x)[xrow + k];
       cv[j] = cvec[k];
     }
-    const int dD = d * D;
+    // kFast: this thread's column c_lo + jj is element e of d-block blk
+    // (c_lo / D once, then a quotient below 576 in fp32, corrected to exact)
+    float mr[16];
+    int blk = 0;
+    if constexpr (kFast) {
+      const int cq = c_lo / D, r0 = c_lo - cq * D;
+      const int tt = r0 + jj;
+      int bq = (int)((float)tt * (1.0f / (float)D));
+      bq += (bq + 1) * D <= tt ? 1 : 0;
+      bq -= bq * D > tt ? 1 : 0;
+      blk = cq + bq;
+      const int e = tt - bq * D;
 #pragma unroll
-    for (int j = 0; j < 4096 / kThreads; ++j) {
-      const int i = tid + kThreads * j;
-      mv[j] = M[i < dD ? i : 0];                   // entries past d*D: stored, never read
+      for (int i = 0; i < 16; ++i) mr[i] = M[min(i, d - 1) * D + e];   // rows past d: never used
+    } else {
+      const int dD = d * D;
+#pragma unroll
+      for (int j = 0; j < 4096 / kThreads; ++j) {
+        const int i = tid + kThreads * j;
+        mv[j] = M[i < dD ? i : 0];                 // entries past d*D: stored, never read
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kFast) {
 #pragma unroll
-    for (int j = 0; j < 4096 / kThreads; ++j) Ms[tid + kThreads * j] = mv[j] * norm;   // 1/sqrt(hb) folded in
+      for (int i = 0; i < 16; ++i) mr[i] *= norm;   // 1/sqrt(hb) folded in
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4096 / kThreads; ++j) Ms[tid + kThreads * j] = mv[j] * norm;
+    }
     float v[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) v[j] = (kXKind == 1 ? bf16_bits_to_f32(xb[j]) : __uint_as_float(xb[j])) * cv[j];
     // Hadamard transform of each hb-block (in groups of 1024; ends with a
     // workgroup barrier, so Ms is complete too)
     block_fwht_1024_regs(xs + 1024 * gi, v, lhb, t);
-    if (jj < width) z = lift_column(Ms, xs, c_lo + jj, d, D, K, ts.h_lo);
+    if (jj < width) {
+      if constexpr (kFast) z = lift_regs(mr, xs, blk, d, K, ts.h_lo);
+      else z = lift_column(Ms, xs, c_lo + jj, d, D, K, ts.h_lo);
+    }
   } else {
     const int64_t zi = (int64_t)b * L + c_lo + (jj < width ? jj : 0);
     float tz;
@@ -225,9 +272,15 @@ hipError_t launch_prep_t(const void* x, int64_t B, int64_t K, const PrepTable& t
                          float* zf32, const OperandShape* s, unsigned* tickets, int n_tickets,
                          hipStream_t stream) {
   const int nt = s ? s->nt : 0, ncv = s ? s->ncv : 0, rec = s ? s->rec : 0;
-  hipLaunchKernelGGL((prep_kernel<kMode, kXKind>), dim3((unsigned)tiles, (unsigned)tab.n, (unsigned)B),
-                     dim3(kThreads), 0, stream, x, (int)B, (int)K, tab, zf32, nt, ncv, rec, tickets,
-                     n_tickets);
+  bool fast = kXKind <= 1;
+  for (int i = 0; i < tab.n; ++i) fast = fast && tab.l[i].lhb == 10 && tab.l[i].d <= 16;
+  const dim3 grid((unsigned)tiles, (unsigned)tab.n, (unsigned)B);
+  if (fast)
+    hipLaunchKernelGGL((prep_kernel<kMode, kXKind, true>), grid, dim3(kThreads), 0, stream, x,
+                       (int)B, (int)K, tab, zf32, nt, ncv, rec, tickets, n_tickets);
+  else
+    hipLaunchKernelGGL((prep_kernel<kMode, kXKind, false>), grid, dim3(kThreads), 0, stream, x,
+                       (int)B, (int)K, tab, zf32, nt, ncv, rec, tickets, n_tickets);
   return hipGetLastError();
 }
 
