@@ -161,8 +161,10 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
       bq -= bq * D > tt ? 1 : 0;
       blk = cq + bq;
       const int e = tt - bq * D;
+      // (column e's address once, then a uniform row offset per entry)
+      const float* __restrict__ Me = M + e;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mr[i] = M[min(i, d - 1) * D + e];   // rows past d: never used
+      for (int i = 0; i < 16; ++i) mr[i] = Me[min(i, d - 1) * D];   // rows past d: never used
     } else {
       const int dD = d * D;
 #pragma unroll
