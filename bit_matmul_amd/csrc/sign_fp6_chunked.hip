@@ -25,8 +25,13 @@ namespace {
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
+// Loader wavefronts: each copies every kLoaders-th kilobyte of a chunk, so
+// that a chunk's copies are spread over that many request queues (one
+// wavefront, with one chunk in flight, filled records at ~40 GB/s).
+constexpr int kLoaders = 2;
+
 template <int P, int CS, int W, int TPC>
-__global__ __launch_bounds__(64 * (W + 1)) void sign_fp6_chunked_kernel(SignTable tab, int rec, int ncv,
+__global__ __launch_bounds__(64 * (W + kLoaders)) void sign_fp6_chunked_kernel(SignTable tab, int rec, int ncv,
                                                                 int B, int chunk_bytes, int y_bf16) {
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr int CT = W * TPC;                       // full tiles per chunk
@@ -45,7 +50,8 @@ __global__ __launch_bounds__(64 * (W + 1)) void sign_fp6_chunked_kernel(SignTabl
   const int nch = ly.nch, N = ly.N;
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int g = lane >> 4, r = lane & 15;
-  const bool loader = wave == W;
+  const bool loader = wave >= W;
+  const int lw = wave - W;                          // loader index (when loader)
   const int pbase = ((int)blockIdx.x - ly.group_begin) * P;
 
   // This lane's MFMA column in each column set; unused columns read the
@@ -128,7 +134,7 @@ __global__ __launch_bounds__(64 * (W + 1)) void sign_fp6_chunked_kernel(SignTabl
     const int t0 = c * CT;
     const int bytes = min(CT, full_tiles - t0) * rec;
     const uint8_t* src = aop + (int64_t)t0 * rec + 16 * lane;
-    for (int off = 0; off < bytes; off += 1024)
+    for (int off = lw * 1024; off < bytes; off += kLoaders * 1024)
       __builtin_amdgcn_global_load_lds((const void*)(src + off),
                                        (__attribute__((address_space(3))) void*)(dst + off), 16, 0, 0);
   };
@@ -159,13 +165,16 @@ __global__ __launch_bounds__(64 * (W + 1)) void sign_fp6_chunked_kernel(SignTabl
   uint8_t* tslot_lds = trec_lds + ((rec + 1023) / 1024) * 1024;
 
   if (loader) {
-    // Row scales of the workgroup's rows (16 bytes per lane, clamped to N).
-    const int n4 = min(pbase * kPanelRows + 4 * lane, N - 4);
-    __builtin_amdgcn_global_load_lds((const void*)(row_scale + n4),
-                                     (__attribute__((address_space(3))) void*)rs_lds, 16, 0, 0);
+    // Row scales of the workgroup's rows (16 bytes per lane, clamped to N),
+    // by the first loader, as are the tail tile's copies and MFMAs.
+    if (lw == 0) {
+      const int n4 = min(pbase * kPanelRows + 4 * lane, N - 4);
+      __builtin_amdgcn_global_load_lds((const void*)(row_scale + n4),
+                                       (__attribute__((address_space(3))) void*)rs_lds, 16, 0, 0);
+    }
     if (nch > 0) dma_chunk(0, buf0);
     if (nch > 1) dma_chunk(1, buf1);
-    if (tail) {
+    if (tail && lw == 0) {
       const uint8_t* trec = aop + (int64_t)full_tiles * rec + 16 * lane;
       for (int off = 0; off < rec; off += 1024)
         __builtin_amdgcn_global_load_lds((const void*)(trec + off),
@@ -183,7 +192,7 @@ __global__ __launch_bounds__(64 * (W + 1)) void sign_fp6_chunked_kernel(SignTabl
     // The tail tile while the compute wavefronts multiply the first chunk
     // (its record and slots landed with chunk 0): at the end it would delay
     // the final reduction.
-    if (tail) {
+    if (tail && lw == 0) {
       // Slot (g, r) of the tail: bytes 16u + 4g .. + 3 of row r (zero past
       // the row's tail_bytes), as in load_tail_slot.
       uint4 TS[P];
@@ -253,18 +262,21 @@ __global__ __launch_bounds__(64 * (W + 1)) void sign_fp6_chunked_kernel(SignTabl
   uint8_t* red_base = buf0;
   f32x4* red = reinterpret_cast<f32x4*>(red_base);                   // [W+1][P][CS][64]
   float* tred = reinterpret_cast<float*>(red_base + (W + 1) * P * CS * 64 * 16);   // [W+1][16]
+  // the compute wavefronts and the first loader (the others hold no products)
+  if (wave <= W) {
 #pragma unroll
-  for (int p = 0; p < P; ++p)
+    for (int p = 0; p < P; ++p)
 #pragma unroll
-    for (int cs = 0; cs < CS; ++cs) red[((wave * P + p) * CS + cs) * 64 + lane] = acc[p][cs];
-  if (lane < 16) tred[wave * 16 + lane] = tacc;
+      for (int cs = 0; cs < CS; ++cs) red[((wave * P + p) * CS + cs) * 64 + lane] = acc[p][cs];
+    if (lane < 16) tred[wave * 16 + lane] = tacc;
+  }
   wg_barrier();
 
   // One output (panel p, row, batch row b) per thread and pass: every LDS
   // read is issued before the sums (fixed order: terms, then wavefronts).
   const int nt = ncv / B;                           // 1..4
   const int items = P * B * 16;
-  for (int item = threadIdx.x; item < items; item += 64 * (W + 1)) {
+  for (int item = threadIdx.x; item < items; item += 64 * (W + kLoaders)) {
     const int row = item & 15;
     const int b = (item >> 4) % B;
     const int p = (item >> 4) / B;
@@ -305,7 +317,7 @@ template <int P, int CS, int W, int TPC>
 hipError_t launch_chunked_t(const SignTable& tab, int groups, const OperandShape& s, int64_t B,
                             bool y_bf16, const Fp6Plan& plan, hipStream_t stream) {
   const dim3 grid((unsigned)groups);
-  const dim3 block(64 * (W + 1));
+  const dim3 block(64 * (W + kLoaders));
   if (plan.lds_bytes > 160 * 1024) return hipErrorInvalidValue;   // a compute unit's LDS
   // Dynamic LDS beyond the default 64 KB limit has to be allowed per kernel.
   static size_t allowed = 0;
@@ -324,8 +336,9 @@ hipError_t launch_chunked_t(const SignTable& tab, int groups, const OperandShape
 
 // Compute wavefronts and tiles per wavefront per chunk for each column-set
 // count: wider operands take fewer tiles per chunk so that two chunks of
-// activation records fit in LDS. (Registers: with W + 1 wavefronts a SIMD
-// runs up to ceil((W + 1) / 4) of them, each with 512 / that many VGPRs.)
+// activation records fit in LDS. (Registers: with W + 2 wavefronts a SIMD
+// runs up to ceil((W + 2) / 4) of them, each with 512 / that many VGPRs:
+// for W = 2, 4, 8 as many as with one loader.)
 int chunked_waves(int p, int cs) { return cs == 1 ? (p >= 4 ? 4 : 8) : (cs == 2 && p < 8 ? 4 : 2); }
 int chunked_tiles(int p, int cs) { return cs == 1 && p <= 4 ? 3 : 1; }
 
