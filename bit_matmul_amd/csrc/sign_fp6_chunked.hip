@@ -26,9 +26,10 @@ namespace {
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 // Loader wavefronts: each copies every kLoaders-th kilobyte of a chunk, so
-// that a chunk's copies are spread over that many request queues (one
-// wavefront, with one chunk in flight, filled records at ~40 GB/s).
-constexpr int kLoaders = 2;
+// that a chunk is requested by that many wavefronts at once. Measured on the
+// 70B down projection at B = 16: one loader 42.8 us, two 40.8, four 34.5,
+// eight 34.4 (and register spills where the compute wavefronts need many).
+constexpr int kLoaders = 4;
 
 template <int P, int CS, int W, int TPC>
 __global__ __launch_bounds__(64 * (W + kLoaders)) void sign_fp6_chunked_kernel(SignTable tab, int rec, int ncv,
@@ -336,9 +337,8 @@ hipError_t launch_chunked_t(const SignTable& tab, int groups, const OperandShape
 
 // Compute wavefronts and tiles per wavefront per chunk for each column-set
 // count: wider operands take fewer tiles per chunk so that two chunks of
-// activation records fit in LDS. (Registers: with W + 2 wavefronts a SIMD
-// runs up to ceil((W + 2) / 4) of them, each with 512 / that many VGPRs:
-// for W = 2, 4, 8 as many as with one loader.)
+// activation records fit in LDS. (Registers: with W + 4 wavefronts a SIMD
+// runs up to ceil((W + 4) / 4) of them, each with 512 / that many VGPRs.)
 int chunked_waves(int p, int cs) { return cs == 1 ? (p >= 4 ? 4 : 8) : (cs == 2 && p < 8 ? 4 : 2); }
 int chunked_tiles(int p, int cs) { return cs == 1 && p <= 4 ? 3 : 1; }
 
