@@ -39,7 +39,11 @@ __device__ __forceinline__ void stage_m2(double* m2, const float* __restrict__ M
 }
 
 // The search over patterns p = prefix | q, q < 2^nfree, for one block.
-// Returns the best (distance, index) of this lane.
+// Returns the best (distance, index) of this lane. Pattern k of the walk is
+// prefix | gray(k); step k flips bit ctz(k). Seven steps in eight flip bit
+// 0, 1 or 2, whose columns are held in registers; the walk is unrolled by
+// eight so those steps need no bit scan and no LDS read (the visiting order
+// and the arithmetic of every step are those of the plain loop).
 template <int DM>
 __device__ __forceinline__ void walk(const double* m2, const double (&wv)[DM], int D,
                                      uint32_t prefix, int nfree, double& best, uint32_t& bidx) {
@@ -61,25 +65,54 @@ __device__ __forceinline__ void walk(const double* m2, const double (&wv)[DM], i
   best = d0 + d1;
   bidx = prefix;
   uint32_t pat = prefix;
-  const uint32_t count = 1u << nfree;
-  for (uint32_t k = 1; k < count; ++k) {
-    const int e = __builtin_ctz(k);
+  // One step: flip bit e (column col), update r and the distance, keep the
+  // least (distance, pattern) — branch-free.
+  auto step = [&](const auto& col, int e) __attribute__((always_inline)) {
     pat ^= 1u << e;
     // s_e became -1: M s lost 2 M[:, e], r gains it; became +1: r loses it
     const double sg = ((pat >> e) & 1) ? 1.0 : -1.0;
-    const double* col = m2 + e * DM;
     // two partial sums: half the dependent chain
-    double d0 = 0.0, d1 = 0.0;
+    double s0 = 0.0, s1 = 0.0;
 #pragma unroll
     for (int i = 0; i < DM; ++i) {
       r[i] = fma(sg, col[i], r[i]);
-      if (i & 1) d1 = fma(r[i], r[i], d1);
-      else d0 = fma(r[i], r[i], d0);
+      if (i & 1) s1 = fma(r[i], r[i], s1);
+      else s0 = fma(r[i], r[i], s0);
     }
-    const double dd = d0 + d1;
-    if (dd < best || (dd == best && pat < bidx)) {
-      best = dd;
-      bidx = pat;
+    const double dd = s0 + s1;
+    const bool take = (dd < best) | ((dd == best) & (pat < bidx));   // no short circuit: no branch
+    best = take ? dd : best;
+    bidx = take ? pat : bidx;
+  };
+  const uint32_t count = 1u << nfree;
+  if (nfree < 3) {
+    for (uint32_t k = 1; k < count; ++k) {
+      const int e = __builtin_ctz(k);
+      step(m2 + e * DM, e);
+    }
+    return;
+  }
+  double c0[DM], c1[DM], c2[DM];
+#pragma unroll
+  for (int i = 0; i < DM; ++i) {
+    c0[i] = m2[i];
+    c1[i] = m2[DM + i];
+    c2[i] = m2[2 * DM + i];
+  }
+  for (uint32_t k0 = 0; k0 < count; k0 += 8) {
+    // steps k0 + 1 .. k0 + 7 flip bits 0 1 0 2 0 1 0
+    step(c0, 0);
+    step(c1, 1);
+    step(c0, 0);
+    step(c2, 2);
+    step(c0, 0);
+    step(c1, 1);
+    step(c0, 0);
+    // step k0 + 8 flips bit ctz(k0 + 8) >= 3 (none after the last pattern)
+    const uint32_t k = k0 + 8;
+    if (k < count) {
+      const int e = __builtin_ctz(k);
+      step(m2 + e * DM, e);
     }
   }
 }
