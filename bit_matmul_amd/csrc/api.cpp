@@ -355,7 +355,7 @@ void fill_plan_info(const Exec& e, int64_t B, lq_plan_info* info) {
       p.workgroups = (int32_t)(((panels + 3) / 4) * e.vp.ksplit * ((B + e.vp.bt - 1) / e.vp.bt));
       break;
     case LQ_ALGO_MFMA_SMALL:
-      p.waves = e.fp.chunked ? e.fp.w + 1 : e.fp.w;
+      p.waves = e.fp.chunked ? e.fp.w + lq::kChunkLoaders : e.fp.w;
       p.panels = e.fp.p;
       p.workgroups = e.fp.groups;
       break;

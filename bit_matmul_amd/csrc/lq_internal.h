@@ -180,6 +180,7 @@ hipError_t launch_timed(Kernel kernel, dim3 grid, dim3 block, size_t lds, hipStr
 // Launch shapes of the product kernels that the plan query reports.
 constexpr int kLargeWaves = 4;         // sign_mfma_large_kernel, wspace_kernel
 constexpr int kWsPanelsPerWave = 4;    // wspace_kernel
+constexpr int kChunkLoaders = 4;       // sign_fp6_chunked_kernel: loader wavefronts
 constexpr int kValuWaves = 4;          // sign_valu_kernel (one panel per wavefront)
 constexpr int kOneLaunchWaves = 8;     // decode_fused / decode_self / decode_split kernels
 constexpr int kSplitPanels = 2 * kOneLaunchWaves;   // decode_split_kernel: panels per workgroup

@@ -25,11 +25,12 @@ namespace {
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
-// Loader wavefronts: each copies every kLoaders-th kilobyte of a chunk, so
-// that a chunk is requested by that many wavefronts at once. Measured on the
-// 70B down projection at B = 16: one loader 42.8 us, two 40.8, four 34.5,
-// eight 34.4 (and register spills where the compute wavefronts need many).
-constexpr int kLoaders = 4;
+// Loader wavefronts (kChunkLoaders): each copies every kLoaders-th kilobyte
+// of a chunk, so that a chunk is requested by that many wavefronts at once.
+// Measured on the 70B down projection at B = 16: one loader 42.8 us, two
+// 40.8, four 34.5, eight 34.4 (and register spills where the compute
+// wavefronts need many).
+constexpr int kLoaders = kChunkLoaders;
 
 template <int P, int CS, int W, int TPC>
 __global__ __launch_bounds__(64 * (W + kLoaders)) void sign_fp6_chunked_kernel(SignTable tab, int rec, int ncv,

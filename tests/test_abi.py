@@ -411,6 +411,19 @@ def test_linear_plan_of_the_benchmarked_layers():
     assert LIB.lq_linear_plan(ctypes.byref(lay), 1, LQ_BF16, 0, None) == LQ_ERR_INVALID_ARG
 
 
+def test_chunked_plan_counts_loader_wavefronts():
+    """The 70B down projection at B = 4 and 16 (bf16 x) runs the chunked
+    small-batch product: its records neither fit LDS nor stream. The plan
+    reports the launch's wavefronts: the compute ones (8 with one column set
+    of 16 (batch row, term) columns, 4 with two) and the four loaders."""
+    info = _lib.LQPlanInfo()
+    lay = LQLayer(8192, 28672, 10, 24, 1024, 0, P, P, P, P)
+    for B, waves in ((4, 8 + 4), (16, 4 + 4)):
+        assert LIB.lq_linear_plan(ctypes.byref(lay), B, LQ_BF16, 0, ctypes.byref(info)) == LQ_OK
+        assert info.algo == 2 and info.panels == 2 and info.workgroups == 256
+        assert info.waves == waves, (B, info.waves)
+
+
 def test_lifted_length_cap():
     """L above LQ_MAX_L (2^28 lifted columns per row) is rejected: byte
     offsets inside a panel (2 L) then stay within 32 bits."""
