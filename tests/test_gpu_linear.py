@@ -9,6 +9,9 @@
   within 10 x the tolerance of the output's RMS (a fault confined to a few
   workgroups would show there).
 * The tiny 2.5-bit layer (fp32 activations) in full.
+* The chunked small-batch product (batches beyond 1 whose records exceed
+  LDS) on small shapes with partial, odd and even chunk counts and no tail,
+  and through one grouped call.
 * Edge cases: empty batch, every batch size 1..17, K not a multiple of d,
   D = d with M = I, hb = 1, a single 16-row panel, D = 32 (the 2-bit LQ-32/16
   configuration), d = 1.
@@ -181,6 +184,56 @@ def test_streamed_records_batch1(lq, N, K, d, D, hb, label):
     y = layer.linear(lq, dev(x, torch.bfloat16), 1, torch.float32)
     want = ref.linear(x, inp.c, hb, inp.M, inp.signs(), inp.row_scale)
     _check_all(host(y), want, 3e-3)
+
+
+# Batches beyond 1 (bf16 x) whose activation records exceed LDS: the chunked
+# small-batch product (loader wavefronts copy chunks of records while the
+# compute wavefronts multiply). Chunks of W x tpc tiles: partial last chunks,
+# odd and even chunk counts, a row with no tail tile, D = 5.
+CHUNKED = [
+    # (N, K, d, D, hb, B, label)
+    (48, 2600, 10, 24, 8, 16, "B=16, 12 full tiles + tail: 3 chunks"),
+    (32, 4480, 10, 24, 128, 16, "B=16, 21 tiles, no tail: 6 chunks, the last of one tile"),
+    (64, 3008, 2, 5, 8, 16, "B=16, D=5, 14 tiles + tail: 4 chunks"),
+    (16, 6840, 10, 24, 8, 5, "B=5, 32 tiles + tail: 4 chunks of 8"),
+    (32, 9000, 10, 24, 8, 4, "B=4, 42 tiles + tail: 6 chunks, the last of two tiles"),
+    (16, 18000, 10, 24, 16, 2, "B=2, 84 tiles + tail: 4 chunks of 24, the last of 12"),
+]
+
+
+def _rec_bytes(B):
+    return -(-(804 * B) // 128) * 128        # two FP6 terms per batch row, bf16 x
+
+
+@pytest.mark.parametrize("N,K,d,D,hb,B,label", CHUNKED, ids=[e[-1] for e in CHUNKED])
+def test_chunked_records(lq, N, K, d, D, hb, B, label):
+    L = -(-K // d) * D
+    assert -(-L // 512) * _rec_bytes(B) > 128 * 1024      # records do not fit LDS
+    inp = make_layer_small(N, K, d, D, hb, seed=N + K + B, B_max=B, xdtype="bf16")
+    layer = DeviceLayer(inp, lq)
+    x = inp.x(B)
+    y = layer.linear(lq, dev(x, torch.bfloat16), B, torch.float32)
+    want = ref.linear(x, inp.c, hb, inp.M, inp.signs(), inp.row_scale)
+    _check_all(host(y), want, 3e-3)
+
+
+def test_chunked_records_grouped(lq):
+    """Two layers on one input through one lq_linear_multi call, B = 16, on
+    the chunked product."""
+    N, K, d, D, hb, B = 48, 2600, 10, 24, 8, 16
+    inps = [make_layer_small(N, K, d, D, hb, seed=s, B_max=B, xdtype="bf16") for s in (5, 6)]
+    layers = [DeviceLayer(i, lq) for i in inps]
+    x = inps[0].x(B)
+    ys = [torch.empty((B, N), dtype=torch.float32, device=DEV) for _ in layers]
+    from tests.gpu_util import workspace
+    structs = [l.struct for l in layers]
+    ws = workspace(lq, lq.lq_linear_multi_workspace_size(structs, B, torch.bfloat16))
+    note("lq_linear_multi chunked B=16")
+    lq.lq_linear_multi(structs, dev(x, torch.bfloat16), B, ys, ws)
+    torch.cuda.synchronize()
+    for inp, y in zip(inps, ys):
+        want = ref.linear(x, inp.c, hb, inp.M, inp.signs(), inp.row_scale)
+        _check_all(host(y), want, 3e-3)
 
 
 def test_every_batch_size_small(lq):
