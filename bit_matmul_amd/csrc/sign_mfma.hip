@@ -72,8 +72,8 @@ __device__ __forceinline__ uint32_t vreg_const(uint32_t v) {
 // kSrc 0: z fp32, 1: z bf16 (B x L, row-major), 2: lift from xt (B x K fp32)
 // with M (the lq_linear path: z is never written in row-major form). For the
 // lift the workgroup stages M and the rows' original columns [k_lo, k_lo +
-// span) (span <= (511 / D + 2) d <= 639) in LDS (dynamic: d D + 16 xstride
-// floats).
+// span) (span <= (511 / D + 2) d <= 639) in LDS (dynamic: max(d D, 256) +
+// 16 xstride floats).
 template <int kSrc, int NTERM>
 __global__ __launch_bounds__(256) void zp_kernel(const void* __restrict__ src, int64_t B, int64_t L,
                                                  int64_t K, int d, int D,
@@ -88,39 +88,80 @@ __global__ __launch_bounds__(256) void zp_kernel(const void* __restrict__ src, i
   const int64_t c_lo = 512 * q + 128 * u + 32 * g;
   float v[32];
   if (kSrc == 2) {
+    // LDS: M (at least 256 slots, one per thread), then the staged rows
+    const int nm = d * D;
     float* Ms = lds_f;
-    float* xs = lds_f + d * D;
-    const int64_t tile_lo = 512 * q;
-    const int64_t blk_lo = tile_lo / D;
-    const int64_t blk_hi = (min(tile_lo + 511, L - 1)) / D;
-    const int64_t k_lo = blk_lo * d;
-    const int span = (int)(min((blk_hi + 1) * d, K) - k_lo);
-    for (int i = t; i < d * D; i += 256) Ms[i] = M[i];
-    for (int rr = 0; rr < 16; ++rr) {
-      const int64_t bb = 16 * jb + rr;
-      for (int k = t; k < span; k += 256)
-        xs[xstride * rr + k] = bb < B ? reinterpret_cast<const float*>(src)[bb * K + k_lo + k] : 0.0f;
-    }
-    __syncthreads();
-    // Column c_lo + k is block blk, element e; walk them in order.
-    const float* xr = xs + xstride * r;
-    int64_t blk = c_lo / D;
-    int e = (int)(c_lo - blk * D);
+    float* xs = lds_f + max(nm, 256);
+    // (32-bit index arithmetic: L <= 2^28)
+    const int tile_lo = 512 * (int)q;
+    const int blk_lo = tile_lo / D;
+    const int blk_hi = min(tile_lo + 511, (int)L - 1) / D;
+    const int64_t k_lo = (int64_t)blk_lo * d;
+    // The tile's blocks cover inputs [k_lo, k_lo + span); those past K (the
+    // virtual pad) are staged as zeros, so every block has d inputs.
+    const int span = (blk_hi + 1 - blk_lo) * d;
+    // All 16 rows' loads go out before the first is stored (span <= 639 <
+    // 3 x 256): loading and storing a row at a time cost one memory round
+    // trip per row. Addresses are clamped (rows to B - 1, inputs to the
+    // span and to K - 1) and no load depends on a condition, so none is
+    // put under a branch (a branch joins only after its load has landed).
+    // Rows past B hold row B - 1's values; their outputs are zeroed below.
+    const float* __restrict__ xsrc = reinterpret_cast<const float*>(src);
+    const float m0 = M[min(t, nm - 1)];          // M's first 256 entries, before x
+    float xv[16][3];
 #pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      float acc = 0.0f;
-      if (b < B && c_lo + k < L) {
-        const int64_t kb = blk * d;
-        const int nk = (int)min((int64_t)d, K - kb);
-        const float* xb = xr + (kb - k_lo);
-        for (int i = 0; i < nk; ++i) acc = fmaf(Ms[i * D + e], xb[i], acc);
+    for (int rr = 0; rr < 16; ++rr) {
+      const float* xrow = xsrc + min(16 * jb + rr, B - 1) * K;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) xv[rr][j] = xrow[min(k_lo + min(t + 256 * j, span - 1), K - 1)];
+    }
+    Ms[t] = m0;                                   // (slots past d D unused)
+    for (int i = t + 256; i < nm; i += 256) Ms[i] = M[i];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr)
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int k = t + 256 * j;
+        if (k < span) xs[xstride * rr + k] = k_lo + k < K ? xv[rr][j] : 0.0f;
       }
-      v[k] = acc;
-      if (++e == D) {
-        e = 0;
-        ++blk;
+    __syncthreads();
+    // Column c_lo + k is element eo[k] of the block whose inputs start at
+    // xo[k] in the row's staged span (clamped for columns past L, whose
+    // values are replaced by 0 below).
+    const float* xr = xs + xstride * r;
+    int xo[32], eo[32];
+    {
+      const int blk = (int)c_lo / D;
+      int e = (int)c_lo - blk * D;
+      int xoff = (blk - blk_lo) * d;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        xo[k] = min(xoff, span - d);
+        eo[k] = e;
+        if (++e == D) {
+          e = 0;
+          xoff += d;
+        }
       }
     }
+    // z = sum_i M[i][e] xt[block d + i], in order of i for every column.
+#pragma unroll
+    for (int k = 0; k < 32; ++k) v[k] = 0.0f;
+    for (int i = 0; i < d; ++i) {
+      // all 64 reads of this i before its multiply-adds (interleaved, each
+      // read would be waited for on its own)
+      float mv[32], xx[32];
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        mv[k] = Ms[i * D + eo[k]];
+        xx[k] = xr[xo[k] + i];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < 32; ++k) v[k] = fmaf(mv[k], xx[k], v[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < 32; ++k) v[k] = b < B && c_lo + k < L ? v[k] : 0.0f;
   } else {
     // 32 consecutive values (L % 8 == 0: every 8-value chunk is in or out).
 #pragma unroll
@@ -505,6 +546,15 @@ LargePlan plan_large(int64_t B, const PackedGeom& g, bool z_bf16) {
   for (int c : {8, 4, 2}) {
     if (((g.panels + 4 * c - 1) / (4 * c)) * bt >= 512) { p.ppw = c; break; }
   }
+  // None does, with 4 batch tiles: 2 panels per wavefront (each B operand
+  // read from LDS then feeds twice the MFMAs) if, with the reduction split
+  // below, the launch still has a workgroup for every compute unit
+  // (Qwen-2.5-32B up / down at B = 64: product 59 -> 55 us).
+  if (p.ppw == 1 && p.jb == 4) {
+    const int64_t w2 = ((g.panels + 7) / 8) * bt;
+    const int64_t k2 = std::min<int64_t>(512 / std::max<int64_t>(w2, 1), g.ext_tiles / 8);
+    if (w2 * std::max<int64_t>(k2, 1) >= 256) p.ppw = 2;
+  }
   // Still fewer than 512 (two per compute unit fit its LDS at these
   // tilings): split the reduction into ranges of at least 8 tiles, as many
   // as keep the workgroups within 512.
@@ -526,7 +576,7 @@ hipError_t launch_zp(const void* src, int kind, int64_t B, int64_t L, int64_t K,
   // Lift: LDS for M and 16 rows of the tile's original columns (odd stride).
   const int span_max = kind >= 2 ? (int)((511 / D + 2) * d) : 0;
   const int xstride = span_max | 1;
-  const size_t lds = kind >= 2 ? (size_t)(d * D + 16 * xstride) * sizeof(float) : 0;
+  const size_t lds = kind >= 2 ? (size_t)(std::max(d * D, 256) + 16 * xstride) * sizeof(float) : 0;
   // Batch tiles map to grid.y, at most 65535 per launch.
   for (int64_t jb0 = 0; jb0 < z.B16; jb0 += 65535) {
     const dim3 grid((unsigned)g.ext_tiles, (unsigned)min(z.B16 - jb0, (int64_t)65535));

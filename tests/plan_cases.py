@@ -6,8 +6,9 @@ lq_sign_gemm_plan; the GPU test compares each with the oracle.
 The plan takes 4 panels x 8 batch tiles for bf16 z when that still gives
 >= 512 workgroups; else up to 4 batch tiles (bf16 z; 2 for fp32 z, whose two
 bf16 planes would not fit LDS otherwise; 1 at B <= 16), with the most panels
-per wavefront (8, 4, 2) that keeps >= 512 workgroups. L is kept short where N
-is large (one or two full tiles and a tail) so that the oracle stays cheap.
+per wavefront (8, 4, 2) that keeps >= 512 workgroups, or, with 4 batch tiles,
+2 if the reduction split still gives >= 256. L is kept short where N is
+large (one or two full tiles and a tail) so that the oracle stays cheap.
 """
 LARGE_PLAN_CASES = [
     # bf16 z
@@ -47,6 +48,7 @@ def case_id(c):
 # tiles, ranges).
 LARGE_SPLIT_CASES = [
     (1024, 8200, 64, "bf16", 1, 4, 2),       # 16 workgroups, 17 tiles (ragged)
+    (2048, 65536, 64, "bf16", 2, 4, 16),     # 2 panels per wavefront: 16 x 16 ranges
     (512, 40000, 48, "bf16", 1, 2, 9),       # 16 workgroups, 79 tiles
     (256, 20000, 200, "f32", 1, 2, 5),       # 28 workgroups, 40 tiles
 ]

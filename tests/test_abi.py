@@ -405,6 +405,12 @@ def test_linear_plan_of_the_benchmarked_layers():
                 if want == 6 and B >= 2048:
                     # 4 panels per wavefront, 8 batch tiles per workgroup
                     assert (info.panels, info.batch_rows) == (16, 128), (s.name, B)
+                if want == 3 and B == 64:
+                    # 2 panels per wavefront, 4 batch tiles, the reduction
+                    # split so that every compute unit has a workgroup
+                    ks = {"up": 2, "down": 12}[s.name]
+                    assert (info.panels, info.batch_rows, info.ksplit) == (8, 64, ks), s.name
+                    assert info.workgroups >= 256
     assert LIB.lq_linear_plan(None, 1, LQ_BF16, 0, ctypes.byref(info)) == LQ_ERR_INVALID_ARG
     lay = LQLayer(16, 64, 2, 8, 64, 0, P, P, P, P)
     assert LIB.lq_linear_plan(ctypes.byref(lay), 0, LQ_BF16, 0, ctypes.byref(info)) == LQ_ERR_INVALID_ARG
