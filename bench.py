@@ -71,7 +71,11 @@ PRODUCT_KERNELS = ("sign_fp6_kernel", "sign_fp6_chunked_kernel", "sign_valu_kern
                    "wspace_kernel", "decode_fused_kernel", "decode_self_kernel",
                    "decode_split_kernel")
 # The files of the kernels whose HBM traffic the committed summary holds.
-TRAFFIC_SOURCES = ("sign_fp6.hip", "prep.hip", "sign_mfma.hip", "wspace.hip")
+# The source file of each kernel whose traffic the counter summary records
+# (with every header, which they share).
+TRAFFIC_SOURCES = {"sign_fp6_kernel": "sign_fp6.hip", "prep_kernel": "prep.hip",
+                   "sign_mfma_large_kernel": "sign_mfma.hip", "wspace_kernel": "wspace.hip",
+                   "xpw_kernel": "wspace.hip"}
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_llama3_70b_b1_step_and_prefill_28672_b2048.txt")
 COPY_BYTES = 256 << 20         # the calibration copy of --pmc-workload
 
@@ -125,16 +129,16 @@ def parse_args():
 
 # ------------------------------------------------------------ profiling aids
 
-def kernel_sources_hash():
-    """Hash of the sources of the kernels the counter summary covers (their
-    .hip files and every header; a summary taken on other code is stale).
-    Host-only files such as the C-ABI dispatch, and kernels the summary does
-    not cover, do not change what these kernels read or write."""
+def kernel_sources_hash(kernel):
+    """Hash of the sources of `kernel` (a key of TRAFFIC_SOURCES): its .hip
+    file and every header. Counters taken on other code are stale for it;
+    host-only files such as the C-ABI dispatch, and the other kernels'
+    files, do not change what it reads or writes."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_matmul_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.endswith(".h") or name in TRAFFIC_SOURCES:
+        if name.endswith(".h") or name == TRAFFIC_SOURCES[kernel]:
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -236,8 +240,8 @@ def summarize_pmc(fetch_dir, write_dir):
             if "copyBuffer" in k:
                 copy[counter] = max(copy.get(counter, 0.0), r["value"])
         out[counter] = {k: sum(v) / len(v) for k, v in per.items() if "copyBuffer" not in k}
-    lines = [f"sources {kernel_sources_hash()}",
-             f"copy_bytes {COPY_BYTES}"]
+    lines = [f"sources {k} {kernel_sources_hash(k)}" for k in sorted(TRAFFIC_SOURCES)]
+    lines.append(f"copy_bytes {COPY_BYTES}")
     if "FETCH_SIZE" in copy and "WRITE_SIZE" in copy:
         lines.append(f"copy_fetch_kib {copy['FETCH_SIZE']:.1f}")
         lines.append(f"copy_write_kib {copy['WRITE_SIZE']:.1f}")
@@ -295,15 +299,17 @@ def traffic_from_summary(kernel):
     except OSError:
         return None
     import re
-    kv, kern = {}, {}
+    kv, kern, src = {}, {}, {}
     for line in text.splitlines():
         parts = line.split()
-        if len(parts) >= 2 and parts[0] in ("sources", "fetch_factor", "write_factor"):
+        if len(parts) == 3 and parts[0] == "sources":
+            src[parts[1]] = parts[2]
+        if len(parts) >= 2 and parts[0] in ("fetch_factor", "write_factor"):
             kv[parts[0]] = parts[1]
         m = re.match(r"^kernel (.*) fetch_kib ([0-9.]+) write_kib ([0-9.]+)$", line)
         if m and kernel in m.group(1):
             kern[m.group(1)] = (float(m.group(2)), float(m.group(3)))
-    if kv.get("sources") != kernel_sources_hash() or not kern:
+    if kernel not in TRAFFIC_SOURCES or src.get(kernel) != kernel_sources_hash(kernel) or not kern:
         return None
     ff, wf = float(kv["fetch_factor"]), float(kv["write_factor"])
     f = sum(v[0] for v in kern.values()) / len(kern)
