@@ -296,7 +296,9 @@ __global__ __launch_bounds__(256) void wspace_kernel(
   // reads a tile's words (at the tile's last step) before it copies the next
   // tile's (at the first step of that tile), so one buffer serves.
   __shared__ uint4 slots[kSlotUnits];
-  __shared__ uint2 lut[kLut];
+  // (the most strictly aligned LDS object, so it is placed at address 0 and a
+  // lookup's address is its index times 8, one shift of the packed byte)
+  __shared__ __align__(2048) uint2 lut[kLut];
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int64_t steps = SPT * (int64_t)ext_tiles;
   const int64_t last = steps - 1;
@@ -319,30 +321,48 @@ __global__ __launch_bounds__(256) void wspace_kernel(
     lut[p] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
   }
 
+  // A copy is a uniform base plus the lane's 16 bytes (a 32-bit offset).
+  const uint32_t lane16 = 16u * (uint32_t)lane;
   auto dma = [&](const void* src, uint4* dst) __attribute__((always_inline)) {
-    __builtin_amdgcn_global_load_lds(
-        (const void*)(reinterpret_cast<const uint8_t*>(src) + 16 * lane),
-        (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const uint8_t*>(src) + lane16),
+                                     (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
   };
   // The B operands of one step: kChunks copies of 1 KB spread over the four
-  // wavefronts (clamped: a repeated copy writes the same bytes again).
+  // wavefronts (clamped: a repeated copy writes the same bytes again). Copy
+  // k of step t reads chunk ch_k (batch tile c, sub-step f) at
+  // xp + ((jb * steps + t) * DD + f) * 64: a base fixed for the workgroup
+  // plus t * DD KB.
   constexpr int kCopies = (kChunks + 3) / 4;
-  auto copy_step = [&](int64_t t, uint4* dst) __attribute__((always_inline)) {
+  const uint4* cbase[kCopies];
+  int cdst[kCopies];
 #pragma unroll
-    for (int k = 0; k < kCopies; ++k) {
-      const int ch = min(wave + 4 * k, kChunks - 1);
-      const int c = ch / DD, f = ch % DD;
-      const int64_t jb = min(jb0 + c, B16 - 1);
-      dma(xp + ((jb * steps + t) * DD + f) * 64, dst + ch * 64);
-    }
+  for (int k = 0; k < kCopies; ++k) {
+    const int ch = min(wave + 4 * k, kChunks - 1);
+    const int c = ch / DD, f = ch % DD;
+    const int64_t jb = min(jb0 + c, B16 - 1);
+    cbase[k] = xp + (jb * steps * DD + f) * 64;
+    cdst[k] = ch * 64;
+  }
+  auto copy_step = [&](int64_t t, uint4* dst) __attribute__((always_inline)) {
+    const int64_t off = t * (DD * 64);
+#pragma unroll
+    for (int k = 0; k < kCopies; ++k) dma(cbase[k] + off, dst + cdst[k]);
   };
+  // The slots of tile q of this wavefront's panels: the panel's packed bytes
+  // plus q KB, or past the full tiles the panel's rebuilt tail slots.
+  const uint8_t* sbase[PW];
+  const uint4* tbase[PW];
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const int64_t pnl = min(pbase + i, panels - 1);
+    sbase[i] = packed + pnl * panel_bytes;
+    tbase[i] = tail_slots + pnl * 64;
+  }
   auto copy_slots = [&](int q, uint4* dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
-      const int64_t pnl = min(pbase + i, panels - 1);
-      const void* src = q < full_tiles
-                            ? (const void*)(packed + pnl * panel_bytes + (int64_t)q * kTileBytes)
-                            : (const void*)(tail_slots + pnl * 64);
+      const void* src = q < full_tiles ? (const void*)(sbase[i] + (int64_t)q * kTileBytes)
+                                       : (const void*)tbase[i];
       dma(src, dst + (wave * PW + i) * 64);
     }
   };
