@@ -263,31 +263,43 @@ __global__ __launch_bounds__(256) void sign_mfma_large_kernel(
   const int64_t jb0 = (int64_t)blockIdx.y * JB;
   const int64_t pbase = (int64_t)blockIdx.x * 4 * PW + wave * PW;
 
+  // A copy is a uniform base plus the lane's 16 bytes (a 32-bit offset).
+  const uint32_t lane16 = 16u * (uint32_t)lane;
   auto dma = [&](const void* src, uint4* dst) {
-    __builtin_amdgcn_global_load_lds(
-        (const void*)(reinterpret_cast<const uint8_t*>(src) + 16 * lane),
-        (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const uint8_t*>(src) + lane16),
+                                     (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
   };
   // zp blocks of one step: NTERM * JB blocks of 4 KB, i.e. 4 NTERM JB
-  // wavefront copies of 1 KB, spread over the 4 wavefronts.
-  auto copy_step = [&](int64_t t, uint4* dst) {
+  // wavefront copies of 1 KB, spread over the 4 wavefronts. Copy c of step
+  // t reads zp + ((term * B16 + jb) * steps + t) * kZpBlock + 1 KB * wave:
+  // a base fixed for the workgroup plus t blocks.
+  const uint8_t* cbase[NTERM * JB];
 #pragma unroll
-    for (int c = 0; c < NTERM * JB; ++c) {
-      const int term = c / JB, j = c % JB;
-      const int64_t jb = min(jb0 + j, B16 - 1);
-      dma(reinterpret_cast<const uint8_t*>(zp) + ((term * B16 + jb) * steps + t) * kZpBlock + 1024 * wave,
-          dst + (c * kZpBlock + 1024 * wave) / 16);
-    }
+  for (int c = 0; c < NTERM * JB; ++c) {
+    const int term = c / JB, j = c % JB;
+    const int64_t jb = min(jb0 + j, B16 - 1);
+    cbase[c] = reinterpret_cast<const uint8_t*>(zp) + (term * B16 + jb) * steps * kZpBlock + 1024 * wave;
+  }
+  auto copy_step = [&](int64_t t, uint4* dst) {
+    const int64_t off = t * kZpBlock;
+#pragma unroll
+    for (int c = 0; c < NTERM * JB; ++c) dma(cbase[c] + off, dst + (c * kZpBlock + 1024 * wave) / 16);
   };
   // The slots (1 KB per panel: the tile itself, or its assembled tail) of
   // tile q for this wavefront's panels.
+  const uint8_t* sbase[PW];
+  const uint4* tbase[PW];
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const int64_t pnl = min(pbase + i, panels - 1);
+    sbase[i] = packed + pnl * panel_bytes;
+    tbase[i] = tail_slots + pnl * 64;
+  }
   auto copy_slots = [&](int q, uint4* dst) {
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
-      const int64_t pnl = min(pbase + i, panels - 1);
-      const void* src = q < full_tiles
-                            ? (const void*)(packed + pnl * panel_bytes + (int64_t)q * kTileBytes)
-                            : (const void*)(tail_slots + pnl * 64);
+      const void* src = q < full_tiles ? (const void*)(sbase[i] + (int64_t)q * kTileBytes)
+                                       : (const void*)tbase[i];
       dma(src, dst + (wave * PW + i) * 64);
     }
   };
