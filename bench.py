@@ -388,6 +388,24 @@ class LayerSets:
         return torch.randn(B, K, device="cuda", generator=self.gen).to(torch.bfloat16)
 
 
+SPIN_MS_PER_CALL = 0.25      # host time to enqueue one timed call, generously
+_SPIN_CYCLES_PER_MS = []
+
+
+def spin_gpu(torch, ms):
+    """Keep the current stream busy for about `ms` milliseconds (torch's
+    bounded spin kernel, calibrated once with events)."""
+    if not _SPIN_CYCLES_PER_MS:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        a.record()
+        torch.cuda._sleep(1_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        _SPIN_CYCLES_PER_MS.append(1_000_000 / max(a.elapsed_time(b), 1e-3))
+    torch.cuda._sleep(int(min(ms, 200.0) * _SPIN_CYCLES_PER_MS[0]))
+
+
 def time_calls(torch, lq, ev, fn, reps, warmup, label, eager=False):
     """Time `reps` calls fn(i), i = 0..reps-1, each enqueuing exactly one
     product launch per lq call it makes; `fn` returns the number of lq calls
@@ -426,6 +444,10 @@ def time_calls(torch, lq, ev, fn, reps, warmup, label, eager=False):
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         phase(f"{label}: timed graph replay", n_launch)
+        # Queue the replay behind a spin kernel, so that its launches run
+        # back to back from a full queue as in the graph replay rather than
+        # each waiting for the host to enqueue it.
+        spin_gpu(torch, SPIN_MS_PER_CALL * reps)
         lq.lq_profile_events(starts, stops)
         for i in range(reps):
             fn(i)
@@ -885,7 +907,8 @@ def main():
             "launches_per_step": dec["launches_per_step"],
             "per_launch": dec["per_launch"],
             "timing": "hipEvents recorded by the dispatch of every sign-product launch of an "
-                      "eager replay of the K timed steps",
+                      "eager replay of the K timed steps, queued behind a spin kernel so that "
+                      "its launches run back to back as in the timed graph replay",
             "algorithmic_bytes_per_launch": dec["bytes_per_launch"],
         },
     }
