@@ -288,6 +288,7 @@ __global__ __launch_bounds__(256) void wspace_kernel(
   constexpr int kStageUnits = kChunks * 64;       // [jb][f][g][r]
   constexpr int kSlotUnits = 4 * PW * 64;         // [wave][panel][lane]
   constexpr int kLut = 1 << D;
+  constexpr int kWaitLds0 = (3 << 14) | (7 << 4) | 15;   // lgkmcnt(0) alone
   __shared__ uint4 stage0[kStageUnits];
   __shared__ uint4 stage1[kStageUnits];
   __shared__ uint4 stage2[kStageUnits];
@@ -486,7 +487,11 @@ __global__ __launch_bounds__(256) void wspace_kernel(
     constexpr int su = (decltype(offc)::value + sg) & 3;
     const int64_t t = (int64_t)q * SPT + sg;
     __builtin_amdgcn_s_waitcnt(kWait1);
-    wg_barrier();
+    // The LDS wait as a builtin, not inline assembly: the compiler then
+    // knows that the reads issued before the barrier have landed and does
+    // not drain the next sub-step's reads to wait for them.
+    __builtin_amdgcn_s_waitcnt(kWaitLds0);
+    __builtin_amdgcn_s_barrier();
     uint2 e[PW][8];
     if constexpr (sg + 1 == SPT) read_words(slots, w);   // the next tile's words
     if constexpr (sg == 0) copy_slots(min(q + 1, ext_tiles - 1), slots);
@@ -506,7 +511,8 @@ __global__ __launch_bounds__(256) void wspace_kernel(
   // sub-step 0 of its B operands (steps 1 and 2 may still be in flight);
   // the barrier also publishes the table.
   __builtin_amdgcn_s_waitcnt(kWait2);
-  wg_barrier();
+  __builtin_amdgcn_s_waitcnt(kWaitLds0);
+  __builtin_amdgcn_s_barrier();
   {
     uint2 e[PW][8];
     read_words(slots, w);
