@@ -394,7 +394,10 @@ _SPIN_CYCLES_PER_MS = []
 
 def spin_gpu(torch, ms):
     """Keep the current stream busy for about `ms` milliseconds (torch's
-    bounded spin kernel, calibrated once with events)."""
+    bounded spin kernel, calibrated once with events). Without that kernel
+    the replay is not queued ahead and its launches wait on the host."""
+    if not hasattr(torch.cuda, "_sleep"):
+        return
     if not _SPIN_CYCLES_PER_MS:
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda._sleep(1000)
