@@ -930,6 +930,9 @@ def main():
             "unit": "TFLOP/s",
             "ms_per_linear": round(pf["linear_us"] / 1e3, 4),
             "lifted_flops": lifted,
+            "note": ("value counts the 2*B*N*L flops of the lifted product for the whole call; "
+                     "it is not a rate the matrix cores ran at when the W-space product (D/d "
+                     "times fewer flops) runs: that rate is roofline.achieved"),
             "roofline": {"bound": "mfma", "achieved": pf["kernel_tflops"],
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": pf["frac_bf16"],
                          "kernel_flops_per_launch": pf["kernel_flops"],
